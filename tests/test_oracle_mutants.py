@@ -1,0 +1,147 @@
+"""Planted mistakes in the oracle (on the CPU) must be caught by its pins.
+
+Each case swaps one oracle function for a plausible wrong variant (a dropped
+term, a wrong sign or index, a transposed operand, a different rounding) and
+runs a pin that must then fail."""
+import numpy as np
+import pytest
+
+import oracle.formats as F
+import oracle.moe as M
+import oracle.quant as Q
+import tests.test_oracle_formats as TF
+import tests.test_oracle_gemm as TG
+import tests.test_oracle_moe as TM
+import tests.test_oracle_quant as TQ
+
+
+def _fails(fn, *a, **kw):
+    try:
+        fn(*a, **kw)
+    except AssertionError:
+        return True
+    return False
+
+
+def test_mutant_e2m1_ties_away(monkeypatch):
+    def bad(v):
+        v = np.minimum(np.asarray(v, np.float64), 6.0)
+        d = np.abs(v[..., None] - F.E2M1_MAGNITUDES)
+        return (7 - np.argmin(d[..., ::-1], axis=-1)).astype(np.uint8)   # ties -> larger
+    monkeypatch.setattr(Q, "e2m1_encode_magnitude", bad)
+    assert _fails(TQ.test_worked_example_by_hand)
+
+
+def test_mutant_scale_not_divided_by_six(monkeypatch):
+    orig = Q.block_scale_codes
+
+    def bad(x32, g):
+        return orig(x32 * np.float32(6.0), g)   # forgets the /6
+    monkeypatch.setattr(Q, "block_scale_codes", bad)
+    assert _fails(TQ.test_worked_example_by_hand)
+
+
+def test_mutant_global_scale_wrong_constant(monkeypatch):
+    monkeypatch.setattr(Q, "F32_2688", np.float32(448.0))
+    assert _fails(TQ.test_global_scale_is_float32_amax_over_2688)
+
+
+def test_mutant_nibble_order_swapped(monkeypatch):
+    def bad_pack(codes):
+        codes = np.asarray(codes, np.uint8)
+        return (codes[:, 1::2] | (codes[:, 0::2] << 4)).astype(np.uint8)
+    monkeypatch.setattr(Q, "pack_codes", bad_pack)
+    assert _fails(TQ.test_worked_example_by_hand)
+
+
+def test_mutant_gemm_transposed_b(monkeypatch):
+    orig = Q.dequantize_unscaled
+
+    def bad(codes, scales):
+        v = orig(codes, scales)
+        return v[::-1] if v.ndim == 2 and v.shape[0] == 5 else v    # rows of B reversed
+    monkeypatch.setattr(M, "dequantize_unscaled", bad)
+    assert _fails(TG.test_grouped_gemm_equals_exact_rational, 0)
+
+
+def test_mutant_gemm_drops_b_global_scale(monkeypatch):
+    def bad(a_codes, a_scales, a_g, b_codes, b_scales, b_g, offsets, a_rows=None, want_absdot=True):
+        return ORIG_GEMM(a_codes, a_scales, a_g, b_codes, b_scales, np.ones_like(b_g), offsets,
+                         a_rows=a_rows, want_absdot=want_absdot)
+    monkeypatch.setattr(TG, "grouped_gemm", bad)
+    assert _fails(TG.test_grouped_gemm_equals_exact_rational, 1)
+
+
+def test_mutant_gemm_ignores_row_gather(monkeypatch):
+    def bad(a_codes, a_scales, a_g, b_codes, b_scales, b_g, offsets, a_rows=None, want_absdot=True):
+        return ORIG_GEMM(a_codes, a_scales, a_g, b_codes, b_scales, b_g, offsets,
+                         a_rows=None, want_absdot=want_absdot)
+    monkeypatch.setattr(TG, "grouped_gemm", bad)
+    assert _fails(TG.test_grouped_gemm_equals_exact_rational, 2)
+
+
+def test_mutant_route_softmax_not_renormalised(monkeypatch):
+    def bad(logits, k):
+        ids, _ = ORIG_ROUTE(logits, k)
+        l = np.asarray(logits, np.float64)
+        p = np.exp(l - l.max(axis=1, keepdims=True))
+        p /= p.sum(axis=1, keepdims=True)
+        return ids, np.take_along_axis(p, ids.astype(np.int64), axis=1).astype(np.float32)
+    monkeypatch.setattr(TM.M, "route", bad)
+    assert _fails(TM.test_route_weights_are_renormalised_softmax)
+
+
+def test_mutant_route_ties_to_higher_id(monkeypatch):
+    def bad(logits, k):
+        l = np.asarray(logits, np.float64)
+        E = l.shape[1]
+        ids = (E - 1 - np.argsort(-l[:, ::-1], axis=1, kind="stable"))[:, :k]
+        sel = np.take_along_axis(l, ids, axis=1)
+        ex = np.exp(sel - sel[:, :1])
+        return ids.astype(np.int32), (ex / ex.sum(axis=1, keepdims=True)).astype(np.float32)
+    monkeypatch.setattr(TM.M, "route", bad)
+    assert _fails(TM.test_route_ties_go_to_lower_id)
+
+
+def test_mutant_permute_unstable(monkeypatch):
+    def bad(topk_ids, topk_w, E):
+        T, k = topk_ids.shape
+        flat = topk_ids.reshape(-1).astype(np.int64)
+        order = np.lexsort((-np.arange(T * k), flat))          # descending inside an expert
+        counts = np.bincount(flat, minlength=E)
+        offsets = np.concatenate([[0], np.cumsum(counts)])
+        perm_of = np.empty(T * k, np.int64)
+        perm_of[order] = np.arange(T * k)
+        return (counts.astype(np.int32), offsets.astype(np.int32), (order // k).astype(np.int32),
+                perm_of.astype(np.int32), topk_w.reshape(-1)[order])
+    monkeypatch.setattr(TM.M, "permute", bad)
+    assert _fails(TM.test_permute_brute_force_and_invariants, 40, 16, 3)
+
+
+def test_mutant_swiglu_halves_swapped(monkeypatch):
+    def bad(y1):
+        y1 = np.asarray(y1, np.float64)
+        I = y1.shape[1] // 2
+        return M.silu(y1[:, I:]) * y1[:, :I]
+    monkeypatch.setattr(TM.M, "swiglu", bad)
+    assert _fails(TM.test_swiglu_gate_then_up)
+
+
+def test_mutant_combine_weights_of_wrong_slot(monkeypatch):
+    def bad(y2, perm_of_assignment, topk_w):
+        return ORIG_COMBINE(y2, perm_of_assignment, np.asarray(topk_w)[:, ::-1])
+    monkeypatch.setattr(TM.M, "combine", bad)
+    assert _fails(TM.test_combine_equal_rows_and_brute_force)
+
+
+def test_mutant_e4m3_truncating_encoder(monkeypatch):
+    def bad(t):
+        t = np.minimum(np.asarray(t, np.float64), 448.0)
+        return (np.searchsorted(F.E4M3_POS, t, side="right") - 1).astype(np.uint8)
+    monkeypatch.setattr(F, "e4m3_encode_satfinite", bad)
+    assert _fails(TF.test_e4m3_encode_matches_torch_rne)
+
+
+ORIG_GEMM = M.grouped_gemm
+ORIG_ROUTE = M.route
+ORIG_COMBINE = M.combine

@@ -1,0 +1,124 @@
+"""Seeded synthetic inputs for the NVFP4 MoE layer.
+
+This module only draws random numbers and fixes shapes.  It holds none of the
+method's arithmetic (no quantisation, routing, GEMM or combine): both the CPU
+oracle and the GPU path receive exactly the arrays produced here.
+
+Every stream is ``numpy.random.default_rng(SeedSequence([2026, cfg, stream, ...]))``
+with streams 0 = router logits, 1 = expert popularity ranks, 2 = activations,
+3 = gate_up weights (one sub-stream per expert), 4 = down weights (one per
+expert), 5/6 = dense A/B.  Activations are drawn in float32 and rounded to
+bfloat16 (round to nearest even, by torch), because the layer's input is a
+bfloat16 tensor; the float32 copy returned here holds the same values.
+
+The workloads stand in for one GPU's share of a 256-expert MoE layer served
+with 8-way tensor parallelism (the per-GPU expert width of 256 comes from
+"Discovering SM120-Specific CUTLASS MoE Kernels", section "Assumptions and
+Potential Missteps": E=256, N=256 at TP8); hidden size 6144 and top-8 routing
+are the stated workload sizes.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+
+import numpy as np
+
+SEED = 2026
+
+
+@dataclass(frozen=True)
+class MoEConfig:
+    name: str
+    T: int          # tokens
+    H: int          # hidden size (K of gate_up, N of down)
+    I: int          # per-expert intermediate size (gate_up has 2I rows)
+    E: int          # experts
+    k: int          # experts per token
+    routing: str = "uniform"          # "uniform" or "zipf"
+    zipf_s: float = 1.1
+    zipf_alpha: float = 0.55
+    zipf_r0: int = 32
+    logit_std: float = 1.0
+    weight_std: float = 0.02
+    dense: bool = False               # single dense GEMM (E=1, no routing)
+    index: int = 0
+    extra: dict = field(default_factory=dict)
+
+
+CONFIGS = {
+    0: MoEConfig("tiny", T=8, H=256, I=128, E=4, k=2, index=0),
+    1: MoEConfig("decode_T256", T=256, H=6144, I=256, E=256, k=8, index=1),
+    2: MoEConfig("decode_T2048_zipf", T=2048, H=6144, I=256, E=256, k=8,
+                 routing="zipf", index=2),
+    3: MoEConfig("prefill_T16384", T=16384, H=6144, I=256, E=256, k=8, index=3),
+    # dense GEMM: M=T rows of A, N=H rows of B, K=I reduction
+    4: MoEConfig("dense_8192", T=8192, H=8192, I=8192, E=1, k=1, dense=True, index=4),
+}
+
+
+def rng(cfg_index: int, stream: int, *sub: int) -> np.random.Generator:
+    return np.random.default_rng(np.random.SeedSequence([SEED, cfg_index, stream, *sub]))
+
+
+def to_bf16_values(x: np.ndarray) -> np.ndarray:
+    """Round float32 values to the nearest bfloat16 (ties to even), returned as float32."""
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32))
+    return t.to(torch.bfloat16).to(torch.float32).numpy()
+
+
+def expert_bias(cfg: MoEConfig) -> np.ndarray:
+    """Per-expert additive logit bias giving a Zipf-like expert popularity.
+
+    b_e = -alpha * s * ln(max(rank_e, r0)) where rank_e is a seeded permutation
+    of 1..E.  Uniform routing gets zeros.
+    """
+    if cfg.routing == "uniform":
+        return np.zeros(cfg.E, dtype=np.float32)
+    ranks = rng(cfg.index, 1).permutation(cfg.E) + 1
+    b = -cfg.zipf_alpha * cfg.zipf_s * np.log(np.maximum(ranks, cfg.zipf_r0).astype(np.float64))
+    return b.astype(np.float32)
+
+
+def logits(cfg: MoEConfig, T: int | None = None) -> np.ndarray:
+    T = cfg.T if T is None else T
+    g = rng(cfg.index, 0)
+    l = g.standard_normal((T, cfg.E), dtype=np.float32) * np.float32(cfg.logit_std)
+    return (l + expert_bias(cfg)[None, :]).astype(np.float32)
+
+
+def activations(cfg: MoEConfig, T: int | None = None) -> np.ndarray:
+    """x ~ N(0,1), rounded to bfloat16, as float32 [T, H]."""
+    T = cfg.T if T is None else T
+    x = rng(cfg.index, 2).standard_normal((T, cfg.H), dtype=np.float32)
+    return to_bf16_values(x)
+
+
+def gate_up_weight(cfg: MoEConfig, e: int) -> np.ndarray:
+    """float32 [2I, H] ~ N(0, weight_std): rows [0, I) gate, [I, 2I) up."""
+    w = rng(cfg.index, 3, e).standard_normal((2 * cfg.I, cfg.H), dtype=np.float32)
+    return w * np.float32(cfg.weight_std)
+
+
+def down_weight(cfg: MoEConfig, e: int) -> np.ndarray:
+    """float32 [H, I] ~ N(0, weight_std)."""
+    w = rng(cfg.index, 4, e).standard_normal((cfg.H, cfg.I), dtype=np.float32)
+    return w * np.float32(cfg.weight_std)
+
+
+def dense_operands(cfg: MoEConfig, M: int | None = None, N: int | None = None,
+                   K: int | None = None) -> tuple[np.ndarray, np.ndarray]:
+    """A [M, K] and B [N, K] ~ N(0,1) float32 for the single dense GEMM."""
+    M = cfg.T if M is None else M
+    N = cfg.H if N is None else N
+    K = cfg.I if K is None else K
+    a = rng(cfg.index, 5).standard_normal((M, K), dtype=np.float32)
+    b = rng(cfg.index, 6).standard_normal((N, K), dtype=np.float32)
+    return a, b
+
+
+def small_variant(cfg: MoEConfig, **over) -> MoEConfig:
+    """Same recipe, other sizes (for parity cases the oracle finishes quickly)."""
+    d = dict(cfg.__dict__)
+    d.update(over)
+    return MoEConfig(**d)
