@@ -1,0 +1,267 @@
+"""Python binding of libnvfp4moe, the NVFP4 block-scaled MoE layer for MI355X.
+
+Argument marshalling only: each function checks tensor devices/dtypes/shapes,
+allocates outputs with torch (device memory is all torch is used for), and
+calls the C entry point of the same name on the current HIP stream.  Every
+step of the computation runs in the library's HIP kernels; there is no CPU or
+eager-PyTorch fallback, and importing a function whose library is missing
+raises.
+
+C entry points (include/nvfp4moe.h): moe_route_permute, nvfp4_quantize,
+nvfp4_grouped_gemm, moe_swiglu, moe_unpermute_combine.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG_DIR, "libnvfp4moe.so")
+
+OK, ERR_INVALID, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = range(5)
+F32, BF16 = 0, 1
+EPI_F32, EPI_BF16, EPI_SWIGLU_NVFP4, EPI_COMBINE_F32 = range(4)
+
+
+class NVFP4MoEError(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        super().__init__(f"nvfp4moe status {status}: {detail}")
+        self.status = status
+        self.detail = detail
+
+
+class GemmArgs(ctypes.Structure):
+    """Mirror of nvfp4moe_gemm_args."""
+    _fields_ = [
+        ("a_codes", ctypes.c_void_p), ("a_scales", ctypes.c_void_p), ("a_g", ctypes.c_void_p),
+        ("a_rows", ctypes.c_void_p), ("a_rows_total", ctypes.c_int64),
+        ("b_codes", ctypes.c_void_p), ("b_scales", ctypes.c_void_p), ("b_g", ctypes.c_void_p),
+        ("offsets", ctypes.c_void_p),
+        ("E", ctypes.c_int32), ("N", ctypes.c_int32), ("K", ctypes.c_int32),
+        ("m_total", ctypes.c_int64), ("epilogue", ctypes.c_int32),
+        ("out", ctypes.c_void_p), ("out_rows", ctypes.c_int64),
+        ("out_codes", ctypes.c_void_p), ("out_scales", ctypes.c_void_p), ("out_g", ctypes.c_void_p),
+        ("row_token", ctypes.c_void_p), ("row_weight", ctypes.c_void_p),
+        ("max_rows_per_expert_hint", ctypes.c_int32),
+    ]
+
+
+_lib = None
+
+_SIGNATURES = {
+    "moe_route_permute_workspace_size": (ctypes.c_size_t, [ctypes.c_int32] * 3),
+    "moe_route_permute": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32]
+                          + [ctypes.c_void_p] * 8 + [ctypes.c_size_t, ctypes.c_void_p]),
+    "nvfp4_quantize_workspace_size": (ctypes.c_size_t, []),
+    "nvfp4_quantize": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_int64]
+                       + [ctypes.c_void_p] * 5 + [ctypes.c_size_t, ctypes.c_void_p]),
+    "nvfp4_grouped_gemm": (ctypes.c_int, [ctypes.POINTER(GemmArgs), ctypes.c_void_p]),
+    "moe_swiglu_workspace_size": (ctypes.c_size_t, []),
+    "moe_swiglu": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_int32]
+                   + [ctypes.c_void_p] * 5 + [ctypes.c_size_t, ctypes.c_void_p]),
+    "moe_unpermute_combine": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p,
+                                             ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p,
+                                             ctypes.c_int32, ctypes.c_void_p]),
+    "nvfp4moe_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "nvfp4moe_last_error_detail": (ctypes.c_char_p, []),
+    "nvfp4moe_version": (ctypes.c_int, []),
+}
+
+
+def lib() -> ctypes.CDLL:
+    """Load libnvfp4moe.so (built in-tree by block_scaled_fp4_permute_amd.build)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: run `python -m block_scaled_fp4_permute_amd.build` "
+                              "(there is no fallback implementation)")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGNATURES.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = L
+    return _lib
+
+
+def _check(status: int):
+    if status != OK:
+        detail = lib().nvfp4moe_last_error_detail().decode()
+        raise NVFP4MoEError(status, detail)
+
+
+def _ptr(t) -> int | None:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream) -> int:
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream
+
+
+def _need(t, dtype, name, device=None):
+    import torch
+    if t.dtype != dtype:
+        raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
+    if not t.is_cuda:
+        raise ValueError(f"{name}: must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name}: on {t.device}, expected {device}")
+
+
+def _dtype_code(t):
+    import torch
+    if t.dtype == torch.float32:
+        return F32
+    if t.dtype == torch.bfloat16:
+        return BF16
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+# --------------------------------------------------------------------------- route
+@dataclass
+class Routing:
+    topk_ids: "object"
+    topk_w: "object"
+    counts: "object"
+    offsets: "object"
+    perm_src_token: "object"
+    perm_of_assignment: "object"
+    perm_weight: "object"
+
+
+def moe_route_permute(logits, k: int, out: Routing | None = None, workspace=None, stream=None) -> Routing:
+    """logits float32 [T, E] -> Routing (see include/nvfp4moe.h)."""
+    import torch
+    _need(logits, torch.float32, "logits")
+    T, E = logits.shape
+    dev = logits.device
+    if out is None:
+        i32 = dict(dtype=torch.int32, device=dev)
+        out = Routing(torch.empty((T, k), **i32), torch.empty((T, k), dtype=torch.float32, device=dev),
+                      torch.empty(E, **i32), torch.empty(E + 1, **i32), torch.empty(T * k, **i32),
+                      torch.empty(T * k, **i32), torch.empty(T * k, dtype=torch.float32, device=dev))
+    nbytes = lib().moe_route_permute_workspace_size(T, E, k)
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=dev)
+    _check(lib().moe_route_permute(
+        logits.data_ptr(), T, E, k, out.topk_ids.data_ptr(), out.topk_w.data_ptr(), out.counts.data_ptr(),
+        out.offsets.data_ptr(), out.perm_src_token.data_ptr(), out.perm_of_assignment.data_ptr(),
+        _ptr(out.perm_weight), workspace.data_ptr(), workspace.numel(), _stream(stream)))
+    return out
+
+
+# ------------------------------------------------------------------------ quantise
+@dataclass
+class NVFP4Tensor:
+    codes: "object"     # uint8 [rows, cols/2]
+    scales: "object"    # uint8 [rows, cols/16]
+    g: "object"         # float32 [1] (device)
+
+
+def nvfp4_quantize(x, g=None, out: NVFP4Tensor | None = None, workspace=None, stream=None) -> NVFP4Tensor:
+    """x bf16/float32 [rows, cols] -> NVFP4Tensor.  g: optional device float32[1]
+    per-tensor scale (None: amax/2688 computed on the device)."""
+    import torch
+    if x.dim() != 2:
+        raise ValueError("x must be 2-D")
+    _need(x, x.dtype, "x")
+    rows, cols = x.shape
+    dev = x.device
+    if out is None:
+        out = NVFP4Tensor(torch.empty((rows, cols // 2), dtype=torch.uint8, device=dev),
+                          torch.empty((rows, cols // 16), dtype=torch.uint8, device=dev),
+                          torch.empty(1, dtype=torch.float32, device=dev))
+    if workspace is None:
+        workspace = torch.empty(lib().nvfp4_quantize_workspace_size(), dtype=torch.uint8, device=dev)
+    _check(lib().nvfp4_quantize(x.data_ptr(), _dtype_code(x), rows, cols, _ptr(g), _ptr(out.g),
+                                out.codes.data_ptr(), out.scales.data_ptr(), workspace.data_ptr(),
+                                workspace.numel(), _stream(stream)))
+    return out
+
+
+# ---------------------------------------------------------------------------- gemm
+def nvfp4_grouped_gemm(a: NVFP4Tensor, b_codes, b_scales, b_g, offsets, *, m_total: int, a_rows=None,
+                       epilogue: int = EPI_F32, out=None, out_rows: int = 0, out_codes=None,
+                       out_scales=None, out_g=None, row_token=None, row_weight=None,
+                       max_rows_per_expert_hint: int = 0, stream=None):
+    """Grouped NVFP4 GEMM (see include/nvfp4moe.h).  b_codes uint8 [E, N, K/2],
+    b_scales uint8 [E, N, K/16], b_g float32 [E], offsets int32 [E+1] (device)."""
+    import torch
+    E, N, K2 = b_codes.shape
+    K = 2 * K2
+    _need(a.codes, torch.uint8, "a.codes")
+    _need(a.scales, torch.uint8, "a.scales")
+    _need(b_codes, torch.uint8, "b_codes")
+    _need(b_scales, torch.uint8, "b_scales")
+    _need(b_g, torch.float32, "b_g")
+    _need(offsets, torch.int32, "offsets")
+    if a.codes.shape[1] != K2 or tuple(b_scales.shape) != (E, N, K // 16):
+        raise ValueError("operand shapes disagree")
+    if a_rows is not None:
+        _need(a_rows, torch.int32, "a_rows")
+    dev = b_codes.device
+    I = N // 2
+    if epilogue in (EPI_F32, EPI_BF16) and out is None:
+        out = torch.empty((m_total, N), dtype=torch.float32 if epilogue == EPI_F32 else torch.bfloat16, device=dev)
+    if epilogue == EPI_SWIGLU_NVFP4 and out_codes is None:
+        out_codes = torch.empty((m_total, I // 2), dtype=torch.uint8, device=dev)
+        out_scales = torch.empty((m_total, I // 16), dtype=torch.uint8, device=dev)
+    args = GemmArgs(
+        a_codes=a.codes.data_ptr(), a_scales=a.scales.data_ptr(), a_g=a.g.data_ptr(), a_rows=_ptr(a_rows),
+        a_rows_total=a.codes.shape[0], b_codes=b_codes.data_ptr(), b_scales=b_scales.data_ptr(),
+        b_g=b_g.data_ptr(), offsets=offsets.data_ptr(), E=E, N=N, K=K, m_total=m_total, epilogue=epilogue,
+        out=_ptr(out), out_rows=out_rows, out_codes=_ptr(out_codes), out_scales=_ptr(out_scales),
+        out_g=_ptr(out_g), row_token=_ptr(row_token), row_weight=_ptr(row_weight),
+        max_rows_per_expert_hint=max_rows_per_expert_hint)
+    _check(lib().nvfp4_grouped_gemm(ctypes.byref(args), _stream(stream)))
+    if epilogue == EPI_SWIGLU_NVFP4:
+        return NVFP4Tensor(out_codes, out_scales, out_g)
+    return out
+
+
+# -------------------------------------------------------------------------- swiglu
+def moe_swiglu(gate_up, g=None, out: NVFP4Tensor | None = None, workspace=None, stream=None) -> NVFP4Tensor:
+    """gate_up float32/bf16 [M, 2I] -> NVFP4 h = silu(gate) * up."""
+    import torch
+    _need(gate_up, gate_up.dtype, "gate_up")
+    M, N2 = gate_up.shape
+    I = N2 // 2
+    dev = gate_up.device
+    if out is None:
+        out = NVFP4Tensor(torch.empty((M, I // 2), dtype=torch.uint8, device=dev),
+                          torch.empty((M, I // 16), dtype=torch.uint8, device=dev),
+                          torch.empty(1, dtype=torch.float32, device=dev))
+    if workspace is None:
+        workspace = torch.empty(lib().moe_swiglu_workspace_size(), dtype=torch.uint8, device=dev)
+    _check(lib().moe_swiglu(gate_up.data_ptr(), _dtype_code(gate_up), M, I, _ptr(g), _ptr(out.g),
+                            out.codes.data_ptr(), out.scales.data_ptr(), workspace.data_ptr(), workspace.numel(),
+                            _stream(stream)))
+    return out
+
+
+# ------------------------------------------------------------------------- combine
+def moe_unpermute_combine(y, perm_of_assignment, topk_w, T: int, k: int, out=None, out_dtype=None, stream=None):
+    """out[t] = sum_j topk_w[t, j] * y[perm_of_assignment[t*k + j]] (bf16 by default)."""
+    import torch
+    _need(y, y.dtype, "y")
+    H = y.shape[1]
+    if out is None:
+        out = torch.empty((T, H), dtype=out_dtype or torch.bfloat16, device=y.device)
+    if perm_of_assignment is not None:
+        _need(perm_of_assignment, torch.int32, "perm_of_assignment")
+    if topk_w is not None:
+        _need(topk_w, torch.float32, "topk_w")
+    _check(lib().moe_unpermute_combine(y.data_ptr(), _dtype_code(y), _ptr(perm_of_assignment), _ptr(topk_w),
+                                       T, k, H, out.data_ptr(), _dtype_code(out), _stream(stream)))
+    return out
+
+
+__all__ = ["lib", "moe_route_permute", "nvfp4_quantize", "nvfp4_grouped_gemm", "moe_swiglu",
+           "moe_unpermute_combine", "NVFP4Tensor", "Routing", "GemmArgs", "NVFP4MoEError",
+           "F32", "BF16", "EPI_F32", "EPI_BF16", "EPI_SWIGLU_NVFP4", "EPI_COMBINE_F32"]

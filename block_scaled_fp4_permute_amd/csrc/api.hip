@@ -1,0 +1,193 @@
+// C-ABI entry points of libnvfp4moe: argument validation on the host, then
+// kernel launches on the caller's stream.  Nothing is allocated here.
+#include <stdio.h>
+#include <stdarg.h>
+
+#include "../../include/nvfp4moe.h"
+#include "nvfp4_internal.h"
+
+namespace {
+
+thread_local char g_detail[512] = "";
+
+int fail(int status, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_detail, sizeof(g_detail), fmt, ap);
+  va_end(ap);
+  return status;
+}
+
+int ok() {
+  g_detail[0] = '\0';
+  return NVFP4MOE_OK;
+}
+
+int hip_status(hipError_t err, const char* what) {
+  if (err == hipSuccess) return ok();
+  return fail(NVFP4MOE_ERR_HIP, "%s: %s", what, hipGetErrorString(err));
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+constexpr size_t kSmallWs = 256;
+
+}  // namespace
+
+extern "C" {
+
+const char* nvfp4moe_status_string(int status) {
+  switch (status) {
+    case NVFP4MOE_OK: return "ok";
+    case NVFP4MOE_ERR_INVALID: return "invalid argument";
+    case NVFP4MOE_ERR_UNSUPPORTED: return "unsupported configuration";
+    case NVFP4MOE_ERR_WORKSPACE: return "workspace too small";
+    case NVFP4MOE_ERR_HIP: return "HIP launch error";
+    default: return "unknown status";
+  }
+}
+
+const char* nvfp4moe_last_error_detail(void) { return g_detail; }
+
+int nvfp4moe_version(void) { return 100; }
+
+// ------------------------------------------------------------------ route + permute
+size_t moe_route_permute_workspace_size(int32_t T, int32_t E, int32_t k) {
+  if (T <= 0 || E <= 0 || k <= 0) return 0;
+  return nvfp4::route_permute_ws_bytes(T, E, k);
+}
+
+int moe_route_permute(const float* logits, int32_t T, int32_t E, int32_t k, int32_t* topk_ids, float* topk_w,
+                      int32_t* counts, int32_t* offsets, int32_t* perm_src_token, int32_t* perm_of_assignment,
+                      float* perm_weight, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!logits || !topk_ids || !topk_w || !counts || !offsets || !perm_src_token || !perm_of_assignment)
+    return fail(NVFP4MOE_ERR_INVALID, "moe_route_permute: null pointer argument");
+  if (T <= 0 || E <= 0 || k <= 0) return fail(NVFP4MOE_ERR_INVALID, "moe_route_permute: T, E, k must be > 0");
+  if (k > E) return fail(NVFP4MOE_ERR_INVALID, "moe_route_permute: k=%d > E=%d", k, E);
+  if (k > 32) return fail(NVFP4MOE_ERR_UNSUPPORTED, "moe_route_permute: k=%d > 32", k);
+  if (E > 4096) return fail(NVFP4MOE_ERR_UNSUPPORTED, "moe_route_permute: E=%d > 4096", E);
+  if (static_cast<int64_t>(T) * k >= (int64_t(1) << 30))
+    return fail(NVFP4MOE_ERR_UNSUPPORTED, "moe_route_permute: T*k >= 2^30");
+  const size_t need = nvfp4::route_permute_ws_bytes(T, E, k);
+  if (!workspace || workspace_bytes < need)
+    return fail(NVFP4MOE_ERR_WORKSPACE, "moe_route_permute: workspace %zu < %zu bytes", workspace_bytes, need);
+  if (!aligned(workspace, 16)) return fail(NVFP4MOE_ERR_INVALID, "moe_route_permute: workspace not 16-byte aligned");
+  return hip_status(nvfp4::launch_route_permute(logits, T, E, k, topk_ids, topk_w, counts, offsets, perm_src_token,
+                                                perm_of_assignment, perm_weight, workspace,
+                                                static_cast<hipStream_t>(stream)),
+                    "moe_route_permute");
+}
+
+// ------------------------------------------------------------------ quantise
+size_t nvfp4_quantize_workspace_size(void) { return kSmallWs; }
+
+int nvfp4_quantize(const void* x, int32_t x_dtype, int64_t rows, int64_t cols, const float* g_in, float* g_out,
+                   uint8_t* codes, uint8_t* scales, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!x || !codes || !scales) return fail(NVFP4MOE_ERR_INVALID, "nvfp4_quantize: null pointer argument");
+  if (x_dtype != NVFP4MOE_F32 && x_dtype != NVFP4MOE_BF16)
+    return fail(NVFP4MOE_ERR_INVALID, "nvfp4_quantize: x_dtype %d", x_dtype);
+  if (rows <= 0 || cols <= 0) return fail(NVFP4MOE_ERR_INVALID, "nvfp4_quantize: rows, cols must be > 0");
+  if (cols % 32 != 0) return fail(NVFP4MOE_ERR_INVALID, "nvfp4_quantize: cols=%lld not a multiple of 32", (long long)cols);
+  if (rows * (cols / 16) >= (int64_t(1) << 40)) return fail(NVFP4MOE_ERR_UNSUPPORTED, "nvfp4_quantize: tensor too large");
+  if (!aligned(x, 16) || !aligned(codes, 8)) return fail(NVFP4MOE_ERR_INVALID, "nvfp4_quantize: misaligned x or codes");
+  if (!g_in && (!workspace || workspace_bytes < kSmallWs))
+    return fail(NVFP4MOE_ERR_WORKSPACE, "nvfp4_quantize: workspace of %zu bytes needed when g_in is NULL", kSmallWs);
+  return hip_status(nvfp4::launch_quantize(x, x_dtype, rows, cols, g_in, g_out, codes, scales, workspace,
+                                           static_cast<hipStream_t>(stream)),
+                    "nvfp4_quantize");
+}
+
+// ------------------------------------------------------------------ grouped GEMM
+int nvfp4_grouped_gemm(const nvfp4moe_gemm_args* a, void* stream) {
+  if (!a) return fail(NVFP4MOE_ERR_INVALID, "nvfp4_grouped_gemm: args is NULL");
+  if (!a->a_codes || !a->a_scales || !a->a_g || !a->b_codes || !a->b_scales || !a->b_g || !a->offsets)
+    return fail(NVFP4MOE_ERR_INVALID, "nvfp4_grouped_gemm: null operand pointer");
+  if (a->E <= 0 || a->N <= 0 || a->K <= 0 || a->m_total < 0 || a->a_rows_total <= 0)
+    return fail(NVFP4MOE_ERR_INVALID, "nvfp4_grouped_gemm: E, N, K, a_rows_total must be > 0 and m_total >= 0");
+  if (a->K % 32 != 0) return fail(NVFP4MOE_ERR_INVALID, "nvfp4_grouped_gemm: K=%d not a multiple of 32", a->K);
+  if (a->N % 16 != 0) return fail(NVFP4MOE_ERR_INVALID, "nvfp4_grouped_gemm: N=%d not a multiple of 16", a->N);
+  if (!aligned(a->a_codes, 16) || !aligned(a->b_codes, 16) || !aligned(a->a_scales, 2) || !aligned(a->b_scales, 2))
+    return fail(NVFP4MOE_ERR_INVALID, "nvfp4_grouped_gemm: codes must be 16-byte and scales 2-byte aligned");
+  if (a->m_total >= (int64_t(1) << 31) || a->a_rows_total >= (int64_t(1) << 31))
+    return fail(NVFP4MOE_ERR_UNSUPPORTED, "nvfp4_grouped_gemm: more than 2^31 rows");
+  if (static_cast<int64_t>(a->E) * a->N >= (int64_t(1) << 31))
+    return fail(NVFP4MOE_ERR_UNSUPPORTED, "nvfp4_grouped_gemm: E*N >= 2^31");
+  switch (a->epilogue) {
+    case NVFP4MOE_EPI_F32:
+    case NVFP4MOE_EPI_BF16:
+      if (!a->out && a->m_total > 0) return fail(NVFP4MOE_ERR_INVALID, "nvfp4_grouped_gemm: out is NULL");
+      break;
+    case NVFP4MOE_EPI_SWIGLU_NVFP4:
+      if (a->N % 32 != 0) return fail(NVFP4MOE_ERR_INVALID, "nvfp4_grouped_gemm: SwiGLU needs N = 2I with I %% 16 == 0");
+      if (!a->out_codes || !a->out_scales || !a->out_g)
+        return fail(NVFP4MOE_ERR_INVALID, "nvfp4_grouped_gemm: SwiGLU needs out_codes, out_scales, out_g");
+      break;
+    case NVFP4MOE_EPI_COMBINE_F32:
+      if (!a->out || !a->row_token || !a->row_weight || a->out_rows <= 0)
+        return fail(NVFP4MOE_ERR_INVALID, "nvfp4_grouped_gemm: combine needs out, row_token, row_weight, out_rows");
+      if (!aligned(a->out, 4)) return fail(NVFP4MOE_ERR_INVALID, "nvfp4_grouped_gemm: out misaligned");
+      break;
+    default:
+      return fail(NVFP4MOE_ERR_INVALID, "nvfp4_grouped_gemm: unknown epilogue %d", a->epilogue);
+  }
+  if (a->m_total == 0) return ok();
+  nvfp4::GemmParams prm{};
+  prm.a_codes = a->a_codes;
+  prm.a_scales = a->a_scales;
+  prm.a_g = a->a_g;
+  prm.a_rows = a->a_rows;
+  prm.b_codes = a->b_codes;
+  prm.b_scales = a->b_scales;
+  prm.b_g = a->b_g;
+  prm.offsets = a->offsets;
+  prm.E = a->E;
+  prm.N = a->N;
+  prm.K = a->K;
+  prm.m_total = static_cast<int>(a->m_total);
+  prm.a_rows_total = static_cast<int>(a->a_rows_total);
+  prm.out_rows = static_cast<int>(a->out_rows < (int64_t(1) << 31) ? a->out_rows : 0);
+  prm.out = a->out;
+  prm.out_codes = a->out_codes;
+  prm.out_scales = a->out_scales;
+  prm.out_g = a->out_g;
+  prm.row_token = a->row_token;
+  prm.row_weight = a->row_weight;
+  return hip_status(nvfp4::launch_grouped_gemm(prm, a->epilogue, a->m_total, a->max_rows_per_expert_hint,
+                                               static_cast<hipStream_t>(stream)),
+                    "nvfp4_grouped_gemm");
+}
+
+// ------------------------------------------------------------------ SwiGLU
+size_t moe_swiglu_workspace_size(void) { return kSmallWs; }
+
+int moe_swiglu(const void* gate_up, int32_t dtype, int64_t M, int32_t I, const float* g_in, float* g_out,
+               uint8_t* codes, uint8_t* scales, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!gate_up || !codes || !scales) return fail(NVFP4MOE_ERR_INVALID, "moe_swiglu: null pointer argument");
+  if (dtype != NVFP4MOE_F32 && dtype != NVFP4MOE_BF16) return fail(NVFP4MOE_ERR_INVALID, "moe_swiglu: dtype %d", dtype);
+  if (M <= 0 || I <= 0) return fail(NVFP4MOE_ERR_INVALID, "moe_swiglu: M, I must be > 0");
+  if (I % 16 != 0) return fail(NVFP4MOE_ERR_INVALID, "moe_swiglu: I=%d not a multiple of 16", I);
+  if (!aligned(gate_up, 16) || !aligned(codes, 8)) return fail(NVFP4MOE_ERR_INVALID, "moe_swiglu: misaligned pointer");
+  if (M * (I / 16) >= (int64_t(1) << 40)) return fail(NVFP4MOE_ERR_UNSUPPORTED, "moe_swiglu: tensor too large");
+  if (!g_in && (!workspace || workspace_bytes < kSmallWs))
+    return fail(NVFP4MOE_ERR_WORKSPACE, "moe_swiglu: workspace of %zu bytes needed when g_in is NULL", kSmallWs);
+  return hip_status(nvfp4::launch_swiglu(gate_up, dtype, M, I, g_in, g_out, codes, scales, workspace,
+                                         static_cast<hipStream_t>(stream)),
+                    "moe_swiglu");
+}
+
+// ------------------------------------------------------------------ combine
+int moe_unpermute_combine(const void* y, int32_t y_dtype, const int32_t* perm_of_assignment, const float* topk_w,
+                          int32_t T, int32_t k, int32_t H, void* out, int32_t out_dtype, void* stream) {
+  if (!y || !out) return fail(NVFP4MOE_ERR_INVALID, "moe_unpermute_combine: null y or out");
+  if ((y_dtype != NVFP4MOE_F32 && y_dtype != NVFP4MOE_BF16) || (out_dtype != NVFP4MOE_F32 && out_dtype != NVFP4MOE_BF16))
+    return fail(NVFP4MOE_ERR_INVALID, "moe_unpermute_combine: dtype");
+  if (T <= 0 || k <= 0 || H <= 0) return fail(NVFP4MOE_ERR_INVALID, "moe_unpermute_combine: T, k, H must be > 0");
+  if (H % 8 != 0) return fail(NVFP4MOE_ERR_INVALID, "moe_unpermute_combine: H=%d not a multiple of 8", H);
+  if (!aligned(y, 16) || !aligned(out, 16)) return fail(NVFP4MOE_ERR_INVALID, "moe_unpermute_combine: misaligned");
+  if (static_cast<int64_t>(T) * k >= (int64_t(1) << 31)) return fail(NVFP4MOE_ERR_UNSUPPORTED, "moe_unpermute_combine: T*k too large");
+  return hip_status(nvfp4::launch_combine(y, y_dtype, perm_of_assignment, topk_w, T, k, H, out, out_dtype,
+                                          static_cast<hipStream_t>(stream)),
+                    "moe_unpermute_combine");
+}
+
+}  // extern "C"

@@ -1,0 +1,232 @@
+// NVFP4 quantisation, the unfused SwiGLU + re-quantisation, and the unfused
+// weighted combine.  All three are HBM-bound streaming kernels: one thread per
+// 16-element block (quantise, SwiGLU) or per 8 output columns (combine), with
+// 16-byte vector loads and stores.
+#include "nvfp4_internal.h"
+
+namespace nvfp4 {
+
+// ------------------------------------------------------------------ helpers
+__global__ void k_zero_u32(uint32_t* p, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0u;
+}
+
+template <int DT>
+__device__ __forceinline__ void load16(const void* base, size_t elem0, float (&x)[16]) {
+  if constexpr (DT == 1) {  // bf16: 32 bytes
+    const uint4* p = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(base) + elem0);
+    const uint4 a = p[0], b = p[1];
+    const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      x[2 * i] = __uint_as_float(w[i] << 16);
+      x[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+    }
+  } else {  // float32: 64 bytes
+    const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(base) + elem0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float4 v = p[i];
+      x[4 * i] = v.x;
+      x[4 * i + 1] = v.y;
+      x[4 * i + 2] = v.z;
+      x[4 * i + 3] = v.w;
+    }
+  }
+}
+
+__device__ __forceinline__ void wave_atomic_max(uint32_t* dst, float v) {
+  // non-negative floats order like their bit patterns
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
+  if ((threadIdx.x & 63) == 0) atomicMax(dst, __float_as_uint(v));
+}
+
+// ------------------------------------------------------------------ quantise
+template <int DT>
+__global__ __launch_bounds__(256) void k_amax_blocks(const void* __restrict__ x, int64_t nblocks,
+                                                     uint32_t* __restrict__ amax_bits) {
+  float m = 0.0f;
+  for (int64_t b = blockIdx.x * 256ll + threadIdx.x; b < nblocks; b += static_cast<int64_t>(gridDim.x) * 256) {
+    float v[16];
+    load16<DT>(x, b * 16, v);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) m = fmaxf(m, fabsf(v[i]));
+  }
+  wave_atomic_max(amax_bits, m);
+}
+
+template <int DT>
+__global__ __launch_bounds__(256) void k_quantize(const void* __restrict__ x, int64_t nblocks,
+                                                  const float* __restrict__ g_in,
+                                                  const uint32_t* __restrict__ amax_bits,
+                                                  float* __restrict__ g_out, uint8_t* __restrict__ codes,
+                                                  uint8_t* __restrict__ scales) {
+  const float g = g_in ? *g_in : global_scale_from_amax(__uint_as_float(*amax_bits));
+  const int64_t b = blockIdx.x * 256ll + threadIdx.x;
+  if (b == 0 && g_out) *g_out = g;
+  if (b >= nblocks) return;
+  float v[16];
+  load16<DT>(x, b * 16, v);
+  uint32_t lo, hi;
+  const uint32_t s = encode_block16(v, g, lo, hi);
+  reinterpret_cast<uint2*>(codes)[b] = make_uint2(lo, hi);
+  scales[b] = static_cast<uint8_t>(s);
+}
+
+hipError_t launch_quantize(const void* x, int dtype, int64_t rows, int64_t cols, const float* g_in, float* g_out,
+                           uint8_t* codes, uint8_t* scales, void* ws, hipStream_t stream) {
+  const int64_t nblocks = rows * (cols / 16);
+  uint32_t* amax_bits = static_cast<uint32_t*>(ws);
+  if (!g_in) {
+    hipLaunchKernelGGL(k_zero_u32, dim3(1), dim3(64), 0, stream, amax_bits, 1);
+    const int64_t want = (nblocks + 255) / 256;
+    const int grid = static_cast<int>(want < 2048 ? (want > 0 ? want : 1) : 2048);
+    if (dtype == 1)
+      hipLaunchKernelGGL(k_amax_blocks<1>, dim3(grid), dim3(256), 0, stream, x, nblocks, amax_bits);
+    else
+      hipLaunchKernelGGL(k_amax_blocks<0>, dim3(grid), dim3(256), 0, stream, x, nblocks, amax_bits);
+  }
+  const dim3 grid(static_cast<unsigned>((nblocks + 255) / 256 > 0 ? (nblocks + 255) / 256 : 1));
+  if (dtype == 1)
+    hipLaunchKernelGGL(k_quantize<1>, grid, dim3(256), 0, stream, x, nblocks, g_in, amax_bits, g_out, codes, scales);
+  else
+    hipLaunchKernelGGL(k_quantize<0>, grid, dim3(256), 0, stream, x, nblocks, g_in, amax_bits, g_out, codes, scales);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------------ SwiGLU
+// h block b of row r covers h columns [16c, 16c+16) with c = b % (I/16): gate
+// columns are the same indices, up columns are I further.
+template <int DT>
+__device__ __forceinline__ void swiglu_block(const void* y, int64_t b, int I, float (&h)[16]) {
+  const int bpr = I / 16;
+  const int64_t r = b / bpr;
+  const int c = static_cast<int>(b % bpr);
+  const size_t g0 = static_cast<size_t>(r) * (2 * static_cast<size_t>(I)) + 16 * static_cast<size_t>(c);
+  float gv[16], uv[16];
+  load16<DT>(y, g0, gv);
+  load16<DT>(y, g0 + I, uv);
+#pragma unroll
+  for (int i = 0; i < 16; ++i) h[i] = silu_f32(gv[i]) * uv[i];
+}
+
+template <int DT>
+__global__ __launch_bounds__(256) void k_swiglu_amax(const void* __restrict__ y, int64_t nblocks, int I,
+                                                     uint32_t* __restrict__ amax_bits) {
+  float m = 0.0f;
+  for (int64_t b = blockIdx.x * 256ll + threadIdx.x; b < nblocks; b += static_cast<int64_t>(gridDim.x) * 256) {
+    float h[16];
+    swiglu_block<DT>(y, b, I, h);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) m = fmaxf(m, fabsf(h[i]));
+  }
+  wave_atomic_max(amax_bits, m);
+}
+
+template <int DT>
+__global__ __launch_bounds__(256) void k_swiglu_quant(const void* __restrict__ y, int64_t nblocks, int I,
+                                                      const float* __restrict__ g_in,
+                                                      const uint32_t* __restrict__ amax_bits,
+                                                      float* __restrict__ g_out, uint8_t* __restrict__ codes,
+                                                      uint8_t* __restrict__ scales) {
+  const float g = g_in ? *g_in : global_scale_from_amax(__uint_as_float(*amax_bits));
+  const int64_t b = blockIdx.x * 256ll + threadIdx.x;
+  if (b == 0 && g_out) *g_out = g;
+  if (b >= nblocks) return;
+  float h[16];
+  swiglu_block<DT>(y, b, I, h);
+  uint32_t lo, hi;
+  const uint32_t s = encode_block16(h, g, lo, hi);
+  reinterpret_cast<uint2*>(codes)[b] = make_uint2(lo, hi);
+  scales[b] = static_cast<uint8_t>(s);
+}
+
+hipError_t launch_swiglu(const void* y, int dtype, int64_t M, int I, const float* g_in, float* g_out,
+                         uint8_t* codes, uint8_t* scales, void* ws, hipStream_t stream) {
+  const int64_t nblocks = M * (I / 16);
+  uint32_t* amax_bits = static_cast<uint32_t*>(ws);
+  if (!g_in) {
+    hipLaunchKernelGGL(k_zero_u32, dim3(1), dim3(64), 0, stream, amax_bits, 1);
+    const int64_t want = (nblocks + 255) / 256;
+    const int grid = static_cast<int>(want < 2048 ? (want > 0 ? want : 1) : 2048);
+    if (dtype == 1)
+      hipLaunchKernelGGL(k_swiglu_amax<1>, dim3(grid), dim3(256), 0, stream, y, nblocks, I, amax_bits);
+    else
+      hipLaunchKernelGGL(k_swiglu_amax<0>, dim3(grid), dim3(256), 0, stream, y, nblocks, I, amax_bits);
+  }
+  const dim3 grid(static_cast<unsigned>((nblocks + 255) / 256 > 0 ? (nblocks + 255) / 256 : 1));
+  if (dtype == 1)
+    hipLaunchKernelGGL(k_swiglu_quant<1>, grid, dim3(256), 0, stream, y, nblocks, I, g_in, amax_bits, g_out,
+                       codes, scales);
+  else
+    hipLaunchKernelGGL(k_swiglu_quant<0>, grid, dim3(256), 0, stream, y, nblocks, I, g_in, amax_bits, g_out,
+                       codes, scales);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------------ combine
+// out[t, 8c .. 8c+8) = sum_j w[t, j] * y[row(t, j), 8c .. 8c+8)
+template <int YT, int OT>
+__global__ __launch_bounds__(256) void k_combine(const void* __restrict__ y, const int* __restrict__ perm,
+                                                 const float* __restrict__ w, int T, int k, int H,
+                                                 void* __restrict__ out) {
+  const int groups = H / 8;
+  const int64_t i = blockIdx.x * 256ll + threadIdx.x;
+  if (i >= static_cast<int64_t>(T) * groups) return;
+  const int t = static_cast<int>(i / groups);
+  const int c = static_cast<int>(i % groups);
+  float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  for (int j = 0; j < k; ++j) {
+    const int64_t a = static_cast<int64_t>(t) * k + j;
+    const int64_t row = perm ? perm[a] : a;
+    const float wt = w ? w[a] : 1.0f;
+    float v[8];
+    if constexpr (YT == 1) {
+      const uint4 q = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(y) + row * H)[c];
+      const uint32_t u[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        v[2 * m] = __uint_as_float(u[m] << 16);
+        v[2 * m + 1] = __uint_as_float(u[m] & 0xFFFF0000u);
+      }
+    } else {
+      const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(y) + row * H) + 2 * c;
+      const float4 a0 = p[0], a1 = p[1];
+      v[0] = a0.x; v[1] = a0.y; v[2] = a0.z; v[3] = a0.w;
+      v[4] = a1.x; v[5] = a1.y; v[6] = a1.z; v[7] = a1.w;
+    }
+#pragma unroll
+    for (int m = 0; m < 8; ++m) acc[m] = fmaf(wt, v[m], acc[m]);
+  }
+  if constexpr (OT == 1) {
+    uint4 q;
+    q.x = f32_to_bf16(acc[0]) | (static_cast<uint32_t>(f32_to_bf16(acc[1])) << 16);
+    q.y = f32_to_bf16(acc[2]) | (static_cast<uint32_t>(f32_to_bf16(acc[3])) << 16);
+    q.z = f32_to_bf16(acc[4]) | (static_cast<uint32_t>(f32_to_bf16(acc[5])) << 16);
+    q.w = f32_to_bf16(acc[6]) | (static_cast<uint32_t>(f32_to_bf16(acc[7])) << 16);
+    reinterpret_cast<uint4*>(static_cast<uint16_t*>(out) + static_cast<int64_t>(t) * H)[c] = q;
+  } else {
+    float4* p = reinterpret_cast<float4*>(static_cast<float*>(out) + static_cast<int64_t>(t) * H) + 2 * c;
+    p[0] = make_float4(acc[0], acc[1], acc[2], acc[3]);
+    p[1] = make_float4(acc[4], acc[5], acc[6], acc[7]);
+  }
+}
+
+hipError_t launch_combine(const void* y, int y_dtype, const int* perm, const float* w, int T, int k, int H,
+                          void* out, int out_dtype, hipStream_t stream) {
+  const int64_t n = static_cast<int64_t>(T) * (H / 8);
+  const dim3 grid(static_cast<unsigned>((n + 255) / 256));
+  if (y_dtype == 1 && out_dtype == 1)
+    hipLaunchKernelGGL((k_combine<1, 1>), grid, dim3(256), 0, stream, y, perm, w, T, k, H, out);
+  else if (y_dtype == 1)
+    hipLaunchKernelGGL((k_combine<1, 0>), grid, dim3(256), 0, stream, y, perm, w, T, k, H, out);
+  else if (out_dtype == 1)
+    hipLaunchKernelGGL((k_combine<0, 1>), grid, dim3(256), 0, stream, y, perm, w, T, k, H, out);
+  else
+    hipLaunchKernelGGL((k_combine<0, 0>), grid, dim3(256), 0, stream, y, perm, w, T, k, H, out);
+  return hipGetLastError();
+}
+
+}  // namespace nvfp4

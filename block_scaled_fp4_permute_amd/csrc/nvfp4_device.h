@@ -1,0 +1,151 @@
+// Device-side helpers of the NVFP4 path for gfx950 (CDNA4).
+//
+// Formats: E2M1 element codes (1 sign, 2 exponent bits with bias 1, 1 mantissa
+// bit), unsigned E4M3 block scales (4 exponent bits with bias 7, 3 mantissa
+// bits, subnormals, max 448), one block per 16 K-elements, FP32 accumulation -
+// the operand types of the block-scaled MMA in "From Empirical Limits to
+// Research-Driven Optimization: The SM120 FP4 Kernel Research Campaign",
+// section "Section 1: CUTLASS Kernels - The Foundation".
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace nvfp4 {
+
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+typedef float float4v __attribute__((ext_vector_type(4)));
+
+// ------------------------------------------------------------------ bfloat16
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+  return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+
+// nearest-even rounding of a finite float32 to bfloat16
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+
+// ------------------------------------------------------------------ E4M3
+// Value of an unsigned E4M3 code (bits 6..0; the NaN code never occurs here).
+__device__ __forceinline__ float e4m3_to_f32(uint32_t code) {
+  const uint32_t e = (code >> 3) & 0xFu;
+  const uint32_t m = code & 7u;
+  // normal: 2^(e-7) * (1 + m/8) -> float32 exponent field e + 120, mantissa m << 20
+  const float normal = __uint_as_float(((e + 120u) << 23) | (m << 20));
+  const float sub = static_cast<float>(m) * 0.001953125f;  // m * 2^-9
+  return e ? normal : sub;
+}
+
+// Non-negative finite float32 -> E4M3 code, nearest with ties to even; values
+// at or above 448 give 448 (saturating), values at or below 2^-10 give 0.
+__device__ __forceinline__ uint32_t f32_to_e4m3_sat(float t) {
+  if (!(t > 0.0f)) return 0u;
+  if (t >= 448.0f) return 0x7Eu;
+  const uint32_t u = __float_as_uint(t);
+  const int ex = static_cast<int>(u >> 23) - 127;
+  if (ex < -6) {
+    // E4M3 subnormal range: value = m * 2^-9.  t * 512 is exact; rintf rounds
+    // half to even; m = 8 is the smallest normal (code 8), which is consistent.
+    return static_cast<uint32_t>(rintf(t * 512.0f));
+  }
+  // keep 3 mantissa bits with round-to-nearest-even at bit 20; a carry moves into
+  // the exponent, which is the correct next binade
+  const uint32_t r = u + 0x7FFFFu + ((u >> 20) & 1u);
+  const uint32_t e = (r >> 23) - 120u;       // biased E4M3 exponent (>= 1 here)
+  const uint32_t code = (e << 3) | ((r >> 20) & 7u);
+  return code > 0x7Eu ? 0x7Eu : code;
+}
+
+// ------------------------------------------------------------------ E2M1
+// |v| -> 3-bit E2M1 magnitude code, nearest with ties to even, saturating at 6.
+// The grid is 0, .5, 1, 1.5, 2, 3, 4, 6; the decision points are the midpoints,
+// and at a midpoint the code with the even mantissa wins (>= or > below).
+__device__ __forceinline__ uint32_t f32_to_e2m1_mag(float v) {
+  return static_cast<uint32_t>(v > 0.25f) + static_cast<uint32_t>(v >= 0.75f) +
+         static_cast<uint32_t>(v > 1.25f) + static_cast<uint32_t>(v >= 1.75f) +
+         static_cast<uint32_t>(v > 2.5f) + static_cast<uint32_t>(v >= 3.5f) +
+         static_cast<uint32_t>(v > 5.0f);
+}
+
+// Per-tensor scale from the absolute maximum: g = amax / 2688 (2688 = 6 * 448),
+// or 1 for an all-zero tensor.
+__device__ __forceinline__ float global_scale_from_amax(float amax) {
+  return amax > 0.0f ? amax / 2688.0f : 1.0f;
+}
+
+// Encode one block of 16 float32 values with per-tensor scale g.  Writes the
+// 8 packed code bytes (element 2i in the low nibble of byte i) as two
+// 32-bit words and returns the E4M3 scale code.
+__device__ __forceinline__ uint32_t encode_block16(const float (&x)[16], float g,
+                                                   uint32_t& lo, uint32_t& hi) {
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(x[i]));
+  const float t = (amax / 6.0f) / g;
+  const uint32_t s = f32_to_e4m3_sat(t);
+  const float scale_eff = e4m3_to_f32(s) * g;
+  uint32_t w[2] = {0u, 0u};
+  if (s != 0u) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const float v = scale_eff > 0.0f ? fabsf(x[i]) / scale_eff : 0.0f;
+      const uint32_t code = f32_to_e2m1_mag(v) | ((__float_as_uint(x[i]) >> 31) << 3);
+      w[i >> 3] |= code << (4 * (i & 7));
+    }
+  }
+  lo = w[0];
+  hi = w[1];
+  return s;
+}
+
+// Encode one value given the block's scale (used by epilogues that computed the
+// block scale cooperatively).
+__device__ __forceinline__ uint32_t encode_one(float x, uint32_t s, float scale_eff) {
+  if (s == 0u) return 0u;
+  const float v = scale_eff > 0.0f ? fabsf(x) / scale_eff : 0.0f;
+  return f32_to_e2m1_mag(v) | ((__float_as_uint(x) >> 31) << 3);
+}
+
+// ------------------------------------------------------------------ decode to FP16
+// Eight E2M1 codes (one 32-bit word, element 2i in the low nibble of byte i)
+// -> eight FP16 values multiplied by the block scale.  E2M1 * E4M3 needs at
+// most 6 significant bits and lies in [2^-10, 2688], so the FP16 result is
+// exact.  The hardware conversion runs with a unit scale (exact E2M1 values
+// whatever the scale operand's semantics) and the block scale is applied with a
+// packed FP16 multiply.
+__device__ __forceinline__ half8 decode8_f16(uint32_t w, _Float16 scale) {
+  const half2v sc = {scale, scale};
+  half2v p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0);
+  half2v p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1);
+  half2v p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2);
+  half2v p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3);
+  p0 *= sc;
+  p1 *= sc;
+  p2 *= sc;
+  p3 *= sc;
+  half8 r;
+  r[0] = p0[0]; r[1] = p0[1]; r[2] = p1[0]; r[3] = p1[1];
+  r[4] = p2[0]; r[5] = p2[1]; r[6] = p3[0]; r[7] = p3[1];
+  return r;
+}
+
+__device__ __forceinline__ _Float16 e4m3_to_f16(uint32_t code) {
+  return static_cast<_Float16>(e4m3_to_f32(code));   // exact: E4M3 fits FP16
+}
+
+// ------------------------------------------------------------------ misc
+__device__ __forceinline__ float silu_f32(float x) { return x / (1.0f + expf(-x)); }
+
+// The 8 XCDs of the chip take workgroups round-robin (workgroup i runs on XCD
+// i % 8).  Remap so that each XCD receives a contiguous range of tasks, which
+// keeps neighbouring tasks (same expert, same A rows) in one L2.
+__device__ __forceinline__ int xcd_task(int bid, int nblocks) {
+  if ((nblocks & 7) != 0) return bid;
+  return (bid & 7) * (nblocks >> 3) + (bid >> 3);
+}
+
+}  // namespace nvfp4

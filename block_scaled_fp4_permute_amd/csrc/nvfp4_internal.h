@@ -1,0 +1,48 @@
+// Internal declarations shared by the HIP sources of libnvfp4moe.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "nvfp4_device.h"
+
+namespace nvfp4 {
+
+enum : int { EPI_F32 = 0, EPI_BF16 = 1, EPI_SWIGLU = 2, EPI_COMBINE = 3 };
+
+// Kernel-side arguments of the grouped GEMM (validated on the host first).
+struct GemmParams {
+  const uint8_t* a_codes;
+  const uint8_t* a_scales;
+  const float* a_g;
+  const int32_t* a_rows;
+  const uint8_t* b_codes;
+  const uint8_t* b_scales;
+  const float* b_g;
+  const int32_t* offsets;
+  int E, N, K;
+  int n_tiles;            // column tiles per expert (set by the launcher)
+  int m_total;            // rows of the outputs indexed by GEMM row
+  int a_rows_total;       // rows of A (bound for gathered row indices)
+  int out_rows;           // rows of the combine accumulator
+  void* out;
+  uint8_t* out_codes;
+  uint8_t* out_scales;
+  const float* out_g;
+  const int32_t* row_token;
+  const float* row_weight;
+};
+
+size_t route_permute_ws_bytes(int T, int E, int k);
+hipError_t launch_route_permute(const float* logits, int T, int E, int k, int* topk_ids, float* topk_w,
+                                int* counts, int* offsets, int* perm_src_token, int* perm_of_assignment,
+                                float* perm_weight, void* ws, hipStream_t stream);
+hipError_t launch_quantize(const void* x, int dtype, int64_t rows, int64_t cols, const float* g_in, float* g_out,
+                           uint8_t* codes, uint8_t* scales, void* ws, hipStream_t stream);
+hipError_t launch_swiglu(const void* y, int dtype, int64_t M, int I, const float* g_in, float* g_out,
+                         uint8_t* codes, uint8_t* scales, void* ws, hipStream_t stream);
+hipError_t launch_combine(const void* y, int y_dtype, const int* perm, const float* w, int T, int k, int H,
+                          void* out, int out_dtype, hipStream_t stream);
+hipError_t launch_grouped_gemm(const GemmParams& prm, int epilogue, int64_t m_total, int hint, hipStream_t stream);
+
+}  // namespace nvfp4

@@ -1,0 +1,242 @@
+// Top-k routing and the expert-first permutation (histogram, prefix scan of
+// expert offsets, stable scatter).
+//
+// The pages motivate both: a router picks a few of 256 experts per token
+// ("Discovering SM120-Specific CUTLASS MoE Kernels", section "Input Knowledge
+// Required"), and grouping rows by expert and reordering tokens is the first
+// tool for raising the batch per expert ("From Empirical Limits to
+// Research-Driven Optimization", section "Sections 5-6: Algorithmic
+// Techniques").
+//
+// Kernels (all on one stream, no host round trip):
+//   k_route        one wave per token: k rounds of a wave-wide argmax over the
+//                  token's logits (ties to the lower id), then the renormalised
+//                  softmax weights in float64.
+//   k_chunk_rank   one workgroup per chunk of 1024 assignments: the stable rank
+//                  of each assignment among the chunk's assignments to the same
+//                  expert (wave ballots) and the chunk's expert histogram.
+//   k_scan         one workgroup: counts = sum of chunk histograms, offsets =
+//                  exclusive scan, and each chunk's base row per expert.
+//   k_scatter      one thread per assignment: row = chunk base + rank.
+// Atomics are used for nothing, so every output is deterministic.
+#include "nvfp4_internal.h"
+
+namespace nvfp4 {
+
+static constexpr int kChunk = 1024;        // assignments per k_chunk_rank workgroup
+static constexpr int kRankThreads = 256;   // 4 waves x 256 assignments
+
+// ------------------------------------------------------------------ routing
+// (v, id) is better than (bv, bid) in the order "larger logit, then lower id"
+__device__ __forceinline__ bool better(float v, int id, float bv, int bid) {
+  return v > bv || (v == bv && id < bid);
+}
+
+__global__ __launch_bounds__(256) void k_route(const float* __restrict__ logits, int T, int E, int k,
+                                               int* __restrict__ topk_ids, float* __restrict__ topk_w) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  const float* row = logits + static_cast<size_t>(t) * E;
+
+  // winners so far: everything strictly better than (last_v, last_id) is taken;
+  // lane j keeps the j-th winner
+  float last_v = __builtin_huge_valf();
+  int last_id = -1;
+  float my_v = 0.0f;
+  int my_id = 0;
+  for (int j = 0; j < k; ++j) {
+    float bv = -__builtin_huge_valf();
+    int bid = 0x7fffffff;
+    for (int i = lane; i < E; i += 64) {
+      const float v = row[i];
+      const bool eligible = v < last_v || (v == last_v && i > last_id);
+      if (eligible && better(v, i, bv, bid)) {
+        bv = v;
+        bid = i;
+      }
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+      const float ov = __shfl_xor(bv, off);
+      const int oid = __shfl_xor(bid, off);
+      if (better(ov, oid, bv, bid)) {
+        bv = ov;
+        bid = oid;
+      }
+    }
+    if (bid < 0 || bid >= E) bid = 0;   // only reachable with non-finite logits
+    last_v = bv;
+    last_id = bid;
+    if (lane == j) {
+      my_v = bv;
+      my_id = bid;
+    }
+  }
+  // weights: exp(l_j - l_max) / sum_i exp(l_i - l_max), in float64; l_max is the
+  // first winner, held by lane 0
+  const double top = static_cast<double>(__shfl(my_v, 0));
+  const double mine = lane < k ? exp(static_cast<double>(my_v) - top) : 0.0;
+  double sum = mine;
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) sum += __shfl_xor(sum, off);
+  if (lane < k) {
+    topk_ids[static_cast<size_t>(t) * k + lane] = my_id;
+    topk_w[static_cast<size_t>(t) * k + lane] = static_cast<float>(mine / sum);
+  }
+}
+
+// ------------------------------------------------------------------ stable ranks
+__device__ __forceinline__ uint64_t ballot64(bool p) { return __ballot(p); }
+
+__global__ __launch_bounds__(kRankThreads) void k_chunk_rank(const int* __restrict__ ids, int n_asg, int E,
+                                                             int nbits, int* __restrict__ local_rank,
+                                                             int* __restrict__ chunk_hist) {
+  extern __shared__ int cnt_sh[];  // [4][E]
+  const int wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  for (int i = threadIdx.x; i < 4 * E; i += kRankThreads) cnt_sh[i] = 0;
+  __syncthreads();
+
+  int* cnt = cnt_sh + wave * E;
+  const int base = blockIdx.x * kChunk + wave * (kChunk / 4);
+  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  int xs[kChunk / 4 / 64];
+#pragma unroll
+  for (int s = 0; s < kChunk / 4 / 64; ++s) {
+    const int f = base + s * 64 + lane;
+    const int id = f < n_asg ? ids[f] : E;
+    const bool valid = id >= 0 && id < E;
+    const int x = valid ? id : E;
+    xs[s] = x;
+    uint64_t peers = ballot64(valid);
+    for (int b = 0; b < nbits; ++b) {
+      const bool bit = (x >> b) & 1;
+      const uint64_t bal = ballot64(bit);
+      peers &= bit ? bal : ~bal;
+    }
+    if (valid) {
+      const int rank_in = __popcll(peers & lt_mask);
+      const int total = __popcll(peers);
+      const int before = cnt[x];
+      local_rank[f] = before + rank_in;
+      // all lanes of the wave read cnt[] in the instruction above; the last lane
+      // of each group of equal ids then advances that expert's counter
+      if (rank_in == total - 1) cnt[x] = before + total;
+    }
+    __builtin_amdgcn_wave_barrier();
+  }
+  __syncthreads();
+  // per expert: exclusive prefix over the 4 waves, and the chunk's histogram
+  for (int e = threadIdx.x; e < E; e += kRankThreads) {
+    int s = 0;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const int c = cnt_sh[w * E + e];
+      cnt_sh[w * E + e] = s;
+      s += c;
+    }
+    chunk_hist[static_cast<size_t>(blockIdx.x) * E + e] = s;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int s = 0; s < kChunk / 4 / 64; ++s) {
+    const int f = base + s * 64 + lane;
+    if (f < n_asg && xs[s] < E) local_rank[f] += cnt_sh[wave * E + xs[s]];
+  }
+}
+
+// ------------------------------------------------------------------ scan
+// One workgroup of 1024 threads.  chunk_hist [nchunks][E] becomes the base row
+// of each (chunk, expert): offsets[e] + number of earlier-chunk assignments.
+__global__ __launch_bounds__(1024) void k_scan(int* __restrict__ chunk_hist, int nchunks, int E,
+                                               int* __restrict__ counts, int* __restrict__ offsets) {
+  __shared__ int part[1024];
+  const int tid = threadIdx.x;
+  const int per = (E + 1023) / 1024;
+  const int e0 = tid * per;
+  int local = 0;
+  for (int e = e0; e < e0 + per && e < E; ++e) {
+    int s = 0;
+    for (int c = 0; c < nchunks; ++c) {
+      int* h = chunk_hist + static_cast<size_t>(c) * E + e;
+      const int v = *h;
+      *h = s;
+      s += v;
+    }
+    counts[e] = s;
+    local += s;
+  }
+  part[tid] = local;
+  __syncthreads();
+  // inclusive Hillis-Steele scan over 1024 partial sums
+  for (int off = 1; off < 1024; off <<= 1) {
+    const int v = tid >= off ? part[tid - off] : 0;
+    __syncthreads();
+    part[tid] += v;
+    __syncthreads();
+  }
+  int run = tid ? part[tid - 1] : 0;
+  for (int e = e0; e < e0 + per && e < E; ++e) {
+    offsets[e] = run;
+    const int c = counts[e];
+    for (int ch = 0; ch < nchunks; ++ch) chunk_hist[static_cast<size_t>(ch) * E + e] += run;
+    run += c;
+  }
+  if (tid == 1023) offsets[E] = part[1023];
+}
+
+// ------------------------------------------------------------------ scatter
+__global__ __launch_bounds__(256) void k_scatter(const int* __restrict__ ids, const float* __restrict__ topk_w,
+                                                 const int* __restrict__ local_rank,
+                                                 const int* __restrict__ chunk_base, int n_asg, int E, int k,
+                                                 int* __restrict__ perm_src_token,
+                                                 int* __restrict__ perm_of_assignment,
+                                                 float* __restrict__ perm_weight) {
+  const int f = blockIdx.x * 256 + threadIdx.x;
+  if (f >= n_asg) return;
+  const int e = min(max(ids[f], 0), E - 1);
+  const int c = f / kChunk;
+  int p = chunk_base[static_cast<size_t>(c) * E + e] + local_rank[f];
+  p = (p >= 0 && p < n_asg) ? p : 0;   // keeps a wrong rank inside the buffers
+  perm_src_token[p] = f / k;
+  perm_of_assignment[f] = p;
+  if (perm_weight) perm_weight[p] = topk_w[f];
+}
+
+// ------------------------------------------------------------------ host side
+size_t route_permute_ws_bytes(int T, int E, int k) {
+  const size_t n = static_cast<size_t>(T) * k;
+  const size_t nchunks = (n + kChunk - 1) / kChunk;
+  const size_t rank = (n * sizeof(int) + 255) & ~size_t(255);
+  const size_t hist = (nchunks * E * sizeof(int) + 255) & ~size_t(255);
+  return rank + hist;
+}
+
+hipError_t launch_route_permute(const float* logits, int T, int E, int k, int* topk_ids, float* topk_w,
+                                int* counts, int* offsets, int* perm_src_token, int* perm_of_assignment,
+                                float* perm_weight, void* ws, hipStream_t stream) {
+  const int n = T * k;
+  const int nchunks = (n + kChunk - 1) / kChunk;
+  int* local_rank = static_cast<int*>(ws);
+  int* chunk_hist = reinterpret_cast<int*>(static_cast<char*>(ws) +
+                                           ((static_cast<size_t>(n) * sizeof(int) + 255) & ~size_t(255)));
+  int nbits = 0;
+  while ((1 << nbits) <= E) ++nbits;   // bits needed for ids 0..E (E is the padding sentinel)
+
+  hipLaunchKernelGGL(k_route, dim3((T + 3) / 4), dim3(256), 0, stream, logits, T, E, k, topk_ids, topk_w);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL(k_chunk_rank, dim3(nchunks), dim3(kRankThreads), 4 * E * sizeof(int), stream, topk_ids,
+                     n, E, nbits, local_rank, chunk_hist);
+  err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL(k_scan, dim3(1), dim3(1024), 0, stream, chunk_hist, nchunks, E, counts, offsets);
+  err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL(k_scatter, dim3((n + 255) / 256), dim3(256), 0, stream, topk_ids, topk_w, local_rank,
+                     chunk_hist, n, E, k, perm_src_token, perm_of_assignment, perm_weight);
+  return hipGetLastError();
+}
+
+}  // namespace nvfp4

@@ -1,0 +1,118 @@
+"""The NVFP4 MoE layer forward, composed from the five C entry points.
+
+route + permute -> quantise x -> gate_up grouped GEMM (rows gathered by token,
+SwiGLU + NVFP4 re-quantisation fused in the epilogue) -> down grouped GEMM
+(weighted scatter-add into a float32 accumulator fused in the epilogue) ->
+accumulator to bfloat16.  ``fused=False`` runs the same math with the
+unfused calls (float32 gate_up output, moe_swiglu, bf16 down output,
+moe_unpermute_combine).
+
+Buffers are allocated once per layer object (torch device memory); a forward
+allocates nothing.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+import torch
+
+from . import (BF16, EPI_BF16, EPI_COMBINE_F32, EPI_F32, EPI_SWIGLU_NVFP4, F32, NVFP4Tensor, Routing, lib,
+               moe_route_permute, moe_swiglu, moe_unpermute_combine, nvfp4_grouped_gemm, nvfp4_quantize)
+
+
+@dataclass
+class ExpertWeights:
+    """Per-expert NVFP4 weights: gate_up [E, 2I, H] and down [E, H, I]."""
+    gu_codes: torch.Tensor
+    gu_scales: torch.Tensor
+    gu_g: torch.Tensor
+    dn_codes: torch.Tensor
+    dn_scales: torch.Tensor
+    dn_g: torch.Tensor
+
+    @property
+    def E(self):
+        return self.gu_codes.shape[0]
+
+    @property
+    def I(self):
+        return self.gu_codes.shape[1] // 2
+
+    @property
+    def H(self):
+        return self.dn_codes.shape[1]
+
+    def nbytes(self) -> int:
+        return sum(t.numel() * t.element_size() for t in
+                   (self.gu_codes, self.gu_scales, self.dn_codes, self.dn_scales))
+
+
+def quantize_expert_weights(w_gu: torch.Tensor, w_dn: torch.Tensor) -> ExpertWeights:
+    """Quantise float32/bf16 weights [E, 2I, H] and [E, H, I] on the GPU with
+    one per-tensor scale per expert matrix (nvfp4_quantize per expert)."""
+    E, I2, H = w_gu.shape
+    dev = w_gu.device
+    out = ExpertWeights(
+        torch.empty((E, I2, H // 2), dtype=torch.uint8, device=dev),
+        torch.empty((E, I2, H // 16), dtype=torch.uint8, device=dev),
+        torch.empty(E, dtype=torch.float32, device=dev),
+        torch.empty((E, H, I2 // 4), dtype=torch.uint8, device=dev),
+        torch.empty((E, H, I2 // 32), dtype=torch.uint8, device=dev),
+        torch.empty(E, dtype=torch.float32, device=dev))
+    ws = torch.empty(lib().nvfp4_quantize_workspace_size(), dtype=torch.uint8, device=dev)
+    for e in range(E):
+        nvfp4_quantize(w_gu[e], out=NVFP4Tensor(out.gu_codes[e], out.gu_scales[e], out.gu_g[e:e + 1]), workspace=ws)
+        nvfp4_quantize(w_dn[e], out=NVFP4Tensor(out.dn_codes[e], out.dn_scales[e], out.dn_g[e:e + 1]), workspace=ws)
+    return out
+
+
+class MoELayer:
+    """Preallocated NVFP4 MoE layer for T tokens."""
+
+    def __init__(self, T: int, H: int, I: int, E: int, k: int, device, fused: bool = True):
+        self.T, self.H, self.I, self.E, self.k = T, H, I, E, k
+        self.fused = fused
+        dev = torch.device(device)
+        i32 = dict(dtype=torch.int32, device=dev)
+        f32 = dict(dtype=torch.float32, device=dev)
+        u8 = dict(dtype=torch.uint8, device=dev)
+        M = T * k
+        self.routing = Routing(torch.empty((T, k), **i32), torch.empty((T, k), **f32), torch.empty(E, **i32),
+                               torch.empty(E + 1, **i32), torch.empty(M, **i32), torch.empty(M, **i32),
+                               torch.empty(M, **f32))
+        self.route_ws = torch.empty(max(16, lib().moe_route_permute_workspace_size(T, E, k)), **u8)
+        self.small_ws = torch.empty(256, **u8)
+        self.xq = NVFP4Tensor(torch.empty((T, H // 2), **u8), torch.empty((T, H // 16), **u8),
+                              torch.empty(1, **f32))
+        self.hq = NVFP4Tensor(torch.empty((M, I // 2), **u8), torch.empty((M, I // 16), **u8),
+                              torch.empty(1, **f32))
+        self.out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+        if fused:
+            self.acc = torch.empty((T, H), **f32)
+        else:
+            self.y1 = torch.empty((M, 2 * I), **f32)
+            self.y2 = torch.empty((M, H), dtype=torch.bfloat16, device=dev)
+
+    def forward(self, logits: torch.Tensor, x: torch.Tensor, w: ExpertWeights, g_h: torch.Tensor,
+                stream=None) -> torch.Tensor:
+        T, k, M = self.T, self.k, self.T * self.k
+        r = moe_route_permute(logits, k, out=self.routing, workspace=self.route_ws, stream=stream)
+        nvfp4_quantize(x, out=self.xq, workspace=self.small_ws, stream=stream)
+        if self.fused:
+            self.hq.g.copy_(g_h)
+            nvfp4_grouped_gemm(self.xq, w.gu_codes, w.gu_scales, w.gu_g, r.offsets, m_total=M,
+                               a_rows=r.perm_src_token, epilogue=EPI_SWIGLU_NVFP4, out_codes=self.hq.codes,
+                               out_scales=self.hq.scales, out_g=self.hq.g, stream=stream)
+            self.acc.zero_()
+            nvfp4_grouped_gemm(self.hq, w.dn_codes, w.dn_scales, w.dn_g, r.offsets, m_total=M,
+                               epilogue=EPI_COMBINE_F32, out=self.acc, out_rows=T, row_token=r.perm_src_token,
+                               row_weight=r.perm_weight, stream=stream)
+            moe_unpermute_combine(self.acc, None, None, T, 1, out=self.out, stream=stream)
+        else:
+            nvfp4_grouped_gemm(self.xq, w.gu_codes, w.gu_scales, w.gu_g, r.offsets, m_total=M,
+                               a_rows=r.perm_src_token, epilogue=EPI_F32, out=self.y1, stream=stream)
+            moe_swiglu(self.y1, g=g_h, out=self.hq, workspace=self.small_ws, stream=stream)
+            nvfp4_grouped_gemm(self.hq, w.dn_codes, w.dn_scales, w.dn_g, r.offsets, m_total=M,
+                               epilogue=EPI_BF16, out=self.y2, stream=stream)
+            moe_unpermute_combine(self.y2, r.perm_of_assignment, r.topk_w, T, k, out=self.out, stream=stream)
+        return self.out

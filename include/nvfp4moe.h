@@ -1,0 +1,188 @@
+/*
+ * nvfp4moe — NVFP4 block-scaled Mixture-of-Experts layer for AMD MI355X (gfx950).
+ *
+ * Plain C ABI.  Every pointer argument is a DEVICE pointer unless stated
+ * otherwise; sizes are host integers.  Every compute call enqueues its kernels
+ * on `stream` (a hipStream_t passed as void*, NULL = the null stream), returns
+ * without synchronising the host, and allocates nothing: the caller owns every
+ * buffer, including workspaces.  The library keeps no pointer past the work it
+ * enqueued and holds no global state, so calls on different streams may run
+ * concurrently (calls that share a workspace or an output must not overlap).
+ *
+ * Number format (the block-scaled MMA described in "From Empirical Limits to
+ * Research-Driven Optimization: The SM120 FP4 Kernel Research Campaign",
+ * section "Section 1: CUTLASS Kernels - The Foundation": E2M1 operands, one
+ * unsigned E4M3 block scale per 16 elements along K, FP32 accumulation), plus a
+ * float32 per-tensor scale:
+ *   codes   uint8 [rows, cols/2]   two E2M1 codes per byte, element 2i in the
+ *                                  low nibble of byte i, row-major, blocks run
+ *                                  along the last (reduction) axis
+ *   scales  uint8 [rows, cols/16]  one E4M3 code per 16-element block
+ *   g       float32 (device)       per-tensor scale; value = E2M1*E4M3*g
+ *
+ * Quantiser (a reading of the pages, which print none):
+ *   g = amax/2688, block scale = E4M3_satfinite((absmax_b/6)/g) (nearest even),
+ *   code = E2M1(x / (scale*g)) (nearest even, saturating at 6, sign copied from
+ *   x, a zero block scale gives code 0).  All decisions in float32 with correctly
+ *   rounded division, so codes are reproducible bit for bit.
+ *
+ * Errors: every call validates its arguments on the host BEFORE enqueuing
+ * anything.  A non-OK status means nothing was enqueued, except
+ * NVFP4MOE_ERR_HIP, which reports a failed kernel launch (earlier kernels of
+ * the same call may have been enqueued).  nvfp4moe_last_error_detail() gives a
+ * thread-local explanation of the last failure on the calling thread.
+ */
+#ifndef NVFP4MOE_H
+#define NVFP4MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum nvfp4moe_status {
+  NVFP4MOE_OK = 0,
+  NVFP4MOE_ERR_INVALID = 1,      /* null pointer, negative/zero size, k > E, K % 32 != 0, misaligned pointer */
+  NVFP4MOE_ERR_UNSUPPORTED = 2,  /* valid request outside what the compiled kernels cover (size limits) */
+  NVFP4MOE_ERR_WORKSPACE = 3,    /* workspace missing or smaller than the *_workspace_size() query */
+  NVFP4MOE_ERR_HIP = 4           /* the HIP runtime rejected a kernel launch */
+} nvfp4moe_status;
+
+typedef enum nvfp4moe_dtype {
+  NVFP4MOE_F32 = 0,
+  NVFP4MOE_BF16 = 1
+} nvfp4moe_dtype;
+
+typedef enum nvfp4moe_epilogue {
+  /* y[p, n] = acc * (g_a * g_b[e]) written as float32 to out[p*N + n], p < m_total */
+  NVFP4MOE_EPI_F32 = 0,
+  /* same, rounded to bfloat16 (nearest even) */
+  NVFP4MOE_EPI_BF16 = 1,
+  /* SwiGLU + NVFP4 re-quantisation of the gate_up output (N = 2I):
+   * h[p, i] = silu(y[p, i]) * y[p, I + i]  (rows [0,I) of each expert's B are the
+   * gate, rows [I,2I) the up projection), quantised with the caller's per-tensor
+   * scale *out_g into out_codes [m_total, I/2] and out_scales [m_total, I/16].
+   * Requires I % 16 == 0. */
+  NVFP4MOE_EPI_SWIGLU_NVFP4 = 2,
+  /* weighted scatter-add (the combine fused into the down GEMM):
+   * out[row_token[p]*N + n] += row_weight[p] * y[p, n]   (float32 atomics;
+   * out is float32 [out_rows, N] and must be zeroed by the caller; the order of
+   * the additions is not fixed, so results may differ in the last bits between
+   * runs). */
+  NVFP4MOE_EPI_COMBINE_F32 = 3
+} nvfp4moe_epilogue;
+
+/* Arguments of nvfp4_grouped_gemm (a struct keeps the ABI stable). */
+typedef struct nvfp4moe_gemm_args {
+  /* A operand: NVFP4 rows (activations). */
+  const uint8_t* a_codes;     /* [a_rows_total, K/2], 16-byte aligned */
+  const uint8_t* a_scales;    /* [a_rows_total, K/16] */
+  const float* a_g;           /* device, 1 float */
+  const int32_t* a_rows;      /* device [m_total]: A row read by GEMM row p, or NULL for row p.
+                                 Every entry must lie in [0, a_rows_total). */
+  int64_t a_rows_total;
+  /* B operand: per-expert NVFP4 weights, row n of expert e is output column n. */
+  const uint8_t* b_codes;     /* [E, N, K/2], 16-byte aligned */
+  const uint8_t* b_scales;    /* [E, N, K/16] */
+  const float* b_g;           /* device [E]: one per-tensor scale per expert */
+  /* grouping: rows [offsets[e], offsets[e+1]) of the GEMM belong to expert e. */
+  const int32_t* offsets;     /* device [E+1], non-decreasing, offsets[0] = 0, offsets[E] <= m_total */
+  int32_t E;
+  int32_t N;                  /* multiple of 16 */
+  int32_t K;                  /* multiple of 32 */
+  int64_t m_total;            /* host-side bound on offsets[E] (rows of out) */
+  int32_t epilogue;           /* nvfp4moe_epilogue */
+  void* out;                  /* EPI_F32: float [m_total, N]; EPI_BF16: bf16 [m_total, N];
+                                 EPI_COMBINE_F32: float [out_rows, N]; unused for SWIGLU */
+  int64_t out_rows;           /* EPI_COMBINE_F32: rows of the accumulator (tokens) */
+  uint8_t* out_codes;         /* EPI_SWIGLU_NVFP4 */
+  uint8_t* out_scales;        /* EPI_SWIGLU_NVFP4 */
+  const float* out_g;         /* EPI_SWIGLU_NVFP4: device, 1 float, > 0 */
+  const int32_t* row_token;   /* EPI_COMBINE_F32: device [m_total], values in [0, out_rows) */
+  const float* row_weight;    /* EPI_COMBINE_F32: device [m_total] */
+  int32_t max_rows_per_expert_hint;  /* 0 = unknown; sizes the grid (the pages' tune_max_num_tokens) */
+} nvfp4moe_gemm_args;
+
+/* ---------------------------------------------------------------- route + permute
+ * Top-k routing and the expert-first permutation ("Discovering SM120-Specific
+ * CUTLASS MoE Kernels", section "Input Knowledge Required": a router picks
+ * experts per token; "From Empirical Limits ...", section "Sections 5-6:
+ * Algorithmic Techniques": expert-first layout, token reordering).
+ *   logits             float32 [T, E]
+ *   topk_ids   (out)   int32 [T, k]   k largest logits by descending value, ties to the lower id
+ *   topk_w     (out)   float32 [T, k] exp(l_j - l_max) / sum over the k chosen (softmax over E,
+ *                                     renormalised over the k), computed in float64
+ *   counts     (out)   int32 [E]      assignments per expert
+ *   offsets    (out)   int32 [E+1]    exclusive prefix sum of counts
+ *   perm_src_token     (out) int32 [T*k]  token of permuted row p
+ *   perm_of_assignment (out) int32 [T*k]  permuted row of assignment t*k+j
+ *   perm_weight        (out, nullable) float32 [T*k]  topk_w of permuted row p
+ * Rows of one expert keep ascending t*k+j (stable): every output is
+ * deterministic and bit-exact.  Limits: 1 <= k <= min(E, 32), E <= 4096,
+ * T*k < 2^30.  Logits must be finite. */
+size_t moe_route_permute_workspace_size(int32_t T, int32_t E, int32_t k);
+int moe_route_permute(const float* logits, int32_t T, int32_t E, int32_t k,
+                      int32_t* topk_ids, float* topk_w, int32_t* counts, int32_t* offsets,
+                      int32_t* perm_src_token, int32_t* perm_of_assignment, float* perm_weight,
+                      void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------- quantise
+ * x [rows, cols] (bf16 or float32, finite) -> NVFP4 codes/scales as described
+ * above.  g_in (device, nullable): a caller-supplied per-tensor scale; NULL
+ * computes g = amax/2688 (1 if the tensor is zero) on the device.  g_out
+ * (device, nullable) receives the scale used.  cols % 32 == 0, x 16-byte
+ * aligned. */
+size_t nvfp4_quantize_workspace_size(void);
+int nvfp4_quantize(const void* x, int32_t x_dtype, int64_t rows, int64_t cols,
+                   const float* g_in, float* g_out, uint8_t* codes, uint8_t* scales,
+                   void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------- grouped GEMM
+ * For expert e and GEMM row p in [offsets[e], offsets[e+1]) with A row
+ * r = a_rows ? a_rows[p] : p:
+ *   y[p, n] = (g_a * g_b[e]) * sum_kb s_a[r,kb] s_b[e,n,kb] sum_{i<16} q_a[r,16kb+i] q_b[e,n,16kb+i]
+ * FP32 accumulation; the block products are formed exactly (E2M1*E4M3 values
+ * are exact in FP16 and their products exact in FP32).  The MoE grouped GEMM of
+ * "From Empirical Limits ...", section "Sections 2-4: Framework and Community
+ * Landscape", with the epilogues listed in nvfp4moe_epilogue (the "finalize"
+ * epilogue of "The Critical Search: Uncovering SM120 CUTLASS Collective
+ * Implementations", section "Context: The Optimization Journey", is
+ * NVFP4MOE_EPI_COMBINE_F32).  Rows p >= offsets[E] are not written.  Experts
+ * with no rows read no weight bytes. */
+int nvfp4_grouped_gemm(const nvfp4moe_gemm_args* args, void* stream);
+
+/* ---------------------------------------------------------------- SwiGLU (unfused)
+ * gate_up [M, 2I] (float32 or bf16) -> h = silu(gate) * up, gate = columns
+ * [0, I), up = [I, 2I), quantised to NVFP4 codes [M, I/2], scales [M, I/16].
+ * g_in (nullable): per-tensor scale of h; NULL computes amax(h)/2688 on the
+ * device (two passes).  g_out (nullable) receives the scale used.  I % 16 == 0. */
+size_t moe_swiglu_workspace_size(void);
+int moe_swiglu(const void* gate_up, int32_t dtype, int64_t M, int32_t I,
+               const float* g_in, float* g_out, uint8_t* codes, uint8_t* scales,
+               void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------- combine (unfused)
+ * out[t, :] = sum_{j<k} topk_w[t, j] * y[perm_of_assignment[t*k + j], :]
+ * ("token reordering with fused reduction", "From Empirical Limits ...", section
+ * "Sections 5-6: Algorithmic Techniques").  y [rows, H] float32 or bf16; out
+ * [T, H] float32 or bf16 (nearest even); float32 accumulation in j order.
+ * perm_of_assignment NULL means row t*k + j; topk_w NULL means weight 1, so
+ * (perm NULL, w NULL, k = 1) converts a float32 accumulator to bf16.
+ * H % 8 == 0. */
+int moe_unpermute_combine(const void* y, int32_t y_dtype, const int32_t* perm_of_assignment,
+                          const float* topk_w, int32_t T, int32_t k, int32_t H,
+                          void* out, int32_t out_dtype, void* stream);
+
+/* ---------------------------------------------------------------- status */
+const char* nvfp4moe_status_string(int status);
+const char* nvfp4moe_last_error_detail(void);
+/* library version: major*10000 + minor*100 + patch */
+int nvfp4moe_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* NVFP4MOE_H */

@@ -1,0 +1,140 @@
+"""Host-side checks of the C ABI (no GPU needed): the library loads, exports every
+function declared in include/*.h, and rejects invalid arguments on the host
+before anything is enqueued (each case below fails validation, so no kernel is
+ever launched here)."""
+import ctypes
+import glob
+import os
+import re
+
+import pytest
+
+import block_scaled_fp4_permute_amd as m
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+FAKE = 1 << 20          # a non-null, 16-byte aligned address that is never dereferenced
+FAKE_MIS = FAKE + 2     # non-null, misaligned
+
+
+def _declared_functions():
+    names = []
+    for h in glob.glob(os.path.join(ROOT, "include", "*.h")):
+        text = open(h).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        for mt in re.finditer(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s*([a-z_][a-z0-9_]*)\s*\(", text, re.M):
+            names.append(mt.group(1))
+    return sorted(set(names))
+
+
+def test_header_declares_the_five_calls():
+    names = _declared_functions()
+    for want in ("moe_route_permute", "nvfp4_quantize", "nvfp4_grouped_gemm", "moe_swiglu",
+                 "moe_unpermute_combine"):
+        assert want in names
+
+
+def test_library_exports_every_declared_symbol():
+    L = m.lib()
+    missing = [n for n in _declared_functions() if not hasattr(L, n)]
+    assert not missing, missing
+
+
+def test_version_and_status_strings():
+    L = m.lib()
+    assert L.nvfp4moe_version() >= 100
+    assert L.nvfp4moe_status_string(0) == b"ok"
+    assert b"workspace" in L.nvfp4moe_status_string(3)
+    assert L.nvfp4moe_status_string(99) == b"unknown status"
+
+
+def _route(T=4, E=8, k=2, logits=FAKE, ws=FAKE, ws_bytes=None):
+    L = m.lib()
+    if ws_bytes is None:
+        ws_bytes = L.moe_route_permute_workspace_size(T, E, k)
+    return L.moe_route_permute(logits, T, E, k, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, ws, ws_bytes, None)
+
+
+def test_route_validation():
+    L = m.lib()
+    assert _route(logits=None) == m.ERR_INVALID
+    assert _route(T=0) == m.ERR_INVALID
+    assert _route(k=9, E=8) == m.ERR_INVALID
+    assert b"k=9" in L.nvfp4moe_last_error_detail()
+    assert _route(k=33, E=64) == m.ERR_UNSUPPORTED
+    assert _route(E=5000, k=2) == m.ERR_UNSUPPORTED
+    assert _route(ws_bytes=4) == m.ERR_WORKSPACE
+    assert _route(ws=None) == m.ERR_WORKSPACE
+    assert L.moe_route_permute_workspace_size(256, 256, 8) >= 256 * 8 * 4 + 2 * 256 * 4
+
+
+def test_quantize_validation():
+    L = m.lib()
+    q = L.nvfp4_quantize
+    assert q(None, m.BF16, 4, 64, None, None, FAKE, FAKE, FAKE, 256, None) == m.ERR_INVALID
+    assert q(FAKE, 7, 4, 64, None, None, FAKE, FAKE, FAKE, 256, None) == m.ERR_INVALID
+    assert q(FAKE, m.BF16, 4, 48, None, None, FAKE, FAKE, FAKE, 256, None) == m.ERR_INVALID
+    assert q(FAKE, m.BF16, 0, 64, None, None, FAKE, FAKE, FAKE, 256, None) == m.ERR_INVALID
+    assert q(FAKE_MIS, m.BF16, 4, 64, None, None, FAKE, FAKE, FAKE, 256, None) == m.ERR_INVALID
+    assert q(FAKE, m.BF16, 4, 64, None, None, FAKE, FAKE, None, 0, None) == m.ERR_WORKSPACE
+    assert q(FAKE, m.F32, 4, 64, None, None, FAKE, FAKE, FAKE, 8, None) == m.ERR_WORKSPACE
+
+
+def _gemm_args(**over):
+    a = m.GemmArgs(a_codes=FAKE, a_scales=FAKE, a_g=FAKE, a_rows=None, a_rows_total=16, b_codes=FAKE,
+                   b_scales=FAKE, b_g=FAKE, offsets=FAKE, E=4, N=64, K=128, m_total=16,
+                   epilogue=m.EPI_F32, out=FAKE, out_rows=0)
+    for k_, v in over.items():
+        setattr(a, k_, v)
+    return a
+
+
+def _gemm(**over):
+    return m.lib().nvfp4_grouped_gemm(ctypes.byref(_gemm_args(**over)), None)
+
+
+def test_gemm_validation():
+    L = m.lib()
+    assert L.nvfp4_grouped_gemm(None, None) == m.ERR_INVALID
+    assert _gemm(K=48) == m.ERR_INVALID
+    assert _gemm(N=24) == m.ERR_INVALID
+    assert _gemm(E=0) == m.ERR_INVALID
+    assert _gemm(b_codes=None) == m.ERR_INVALID
+    assert _gemm(a_codes=FAKE_MIS) == m.ERR_INVALID
+    assert _gemm(epilogue=9) == m.ERR_INVALID
+    assert _gemm(epilogue=m.EPI_SWIGLU_NVFP4, out_codes=FAKE, out_scales=FAKE) == m.ERR_INVALID
+    assert _gemm(epilogue=m.EPI_SWIGLU_NVFP4, N=48, out_codes=FAKE, out_scales=FAKE, out_g=FAKE) == m.ERR_INVALID
+    assert _gemm(epilogue=m.EPI_COMBINE_F32, out_rows=4) == m.ERR_INVALID
+    assert _gemm(E=1 << 16, N=1 << 16) == m.ERR_UNSUPPORTED
+    assert _gemm(m_total=1 << 31) == m.ERR_UNSUPPORTED
+    # an empty problem is valid and enqueues nothing
+    assert _gemm(m_total=0) == m.OK
+
+
+def test_swiglu_and_combine_validation():
+    L = m.lib()
+    assert L.moe_swiglu(FAKE, m.F32, 4, 24, FAKE, None, FAKE, FAKE, None, 0, None) == m.ERR_INVALID
+    assert L.moe_swiglu(FAKE, m.F32, 4, 32, None, None, FAKE, FAKE, None, 0, None) == m.ERR_WORKSPACE
+    assert L.moe_swiglu(None, m.F32, 4, 32, FAKE, None, FAKE, FAKE, None, 0, None) == m.ERR_INVALID
+    c = L.moe_unpermute_combine
+    assert c(FAKE, m.BF16, FAKE, FAKE, 4, 2, 12, FAKE, m.BF16, None) == m.ERR_INVALID
+    assert c(FAKE, 5, FAKE, FAKE, 4, 2, 16, FAKE, m.BF16, None) == m.ERR_INVALID
+    assert c(None, m.BF16, FAKE, FAKE, 4, 2, 16, FAKE, m.BF16, None) == m.ERR_INVALID
+    assert c(FAKE, m.BF16, FAKE, FAKE, 0, 2, 16, FAKE, m.BF16, None) == m.ERR_INVALID
+
+
+def test_binding_has_no_oracle_or_fallback():
+    # the product path must not import the oracle or route through a CPU fallback
+    import sys
+    pkg = os.path.join(ROOT, "block_scaled_fp4_permute_amd")
+    for f in glob.glob(os.path.join(pkg, "*.py")):
+        src = open(f).read()
+        assert "oracle" not in src.replace("no oracle", ""), f
+        assert "import numpy" not in src, f
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    monkeypatch.setattr(m, "_lib", None)
+    monkeypatch.setattr(m, "LIB_PATH", str(tmp_path / "libnvfp4moe.so"))
+    with pytest.raises(ImportError):
+        m.lib()

@@ -1,0 +1,227 @@
+"""GPU parity of the grouped NVFP4 GEMM and its epilogues against the oracle.
+
+Inputs of every GPU stage here come from the seeded generators or from the
+oracle (its quantiser, its previous stage), never from another GPU stage."""
+import numpy as np
+import pytest
+import torch
+
+import block_scaled_fp4_permute_amd as m
+import workloads
+from oracle import moe as OM
+from oracle import quant as OQ
+from tests.gpu_common import DEV, assert_gemm_close, bf16_to_f32, check_requant, down, up
+
+pytestmark = pytest.mark.gpu
+
+
+def _rand_nvfp4(rng, shape_rows, K, scale_lo=0x28, scale_hi=0x48):
+    codes = rng.integers(0, 256, shape_rows + (K // 2,), dtype=np.uint8)
+    scales = rng.integers(scale_lo, scale_hi, shape_rows + (K // 16,), dtype=np.uint8)
+    return codes, scales
+
+
+def _run_gemm(a_codes, a_scales, a_g, b_codes, b_scales, b_g, counts, a_rows=None, epilogue=m.EPI_F32,
+              m_extra=0, hint=0):
+    offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    m_total = int(offsets[-1]) + m_extra
+    a = m.NVFP4Tensor(up(a_codes), up(a_scales), up(np.array([a_g], np.float32)))
+    y = m.nvfp4_grouped_gemm(a, up(b_codes), up(b_scales), up(np.asarray(b_g, np.float32)), up(offsets),
+                             m_total=m_total, a_rows=None if a_rows is None else up(a_rows.astype(np.int32)),
+                             epilogue=epilogue, max_rows_per_expert_hint=hint)
+    torch.cuda.synchronize()
+    return y, offsets
+
+
+GEMM_CASES = [
+    # E, counts, N, K, rows_a, hint
+    (3, [5, 0, 17], 64, 128, 30, 0),
+    (4, [1, 100, 64, 65], 48, 32, 300, 0),
+    (2, [200, 3], 512, 6144, 203, 0),
+    (1, [300], 96, 96, 300, 16),
+    (5, [0, 0, 0, 0, 7], 256, 256, 7, 0),
+    (8, [16, 31, 33, 64, 2, 0, 129, 8], 160, 224, 283, 4),
+]
+
+
+@pytest.mark.parametrize("case", range(len(GEMM_CASES)))
+@pytest.mark.parametrize("gather", [False, True])
+def test_gemm_f32_random(case, gather):
+    E, counts, N, K, rows_a, hint = GEMM_CASES[case]
+    print(f"gemm case {case} gather={gather} E={E} N={N} K={K}", flush=True)
+    rng = np.random.default_rng(100 + case)
+    a_codes, a_scales = _rand_nvfp4(rng, (rows_a,), K)
+    b_codes, b_scales = _rand_nvfp4(rng, (E, N), K)
+    a_g = np.float32(0.0123)
+    b_g = rng.uniform(0.001, 0.01, E).astype(np.float32)
+    M = int(np.sum(counts))
+    a_rows = rng.integers(0, rows_a, M).astype(np.int32) if gather else None
+    if not gather:
+        a_codes, a_scales = a_codes[:max(M, 1)], a_scales[:max(M, 1)]
+    y, offsets = _run_gemm(a_codes, a_scales, a_g, b_codes, b_scales, b_g, counts, a_rows, hint=hint)
+    y_ref, absdot = OM.grouped_gemm(a_codes, a_scales, a_g, b_codes, b_scales, b_g, offsets, a_rows=a_rows)
+    assert_gemm_close(down(y)[:M], y_ref, absdot, what=f"case {case}")
+
+
+def test_gemm_bf16_epilogue_and_untouched_tail_rows():
+    rng = np.random.default_rng(7)
+    E, counts, N, K = 3, [9, 40, 2], 128, 256
+    a_codes, a_scales = _rand_nvfp4(rng, (51,), K)
+    b_codes, b_scales = _rand_nvfp4(rng, (E, N), K)
+    b_g = np.array([0.5, 0.25, 0.125], np.float32)
+    offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    a = m.NVFP4Tensor(up(a_codes), up(a_scales), up(np.array([0.01], np.float32)))
+    out = torch.full((60, N), 7.0, dtype=torch.bfloat16, device=DEV)     # 9 rows past offsets[E]
+    m.nvfp4_grouped_gemm(a, up(b_codes), up(b_scales), up(b_g), up(offsets), m_total=60, epilogue=m.EPI_BF16,
+                         out=out)
+    torch.cuda.synchronize()
+    y_ref, absdot = OM.grouped_gemm(a_codes, a_scales, 0.01, b_codes, b_scales, b_g, offsets)
+    got = bf16_to_f32(out)
+    assert_gemm_close(got[:51], y_ref, absdot, bf16_out=True)
+    assert np.all(got[51:] == 7.0)
+
+
+@pytest.mark.parametrize("K", [32, 4096, 6144])
+def test_gemm_constant_scales_bit_exact(K):
+    # constant block scales and unit per-tensor scales make every FP32 partial
+    # sum exact, so the GPU must reproduce the oracle bit for bit
+    rng = np.random.default_rng(K)
+    E, counts, N = 2, [37, 70], 80
+    M = sum(counts)
+    a_codes = rng.integers(0, 256, (M, K // 2), dtype=np.uint8)
+    b_codes = rng.integers(0, 256, (E, N, K // 2), dtype=np.uint8)
+    a_scales = np.full((M, K // 16), 0x3A, np.uint8)          # 1.25
+    b_scales = np.full((E, N, K // 16), 0x30, np.uint8)       # 0.5
+    y, offsets = _run_gemm(a_codes, a_scales, 1.0, b_codes, b_scales, np.ones(E, np.float32), counts)
+    y_ref, _ = OM.grouped_gemm(a_codes, a_scales, 1.0, b_codes, b_scales, np.ones(E, np.float32), offsets)
+    assert np.array_equal(down(y), y_ref)
+
+
+def test_gemm_single_block_products_exact():
+    # K = 32 with extreme scales: each output is one or two exact block terms
+    rng = np.random.default_rng(3)
+    a_codes, a_scales = _rand_nvfp4(rng, (16,), 32, 0x01, 0x7F)
+    b_codes, b_scales = _rand_nvfp4(rng, (1, 16), 32, 0x01, 0x7F)
+    a_scales[:, 1] = 0                                      # second block contributes nothing
+    y, offsets = _run_gemm(a_codes, a_scales, 1.0, b_codes, b_scales, np.ones(1, np.float32), [16])
+    y_ref, _ = OM.grouped_gemm(a_codes, a_scales, 1.0, b_codes, b_scales, np.ones(1, np.float32), offsets)
+    assert np.array_equal(down(y), y_ref)
+
+
+# ------------------------------------------------------------------ config 0 stages
+def _config0():
+    c = workloads.CONFIGS[0]
+    logits = workloads.logits(c)
+    x = workloads.activations(c)
+    wgu = OM.quantize_experts([workloads.gate_up_weight(c, e) for e in range(c.E)])
+    wdn = OM.quantize_experts([workloads.down_weight(c, e) for e in range(c.E)])
+    ids, w = OM.route(logits, c.k)
+    counts, offsets, src, perm_of, pw = OM.permute(ids, w, c.E)
+    xq = OQ.quantize(x)
+    return c, logits, x, wgu, wdn, ids, w, counts, offsets, src, perm_of, pw, xq
+
+
+def test_config0_gate_up_f32_gathered():
+    c, logits, x, wgu, wdn, ids, w, counts, offsets, src, perm_of, pw, xq = _config0()
+    y, _ = _run_gemm(xq[0], xq[1], xq[2], *wgu, counts, a_rows=src)
+    y_ref, absdot = OM.grouped_gemm(*xq, *wgu, offsets, a_rows=src)
+    assert_gemm_close(down(y), y_ref, absdot)
+
+
+def _swiglu_tol(y1_ref, absdot1):
+    I = y1_ref.shape[1] // 2
+    tol_y = 1e-3 * absdot1 + 1e-6
+    g, u = y1_ref[:, :I].astype(np.float64), y1_ref[:, I:].astype(np.float64)
+    silu = OM.silu(g)
+    h = silu * u
+    return 1.1 * tol_y[:, :I] * np.abs(u) + np.abs(silu) * tol_y[:, I:] + 2.0 ** -20 * np.abs(h) + 1e-7
+
+
+def test_swiglu_unfused_stage():
+    c, logits, x, wgu, wdn, ids, w, counts, offsets, src, perm_of, pw, xq = _config0()
+    y1, _ = OM.grouped_gemm(*xq, *wgu, offsets, a_rows=src)
+    h64 = OM.swiglu(y1)
+    g_h = np.float32(np.abs(h64.astype(np.float32)).max() / np.float32(2688))
+    for dt in (torch.float32, torch.bfloat16):
+        y_in = y1 if dt == torch.float32 else workloads.to_bf16_values(y1)
+        hq = m.moe_swiglu(up(y_in).to(dt), g=up(np.array([g_h], np.float32)))
+        torch.cuda.synchronize()
+        h_ref = OM.swiglu(y_in)
+        check_requant(down(hq.codes), down(hq.scales), h_ref, g_h, 2.0 ** -20 * np.abs(h_ref) + 1e-30,
+                      what=f"moe_swiglu {dt}")
+    # amax computed on the device
+    hq = m.moe_swiglu(up(y1))
+    torch.cuda.synchronize()
+    g_dev = down(hq.g)[0]
+    assert abs(g_dev - g_h) <= 2.0 ** -20 * g_h
+
+
+def test_config0_gate_up_fused_swiglu():
+    c, logits, x, wgu, wdn, ids, w, counts, offsets, src, perm_of, pw, xq = _config0()
+    y1, absdot1 = OM.grouped_gemm(*xq, *wgu, offsets, a_rows=src)
+    h64 = OM.swiglu(y1)
+    g_h = np.float32(np.abs(h64.astype(np.float32)).max() / np.float32(2688))
+    a = m.NVFP4Tensor(up(xq[0]), up(xq[1]), up(np.array([xq[2]], np.float32)))
+    hq = m.nvfp4_grouped_gemm(a, up(wgu[0]), up(wgu[1]), up(wgu[2]), up(offsets), m_total=int(offsets[-1]),
+                              a_rows=up(src), epilogue=m.EPI_SWIGLU_NVFP4, out_g=up(np.array([g_h], np.float32)))
+    torch.cuda.synchronize()
+    check_requant(down(hq.codes), down(hq.scales), h64, g_h, _swiglu_tol(y1, absdot1), max_flip_frac=0.02,
+                  what="fused swiglu")
+
+
+def test_fused_swiglu_exact_accumulation():
+    # constant scales, unit per-tensor scales: y1 is exact on both sides, so
+    # the fused re-quantisation differs from the oracle only through silu's
+    # float32 rounding
+    rng = np.random.default_rng(21)
+    E, counts, I, K = 2, [19, 45], 64, 512
+    M = sum(counts)
+    a_codes = rng.integers(0, 256, (M, K // 2), dtype=np.uint8)
+    b_codes = rng.integers(0, 256, (E, 2 * I, K // 2), dtype=np.uint8)
+    a_scales = np.full((M, K // 16), 0x20, np.uint8)         # 2^-3
+    b_scales = np.full((E, 2 * I, K // 16), 0x28, np.uint8)   # 2^-2
+    offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    y1, _ = OM.grouped_gemm(a_codes, a_scales, 1.0, b_codes, b_scales, np.ones(E, np.float32), offsets)
+    h64 = OM.swiglu(y1)
+    g_h = np.float32(np.abs(h64).max() / 2688)
+    a = m.NVFP4Tensor(up(a_codes), up(a_scales), up(np.ones(1, np.float32)))
+    hq = m.nvfp4_grouped_gemm(a, up(b_codes), up(b_scales), up(np.ones(E, np.float32)), up(offsets), m_total=M,
+                              epilogue=m.EPI_SWIGLU_NVFP4, out_g=up(np.array([g_h], np.float32)))
+    torch.cuda.synchronize()
+    ns, nc = check_requant(down(hq.codes), down(hq.scales), h64, g_h, 2.0 ** -20 * np.abs(h64) + 1e-30,
+                           max_flip_frac=1e-3, what="fused swiglu exact")
+
+
+def test_config0_down_fused_combine_and_unfused_combine():
+    c, logits, x, wgu, wdn, ids, w, counts, offsets, src, perm_of, pw, xq = _config0()
+    y1, _ = OM.grouped_gemm(*xq, *wgu, offsets, a_rows=src)
+    h64 = OM.swiglu(y1)
+    g_h = np.float32(np.abs(h64.astype(np.float32)).max() / np.float32(2688))
+    hq = OQ.quantize(h64.astype(np.float32), g=g_h)
+    y2, absdot2 = OM.grouped_gemm(*hq, *wdn, offsets)
+    out64, out_ref = OM.combine(y2, perm_of, w)
+    # tolerance: weighted GEMM tolerance of the k rows + bf16 rounding of the sum
+    tol_rows = 1e-3 * absdot2 + 1e-6
+    tol = np.einsum("tj,tjh->th", np.abs(w.astype(np.float64)), tol_rows[perm_of.reshape(w.shape)]) \
+        + 2.0 ** -8 * np.abs(out64) + 1e-6
+    # fused: scatter-add epilogue into a float32 accumulator, then to bf16
+    a = m.NVFP4Tensor(up(hq[0]), up(hq[1]), up(np.array([hq[2]], np.float32)))
+    acc = torch.zeros((c.T, c.H), dtype=torch.float32, device=DEV)
+    m.nvfp4_grouped_gemm(a, up(wdn[0]), up(wdn[1]), up(wdn[2]), up(offsets), m_total=int(offsets[-1]),
+                         epilogue=m.EPI_COMBINE_F32, out=acc, out_rows=c.T, row_token=up(src), row_weight=up(pw))
+    out = m.moe_unpermute_combine(acc, None, None, c.T, 1)
+    torch.cuda.synchronize()
+    assert np.all(np.abs(bf16_to_f32(out) - out64) <= tol), "fused combine"
+    # unfused: combine of the oracle's y2 (float32 and bf16 inputs)
+    for dt in (torch.float32, torch.bfloat16):
+        y_in = y2 if dt == torch.float32 else workloads.to_bf16_values(y2)
+        o = m.moe_unpermute_combine(up(y_in).to(dt), up(perm_of), up(w), c.T, c.k)
+        torch.cuda.synchronize()
+        ref64, _ = OM.combine(y_in, perm_of, w)
+        t2 = 2.0 ** -8 * np.abs(ref64) + c.k * 2.0 ** -23 * np.einsum(
+            "tj,tjh->th", np.abs(w.astype(np.float64)), np.abs(y_in.astype(np.float64))[perm_of.reshape(w.shape)]) + 1e-30
+        assert np.all(np.abs(bf16_to_f32(o) - ref64) <= t2), f"unfused combine {dt}"
+    # combine with k = 1, unit weights, identity permutation is exact conversion
+    o = m.moe_unpermute_combine(up(y2), None, None, y2.shape[0], 1, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert np.array_equal(down(o), y2)
