@@ -1,0 +1,258 @@
+#!/usr/bin/env python3
+"""Benchmark of the NVFP4 MoE layer on one MI355X.
+
+One step = one forward of the whole hot path on one batch: route + permute,
+NVFP4 quantisation of the activations, gate_up grouped GEMM with the fused
+SwiGLU + re-quantisation, down grouped GEMM with the fused weighted
+scatter-add, accumulator to bfloat16.  Default workload: the decode MoE at
+16-64 tokens per expert (T=2048, H=6144, I=256, E=256, top-8, Zipf-skewed
+routing), seeded synthetic inputs, weights drawn N(0, 0.02) and quantised to
+NVFP4 on the GPU (untimed).  Two weight copies alternate between steps so the
+256 MB last-level cache cannot serve a step's weights from the previous step.
+
+Prints ONE JSON line: value = touched expert weight bytes (codes + scales of
+both GEMMs, experts that received tokens) per second of layer step, plus the
+layer's TFLOPS, per-stage times, the roofline of the dominant kernel (the
+gate_up GEMM), and the CPU oracle timed on a sample of the same workload.
+
+    python bench.py [--gpus 1] [--steps 50] [--warmup 5] [--workload 2]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense FP16/BF16 MFMA, published
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", type=int, default=2, help="workload index (0..3); 2 is the reported one")
+    ap.add_argument("--unfused", action="store_true", help="unfused SwiGLU / combine calls")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-experts", type=int, default=0, help="experts in the CPU-oracle sample (0: auto)")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device-to-device copy of MIB MiB 5 times (to scale HBM byte counters)")
+    return ap.parse_args()
+
+
+def copy_calibration(mib: int):
+    import torch
+    n = mib * (1 << 20) // 4
+    a = torch.ones(n, dtype=torch.float32, device="cuda:0")
+    b = torch.empty_like(a)
+    for _ in range(5):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes_read": n * 4, "bytes_written": n * 4, "launches": 5}), flush=True)
+
+
+def gemm_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in ("grouped_gemm.hip", "nvfp4_device.h"):
+        with open(os.path.join(ROOT, "block_scaled_fp4_permute_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel: str, workload: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or
+    None if absent or taken on other kernel sources."""
+    p = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(p):
+        return None
+    with open(p) as fh:
+        d = json.load(fh)
+    ent = d.get(f"{kernel}@{workload}")
+    if not ent or ent.get("source_hash") != gemm_source_hash():
+        return None
+    return ent.get("bytes_per_launch")
+
+
+def cpu_baseline(cfg, logits_np, x_np, w_gu_dev, w_dn_dev, g_h, n_experts):
+    """The CPU oracle, as it stands, on a bounded sample of the same workload:
+    routing, permutation and activation quantisation over all T tokens, then for
+    ``n_experts`` experts (those with the lowest ids among the experts that got
+    tokens) gate_up GEMM of their routed rows, SwiGLU + re-quantisation, down
+    GEMM and the weighted combine of their rows.  Expert weights are quantised
+    by the oracle outside the timed region.  Returns the throughput in the
+    benchmark's unit (touched weight bytes per second)."""
+    import numpy as np
+    from oracle import moe as OM
+    from oracle import quant as OQ
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    ids, w = OM.route(logits_np, cfg.k)
+    counts, offsets, src, perm_of, pw = OM.permute(ids, w, cfg.E)
+    experts = [e for e in range(cfg.E) if counts[e] > 0][:n_experts]
+    wq = {}
+    for e in experts:
+        wq[e] = (OQ.quantize(w_gu_dev[e].float().cpu().numpy()), OQ.quantize(w_dn_dev[e].float().cpu().numpy()))
+    t0 = time.perf_counter()
+    ids, w = OM.route(logits_np, cfg.k)
+    counts, offsets, src, perm_of, pw = OM.permute(ids, w, cfg.E)
+    xq = OQ.quantize(x_np)
+    out = np.zeros((cfg.T, cfg.H), np.float64)
+    for e in experts:
+        (gc, gs, gg), (dc, ds, dg) = wq[e]
+        p0, p1 = int(offsets[e]), int(offsets[e + 1])
+        rows = src[p0:p1]
+        off = np.array([0, p1 - p0])
+        y1, _ = OM.grouped_gemm(*xq, gc[None], gs[None], np.array([gg]), off, a_rows=rows, want_absdot=False)
+        hc, hs, hg, _ = OM.swiglu_quantize(y1, g_h)
+        y2, _ = OM.grouped_gemm(hc, hs, hg, dc[None], ds[None], np.array([dg]), off, want_absdot=False)
+        np.add.at(out, rows, pw[p0:p1, None].astype(np.float64) * y2)
+    dt = time.perf_counter() - t0
+    per_expert = 3 * cfg.I * cfg.H * 9 // 16
+    return {"value": round(len(experts) * per_expert / dt / 1e9, 6), "unit": "GB/s", "cores": int(threads),
+            "kind": "oracle", "seconds": round(dt, 3),
+            "sample": f"{len(experts)} of {cfg.E} experts (their {int(sum(counts[e] for e in experts))} routed rows): "
+                      f"gate_up, SwiGLU+requant, down, weighted combine; routing, permutation and "
+                      f"activation quantisation over all {cfg.T} tokens; numpy, float64"}
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}); the layer runs "
+              "unsharded on a single MI355X and multi-GPU runs are not part of this benchmark", file=sys.stderr)
+        sys.exit(2)
+
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return
+
+    import numpy as np
+    import torch
+
+    import workloads
+    from block_scaled_fp4_permute_amd import EPI_F32, lib, moe_route_permute, moe_swiglu, nvfp4_grouped_gemm, \
+        nvfp4_quantize
+    from block_scaled_fp4_permute_amd.layer import MoELayer, quantize_expert_weights
+
+    lib()
+    dev = torch.device("cuda:0")
+    cfg = workloads.CONFIGS[args.workload]
+    assert not cfg.dense, "the layer benchmark runs an MoE workload"
+    T, H, I, E, k = cfg.T, cfg.H, cfg.I, cfg.E, cfg.k
+
+    logits_np = workloads.logits(cfg)
+    x_np = workloads.activations(cfg)
+    logits = torch.from_numpy(logits_np).to(dev)
+    x = torch.from_numpy(x_np).to(dev).to(torch.bfloat16)
+    copies = []
+    w_gu0 = w_dn0 = None
+    for c in range(2):
+        w_gu, w_dn = workloads.torch_expert_weights(cfg, dev, copy=c)
+        copies.append(quantize_expert_weights(w_gu, w_dn).pack())
+        if c == 0:
+            w_gu0, w_dn0 = w_gu, w_dn
+        else:
+            del w_gu, w_dn
+    torch.cuda.synchronize()
+
+    # static calibration of the intermediate's per-tensor scale from one
+    # unfused pass (amax of h computed on the device)
+    r = moe_route_permute(logits, k)
+    xq = nvfp4_quantize(x)
+    y1 = nvfp4_grouped_gemm(xq, copies[0].gu_codes, copies[0].gu_scales, copies[0].gu_g, r.offsets, m_total=T * k,
+                            a_rows=r.perm_src_token, epilogue=EPI_F32)
+    g_h = moe_swiglu(y1).g.clone()
+    counts = r.counts.cpu().numpy()
+    del y1
+    torch.cuda.synchronize()
+
+    layer = MoELayer(T, H, I, E, k, dev, fused=not args.unfused)
+    for i in range(args.warmup):
+        layer.forward(logits, x, copies[i % 2], g_h)
+    torch.cuda.synchronize()
+
+    # ---- timed region: exactly K steps
+    t0 = time.perf_counter()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    for i in range(args.steps):
+        layer.forward(logits, x, copies[i % 2], g_h)
+    ev1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = ev0.elapsed_time(ev1) / args.steps
+
+    # ---- per-stage times (events on the launch stream around each call)
+    marks = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
+    for i in range(args.steps):
+        layer.forward(logits, x, copies[i % 2], g_h, marks=marks[i])
+    torch.cuda.synchronize()
+    names = ["route_permute", "quantize_x", "gate_up_swiglu" if not args.unfused else "gate_up+swiglu",
+             "down_combine" if not args.unfused else "down", "finalize_bf16" if not args.unfused else "combine"]
+    stage_ms = {n: float(np.mean([m[j].elapsed_time(m[j + 1]) for m in marks])) for j, n in enumerate(names)}
+
+    touched = int((counts > 0).sum())
+    gu_bytes_e = 2 * I * H * 9 // 16
+    dn_bytes_e = H * I * 9 // 16
+    weight_bytes = touched * (gu_bytes_e + dn_bytes_e)
+    flops = 2.0 * T * k * 3 * I * H
+    gbs = weight_bytes / (ms_per_step * 1e-3) / 1e9
+    tflops = flops / (ms_per_step * 1e-3) / 1e12
+
+    # dominant kernel: gate_up GEMM.  Algorithmic bytes per launch = touched
+    # gate_up weights + the NVFP4 activations read once + the NVFP4 h written.
+    gu_ms = stage_ms[names[2]]
+    gu_alg = touched * gu_bytes_e + T * H * 9 // 16 + T * k * I * 9 // 16
+    achieved = gu_alg / (gu_ms * 1e-3) / 1e9
+    wl_name = f"decode_moe_T{T}_H{H}_I{I}_E{E}_top{k}_{cfg.routing}"
+    traffic = measured_traffic("gate_up_swiglu", wl_name) if not args.unfused else None
+
+    res = {
+        "metric": "NVFP4 MoE grouped-GEMM TFLOPS & weight GB/s at 16-64 tok/expert, 1 MI355X",
+        "value": round(gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "wall_ms_per_step": round(wall * 1e3 / args.steps, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "nvfp4 operands, f16 mfma, f32 accumulate",
+        "data": "synthetic",
+        "tflops": round(tflops, 3),
+        "tflops_frac_f16_peak": round(tflops / MFMA_F16_PEAK_TFLOPS, 4),
+        "weight_bytes": weight_bytes,
+        "layer_flops": flops,
+        "stage_ms": {k_: round(v, 5) for k_, v in stage_ms.items()},
+        "tokens_per_expert": {"min": int(counts.min()), "median": float(np.median(counts)),
+                              "max": int(counts.max()), "touched_experts": touched},
+        "config": {"workload": wl_name, "T": T, "H": H, "I": I, "E": E, "top_k": k, "routing": cfg.routing,
+                   "fused": not args.unfused, "weight_copies": 2},
+        "roofline": {"kernel": "nvfp4 grouped GEMM gate_up + SwiGLU/requant epilogue", "bound": "hbm",
+                     "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                     "alg_bytes_per_launch": gu_alg, "avg_launch_ms": round(gu_ms, 5)},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        n = args.cpu_experts or (16 if args.workload >= 2 else 24)
+        gh = float(g_h.cpu().numpy()[0])
+        res["cpu_baseline"] = cpu_baseline(cfg, logits_np, x_np, w_gu0, w_dn0, gh, n)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

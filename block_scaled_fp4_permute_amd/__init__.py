@@ -44,6 +44,7 @@ class GemmArgs(ctypes.Structure):
         ("out_codes", ctypes.c_void_p), ("out_scales", ctypes.c_void_p), ("out_g", ctypes.c_void_p),
         ("row_token", ctypes.c_void_p), ("row_weight", ctypes.c_void_p),
         ("max_rows_per_expert_hint", ctypes.c_int32),
+        ("b_packed", ctypes.c_void_p),
     ]
 
 
@@ -57,6 +58,9 @@ _SIGNATURES = {
     "nvfp4_quantize": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_int64]
                        + [ctypes.c_void_p] * 5 + [ctypes.c_size_t, ctypes.c_void_p]),
     "nvfp4_grouped_gemm": (ctypes.c_int, [ctypes.POINTER(GemmArgs), ctypes.c_void_p]),
+    "nvfp4_weight_packed_size": (ctypes.c_size_t, [ctypes.c_int32] * 3),
+    "nvfp4_weight_repack": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
+                                           ctypes.c_int32, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
     "moe_swiglu_workspace_size": (ctypes.c_size_t, []),
     "moe_swiglu": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_int32]
                    + [ctypes.c_void_p] * 5 + [ctypes.c_size_t, ctypes.c_void_p]),
@@ -185,20 +189,43 @@ def nvfp4_quantize(x, g=None, out: NVFP4Tensor | None = None, workspace=None, st
     return out
 
 
+# ------------------------------------------------------------------ packed weights
+def nvfp4_weight_repack(codes, scales, out=None, stream=None):
+    """Row-major NVFP4 weights codes uint8 [E, N, K/2], scales uint8 [E, N, K/16]
+    -> packed tile layout (uint8 tensor) read by nvfp4_grouped_gemm(b_packed=...)."""
+    import torch
+    _need(codes, torch.uint8, "codes")
+    _need(scales, torch.uint8, "scales")
+    E, N, K2 = codes.shape
+    nbytes = lib().nvfp4_weight_packed_size(E, N, 2 * K2)
+    if out is None:
+        out = torch.empty(nbytes, dtype=torch.uint8, device=codes.device)
+    _check(lib().nvfp4_weight_repack(codes.data_ptr(), scales.data_ptr(), E, N, 2 * K2, out.data_ptr(),
+                                     out.numel(), _stream(stream)))
+    return out
+
+
 # ---------------------------------------------------------------------------- gemm
 def nvfp4_grouped_gemm(a: NVFP4Tensor, b_codes, b_scales, b_g, offsets, *, m_total: int, a_rows=None,
                        epilogue: int = EPI_F32, out=None, out_rows: int = 0, out_codes=None,
                        out_scales=None, out_g=None, row_token=None, row_weight=None,
-                       max_rows_per_expert_hint: int = 0, stream=None):
+                       max_rows_per_expert_hint: int = 0, b_packed=None, stream=None):
     """Grouped NVFP4 GEMM (see include/nvfp4moe.h).  b_codes uint8 [E, N, K/2],
-    b_scales uint8 [E, N, K/16], b_g float32 [E], offsets int32 [E+1] (device)."""
+    b_scales uint8 [E, N, K/16], b_g float32 [E], offsets int32 [E+1] (device).
+    With b_packed (from nvfp4_weight_repack), b_codes/b_scales give only the
+    shapes (they may be meta or empty-strided tensors) and are not read."""
     import torch
     E, N, K2 = b_codes.shape
     K = 2 * K2
     _need(a.codes, torch.uint8, "a.codes")
     _need(a.scales, torch.uint8, "a.scales")
-    _need(b_codes, torch.uint8, "b_codes")
-    _need(b_scales, torch.uint8, "b_scales")
+    if b_packed is None:
+        _need(b_codes, torch.uint8, "b_codes")
+        _need(b_scales, torch.uint8, "b_scales")
+    else:
+        _need(b_packed, torch.uint8, "b_packed")
+        if b_packed.numel() < lib().nvfp4_weight_packed_size(E, N, K):
+            raise ValueError("b_packed is smaller than the packed size of [E, N, K]")
     _need(b_g, torch.float32, "b_g")
     _need(offsets, torch.int32, "offsets")
     if a.codes.shape[1] != K2 or tuple(b_scales.shape) != (E, N, K // 16):
@@ -214,7 +241,9 @@ def nvfp4_grouped_gemm(a: NVFP4Tensor, b_codes, b_scales, b_g, offsets, *, m_tot
         out_scales = torch.empty((m_total, I // 16), dtype=torch.uint8, device=dev)
     args = GemmArgs(
         a_codes=a.codes.data_ptr(), a_scales=a.scales.data_ptr(), a_g=a.g.data_ptr(), a_rows=_ptr(a_rows),
-        a_rows_total=a.codes.shape[0], b_codes=b_codes.data_ptr(), b_scales=b_scales.data_ptr(),
+        a_rows_total=a.codes.shape[0],
+        b_codes=None if b_packed is not None else b_codes.data_ptr(),
+        b_scales=None if b_packed is not None else b_scales.data_ptr(), b_packed=_ptr(b_packed),
         b_g=b_g.data_ptr(), offsets=offsets.data_ptr(), E=E, N=N, K=K, m_total=m_total, epilogue=epilogue,
         out=_ptr(out), out_rows=out_rows, out_codes=_ptr(out_codes), out_scales=_ptr(out_scales),
         out_g=_ptr(out_g), row_token=_ptr(row_token), row_weight=_ptr(row_weight),
@@ -262,6 +291,6 @@ def moe_unpermute_combine(y, perm_of_assignment, topk_w, T: int, k: int, out=Non
     return out
 
 
-__all__ = ["lib", "moe_route_permute", "nvfp4_quantize", "nvfp4_grouped_gemm", "moe_swiglu",
+__all__ = ["lib", "moe_route_permute", "nvfp4_quantize", "nvfp4_grouped_gemm", "moe_swiglu", "nvfp4_weight_repack",
            "moe_unpermute_combine", "NVFP4Tensor", "Routing", "GemmArgs", "NVFP4MoEError",
            "F32", "BF16", "EPI_F32", "EPI_BF16", "EPI_SWIGLU_NVFP4", "EPI_COMBINE_F32"]

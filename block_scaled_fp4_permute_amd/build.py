@@ -24,6 +24,8 @@ HIPCC_FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-fPIC", "-std=c++17",
     # no packed-FP32 instructions in generated code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA accumulators live in ordinary VGPRs (no AGPR copies around loops)
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-Wall", "-Wno-unused-function", "-Wno-unused-variable",
     "-I", os.path.join(ROOT, "include"),
 ]

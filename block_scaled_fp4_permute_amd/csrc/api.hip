@@ -30,7 +30,7 @@ int hip_status(hipError_t err, const char* what) {
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
-constexpr size_t kSmallWs = 256;
+constexpr size_t kSmallWs = 4096;   // 1024 partial maxima of the amax reduction
 
 }  // namespace
 
@@ -49,7 +49,7 @@ const char* nvfp4moe_status_string(int status) {
 
 const char* nvfp4moe_last_error_detail(void) { return g_detail; }
 
-int nvfp4moe_version(void) { return 100; }
+int nvfp4moe_version(void) { return 101; }
 
 // ------------------------------------------------------------------ route + permute
 size_t moe_route_permute_workspace_size(int32_t T, int32_t E, int32_t k) {
@@ -100,14 +100,17 @@ int nvfp4_quantize(const void* x, int32_t x_dtype, int64_t rows, int64_t cols, c
 // ------------------------------------------------------------------ grouped GEMM
 int nvfp4_grouped_gemm(const nvfp4moe_gemm_args* a, void* stream) {
   if (!a) return fail(NVFP4MOE_ERR_INVALID, "nvfp4_grouped_gemm: args is NULL");
-  if (!a->a_codes || !a->a_scales || !a->a_g || !a->b_codes || !a->b_scales || !a->b_g || !a->offsets)
+  if (!a->a_codes || !a->a_scales || !a->a_g || !a->b_g || !a->offsets)
     return fail(NVFP4MOE_ERR_INVALID, "nvfp4_grouped_gemm: null operand pointer");
+  if (!a->b_packed && (!a->b_codes || !a->b_scales))
+    return fail(NVFP4MOE_ERR_INVALID, "nvfp4_grouped_gemm: B needs b_codes and b_scales, or b_packed");
   if (a->E <= 0 || a->N <= 0 || a->K <= 0 || a->m_total < 0 || a->a_rows_total <= 0)
     return fail(NVFP4MOE_ERR_INVALID, "nvfp4_grouped_gemm: E, N, K, a_rows_total must be > 0 and m_total >= 0");
   if (a->K % 32 != 0) return fail(NVFP4MOE_ERR_INVALID, "nvfp4_grouped_gemm: K=%d not a multiple of 32", a->K);
   if (a->N % 16 != 0) return fail(NVFP4MOE_ERR_INVALID, "nvfp4_grouped_gemm: N=%d not a multiple of 16", a->N);
-  if (!aligned(a->a_codes, 16) || !aligned(a->b_codes, 16) || !aligned(a->a_scales, 2) || !aligned(a->b_scales, 2))
-    return fail(NVFP4MOE_ERR_INVALID, "nvfp4_grouped_gemm: codes must be 16-byte and scales 2-byte aligned");
+  if (!aligned(a->a_codes, 16) || !aligned(a->a_scales, 2) || !aligned(a->b_packed, 16) ||
+      (!a->b_packed && (!aligned(a->b_codes, 16) || !aligned(a->b_scales, 2))))
+    return fail(NVFP4MOE_ERR_INVALID, "nvfp4_grouped_gemm: codes and packed tiles must be 16-byte, scales 2-byte aligned");
   if (a->m_total >= (int64_t(1) << 31) || a->a_rows_total >= (int64_t(1) << 31))
     return fail(NVFP4MOE_ERR_UNSUPPORTED, "nvfp4_grouped_gemm: more than 2^31 rows");
   if (static_cast<int64_t>(a->E) * a->N >= (int64_t(1) << 31))
@@ -138,6 +141,7 @@ int nvfp4_grouped_gemm(const nvfp4moe_gemm_args* a, void* stream) {
   prm.a_rows = a->a_rows;
   prm.b_codes = a->b_codes;
   prm.b_scales = a->b_scales;
+  prm.b_packed = a->b_packed;
   prm.b_g = a->b_g;
   prm.offsets = a->offsets;
   prm.E = a->E;
@@ -155,6 +159,27 @@ int nvfp4_grouped_gemm(const nvfp4moe_gemm_args* a, void* stream) {
   return hip_status(nvfp4::launch_grouped_gemm(prm, a->epilogue, a->m_total, a->max_rows_per_expert_hint,
                                                static_cast<hipStream_t>(stream)),
                     "nvfp4_grouped_gemm");
+}
+
+// ------------------------------------------------------------------ packed weights
+size_t nvfp4_weight_packed_size(int32_t E, int32_t N, int32_t K) {
+  if (E <= 0 || N <= 0 || K <= 0) return 0;
+  return nvfp4::packed_weight_bytes(E, N, K);
+}
+
+int nvfp4_weight_repack(const uint8_t* codes, const uint8_t* scales, int32_t E, int32_t N, int32_t K,
+                        uint8_t* packed, size_t packed_bytes, void* stream) {
+  if (!codes || !scales || !packed) return fail(NVFP4MOE_ERR_INVALID, "nvfp4_weight_repack: null pointer argument");
+  if (E <= 0 || N <= 0 || K <= 0) return fail(NVFP4MOE_ERR_INVALID, "nvfp4_weight_repack: E, N, K must be > 0");
+  if (K % 32 != 0) return fail(NVFP4MOE_ERR_INVALID, "nvfp4_weight_repack: K=%d not a multiple of 32", K);
+  if (!aligned(codes, 16) || !aligned(packed, 16))
+    return fail(NVFP4MOE_ERR_INVALID, "nvfp4_weight_repack: codes and packed must be 16-byte aligned");
+  if (static_cast<int64_t>(E) * N >= (int64_t(1) << 31)) return fail(NVFP4MOE_ERR_UNSUPPORTED, "nvfp4_weight_repack: E*N >= 2^31");
+  const size_t need = nvfp4::packed_weight_bytes(E, N, K);
+  if (packed_bytes < need)
+    return fail(NVFP4MOE_ERR_WORKSPACE, "nvfp4_weight_repack: packed buffer %zu < %zu bytes", packed_bytes, need);
+  return hip_status(nvfp4::launch_repack(codes, scales, E, N, K, packed, static_cast<hipStream_t>(stream)),
+                    "nvfp4_weight_repack");
 }
 
 // ------------------------------------------------------------------ SwiGLU

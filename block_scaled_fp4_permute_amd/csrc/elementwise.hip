@@ -7,11 +7,6 @@
 namespace nvfp4 {
 
 // ------------------------------------------------------------------ helpers
-__global__ void k_zero_u32(uint32_t* p, int n) {
-  const int i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < n) p[i] = 0u;
-}
-
 template <int DT>
 __device__ __forceinline__ void load16(const void* base, size_t elem0, float (&x)[16]) {
   if constexpr (DT == 1) {  // bf16: 32 bytes
@@ -36,17 +31,44 @@ __device__ __forceinline__ void load16(const void* base, size_t elem0, float (&x
   }
 }
 
-__device__ __forceinline__ void wave_atomic_max(uint32_t* dst, float v) {
-  // non-negative floats order like their bit patterns
+// Global absolute maximum in two deterministic levels: k_*_amax writes one
+// partial maximum per workgroup (no atomics), and every workgroup of the
+// encoder reduces the partials before it computes g.
+static constexpr int kAmaxBlocks = 1024;
+
+__device__ __forceinline__ void block_max_store(float v, float* partial) {
+  __shared__ float s_red[4];
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
-  if ((threadIdx.x & 63) == 0) atomicMax(dst, __float_as_uint(v));
+  if ((threadIdx.x & 63) == 0) s_red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  if (threadIdx.x == 0) partial[blockIdx.x] = fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
+}
+
+// per-tensor scale from the partial maxima (or the caller's scale)
+__device__ __forceinline__ float reduce_scale(const float* g_in, const float* partial, int nparts) {
+  if (g_in) return *g_in;
+  __shared__ float s_g;
+  if (threadIdx.x < 64) {
+    float m = 0.0f;
+    for (int i = threadIdx.x; i < nparts; i += 64) m = fmaxf(m, partial[i]);
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+    if (threadIdx.x == 0) s_g = global_scale_from_amax(m);
+  }
+  __syncthreads();
+  return s_g;
+}
+
+static int amax_grid(int64_t nblocks) {
+  const int64_t want = (nblocks + 255) / 256;
+  return static_cast<int>(want < kAmaxBlocks ? (want > 0 ? want : 1) : kAmaxBlocks);
 }
 
 // ------------------------------------------------------------------ quantise
 template <int DT>
 __global__ __launch_bounds__(256) void k_amax_blocks(const void* __restrict__ x, int64_t nblocks,
-                                                     uint32_t* __restrict__ amax_bits) {
+                                                     float* __restrict__ partial) {
   float m = 0.0f;
   for (int64_t b = blockIdx.x * 256ll + threadIdx.x; b < nblocks; b += static_cast<int64_t>(gridDim.x) * 256) {
     float v[16];
@@ -54,16 +76,16 @@ __global__ __launch_bounds__(256) void k_amax_blocks(const void* __restrict__ x,
 #pragma unroll
     for (int i = 0; i < 16; ++i) m = fmaxf(m, fabsf(v[i]));
   }
-  wave_atomic_max(amax_bits, m);
+  block_max_store(m, partial);
 }
 
 template <int DT>
 __global__ __launch_bounds__(256) void k_quantize(const void* __restrict__ x, int64_t nblocks,
                                                   const float* __restrict__ g_in,
-                                                  const uint32_t* __restrict__ amax_bits,
+                                                  const float* __restrict__ partial, int nparts,
                                                   float* __restrict__ g_out, uint8_t* __restrict__ codes,
                                                   uint8_t* __restrict__ scales) {
-  const float g = g_in ? *g_in : global_scale_from_amax(__uint_as_float(*amax_bits));
+  const float g = reduce_scale(g_in, partial, nparts);
   const int64_t b = blockIdx.x * 256ll + threadIdx.x;
   if (b == 0 && g_out) *g_out = g;
   if (b >= nblocks) return;
@@ -78,21 +100,21 @@ __global__ __launch_bounds__(256) void k_quantize(const void* __restrict__ x, in
 hipError_t launch_quantize(const void* x, int dtype, int64_t rows, int64_t cols, const float* g_in, float* g_out,
                            uint8_t* codes, uint8_t* scales, void* ws, hipStream_t stream) {
   const int64_t nblocks = rows * (cols / 16);
-  uint32_t* amax_bits = static_cast<uint32_t*>(ws);
+  float* partial = static_cast<float*>(ws);
+  const int nparts = g_in ? 0 : amax_grid(nblocks);
   if (!g_in) {
-    hipLaunchKernelGGL(k_zero_u32, dim3(1), dim3(64), 0, stream, amax_bits, 1);
-    const int64_t want = (nblocks + 255) / 256;
-    const int grid = static_cast<int>(want < 2048 ? (want > 0 ? want : 1) : 2048);
     if (dtype == 1)
-      hipLaunchKernelGGL(k_amax_blocks<1>, dim3(grid), dim3(256), 0, stream, x, nblocks, amax_bits);
+      hipLaunchKernelGGL(k_amax_blocks<1>, dim3(nparts), dim3(256), 0, stream, x, nblocks, partial);
     else
-      hipLaunchKernelGGL(k_amax_blocks<0>, dim3(grid), dim3(256), 0, stream, x, nblocks, amax_bits);
+      hipLaunchKernelGGL(k_amax_blocks<0>, dim3(nparts), dim3(256), 0, stream, x, nblocks, partial);
   }
   const dim3 grid(static_cast<unsigned>((nblocks + 255) / 256 > 0 ? (nblocks + 255) / 256 : 1));
   if (dtype == 1)
-    hipLaunchKernelGGL(k_quantize<1>, grid, dim3(256), 0, stream, x, nblocks, g_in, amax_bits, g_out, codes, scales);
+    hipLaunchKernelGGL(k_quantize<1>, grid, dim3(256), 0, stream, x, nblocks, g_in, partial, nparts, g_out, codes,
+                       scales);
   else
-    hipLaunchKernelGGL(k_quantize<0>, grid, dim3(256), 0, stream, x, nblocks, g_in, amax_bits, g_out, codes, scales);
+    hipLaunchKernelGGL(k_quantize<0>, grid, dim3(256), 0, stream, x, nblocks, g_in, partial, nparts, g_out, codes,
+                       scales);
   return hipGetLastError();
 }
 
@@ -114,7 +136,7 @@ __device__ __forceinline__ void swiglu_block(const void* y, int64_t b, int I, fl
 
 template <int DT>
 __global__ __launch_bounds__(256) void k_swiglu_amax(const void* __restrict__ y, int64_t nblocks, int I,
-                                                     uint32_t* __restrict__ amax_bits) {
+                                                     float* __restrict__ partial) {
   float m = 0.0f;
   for (int64_t b = blockIdx.x * 256ll + threadIdx.x; b < nblocks; b += static_cast<int64_t>(gridDim.x) * 256) {
     float h[16];
@@ -122,16 +144,16 @@ __global__ __launch_bounds__(256) void k_swiglu_amax(const void* __restrict__ y,
 #pragma unroll
     for (int i = 0; i < 16; ++i) m = fmaxf(m, fabsf(h[i]));
   }
-  wave_atomic_max(amax_bits, m);
+  block_max_store(m, partial);
 }
 
 template <int DT>
 __global__ __launch_bounds__(256) void k_swiglu_quant(const void* __restrict__ y, int64_t nblocks, int I,
                                                       const float* __restrict__ g_in,
-                                                      const uint32_t* __restrict__ amax_bits,
+                                                      const float* __restrict__ partial, int nparts,
                                                       float* __restrict__ g_out, uint8_t* __restrict__ codes,
                                                       uint8_t* __restrict__ scales) {
-  const float g = g_in ? *g_in : global_scale_from_amax(__uint_as_float(*amax_bits));
+  const float g = reduce_scale(g_in, partial, nparts);
   const int64_t b = blockIdx.x * 256ll + threadIdx.x;
   if (b == 0 && g_out) *g_out = g;
   if (b >= nblocks) return;
@@ -146,22 +168,20 @@ __global__ __launch_bounds__(256) void k_swiglu_quant(const void* __restrict__ y
 hipError_t launch_swiglu(const void* y, int dtype, int64_t M, int I, const float* g_in, float* g_out,
                          uint8_t* codes, uint8_t* scales, void* ws, hipStream_t stream) {
   const int64_t nblocks = M * (I / 16);
-  uint32_t* amax_bits = static_cast<uint32_t*>(ws);
+  float* partial = static_cast<float*>(ws);
+  const int nparts = g_in ? 0 : amax_grid(nblocks);
   if (!g_in) {
-    hipLaunchKernelGGL(k_zero_u32, dim3(1), dim3(64), 0, stream, amax_bits, 1);
-    const int64_t want = (nblocks + 255) / 256;
-    const int grid = static_cast<int>(want < 2048 ? (want > 0 ? want : 1) : 2048);
     if (dtype == 1)
-      hipLaunchKernelGGL(k_swiglu_amax<1>, dim3(grid), dim3(256), 0, stream, y, nblocks, I, amax_bits);
+      hipLaunchKernelGGL(k_swiglu_amax<1>, dim3(nparts), dim3(256), 0, stream, y, nblocks, I, partial);
     else
-      hipLaunchKernelGGL(k_swiglu_amax<0>, dim3(grid), dim3(256), 0, stream, y, nblocks, I, amax_bits);
+      hipLaunchKernelGGL(k_swiglu_amax<0>, dim3(nparts), dim3(256), 0, stream, y, nblocks, I, partial);
   }
   const dim3 grid(static_cast<unsigned>((nblocks + 255) / 256 > 0 ? (nblocks + 255) / 256 : 1));
   if (dtype == 1)
-    hipLaunchKernelGGL(k_swiglu_quant<1>, grid, dim3(256), 0, stream, y, nblocks, I, g_in, amax_bits, g_out,
+    hipLaunchKernelGGL(k_swiglu_quant<1>, grid, dim3(256), 0, stream, y, nblocks, I, g_in, partial, nparts, g_out,
                        codes, scales);
   else
-    hipLaunchKernelGGL(k_swiglu_quant<0>, grid, dim3(256), 0, stream, y, nblocks, I, g_in, amax_bits, g_out,
+    hipLaunchKernelGGL(k_swiglu_quant<0>, grid, dim3(256), 0, stream, y, nblocks, I, g_in, partial, nparts, g_out,
                        codes, scales);
   return hipGetLastError();
 }

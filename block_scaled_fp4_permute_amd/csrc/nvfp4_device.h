@@ -111,18 +111,25 @@ __device__ __forceinline__ uint32_t encode_one(float x, uint32_t s, float scale_
 }
 
 // ------------------------------------------------------------------ decode to FP16
+// E4M3 (bias 7) and FP16 (bias 15) subnormals line up, so the E4M3 code shifted
+// into the FP16 exponent/mantissa position is the FP16 bit pattern of
+// scale * 2^-8 for every code (subnormal codes land on FP16 subnormals).
+__device__ __forceinline__ _Float16 e4m3_to_f16_div256(uint32_t code) {
+  return __builtin_bit_cast(_Float16, static_cast<uint16_t>((code & 0x7Fu) << 7));
+}
+
 // Eight E2M1 codes (one 32-bit word, element 2i in the low nibble of byte i)
-// -> eight FP16 values multiplied by the block scale.  E2M1 * E4M3 needs at
-// most 6 significant bits and lies in [2^-10, 2688], so the FP16 result is
-// exact.  The hardware conversion runs with a unit scale (exact E2M1 values
-// whatever the scale operand's semantics) and the block scale is applied with a
-// packed FP16 multiply.
-__device__ __forceinline__ half8 decode8_f16(uint32_t w, _Float16 scale) {
-  const half2v sc = {scale, scale};
-  half2v p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0);
-  half2v p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1);
-  half2v p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2);
-  half2v p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3);
+// -> eight FP16 values multiplied by the block scale.  The hardware conversion
+// applies the exponent of its scale operand, so 256 is exact and yields
+// E2M1 * 256; one packed FP16 multiply by scale * 2^-8 then gives E2M1 * scale.
+// E2M1 * E4M3 needs at most 6 significant bits and lies in [2^-10, 2688], so
+// every result is an exact, normal FP16 value.
+__device__ __forceinline__ half8 decode8_f16(uint32_t w, _Float16 scale_div256) {
+  const half2v sc = {scale_div256, scale_div256};
+  half2v p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 256.0f, 0);
+  half2v p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 256.0f, 1);
+  half2v p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 256.0f, 2);
+  half2v p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 256.0f, 3);
   p0 *= sc;
   p1 *= sc;
   p2 *= sc;
@@ -131,10 +138,6 @@ __device__ __forceinline__ half8 decode8_f16(uint32_t w, _Float16 scale) {
   r[0] = p0[0]; r[1] = p0[1]; r[2] = p1[0]; r[3] = p1[1];
   r[4] = p2[0]; r[5] = p2[1]; r[6] = p3[0]; r[7] = p3[1];
   return r;
-}
-
-__device__ __forceinline__ _Float16 e4m3_to_f16(uint32_t code) {
-  return static_cast<_Float16>(e4m3_to_f32(code));   // exact: E4M3 fits FP16
 }
 
 // ------------------------------------------------------------------ misc

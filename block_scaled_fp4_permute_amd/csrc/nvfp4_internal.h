@@ -18,6 +18,7 @@ struct GemmParams {
   const int32_t* a_rows;
   const uint8_t* b_codes;
   const uint8_t* b_scales;
+  const uint8_t* b_packed;   // packed weight tiles (nvfp4_weight_repack) or nullptr
   const float* b_g;
   const int32_t* offsets;
   int E, N, K;
@@ -43,6 +44,9 @@ hipError_t launch_swiglu(const void* y, int dtype, int64_t M, int I, const float
                          uint8_t* codes, uint8_t* scales, void* ws, hipStream_t stream);
 hipError_t launch_combine(const void* y, int y_dtype, const int* perm, const float* w, int T, int k, int H,
                           void* out, int out_dtype, hipStream_t stream);
+size_t packed_weight_bytes(int E, int N, int K);
+hipError_t launch_repack(const uint8_t* codes, const uint8_t* scales, int E, int N, int K, uint8_t* packed,
+                         hipStream_t stream);
 hipError_t launch_grouped_gemm(const GemmParams& prm, int epilogue, int64_t m_total, int hint, hipStream_t stream);
 
 }  // namespace nvfp4

@@ -17,7 +17,8 @@ from dataclasses import dataclass
 import torch
 
 from . import (BF16, EPI_BF16, EPI_COMBINE_F32, EPI_F32, EPI_SWIGLU_NVFP4, F32, NVFP4Tensor, Routing, lib,
-               moe_route_permute, moe_swiglu, moe_unpermute_combine, nvfp4_grouped_gemm, nvfp4_quantize)
+               moe_route_permute, moe_swiglu, moe_unpermute_combine, nvfp4_grouped_gemm, nvfp4_quantize,
+               nvfp4_weight_repack)
 
 
 @dataclass
@@ -29,6 +30,14 @@ class ExpertWeights:
     dn_codes: torch.Tensor
     dn_scales: torch.Tensor
     dn_g: torch.Tensor
+    gu_packed: torch.Tensor | None = None    # tile layout from nvfp4_weight_repack
+    dn_packed: torch.Tensor | None = None
+
+    def pack(self) -> "ExpertWeights":
+        """Repack both matrices into the GEMM's streaming tile layout (once, offline)."""
+        self.gu_packed = nvfp4_weight_repack(self.gu_codes, self.gu_scales)
+        self.dn_packed = nvfp4_weight_repack(self.dn_codes, self.dn_scales)
+        return self
 
     @property
     def E(self):
@@ -81,11 +90,10 @@ class MoELayer:
                                torch.empty(E + 1, **i32), torch.empty(M, **i32), torch.empty(M, **i32),
                                torch.empty(M, **f32))
         self.route_ws = torch.empty(max(16, lib().moe_route_permute_workspace_size(T, E, k)), **u8)
-        self.small_ws = torch.empty(256, **u8)
+        self.small_ws = torch.empty(lib().nvfp4_quantize_workspace_size(), **u8)
         self.xq = NVFP4Tensor(torch.empty((T, H // 2), **u8), torch.empty((T, H // 16), **u8),
                               torch.empty(1, **f32))
-        self.hq = NVFP4Tensor(torch.empty((M, I // 2), **u8), torch.empty((M, I // 16), **u8),
-                              torch.empty(1, **f32))
+        self.hq = NVFP4Tensor(torch.empty((M, I // 2), **u8), torch.empty((M, I // 16), **u8), None)
         self.out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
         if fused:
             self.acc = torch.empty((T, H), **f32)
@@ -94,25 +102,42 @@ class MoELayer:
             self.y2 = torch.empty((M, H), dtype=torch.bfloat16, device=dev)
 
     def forward(self, logits: torch.Tensor, x: torch.Tensor, w: ExpertWeights, g_h: torch.Tensor,
-                stream=None) -> torch.Tensor:
+                stream=None, marks=None) -> torch.Tensor:
+        """One layer step.  ``marks``: optional list of 6 torch.cuda.Event that are
+        recorded before routing and after each stage (route+permute, quantise x,
+        gate_up, down, to-bf16/combine) on the launch stream."""
         T, k, M = self.T, self.k, self.T * self.k
+        hq = NVFP4Tensor(self.hq.codes, self.hq.scales, g_h)
+
+        def mark(i):
+            if marks is not None:
+                marks[i].record(stream)
+
+        mark(0)
         r = moe_route_permute(logits, k, out=self.routing, workspace=self.route_ws, stream=stream)
+        mark(1)
         nvfp4_quantize(x, out=self.xq, workspace=self.small_ws, stream=stream)
+        mark(2)
         if self.fused:
-            self.hq.g.copy_(g_h)
             nvfp4_grouped_gemm(self.xq, w.gu_codes, w.gu_scales, w.gu_g, r.offsets, m_total=M,
                                a_rows=r.perm_src_token, epilogue=EPI_SWIGLU_NVFP4, out_codes=self.hq.codes,
-                               out_scales=self.hq.scales, out_g=self.hq.g, stream=stream)
+                               out_scales=self.hq.scales, out_g=g_h, b_packed=w.gu_packed, stream=stream)
+            mark(3)
             self.acc.zero_()
-            nvfp4_grouped_gemm(self.hq, w.dn_codes, w.dn_scales, w.dn_g, r.offsets, m_total=M,
+            nvfp4_grouped_gemm(hq, w.dn_codes, w.dn_scales, w.dn_g, r.offsets, m_total=M,
                                epilogue=EPI_COMBINE_F32, out=self.acc, out_rows=T, row_token=r.perm_src_token,
-                               row_weight=r.perm_weight, stream=stream)
+                               row_weight=r.perm_weight, b_packed=w.dn_packed, stream=stream)
+            mark(4)
             moe_unpermute_combine(self.acc, None, None, T, 1, out=self.out, stream=stream)
         else:
             nvfp4_grouped_gemm(self.xq, w.gu_codes, w.gu_scales, w.gu_g, r.offsets, m_total=M,
-                               a_rows=r.perm_src_token, epilogue=EPI_F32, out=self.y1, stream=stream)
+                               a_rows=r.perm_src_token, epilogue=EPI_F32, out=self.y1, b_packed=w.gu_packed,
+                               stream=stream)
             moe_swiglu(self.y1, g=g_h, out=self.hq, workspace=self.small_ws, stream=stream)
-            nvfp4_grouped_gemm(self.hq, w.dn_codes, w.dn_scales, w.dn_g, r.offsets, m_total=M,
-                               epilogue=EPI_BF16, out=self.y2, stream=stream)
+            mark(3)
+            nvfp4_grouped_gemm(hq, w.dn_codes, w.dn_scales, w.dn_g, r.offsets, m_total=M,
+                               epilogue=EPI_BF16, out=self.y2, b_packed=w.dn_packed, stream=stream)
+            mark(4)
             moe_unpermute_combine(self.y2, r.perm_of_assignment, r.topk_w, T, k, out=self.out, stream=stream)
+        mark(5)
         return self.out

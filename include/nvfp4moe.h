@@ -102,7 +102,10 @@ typedef struct nvfp4moe_gemm_args {
   const float* out_g;         /* EPI_SWIGLU_NVFP4: device, 1 float, > 0 */
   const int32_t* row_token;   /* EPI_COMBINE_F32: device [m_total], values in [0, out_rows) */
   const float* row_weight;    /* EPI_COMBINE_F32: device [m_total] */
-  int32_t max_rows_per_expert_hint;  /* 0 = unknown; sizes the grid (the pages' tune_max_num_tokens) */
+  int32_t max_rows_per_expert_hint;  /* 0 = unknown; reserved as a sizing hint (the pages' tune_max_num_tokens) */
+  /* Optional: B in the packed tile layout written by nvfp4_weight_repack (16-byte
+     aligned).  When set, b_codes / b_scales are not read (and may be NULL). */
+  const uint8_t* b_packed;
 } nvfp4moe_gemm_args;
 
 /* ---------------------------------------------------------------- route + permute
@@ -153,6 +156,22 @@ int nvfp4_quantize(const void* x, int32_t x_dtype, int64_t rows, int64_t cols,
  * with no rows read no weight bytes. */
 int nvfp4_grouped_gemm(const nvfp4moe_gemm_args* args, void* stream);
 
+/* ---------------------------------------------------------------- packed weights
+ * Weights are static, so they can be repacked once into a tile layout that the
+ * grouped GEMM streams with fully contiguous, non-temporal loads: tile
+ * (e, 16-row tile rt, 256-K step st) is 2304 bytes (the 16 rows' 128 code bytes
+ * and 16 scale bytes of the step, ordered by the lane that consumes them),
+ * tiles ordered by (e, rt, st), zero padded past N and K.  The layout is private
+ * to this library (it may change between versions; nvfp4moe_version() tells
+ * them apart); the row-major NVFP4 tensors stay the reference format.
+ *   codes   [E, N, K/2]  row-major NVFP4 codes (16-byte aligned)
+ *   scales  [E, N, K/16] E4M3 block scales
+ *   packed  (out) nvfp4_weight_packed_size(E, N, K) bytes, 16-byte aligned
+ * K % 32 == 0.  Pure data movement: no rounding, bit-exact. */
+size_t nvfp4_weight_packed_size(int32_t E, int32_t N, int32_t K);
+int nvfp4_weight_repack(const uint8_t* codes, const uint8_t* scales, int32_t E, int32_t N, int32_t K,
+                        uint8_t* packed, size_t packed_bytes, void* stream);
+
 /* ---------------------------------------------------------------- SwiGLU (unfused)
  * gate_up [M, 2I] (float32 or bf16) -> h = silu(gate) * up, gate = columns
  * [0, I), up = [I, 2I), quantised to NVFP4 codes [M, I/2], scales [M, I/16].
@@ -179,7 +198,7 @@ int moe_unpermute_combine(const void* y, int32_t y_dtype, const int32_t* perm_of
 const char* nvfp4moe_status_string(int status);
 const char* nvfp4moe_last_error_detail(void);
 /* library version: major*10000 + minor*100 + patch */
-int nvfp4moe_version(void);
+int nvfp4moe_version(void);   /* 101: packed weight tiles of 16 rows x 256 K */
 
 #ifdef __cplusplus
 }

@@ -1,0 +1,114 @@
+"""Full-size parity at the workloads' real shapes, in the launch configuration
+the benchmark times (MoELayer, fused epilogues), checked on sampled outputs
+that the oracle computes row by row; plus the dense 8192^3 GEMM on sampled
+entries.  Both sides start from the same seeded raw inputs (logits, bf16
+activations, float32 weights) and run their own chains."""
+import numpy as np
+import pytest
+import torch
+
+import block_scaled_fp4_permute_amd as m
+import workloads
+from block_scaled_fp4_permute_amd.layer import MoELayer, quantize_expert_weights
+from oracle import moe as OM
+from oracle import quant as OQ
+from tests.gpu_common import DEV, assert_gemm_close, bf16_to_f32, check_requant, down, up
+
+pytestmark = pytest.mark.gpu
+
+
+def _g_h(cfg):
+    return np.float32(np.float32(workloads.H_CALIBRATION_AMAX[cfg.index]) / np.float32(2688.0))
+
+
+@pytest.mark.parametrize("cfg_index", [1, 2, 3])
+@pytest.mark.parametrize("fused", [True, False])
+def test_full_layer_sampled_tokens(cfg_index, fused):
+    cfg = workloads.CONFIGS[cfg_index]
+    print(f"full layer cfg={cfg_index} fused={fused}", flush=True)
+    T, H, I, E, k = cfg.T, cfg.H, cfg.I, cfg.E, cfg.k
+    logits = workloads.logits(cfg)
+    x = workloads.activations(cfg)
+    w_gu, w_dn = workloads.torch_expert_weights(cfg, DEV)
+    wq = quantize_expert_weights(w_gu, w_dn).pack()     # the benchmark's configuration
+    g_h = _g_h(cfg)
+    layer = MoELayer(T, H, I, E, k, DEV, fused=fused)
+    out = layer.forward(up(logits), up(x).to(torch.bfloat16), wq, up(np.array([g_h], np.float32)))
+    torch.cuda.synchronize()
+    out = bf16_to_f32(out)
+
+    # oracle: routing over all tokens, then a few tokens end to end
+    ids, w = OM.route(logits, k)
+    counts, offsets, src, perm_of, pw = OM.permute(ids, w, E)
+    assert np.array_equal(down(layer.routing.topk_ids), ids)
+    assert np.array_equal(down(layer.routing.perm_of_assignment), perm_of)
+    g_x = OQ.global_scale(x)
+    assert down(layer.xq.g)[0] == g_x
+    rng = np.random.default_rng(cfg_index)
+    tokens = rng.choice(T, size=4, replace=False)
+    experts = sorted(set(ids[tokens].reshape(-1).tolist()))
+    wq_ref = {}
+    for e in experts:
+        wq_ref[e] = (OQ.quantize(w_gu[e].cpu().numpy()), OQ.quantize(w_dn[e].cpu().numpy()))
+        assert np.array_equal(down(wq.gu_codes[e]), wq_ref[e][0][0]), "gate_up weight codes"
+        assert np.array_equal(down(wq.dn_scales[e]), wq_ref[e][1][1]), "down weight scales"
+    h_codes_gpu, h_scales_gpu = down(layer.hq.codes), down(layer.hq.scales)
+    flipped_tokens = 0
+    for t in tokens:
+        xc, xs, _ = OQ.quantize(x[t:t + 1], g=g_x)
+        acc = np.zeros(H)
+        tol = np.zeros(H)
+        absterm = np.zeros(H)
+        flips = 0
+        for j in range(k):
+            e = int(ids[t, j])
+            p = int(perm_of[t * k + j])
+            (gc, gs, gg), (dc, ds, dg) = wq_ref[e]
+            y1, ad1 = OM.grouped_gemm(xc, xs, g_x, gc[None], gs[None], np.array([gg]), np.array([0, 1]))
+            h64 = OM.swiglu(y1)
+            tol_y = 1e-3 * ad1 + 1e-6
+            uu, gg_ = y1[:, I:].astype(np.float64), y1[:, :I].astype(np.float64)
+            tol_h = 1.1 * tol_y[:, :I] * np.abs(uu) + np.abs(OM.silu(gg_)) * tol_y[:, I:] + 2.0 ** -20 * np.abs(h64) + 1e-7
+            ns, nc = check_requant(h_codes_gpu[p:p + 1], h_scales_gpu[p:p + 1], h64, g_h, tol_h, max_flip_frac=0.05,
+                                   what=f"h row of token {t} slot {j}")
+            flips += ns + nc
+            hc, hs, _ = OQ.quantize(h64.astype(np.float32), g=g_h)
+            y2, ad2 = OM.grouped_gemm(hc, hs, g_h, dc[None], ds[None], np.array([dg]), np.array([0, 1]))
+            acc += float(w[t, j]) * y2[0].astype(np.float64)
+            tol += abs(float(w[t, j])) * (1e-3 * ad2[0] + 1e-6)
+            absterm += abs(float(w[t, j])) * np.abs(y2[0].astype(np.float64))
+        tol += 2.0 ** -8 * np.abs(acc) + 1e-6
+        if not fused:
+            tol += 2.0 ** -8 * absterm            # the bf16 rounding of each y2 row before the combine
+        err = np.abs(out[t] - acc)
+        if flips == 0:
+            assert np.all(err <= tol), f"token {t}: max err {err.max()} (tol there {tol[np.argmax(err)]})"
+        else:
+            flipped_tokens += 1
+            assert np.linalg.norm(out[t] - acc) <= 0.05 * np.linalg.norm(acc), f"token {t} with {flips} flips"
+    assert flipped_tokens <= 2
+
+
+def test_full_dense_gemm_8192_sampled():
+    cfg = workloads.CONFIGS[4]
+    M_, N_, K_ = cfg.T, cfg.H, cfg.I
+    print("dense 8192^3", flush=True)
+    a, b = workloads.torch_dense_operands(cfg, DEV)
+    aq = m.nvfp4_quantize(a)
+    bq = m.nvfp4_quantize(b)
+    offsets = torch.tensor([0, M_], dtype=torch.int32, device=DEV)
+    y = m.nvfp4_grouped_gemm(aq, bq.codes[None], bq.scales[None], bq.g, offsets, m_total=M_, epilogue=m.EPI_BF16)
+    torch.cuda.synchronize()
+    a_np, b_np = a.cpu().numpy(), b.cpu().numpy()
+    g_a, g_b = OQ.global_scale(a_np), OQ.global_scale(b_np)
+    assert down(aq.g)[0] == g_a and down(bq.g)[0] == g_b
+    rng = np.random.default_rng(4)
+    rows = np.sort(rng.choice(M_, 48, replace=False))
+    cols = np.sort(rng.choice(N_, 48, replace=False))
+    ac, as_, _ = OQ.quantize(a_np[rows], g=g_a)
+    bc, bs, _ = OQ.quantize(b_np[cols], g=g_b)
+    assert np.array_equal(down(aq.codes[torch.from_numpy(rows).to(DEV)]), ac)
+    assert np.array_equal(down(bq.scales[torch.from_numpy(cols).to(DEV)]), bs)
+    y_ref, absdot = OM.grouped_gemm(ac, as_, g_a, bc[None], bs[None], np.array([g_b]), np.array([0, len(rows)]))
+    got = bf16_to_f32(y)[np.ix_(rows, cols)]
+    assert_gemm_close(got, y_ref, absdot, bf16_out=True, what="dense 8192")

@@ -22,15 +22,48 @@ def _rand_nvfp4(rng, shape_rows, K, scale_lo=0x28, scale_hi=0x48):
 
 
 def _run_gemm(a_codes, a_scales, a_g, b_codes, b_scales, b_g, counts, a_rows=None, epilogue=m.EPI_F32,
-              m_extra=0, hint=0):
+              m_extra=0, hint=0, packed=False):
     offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
     m_total = int(offsets[-1]) + m_extra
     a = m.NVFP4Tensor(up(a_codes), up(a_scales), up(np.array([a_g], np.float32)))
-    y = m.nvfp4_grouped_gemm(a, up(b_codes), up(b_scales), up(np.asarray(b_g, np.float32)), up(offsets),
+    bc, bs = up(b_codes), up(b_scales)
+    bp = m.nvfp4_weight_repack(bc, bs) if packed else None
+    y = m.nvfp4_grouped_gemm(a, bc, bs, up(np.asarray(b_g, np.float32)), up(offsets),
                              m_total=m_total, a_rows=None if a_rows is None else up(a_rows.astype(np.int32)),
-                             epilogue=epilogue, max_rows_per_expert_hint=hint)
+                             epilogue=epilogue, max_rows_per_expert_hint=hint, b_packed=bp)
     torch.cuda.synchronize()
     return y, offsets
+
+
+def _unpack_tiles(packed, E, N, K):
+    """Inverse of the documented packed layout (tile (e, rt, st) of 2304 bytes;
+    lane l = 16g + n holds row 16rt+n, code bytes [128st+32g, +32) at [16l, +16)
+    and [1024+16l, +16), scale bytes [16st+4g, +4) at [2048+4l, +4))."""
+    ntr, nst = (N + 15) // 16, (K + 255) // 256
+    t = np.asarray(packed, np.uint8)[: E * ntr * nst * 2304].reshape(E, ntr, nst, 2304)
+    codes = np.zeros((E, ntr * 16, nst * 128), np.uint8)
+    scales = np.zeros((E, ntr * 16, nst * 16), np.uint8)
+    for l in range(64):
+        n, g = l % 16, l // 16
+        rows = np.arange(ntr) * 16 + n
+        for st in range(nst):
+            codes[:, rows, 128 * st + 32 * g: 128 * st + 32 * g + 16] = t[:, :, st, 16 * l: 16 * l + 16]
+            codes[:, rows, 128 * st + 32 * g + 16: 128 * st + 32 * g + 32] = t[:, :, st, 1024 + 16 * l: 1024 + 16 * l + 16]
+            scales[:, rows, 16 * st + 4 * g: 16 * st + 4 * g + 4] = t[:, :, st, 2048 + 4 * l: 2048 + 4 * l + 4]
+    return codes, scales
+
+
+@pytest.mark.parametrize("E,N,K", [(3, 48, 288), (1, 16, 32), (2, 512, 6144), (4, 64, 256)])
+def test_weight_repack_layout(E, N, K):
+    rng = np.random.default_rng(E * N + K)
+    codes = rng.integers(0, 256, (E, N, K // 2), dtype=np.uint8)
+    scales = rng.integers(0, 256, (E, N, K // 16), dtype=np.uint8)
+    packed = down(m.nvfp4_weight_repack(up(codes), up(scales)))
+    torch.cuda.synchronize()
+    assert packed.size == m.lib().nvfp4_weight_packed_size(E, N, K)
+    uc, us = _unpack_tiles(packed, E, N, K)
+    assert np.array_equal(uc[:, :N, :K // 2], codes) and np.array_equal(us[:, :N, :K // 16], scales)
+    assert not uc[:, N:].any() and not uc[:, :, K // 2:].any() and not us[:, :, K // 16:].any()
 
 
 GEMM_CASES = [
@@ -46,9 +79,10 @@ GEMM_CASES = [
 
 @pytest.mark.parametrize("case", range(len(GEMM_CASES)))
 @pytest.mark.parametrize("gather", [False, True])
-def test_gemm_f32_random(case, gather):
+@pytest.mark.parametrize("packed", [False, True])
+def test_gemm_f32_random(case, gather, packed):
     E, counts, N, K, rows_a, hint = GEMM_CASES[case]
-    print(f"gemm case {case} gather={gather} E={E} N={N} K={K}", flush=True)
+    print(f"gemm case {case} gather={gather} packed={packed} E={E} N={N} K={K}", flush=True)
     rng = np.random.default_rng(100 + case)
     a_codes, a_scales = _rand_nvfp4(rng, (rows_a,), K)
     b_codes, b_scales = _rand_nvfp4(rng, (E, N), K)
@@ -58,7 +92,7 @@ def test_gemm_f32_random(case, gather):
     a_rows = rng.integers(0, rows_a, M).astype(np.int32) if gather else None
     if not gather:
         a_codes, a_scales = a_codes[:max(M, 1)], a_scales[:max(M, 1)]
-    y, offsets = _run_gemm(a_codes, a_scales, a_g, b_codes, b_scales, b_g, counts, a_rows, hint=hint)
+    y, offsets = _run_gemm(a_codes, a_scales, a_g, b_codes, b_scales, b_g, counts, a_rows, hint=hint, packed=packed)
     y_ref, absdot = OM.grouped_gemm(a_codes, a_scales, a_g, b_codes, b_scales, b_g, offsets, a_rows=a_rows)
     assert_gemm_close(down(y)[:M], y_ref, absdot, what=f"case {case}")
 
@@ -81,8 +115,9 @@ def test_gemm_bf16_epilogue_and_untouched_tail_rows():
     assert np.all(got[51:] == 7.0)
 
 
-@pytest.mark.parametrize("K", [32, 4096, 6144])
-def test_gemm_constant_scales_bit_exact(K):
+@pytest.mark.parametrize("K", [32, 256, 4096, 6144])
+@pytest.mark.parametrize("packed", [False, True])
+def test_gemm_constant_scales_bit_exact(K, packed):
     # constant block scales and unit per-tensor scales make every FP32 partial
     # sum exact, so the GPU must reproduce the oracle bit for bit
     rng = np.random.default_rng(K)
@@ -92,7 +127,25 @@ def test_gemm_constant_scales_bit_exact(K):
     b_codes = rng.integers(0, 256, (E, N, K // 2), dtype=np.uint8)
     a_scales = np.full((M, K // 16), 0x3A, np.uint8)          # 1.25
     b_scales = np.full((E, N, K // 16), 0x30, np.uint8)       # 0.5
-    y, offsets = _run_gemm(a_codes, a_scales, 1.0, b_codes, b_scales, np.ones(E, np.float32), counts)
+    y, offsets = _run_gemm(a_codes, a_scales, 1.0, b_codes, b_scales, np.ones(E, np.float32), counts, packed=packed)
+    y_ref, _ = OM.grouped_gemm(a_codes, a_scales, 1.0, b_codes, b_scales, np.ones(E, np.float32), offsets)
+    assert np.array_equal(down(y), y_ref)
+
+
+@pytest.mark.parametrize("sa,sb", [(0x03, 0x05), (0x01, 0x7E), (0x07, 0x08), (0x00, 0x40)])
+@pytest.mark.parametrize("packed", [False, True])
+def test_gemm_subnormal_and_extreme_scales_bit_exact(sa, sb, packed):
+    # E4M3 subnormal block scales (codes 1..7) pass through FP16 subnormals in
+    # the decode; with one scale per operand and unit per-tensor scales the
+    # float32 result is exact in any summation order, so it must match exactly
+    rng = np.random.default_rng(sa * 256 + sb)
+    E, counts, N, K = 2, [21, 50], 48, 1024
+    M = sum(counts)
+    a_codes = rng.integers(0, 256, (M, K // 2), dtype=np.uint8)
+    b_codes = rng.integers(0, 256, (E, N, K // 2), dtype=np.uint8)
+    a_scales = np.full((M, K // 16), sa, np.uint8)
+    b_scales = np.full((E, N, K // 16), sb, np.uint8)
+    y, offsets = _run_gemm(a_codes, a_scales, 1.0, b_codes, b_scales, np.ones(E, np.float32), counts, packed=packed)
     y_ref, _ = OM.grouped_gemm(a_codes, a_scales, 1.0, b_codes, b_scales, np.ones(E, np.float32), offsets)
     assert np.array_equal(down(y), y_ref)
 
@@ -156,14 +209,17 @@ def test_swiglu_unfused_stage():
     assert abs(g_dev - g_h) <= 2.0 ** -20 * g_h
 
 
-def test_config0_gate_up_fused_swiglu():
+@pytest.mark.parametrize("packed", [False, True])
+def test_config0_gate_up_fused_swiglu(packed):
     c, logits, x, wgu, wdn, ids, w, counts, offsets, src, perm_of, pw, xq = _config0()
     y1, absdot1 = OM.grouped_gemm(*xq, *wgu, offsets, a_rows=src)
     h64 = OM.swiglu(y1)
     g_h = np.float32(np.abs(h64.astype(np.float32)).max() / np.float32(2688))
     a = m.NVFP4Tensor(up(xq[0]), up(xq[1]), up(np.array([xq[2]], np.float32)))
-    hq = m.nvfp4_grouped_gemm(a, up(wgu[0]), up(wgu[1]), up(wgu[2]), up(offsets), m_total=int(offsets[-1]),
-                              a_rows=up(src), epilogue=m.EPI_SWIGLU_NVFP4, out_g=up(np.array([g_h], np.float32)))
+    bc, bs = up(wgu[0]), up(wgu[1])
+    hq = m.nvfp4_grouped_gemm(a, bc, bs, up(wgu[2]), up(offsets), m_total=int(offsets[-1]),
+                              a_rows=up(src), epilogue=m.EPI_SWIGLU_NVFP4, out_g=up(np.array([g_h], np.float32)),
+                              b_packed=m.nvfp4_weight_repack(bc, bs) if packed else None)
     torch.cuda.synchronize()
     check_requant(down(hq.codes), down(hq.scales), h64, g_h, _swiglu_tol(y1, absdot1), max_flip_frac=0.02,
                   what="fused swiglu")
@@ -192,7 +248,8 @@ def test_fused_swiglu_exact_accumulation():
                            max_flip_frac=1e-3, what="fused swiglu exact")
 
 
-def test_config0_down_fused_combine_and_unfused_combine():
+@pytest.mark.parametrize("packed", [False, True])
+def test_config0_down_fused_combine_and_unfused_combine(packed):
     c, logits, x, wgu, wdn, ids, w, counts, offsets, src, perm_of, pw, xq = _config0()
     y1, _ = OM.grouped_gemm(*xq, *wgu, offsets, a_rows=src)
     h64 = OM.swiglu(y1)
@@ -207,8 +264,10 @@ def test_config0_down_fused_combine_and_unfused_combine():
     # fused: scatter-add epilogue into a float32 accumulator, then to bf16
     a = m.NVFP4Tensor(up(hq[0]), up(hq[1]), up(np.array([hq[2]], np.float32)))
     acc = torch.zeros((c.T, c.H), dtype=torch.float32, device=DEV)
-    m.nvfp4_grouped_gemm(a, up(wdn[0]), up(wdn[1]), up(wdn[2]), up(offsets), m_total=int(offsets[-1]),
-                         epilogue=m.EPI_COMBINE_F32, out=acc, out_rows=c.T, row_token=up(src), row_weight=up(pw))
+    bc, bs = up(wdn[0]), up(wdn[1])
+    m.nvfp4_grouped_gemm(a, bc, bs, up(wdn[2]), up(offsets), m_total=int(offsets[-1]),
+                         epilogue=m.EPI_COMBINE_F32, out=acc, out_rows=c.T, row_token=up(src), row_weight=up(pw),
+                         b_packed=m.nvfp4_weight_repack(bc, bs) if packed else None)
     out = m.moe_unpermute_combine(acc, None, None, c.T, 1)
     torch.cuda.synchronize()
     assert np.all(np.abs(bf16_to_f32(out) - out64) <= tol), "fused combine"

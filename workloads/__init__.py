@@ -122,3 +122,35 @@ def small_variant(cfg: MoEConfig, **over) -> MoEConfig:
     d = dict(cfg.__dict__)
     d.update(over)
     return MoEConfig(**d)
+
+
+def torch_expert_weights(cfg: MoEConfig, device, copy: int = 0):
+    """float32 gate_up [E, 2I, H] and down [E, H, I] ~ N(0, weight_std) drawn on
+    ``device`` with torch's seeded generator (for the full-size workloads, where
+    drawing 1.2e9 normals on the host would dominate).  Deterministic for a given
+    (cfg, copy, device type)."""
+    import torch
+    gen = torch.Generator(device=device)
+    gen.manual_seed(SEED * 1000 + cfg.index * 10 + copy)
+    w_gu = torch.randn((cfg.E, 2 * cfg.I, cfg.H), generator=gen, device=device, dtype=torch.float32)
+    w_gu.mul_(cfg.weight_std)
+    w_dn = torch.randn((cfg.E, cfg.H, cfg.I), generator=gen, device=device, dtype=torch.float32)
+    w_dn.mul_(cfg.weight_std)
+    return w_gu, w_dn
+
+
+def torch_dense_operands(cfg: MoEConfig, device):
+    """A [M, K] and B [N, K] ~ N(0, 1) float32 on ``device`` (seeded torch generator)."""
+    import torch
+    gen = torch.Generator(device=device)
+    gen.manual_seed(SEED * 1000 + cfg.index * 10 + 7)
+    a = torch.randn((cfg.T, cfg.I), generator=gen, device=device, dtype=torch.float32)
+    b = torch.randn((cfg.H, cfg.I), generator=gen, device=device, dtype=torch.float32)
+    return a, b
+
+
+# Static calibration of the intermediate's per-tensor scale: an expected
+# absolute maximum of h = silu(gate) * up for each workload (gate and up are
+# roughly N(0, (sqrt(H) * 0.02)^2) for x ~ N(0,1)).  Both sides receive the same
+# per-tensor scale derived from it.
+H_CALIBRATION_AMAX = {0: 0.5, 1: 24.0, 2: 32.0, 3: 40.0}
