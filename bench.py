@@ -3,11 +3,12 @@
 
 One step = one forward of the whole hot path on one batch: route + permute,
 NVFP4 quantisation of the activations, gate_up grouped GEMM with the fused
-SwiGLU + re-quantisation, down grouped GEMM with the fused weighted
-scatter-add, accumulator to bfloat16.  Default workload: the decode MoE at
+SwiGLU + re-quantisation, down grouped GEMM (bf16 rows), weighted gather
+combine to bf16 token order.  Default workload: the decode MoE at
 16-64 tokens per expert (T=2048, H=6144, I=256, E=256, top-8, Zipf-skewed
 routing), seeded synthetic inputs, weights drawn N(0, 0.02) and quantised to
-NVFP4 on the GPU (untimed).  Two weight copies alternate between steps so the
+NVFP4 on the GPU and repacked into the streaming tile layout (untimed).  Two
+weight copies alternate between steps so the
 256 MB last-level cache cannot serve a step's weights from the previous step.
 
 Prints ONE JSON line: value = touched expert weight bytes (codes + scales of
@@ -39,7 +40,10 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", type=int, default=2, help="workload index (0..3); 2 is the reported one")
-    ap.add_argument("--unfused", action="store_true", help="unfused SwiGLU / combine calls")
+    ap.add_argument("--swiglu", choices=["fused", "separate"], default="fused",
+                    help="SwiGLU + requant in the gate_up epilogue, or a separate call")
+    ap.add_argument("--combine", choices=["gather", "atomic"], default="gather",
+                    help="bf16 down output + gather combine, or float32 atomic scatter-add epilogue")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-experts", type=int, default=0, help="experts in the CPU-oracle sample (0: auto)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -177,7 +181,7 @@ def main():
     del y1
     torch.cuda.synchronize()
 
-    layer = MoELayer(T, H, I, E, k, dev, fused=not args.unfused)
+    layer = MoELayer(T, H, I, E, k, dev, swiglu=args.swiglu, combine=args.combine)
     for i in range(args.warmup):
         layer.forward(logits, x, copies[i % 2], g_h)
     torch.cuda.synchronize()
@@ -198,8 +202,9 @@ def main():
     for i in range(args.steps):
         layer.forward(logits, x, copies[i % 2], g_h, marks=marks[i])
     torch.cuda.synchronize()
-    names = ["route_permute", "quantize_x", "gate_up_swiglu" if not args.unfused else "gate_up+swiglu",
-             "down_combine" if not args.unfused else "down", "finalize_bf16" if not args.unfused else "combine"]
+    names = ["route_permute", "quantize_x", "gate_up_swiglu",
+             "down" if args.combine == "gather" else "down_scatter_add",
+             "combine" if args.combine == "gather" else "to_bf16"]
     stage_ms = {n: float(np.mean([m[j].elapsed_time(m[j + 1]) for m in marks])) for j, n in enumerate(names)}
 
     touched = int((counts > 0).sum())
@@ -216,7 +221,7 @@ def main():
     gu_alg = touched * gu_bytes_e + T * H * 9 // 16 + T * k * I * 9 // 16
     achieved = gu_alg / (gu_ms * 1e-3) / 1e9
     wl_name = f"decode_moe_T{T}_H{H}_I{I}_E{E}_top{k}_{cfg.routing}"
-    traffic = measured_traffic("gate_up_swiglu", wl_name) if not args.unfused else None
+    traffic = measured_traffic("gate_up_swiglu", wl_name) if args.swiglu == "fused" else None
 
     res = {
         "metric": "NVFP4 MoE grouped-GEMM TFLOPS & weight GB/s at 16-64 tok/expert, 1 MI355X",
@@ -240,7 +245,8 @@ def main():
         "tokens_per_expert": {"min": int(counts.min()), "median": float(np.median(counts)),
                               "max": int(counts.max()), "touched_experts": touched},
         "config": {"workload": wl_name, "T": T, "H": H, "I": I, "E": E, "top_k": k, "routing": cfg.routing,
-                   "fused": not args.unfused, "weight_copies": 2},
+                   "swiglu": args.swiglu, "combine": args.combine, "weight_layout": "packed tiles",
+                   "weight_copies": 2},
         "roofline": {"kernel": "nvfp4 grouped GEMM gate_up + SwiGLU/requant epilogue", "bound": "hbm",
                      "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,

@@ -85,12 +85,14 @@ __global__ __launch_bounds__(256) void k_quantize(const void* __restrict__ x, in
                                                   const float* __restrict__ partial, int nparts,
                                                   float* __restrict__ g_out, uint8_t* __restrict__ codes,
                                                   uint8_t* __restrict__ scales) {
-  const float g = reduce_scale(g_in, partial, nparts);
+  // the block's loads are issued before the scale reduction so that their
+  // latency overlaps it
   const int64_t b = blockIdx.x * 256ll + threadIdx.x;
+  float v[16];
+  load16<DT>(x, (b < nblocks ? b : 0) * 16, v);
+  const float g = reduce_scale(g_in, partial, nparts);
   if (b == 0 && g_out) *g_out = g;
   if (b >= nblocks) return;
-  float v[16];
-  load16<DT>(x, b * 16, v);
   uint32_t lo, hi;
   const uint32_t s = encode_block16(v, g, lo, hi);
   reinterpret_cast<uint2*>(codes)[b] = make_uint2(lo, hi);
@@ -153,12 +155,12 @@ __global__ __launch_bounds__(256) void k_swiglu_quant(const void* __restrict__ y
                                                       const float* __restrict__ partial, int nparts,
                                                       float* __restrict__ g_out, uint8_t* __restrict__ codes,
                                                       uint8_t* __restrict__ scales) {
-  const float g = reduce_scale(g_in, partial, nparts);
   const int64_t b = blockIdx.x * 256ll + threadIdx.x;
+  float h[16];
+  swiglu_block<DT>(y, b < nblocks ? b : 0, I, h);
+  const float g = reduce_scale(g_in, partial, nparts);
   if (b == 0 && g_out) *g_out = g;
   if (b >= nblocks) return;
-  float h[16];
-  swiglu_block<DT>(y, b, I, h);
   uint32_t lo, hi;
   const uint32_t s = encode_block16(h, g, lo, hi);
   reinterpret_cast<uint2*>(codes)[b] = make_uint2(lo, hi);

@@ -505,49 +505,117 @@ __global__ __launch_bounds__(NW * 64) void k_gemm_streamk(const GemmParams p) {
 
 // ================================================================== stream-N
 // K <= 256 (one packed tile per 16 columns) and packed weights.  Workgroup =
-// (row chunk, group of NW*TPW column tiles).  The chunk's A is decoded into
-// LDS once; wave w then streams column tiles w*TPW .. w*TPW+TPW-1 of the group
-// with the next two tiles' loads in flight.
-template <int NW, int MT, int MTA, int TPW, int EPI>
-__device__ __forceinline__ void n_main_loop(const GemmParams& p, const half8* __restrict__ lds,
-                                            const uint8_t* tiles, int t_first, int t_count, int prow0, int rows,
-                                            float gab) {
+// (row chunk, group of NW * UPW units of 64 columns).  The chunk's A is
+// decoded into LDS once; wave w then streams its units (4 weight tiles each),
+// with the next unit's loads in flight.  Float32 / bf16 results go through a
+// per-wave LDS tile so that each row's 64 columns leave as whole 128- or
+// 256-byte segments (16 bytes per lane) instead of 2- or 4-byte scattered
+// stores.
+constexpr int UNIT = 4;   // 16-column tiles per unit
+
+template <int EPI>
+__device__ __forceinline__ void store_unit(const GemmParams& p, const float4v (&acc)[UNIT], float* __restrict__ stage,
+                                           int prow0, int rows_left, int col0, float gab) {
+  // stage[16 rows][64 cols] float32 of this wave; lane (lr, lg) holds rows 4lg+i, cols 16u+lr
   const int lane = threadIdx.x & 63;
   const int lr = lane & 15;
-  BRegs R0, R1;
-  b_load_packed(tiles + static_cast<size_t>(t_first + min(0, t_count - 1)) * PTILE, R0);
-  b_load_packed(tiles + static_cast<size_t>(t_first + min(1, t_count - 1)) * PTILE, R1);
-  auto consume = [&](const BRegs& b, int i) {
-    float4v acc[MTA];
+  const int lg = lane >> 4;
 #pragma unroll
-    for (int r = 0; r < MTA; ++r) acc[r] = float4v{0.f, 0.f, 0.f, 0.f};
+  for (int u = 0; u < UNIT; ++u)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) stage[(4 * lg + i) * 68 + 16 * u + lr] = acc[u][i] * gab;
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  // lane -> (row lane / 4, 16 columns starting at 16 * (lane % 4))
+  const int r = lane >> 2;
+  const int c = 16 * (lane & 3);
+  if (r < rows_left && col0 + c < p.N) {
+    const float* src = stage + r * 68 + c;
+    const size_t base = static_cast<size_t>(prow0 + r) * p.N + col0 + c;
+    if constexpr (EPI == EPI_F32) {
+      float4* dst = reinterpret_cast<float4*>(static_cast<float*>(p.out) + base);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) dst[q] = make_float4(src[4 * q], src[4 * q + 1], src[4 * q + 2], src[4 * q + 3]);
+    } else {
+      uint32_t w[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q)
+        w[q] = static_cast<uint32_t>(f32_to_bf16(src[2 * q])) | (static_cast<uint32_t>(f32_to_bf16(src[2 * q + 1])) << 16);
+      uint4* dst = reinterpret_cast<uint4*>(static_cast<uint16_t*>(p.out) + base);
+      dst[0] = make_uint4(w[0], w[1], w[2], w[3]);
+      dst[1] = make_uint4(w[4], w[5], w[6], w[7]);
+    }
+  }
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+template <int NW, int MT, int MTA, int UPW, int EPI>
+__device__ __forceinline__ void n_main_loop(const GemmParams& p, const half8* __restrict__ lds, float* stage,
+                                            const uint8_t* tiles, int u_first, int u_count, int ntr, int prow0,
+                                            int rows, float gab) {
+  const int lane = threadIdx.x & 63;
+  const int lr = lane & 15;
+  BRegs R0[UNIT], R1[UNIT];
+  auto load_unit = [&](BRegs (&R)[UNIT], int i) {
+    const int ui = u_first + min(i, u_count - 1);
+#pragma unroll
+    for (int t = 0; t < UNIT; ++t)
+      b_load_packed(tiles + static_cast<size_t>(min(UNIT * ui + t, ntr - 1)) * PTILE, R[t]);
+  };
+  auto consume = [&](const BRegs (&R)[UNIT], int i) {
+    float4v acc[MTA][UNIT];
+#pragma unroll
+    for (int r = 0; r < MTA; ++r)
+#pragma unroll
+      for (int t = 0; t < UNIT; ++t) acc[r][t] = float4v{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
-      const half8 bf = b_frag(b, b.s, s);
+      half8 bf[UNIT];
 #pragma unroll
-      for (int r = 0; r < MTA; ++r)
-        acc[r] = __builtin_amdgcn_mfma_f32_16x16x32_f16(lds[(r * 8 + s) * 64 + lane], bf, acc[r], 0, 0, 0);
+      for (int t = 0; t < UNIT; ++t) bf[t] = b_frag(R[t], R[t].s, s);
+#pragma unroll
+      for (int r = 0; r < MTA; ++r) {
+        const half8 af = lds[(r * 8 + s) * 64 + lane];
+#pragma unroll
+        for (int t = 0; t < UNIT; ++t) acc[r][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af, bf[t], acc[r][t], 0, 0, 0);
+      }
     }
-    const int col = 16 * (t_first + i) + lr;
-    const bool ok = i < t_count && col < p.N;
+    if (i < u_count) {
+      const int col0 = 64 * (u_first + i);
 #pragma unroll
-    for (int r = 0; r < MTA; ++r) epilogue_tile<EPI>(p, acc[r], prow0 + 16 * r, rows - 16 * r, col, ok, gab);
+      for (int r = 0; r < MTA; ++r) {
+        if constexpr (EPI == EPI_F32 || EPI == EPI_BF16) {
+          store_unit<EPI>(p, acc[r], stage, prow0 + 16 * r, rows - 16 * r, col0, gab);
+        } else {
+#pragma unroll
+          for (int t = 0; t < UNIT; ++t)
+            epilogue_tile<EPI>(p, acc[r][t], prow0 + 16 * r, rows - 16 * r, col0 + 16 * t + lr,
+                               col0 + 16 * t + lr < p.N, gab);
+        }
+      }
+    }
   };
-  for (int i = 0; i < TPW; i += 2) {
+  load_unit(R0, 0);
+  load_unit(R1, 1);
+  for (int i = 0; i < UPW; i += 2) {
     consume(R0, i);
-    b_load_packed(tiles + static_cast<size_t>(t_first + min(i + 2, t_count - 1)) * PTILE, R0);
+    load_unit(R0, i + 2);
     consume(R1, i + 1);
-    b_load_packed(tiles + static_cast<size_t>(t_first + min(i + 3, t_count - 1)) * PTILE, R1);
+    load_unit(R1, i + 3);
   }
 }
 
-template <int NW, int MT, int TPW, int EPI>
+template <int NW, int MT, int UPW, int EPI>
 __global__ __launch_bounds__(NW * 64) void k_gemm_streamn(const GemmParams p) {
   constexpr int THREADS = NW * 64;
   constexpr int MC = MT * 16;
   constexpr int PPT = (MT * 64 + THREADS - 1) / THREADS;
-  static_assert(TPW % 2 == 0, "tiles per wave come in pairs");
+  static_assert(UPW % 2 == 0, "units per wave come in pairs");
   __shared__ half8 a_lds[MT * 8 * 64];
+  __shared__ float stage_lds[NW][16 * 68];   // per-wave output staging (row pitch 68 floats)
   __shared__ int s_part[NW];
   __shared__ int s_work[2];
 
@@ -571,17 +639,19 @@ __global__ __launch_bounds__(NW * 64) void k_gemm_streamn(const GemmParams p) {
   __syncthreads();
 
   const int ntr = (p.N + 15) / 16;
-  const int t_first = (ng * NW + wave) * TPW;
-  const int t_count = min(TPW, ntr - t_first);
-  if (t_count <= 0) return;
+  const int nunits = (ntr + UNIT - 1) / UNIT;
+  const int u_first = (ng * NW + wave) * UPW;
+  const int u_count = min(UPW, nunits - u_first);
+  if (u_count <= 0) return;
   const uint8_t* tiles = p.b_packed + static_cast<size_t>(e) * ntr * PTILE;
   const float gab = p.a_g[0] * p.b_g[e];
   const int prow0 = row0 + m0;
+  float* stage = stage_lds[wave];
   switch (mt_active) {
-    case 1: n_main_loop<NW, MT, 1, TPW, EPI>(p, a_lds, tiles, t_first, t_count, prow0, rows, gab); break;
-    case 2: if constexpr (MT >= 2) n_main_loop<NW, MT, 2, TPW, EPI>(p, a_lds, tiles, t_first, t_count, prow0, rows, gab); break;
-    case 3: if constexpr (MT >= 3) n_main_loop<NW, MT, 3, TPW, EPI>(p, a_lds, tiles, t_first, t_count, prow0, rows, gab); break;
-    default: if constexpr (MT >= 4) n_main_loop<NW, MT, MT, TPW, EPI>(p, a_lds, tiles, t_first, t_count, prow0, rows, gab); break;
+    case 1: n_main_loop<NW, MT, 1, UPW, EPI>(p, a_lds, stage, tiles, u_first, u_count, ntr, prow0, rows, gab); break;
+    case 2: if constexpr (MT >= 2) n_main_loop<NW, MT, 2, UPW, EPI>(p, a_lds, stage, tiles, u_first, u_count, ntr, prow0, rows, gab); break;
+    case 3: if constexpr (MT >= 3) n_main_loop<NW, MT, 3, UPW, EPI>(p, a_lds, stage, tiles, u_first, u_count, ntr, prow0, rows, gab); break;
+    default: if constexpr (MT >= 4) n_main_loop<NW, MT, MT, UPW, EPI>(p, a_lds, stage, tiles, u_first, u_count, ntr, prow0, rows, gab); break;
   }
 }
 
@@ -605,14 +675,14 @@ static hipError_t launch_streamk(GemmParams prm, int64_t m_total, hipStream_t st
   return hipGetLastError();
 }
 
-template <int NW, int MT, int TPW, int EPI>
+template <int NW, int MT, int UPW, int EPI>
 static hipError_t launch_streamn(GemmParams prm, int64_t m_total, hipStream_t stream) {
   constexpr int MC = MT * 16;
-  const int ntr = (prm.N + 15) / 16;
-  prm.n_tiles = (ntr + NW * TPW - 1) / (NW * TPW);     // column-tile groups per chunk
+  const int nunits = ((prm.N + 15) / 16 + UNIT - 1) / UNIT;
+  prm.n_tiles = (nunits + NW * UPW - 1) / (NW * UPW);     // column-unit groups per chunk
   const int64_t blocks = ((m_total + MC - 1) / MC + prm.E) * prm.n_tiles;
   if (grid_check(blocks) != hipSuccess) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((k_gemm_streamn<NW, MT, TPW, EPI>), dim3(static_cast<unsigned>(blocks)), dim3(NW * 64), 0,
+  hipLaunchKernelGGL((k_gemm_streamn<NW, MT, UPW, EPI>), dim3(static_cast<unsigned>(blocks)), dim3(NW * 64), 0,
                      stream, prm);
   return hipGetLastError();
 }
@@ -632,9 +702,9 @@ hipError_t launch_grouped_gemm(const GemmParams& prm, int epilogue, int64_t m_to
   (void)hint;
   if (prm.b_packed && prm.K <= KSTEP && epilogue != EPI_SWIGLU) {
     switch (epilogue) {
-      case EPI_F32: return launch_streamn<4, 4, 8, EPI_F32>(prm, m_total, stream);
-      case EPI_BF16: return launch_streamn<4, 4, 8, EPI_BF16>(prm, m_total, stream);
-      case EPI_COMBINE: return launch_streamn<4, 4, 8, EPI_COMBINE>(prm, m_total, stream);
+      case EPI_F32: return launch_streamn<4, 4, 6, EPI_F32>(prm, m_total, stream);
+      case EPI_BF16: return launch_streamn<4, 4, 6, EPI_BF16>(prm, m_total, stream);
+      case EPI_COMBINE: return launch_streamn<4, 4, 6, EPI_COMBINE>(prm, m_total, stream);
       default: return hipErrorInvalidValue;
     }
   }

@@ -32,12 +32,23 @@ __device__ __forceinline__ bool better(float v, int id, float bv, int bid) {
   return v > bv || (v == bv && id < bid);
 }
 
+// One wave per token.  For E <= 64 * CACHE the token's logits stay in
+// registers for all k rounds; larger E re-reads them (L1-resident) per round.
+template <int CACHE>
 __global__ __launch_bounds__(256) void k_route(const float* __restrict__ logits, int T, int E, int k,
                                                int* __restrict__ topk_ids, float* __restrict__ topk_w) {
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
   const float* row = logits + static_cast<size_t>(t) * E;
+  float cache[CACHE > 0 ? CACHE : 1];
+  if constexpr (CACHE > 0) {
+#pragma unroll
+    for (int c = 0; c < CACHE; ++c) {
+      const int i = lane + 64 * c;
+      cache[c] = i < E ? row[i] : -__builtin_huge_valf();
+    }
+  }
 
   // winners so far: everything strictly better than (last_v, last_id) is taken;
   // lane j keeps the j-th winner
@@ -48,12 +59,25 @@ __global__ __launch_bounds__(256) void k_route(const float* __restrict__ logits,
   for (int j = 0; j < k; ++j) {
     float bv = -__builtin_huge_valf();
     int bid = 0x7fffffff;
-    for (int i = lane; i < E; i += 64) {
-      const float v = row[i];
-      const bool eligible = v < last_v || (v == last_v && i > last_id);
-      if (eligible && better(v, i, bv, bid)) {
-        bv = v;
-        bid = i;
+    if constexpr (CACHE > 0) {
+#pragma unroll
+      for (int c = 0; c < CACHE; ++c) {
+        const int i = lane + 64 * c;
+        const float v = cache[c];
+        const bool eligible = i < E && (v < last_v || (v == last_v && i > last_id));
+        if (eligible && better(v, i, bv, bid)) {
+          bv = v;
+          bid = i;
+        }
+      }
+    } else {
+      for (int i = lane; i < E; i += 64) {
+        const float v = row[i];
+        const bool eligible = v < last_v || (v == last_v && i > last_id);
+        if (eligible && better(v, i, bv, bid)) {
+          bv = v;
+          bid = i;
+        }
       }
     }
 #pragma unroll
@@ -204,6 +228,66 @@ __global__ __launch_bounds__(256) void k_scatter(const int* __restrict__ ids, co
   if (perm_weight) perm_weight[p] = topk_w[f];
 }
 
+// ------------------------------------------------------------------ scan + scatter, one workgroup
+// For up to kSmallScatter assignments the scan and the scatter run in one
+// 1024-thread workgroup (one launch instead of two).
+static constexpr int kSmallScatter = 2048;
+
+__global__ __launch_bounds__(1024) void k_scan_scatter(int* __restrict__ chunk_hist, int nchunks, int E,
+                                                       int* __restrict__ counts, int* __restrict__ offsets,
+                                                       const int* __restrict__ ids, const float* __restrict__ topk_w,
+                                                       const int* __restrict__ local_rank, int n_asg, int k,
+                                                       int* __restrict__ perm_src_token,
+                                                       int* __restrict__ perm_of_assignment,
+                                                       float* __restrict__ perm_weight) {
+  __shared__ int part[1024];
+  const int tid = threadIdx.x;
+  const int per = (E + 1023) / 1024;
+  const int e0 = tid * per;
+  int local = 0;
+  for (int e = e0; e < e0 + per && e < E; ++e) {
+    int s = 0;
+    for (int c = 0; c < nchunks; ++c) {
+      int* h = chunk_hist + static_cast<size_t>(c) * E + e;
+      const int v = *h;
+      *h = s;
+      s += v;
+    }
+    counts[e] = s;
+    local += s;
+  }
+  part[tid] = local;
+  __syncthreads();
+  for (int off = 1; off < 1024; off <<= 1) {
+    const int v = tid >= off ? part[tid - off] : 0;
+    __syncthreads();
+    part[tid] += v;
+    __syncthreads();
+  }
+  int run = tid ? part[tid - 1] : 0;
+  for (int e = e0; e < e0 + per && e < E; ++e) {
+    offsets[e] = run;
+    const int c = counts[e];
+    for (int ch = 0; ch < nchunks; ++ch) chunk_hist[static_cast<size_t>(ch) * E + e] += run;
+    run += c;
+  }
+  if (tid == 1023) offsets[E] = part[1023];
+  // the scatter reads chunk bases that other threads just wrote to global
+  // memory: release them, then acquire (which also drops stale L1 lines) after
+  // the barrier
+  __threadfence();
+  __syncthreads();
+  __threadfence();
+  for (int f = tid; f < n_asg; f += 1024) {
+    const int e = min(max(ids[f], 0), E - 1);
+    int p = chunk_hist[static_cast<size_t>(f / kChunk) * E + e] + local_rank[f];
+    p = (p >= 0 && p < n_asg) ? p : 0;   // keeps a wrong rank inside the buffers
+    perm_src_token[p] = f / k;
+    perm_of_assignment[f] = p;
+    if (perm_weight) perm_weight[p] = topk_w[f];
+  }
+}
+
 // ------------------------------------------------------------------ host side
 size_t route_permute_ws_bytes(int T, int E, int k) {
   const size_t n = static_cast<size_t>(T) * k;
@@ -224,13 +308,23 @@ hipError_t launch_route_permute(const float* logits, int T, int E, int k, int* t
   int nbits = 0;
   while ((1 << nbits) <= E) ++nbits;   // bits needed for ids 0..E (E is the padding sentinel)
 
-  hipLaunchKernelGGL(k_route, dim3((T + 3) / 4), dim3(256), 0, stream, logits, T, E, k, topk_ids, topk_w);
+  if (E <= 256)
+    hipLaunchKernelGGL(k_route<4>, dim3((T + 3) / 4), dim3(256), 0, stream, logits, T, E, k, topk_ids, topk_w);
+  else if (E <= 1024)
+    hipLaunchKernelGGL(k_route<16>, dim3((T + 3) / 4), dim3(256), 0, stream, logits, T, E, k, topk_ids, topk_w);
+  else
+    hipLaunchKernelGGL(k_route<0>, dim3((T + 3) / 4), dim3(256), 0, stream, logits, T, E, k, topk_ids, topk_w);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL(k_chunk_rank, dim3(nchunks), dim3(kRankThreads), 4 * E * sizeof(int), stream, topk_ids,
                      n, E, nbits, local_rank, chunk_hist);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
+  if (n <= kSmallScatter) {
+    hipLaunchKernelGGL(k_scan_scatter, dim3(1), dim3(1024), 0, stream, chunk_hist, nchunks, E, counts, offsets,
+                       topk_ids, topk_w, local_rank, n, k, perm_src_token, perm_of_assignment, perm_weight);
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL(k_scan, dim3(1), dim3(1024), 0, stream, chunk_hist, nchunks, E, counts, offsets);
   err = hipGetLastError();
   if (err != hipSuccess) return err;

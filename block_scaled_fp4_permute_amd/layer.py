@@ -1,11 +1,18 @@
 """The NVFP4 MoE layer forward, composed from the five C entry points.
 
-route + permute -> quantise x -> gate_up grouped GEMM (rows gathered by token,
-SwiGLU + NVFP4 re-quantisation fused in the epilogue) -> down grouped GEMM
-(weighted scatter-add into a float32 accumulator fused in the epilogue) ->
-accumulator to bfloat16.  ``fused=False`` runs the same math with the
-unfused calls (float32 gate_up output, moe_swiglu, bf16 down output,
-moe_unpermute_combine).
+route + permute -> quantise x -> gate_up grouped GEMM (rows gathered by token)
+-> SwiGLU + NVFP4 re-quantisation -> down grouped GEMM -> weighted combine back
+to token order, bfloat16 out.
+
+Two independent choices:
+  swiglu="fused"   (default) the gate_up GEMM epilogue computes SwiGLU and
+                   writes NVFP4 h directly;
+  swiglu="separate" float32 gate_up output, then moe_swiglu;
+  combine="gather" (default) the down GEMM writes bf16 rows, then
+                   moe_unpermute_combine gathers each token's k rows
+                   (deterministic);
+  combine="atomic" the down GEMM epilogue scatter-adds weighted rows into a
+                   float32 accumulator (float32 atomics), then converts it.
 
 Buffers are allocated once per layer object (torch device memory); a forward
 allocates nothing.
@@ -78,9 +85,11 @@ def quantize_expert_weights(w_gu: torch.Tensor, w_dn: torch.Tensor) -> ExpertWei
 class MoELayer:
     """Preallocated NVFP4 MoE layer for T tokens."""
 
-    def __init__(self, T: int, H: int, I: int, E: int, k: int, device, fused: bool = True):
+    def __init__(self, T: int, H: int, I: int, E: int, k: int, device, swiglu: str = "fused",
+                 combine: str = "gather"):
+        assert swiglu in ("fused", "separate") and combine in ("gather", "atomic")
         self.T, self.H, self.I, self.E, self.k = T, H, I, E, k
-        self.fused = fused
+        self.swiglu, self.combine = swiglu, combine
         dev = torch.device(device)
         i32 = dict(dtype=torch.int32, device=dev)
         f32 = dict(dtype=torch.float32, device=dev)
@@ -95,10 +104,11 @@ class MoELayer:
                               torch.empty(1, **f32))
         self.hq = NVFP4Tensor(torch.empty((M, I // 2), **u8), torch.empty((M, I // 16), **u8), None)
         self.out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
-        if fused:
+        if swiglu == "separate":
+            self.y1 = torch.empty((M, 2 * I), **f32)
+        if combine == "atomic":
             self.acc = torch.empty((T, H), **f32)
         else:
-            self.y1 = torch.empty((M, 2 * I), **f32)
             self.y2 = torch.empty((M, H), dtype=torch.bfloat16, device=dev)
 
     def forward(self, logits: torch.Tensor, x: torch.Tensor, w: ExpertWeights, g_h: torch.Tensor,
@@ -118,11 +128,17 @@ class MoELayer:
         mark(1)
         nvfp4_quantize(x, out=self.xq, workspace=self.small_ws, stream=stream)
         mark(2)
-        if self.fused:
+        if self.swiglu == "fused":
             nvfp4_grouped_gemm(self.xq, w.gu_codes, w.gu_scales, w.gu_g, r.offsets, m_total=M,
                                a_rows=r.perm_src_token, epilogue=EPI_SWIGLU_NVFP4, out_codes=self.hq.codes,
                                out_scales=self.hq.scales, out_g=g_h, b_packed=w.gu_packed, stream=stream)
-            mark(3)
+        else:
+            nvfp4_grouped_gemm(self.xq, w.gu_codes, w.gu_scales, w.gu_g, r.offsets, m_total=M,
+                               a_rows=r.perm_src_token, epilogue=EPI_F32, out=self.y1, b_packed=w.gu_packed,
+                               stream=stream)
+            moe_swiglu(self.y1, g=g_h, out=self.hq, workspace=self.small_ws, stream=stream)
+        mark(3)
+        if self.combine == "atomic":
             self.acc.zero_()
             nvfp4_grouped_gemm(hq, w.dn_codes, w.dn_scales, w.dn_g, r.offsets, m_total=M,
                                epilogue=EPI_COMBINE_F32, out=self.acc, out_rows=T, row_token=r.perm_src_token,
@@ -130,11 +146,6 @@ class MoELayer:
             mark(4)
             moe_unpermute_combine(self.acc, None, None, T, 1, out=self.out, stream=stream)
         else:
-            nvfp4_grouped_gemm(self.xq, w.gu_codes, w.gu_scales, w.gu_g, r.offsets, m_total=M,
-                               a_rows=r.perm_src_token, epilogue=EPI_F32, out=self.y1, b_packed=w.gu_packed,
-                               stream=stream)
-            moe_swiglu(self.y1, g=g_h, out=self.hq, workspace=self.small_ws, stream=stream)
-            mark(3)
             nvfp4_grouped_gemm(hq, w.dn_codes, w.dn_scales, w.dn_g, r.offsets, m_total=M,
                                epilogue=EPI_BF16, out=self.y2, b_packed=w.dn_packed, stream=stream)
             mark(4)

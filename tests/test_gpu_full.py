@@ -21,18 +21,23 @@ def _g_h(cfg):
     return np.float32(np.float32(workloads.H_CALIBRATION_AMAX[cfg.index]) / np.float32(2688.0))
 
 
+MODES = [("fused", "gather"), ("separate", "atomic")]
+
+
 @pytest.mark.parametrize("cfg_index", [1, 2, 3])
-@pytest.mark.parametrize("fused", [True, False])
-def test_full_layer_sampled_tokens(cfg_index, fused):
+@pytest.mark.parametrize("mode", MODES)
+def test_full_layer_sampled_tokens(cfg_index, mode):
     cfg = workloads.CONFIGS[cfg_index]
-    print(f"full layer cfg={cfg_index} fused={fused}", flush=True)
+    swiglu, combine = mode
+    fused = combine == "atomic"          # float32 accumulation of the k rows (no bf16 rounding of y2)
+    print(f"full layer cfg={cfg_index} swiglu={swiglu} combine={combine}", flush=True)
     T, H, I, E, k = cfg.T, cfg.H, cfg.I, cfg.E, cfg.k
     logits = workloads.logits(cfg)
     x = workloads.activations(cfg)
     w_gu, w_dn = workloads.torch_expert_weights(cfg, DEV)
     wq = quantize_expert_weights(w_gu, w_dn).pack()     # the benchmark's configuration
     g_h = _g_h(cfg)
-    layer = MoELayer(T, H, I, E, k, DEV, fused=fused)
+    layer = MoELayer(T, H, I, E, k, DEV, swiglu=swiglu, combine=combine)
     out = layer.forward(up(logits), up(x).to(torch.bfloat16), wq, up(np.array([g_h], np.float32)))
     torch.cuda.synchronize()
     out = bf16_to_f32(out)
