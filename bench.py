@@ -45,7 +45,7 @@ def parse():
     ap.add_argument("--combine", choices=["gather", "atomic"], default="gather",
                     help="bf16 down output + gather combine, or float32 atomic scatter-add epilogue")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-experts", type=int, default=0, help="experts in the CPU-oracle sample (0: auto)")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="time budget of the CPU-oracle sample")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB 5 times (to scale HBM byte counters)")
     return ap.parse_args()
@@ -84,14 +84,19 @@ def measured_traffic(kernel: str, workload: str):
     return ent.get("bytes_per_launch")
 
 
-def cpu_baseline(cfg, logits_np, x_np, w_gu_dev, w_dn_dev, g_h, n_experts):
-    """The CPU oracle, as it stands, on a bounded sample of the same workload:
-    routing, permutation and activation quantisation over all T tokens, then for
-    ``n_experts`` experts (those with the lowest ids among the experts that got
-    tokens) gate_up GEMM of their routed rows, SwiGLU + re-quantisation, down
-    GEMM and the weighted combine of their rows.  Expert weights are quantised
-    by the oracle outside the timed region.  Returns the throughput in the
-    benchmark's unit (touched weight bytes per second)."""
+def cpu_baseline(cfg, logits_np, x_np, w_gu_dev, w_dn_dev, g_h, budget_s=15.0, pool=8):
+    """The CPU oracle, as it stands, on a bounded sample of the same workload.
+
+    Timed: whole layer steps, repeated - routing, permutation and activation
+    quantisation over all T tokens, then expert by expert (in id order, experts
+    with tokens only) the gate_up GEMM of the expert's routed rows, SwiGLU +
+    re-quantisation, the down GEMM and the weighted combine of its rows - until
+    ``budget_s`` seconds have passed (checked after each expert).  Expert
+    weights are quantised by the oracle outside the timed region; to keep that
+    preparation short, ``pool`` experts' weights are quantised and expert e
+    computes with pool[e % pool] (same shapes, so the same arithmetic volume).
+    Returns the throughput in the benchmark's unit: weight bytes of the experts
+    done per second."""
     import numpy as np
     from oracle import moe as OM
     from oracle import quant as OQ
@@ -100,33 +105,41 @@ def cpu_baseline(cfg, logits_np, x_np, w_gu_dev, w_dn_dev, g_h, n_experts):
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
     except Exception:  # pragma: no cover
         threads = 1
-    ids, w = OM.route(logits_np, cfg.k)
-    counts, offsets, src, perm_of, pw = OM.permute(ids, w, cfg.E)
-    experts = [e for e in range(cfg.E) if counts[e] > 0][:n_experts]
-    wq = {}
-    for e in experts:
-        wq[e] = (OQ.quantize(w_gu_dev[e].float().cpu().numpy()), OQ.quantize(w_dn_dev[e].float().cpu().numpy()))
+    wq = [(OQ.quantize(w_gu_dev[e].float().cpu().numpy()), OQ.quantize(w_dn_dev[e].float().cpu().numpy()))
+          for e in range(min(pool, cfg.E))]
+    done = rows_done = passes = 0
+    n_touched = 0
     t0 = time.perf_counter()
-    ids, w = OM.route(logits_np, cfg.k)
-    counts, offsets, src, perm_of, pw = OM.permute(ids, w, cfg.E)
-    xq = OQ.quantize(x_np)
-    out = np.zeros((cfg.T, cfg.H), np.float64)
-    for e in experts:
-        (gc, gs, gg), (dc, ds, dg) = wq[e]
-        p0, p1 = int(offsets[e]), int(offsets[e + 1])
-        rows = src[p0:p1]
-        off = np.array([0, p1 - p0])
-        y1, _ = OM.grouped_gemm(*xq, gc[None], gs[None], np.array([gg]), off, a_rows=rows, want_absdot=False)
-        hc, hs, hg, _ = OM.swiglu_quantize(y1, g_h)
-        y2, _ = OM.grouped_gemm(hc, hs, hg, dc[None], ds[None], np.array([dg]), off, want_absdot=False)
-        np.add.at(out, rows, pw[p0:p1, None].astype(np.float64) * y2)
+    while time.perf_counter() - t0 < budget_s:
+        ids, w = OM.route(logits_np, cfg.k)
+        counts, offsets, src, perm_of, pw = OM.permute(ids, w, cfg.E)
+        xq = OQ.quantize(x_np)
+        out = np.zeros((cfg.T, cfg.H), np.float64)
+        touched = [e for e in range(cfg.E) if counts[e] > 0]
+        n_touched = len(touched)
+        for e in touched:
+            (gc, gs, gg), (dc, ds, dg) = wq[e % len(wq)]
+            p0, p1 = int(offsets[e]), int(offsets[e + 1])
+            rows = src[p0:p1]
+            off = np.array([0, p1 - p0])
+            y1, _ = OM.grouped_gemm(*xq, gc[None], gs[None], np.array([gg]), off, a_rows=rows, want_absdot=False)
+            hc, hs, hg, _ = OM.swiglu_quantize(y1, g_h)
+            y2, _ = OM.grouped_gemm(hc, hs, hg, dc[None], ds[None], np.array([dg]), off, want_absdot=False)
+            np.add.at(out, rows, pw[p0:p1, None].astype(np.float64) * y2)
+            done += 1
+            rows_done += p1 - p0
+            if time.perf_counter() - t0 >= budget_s:
+                break
+        passes += 1
     dt = time.perf_counter() - t0
     per_expert = 3 * cfg.I * cfg.H * 9 // 16
-    return {"value": round(len(experts) * per_expert / dt / 1e9, 6), "unit": "GB/s", "cores": int(threads),
+    return {"value": round(done * per_expert / dt / 1e9, 6), "unit": "GB/s", "cores": int(threads),
             "kind": "oracle", "seconds": round(dt, 3),
-            "sample": f"{len(experts)} of {cfg.E} experts (their {int(sum(counts[e] for e in experts))} routed rows): "
-                      f"gate_up, SwiGLU+requant, down, weighted combine; routing, permutation and "
-                      f"activation quantisation over all {cfg.T} tokens; numpy, float64"}
+            "sample": f"{passes} pass(es) of the layer step, {done} expert GEMM pairs in all ({n_touched} touched "
+                      f"experts per step; {rows_done} routed rows; weights from a pool of {len(wq)} "
+                      f"oracle-quantised experts): gate_up, SwiGLU+requant, down, weighted combine, with routing, "
+                      f"permutation and activation quantisation over all {cfg.T} tokens each pass; numpy, float64; "
+                      f"stopped after {budget_s:g} s"}
 
 
 def main():
@@ -186,25 +199,34 @@ def main():
         layer.forward(logits, x, copies[i % 2], g_h)
     torch.cuda.synchronize()
 
-    # ---- timed region: exactly K steps
-    t0 = time.perf_counter()
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    ev0.record()
-    for i in range(args.steps):
-        layer.forward(logits, x, copies[i % 2], g_h)
-    ev1.record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms_per_step = ev0.elapsed_time(ev1) / args.steps
-
-    # ---- per-stage times (events on the launch stream around each call)
-    marks = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
-    for i in range(args.steps):
-        layer.forward(logits, x, copies[i % 2], g_h, marks=marks[i])
-    torch.cuda.synchronize()
+    # ---- timed region: exactly K steps.  Two events per step bracket the
+    # gate_up launch on the launch stream (its live average duration); the
+    # step time is the first event to the last.
     names = ["route_permute", "quantize_x", "gate_up_swiglu",
              "down" if args.combine == "gather" else "down_scatter_add",
              "combine" if args.combine == "gather" else "to_bf16"]
+
+    def ev():
+        return torch.cuda.Event(enable_timing=True)
+
+    t_start, t_end = ev(), ev()
+    gu_marks = [[None, None, ev(), ev(), None, None] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    t_start.record()
+    for i in range(args.steps):
+        layer.forward(logits, x, copies[i % 2], g_h, marks=gu_marks[i])
+    t_end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = t_start.elapsed_time(t_end) / args.steps
+    gu_ms = float(np.mean([m[2].elapsed_time(m[3]) for m in gu_marks]))
+
+    # ---- per-stage breakdown (after the timed region; events between all stages)
+    marks = [[ev() for _ in range(6)] for _ in range(args.steps)]
+    for i in range(args.steps):
+        layer.forward(logits, x, copies[i % 2], g_h, marks=marks[i])
+    torch.cuda.synchronize()
     stage_ms = {n: float(np.mean([m[j].elapsed_time(m[j + 1]) for m in marks])) for j, n in enumerate(names)}
 
     touched = int((counts > 0).sum())
@@ -217,7 +239,6 @@ def main():
 
     # dominant kernel: gate_up GEMM.  Algorithmic bytes per launch = touched
     # gate_up weights + the NVFP4 activations read once + the NVFP4 h written.
-    gu_ms = stage_ms[names[2]]
     gu_alg = touched * gu_bytes_e + T * H * 9 // 16 + T * k * I * 9 // 16
     achieved = gu_alg / (gu_ms * 1e-3) / 1e9
     wl_name = f"decode_moe_T{T}_H{H}_I{I}_E{E}_top{k}_{cfg.routing}"
@@ -238,6 +259,7 @@ def main():
         "dtype": "nvfp4 operands, f16 mfma, f32 accumulate",
         "data": "synthetic",
         "tflops": round(tflops, 3),
+        "gemm_weight_gbs": round(weight_bytes / ((stage_ms[names[2]] + stage_ms[names[3]]) * 1e-3) / 1e9, 2),
         "tflops_frac_f16_peak": round(tflops / MFMA_F16_PEAK_TFLOPS, 4),
         "weight_bytes": weight_bytes,
         "layer_flops": flops,
@@ -254,9 +276,8 @@ def main():
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
-        n = args.cpu_experts or (16 if args.workload >= 2 else 24)
         gh = float(g_h.cpu().numpy()[0])
-        res["cpu_baseline"] = cpu_baseline(cfg, logits_np, x_np, w_gu0, w_dn0, gh, n)
+        res["cpu_baseline"] = cpu_baseline(cfg, logits_np, x_np, w_gu0, w_dn0, gh, budget_s=args.cpu_seconds)
     print(json.dumps(res), flush=True)
 
 

@@ -113,14 +113,14 @@ class MoELayer:
 
     def forward(self, logits: torch.Tensor, x: torch.Tensor, w: ExpertWeights, g_h: torch.Tensor,
                 stream=None, marks=None) -> torch.Tensor:
-        """One layer step.  ``marks``: optional list of 6 torch.cuda.Event that are
-        recorded before routing and after each stage (route+permute, quantise x,
-        gate_up, down, to-bf16/combine) on the launch stream."""
+        """One layer step.  ``marks``: optional list of 6 torch.cuda.Event (or None
+        entries) recorded before routing and after each stage (route+permute,
+        quantise x, gate_up, down, to-bf16/combine) on the launch stream."""
         T, k, M = self.T, self.k, self.T * self.k
         hq = NVFP4Tensor(self.hq.codes, self.hq.scales, g_h)
 
         def mark(i):
-            if marks is not None:
+            if marks is not None and marks[i] is not None:
                 marks[i].record(stream)
 
         mark(0)
