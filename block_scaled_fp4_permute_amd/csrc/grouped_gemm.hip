@@ -152,10 +152,22 @@ __device__ __forceinline__ bool find_chunk(const GemmParams& p, int chunk, int& 
 // A rows (activations, row-major NVFP4) staged by this thread: pair pi ->
 // (row ar = (pi & 15) + 16 (pi >> 6), K group ag = (pi >> 4) & 3); the decoded
 // fragments of the pair go to LDS slot [(pi >> 6)][sub-step][pi & 63].
+// Buffer resources: loads give zero past the resource's byte count (the
+// hardware range check), so reads past the end of a row set or weight block
+// need no clamping.  The per-lane offset carries the whole byte offset, which
+// is what the range check sees.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr int kRawBufferFlags = 0x00020000;   // resource dword 3 for raw (untyped) buffer access
+constexpr int kLoadNT = 2;                    // cache policy: non-temporal
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0), static_cast<int>(bytes),
+                                           kRawBufferFlags);
+}
+
 template <int PPT>
 struct AState {
-  const uint8_t* row_code[PPT];    // start of the A row (always a valid row)
-  const uint8_t* row_scale[PPT];
+  rsrc_t rc, rs;                   // all A codes / all A scales
+  uint32_t vc[PPT], vs[PPT];       // byte offsets of the lane's K group in its A row
   bool ok[PPT];
   int ag[PPT];
 };
@@ -168,8 +180,10 @@ struct ARegs {
 
 template <int THREADS, int MT, int PPT>
 __device__ __forceinline__ void a_setup(const GemmParams& p, int row0, int m0, int rows, AState<PPT>& A) {
-  const size_t krow = static_cast<size_t>(p.K) / 2;
-  const size_t srow = static_cast<size_t>(p.K) / 16;
+  const uint32_t krow = static_cast<uint32_t>(p.K) / 2;
+  const uint32_t srow = static_cast<uint32_t>(p.K) / 16;
+  A.rc = make_rsrc(p.a_codes, static_cast<uint32_t>(p.a_rows_total) * krow);
+  A.rs = make_rsrc(p.a_scales, static_cast<uint32_t>(p.a_rows_total) * srow);
 #pragma unroll
   for (int q = 0; q < PPT; ++q) {
     const int pi = threadIdx.x + q * THREADS;
@@ -179,28 +193,29 @@ __device__ __forceinline__ void a_setup(const GemmParams& p, int row0, int m0, i
     int arow = row0 + m0 + (A.ok[q] ? ar : 0);
     if (p.a_rows) arow = p.a_rows[arow];
     arow = (arow >= 0 && arow < p.a_rows_total) ? arow : 0;
-    A.row_code[q] = p.a_codes + static_cast<size_t>(arow) * krow;
-    A.row_scale[q] = p.a_scales + static_cast<size_t>(arow) * srow;
+    A.vc[q] = static_cast<uint32_t>(arow) * krow + 32u * ag;
+    A.vs[q] = static_cast<uint32_t>(arow) * srow + 4u * ag;
     A.ag[q] = ag;
   }
 }
 
-// Loads are unconditional from always-valid addresses (each 32-K half is
-// clamped into its row) so the compiler can keep steps in flight; a half past
-// K, or a row that does not exist, gets a zero block scale where it is used,
-// which zeroes all its decoded values.  Activation rows are re-read by the
-// column tiles of a chunk, so they use ordinary (L2-allocating) loads.
-__device__ __forceinline__ int clamp_k(int k, int K) { return min(k, K - 32); }
-
+// Loads are unconditional (no branch keeps steps in flight with exact wait
+// counts); a half past K reads the next row (or zeros past the last row) and
+// gets a zero block scale where it is used, which zeroes all its decoded
+// values, as does a row that does not exist.  Activation rows are re-read by
+// the column tiles of a chunk, so they use ordinary (L2-allocating) loads.
 template <int PPT>
 __device__ __forceinline__ void a_load(const AState<PPT>& A, ARegs<PPT>& R, int k0, int K) {
+  // steps past K re-read the last step (cached) instead of fetching new bytes
+  const uint32_t kq = static_cast<uint32_t>(min(k0, ((K - 1) / KSTEP) * KSTEP));
+  const uint32_t kc = kq / 2;
+  const uint32_t ks = kq / 16;
 #pragma unroll
   for (int q = 0; q < PPT; ++q)
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      const int kk = clamp_k(k0 + 64 * A.ag[q] + 32 * h, K);
-      R.c[q][h] = *reinterpret_cast<const u32x4*>(A.row_code[q] + kk / 2);
-      R.s[q][h] = *reinterpret_cast<const uint16_t*>(A.row_scale[q] + kk / 16);
+      R.c[q][h] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(A.rc, A.vc[q] + kc + 16u * h, 0, 0));
+      R.s[q][h] = __builtin_amdgcn_raw_buffer_load_b16(A.rs, A.vs[q] + ks + 2u * h, 0, 0);
     }
 }
 
@@ -211,7 +226,10 @@ __device__ __forceinline__ void a_store(const AState<PPT>& A, const ARegs<PPT>& 
 #pragma unroll
   for (int q = 0; q < PPT; ++q) {
     const int pi = threadIdx.x + q * THREADS;
-    if (pi < MT * 64 && (pi >> 6) < MTA) {
+    // compile-time true in the common shapes, so the store stays branch-free
+    const bool in_chunk = (THREADS * PPT <= MT * 64) || pi < MT * 64;
+    const bool active = (MTA == MT) || (pi >> 6) < MTA;
+    if (in_chunk && active) {
       half8* dst = lds + (pi >> 6) * 8 * 64 + (pi & 63);
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
@@ -228,6 +246,44 @@ __device__ __forceinline__ void a_store(const AState<PPT>& A, const ARegs<PPT>& 
         dst[(4 * h + 3) * 64] = decode8_f16(c.w, s1);
       }
     }
+  }
+}
+
+// The same decode split into 8 * PPT pieces (pair q, 32-K half h, code dword
+// w), so that it can be interleaved with MFMAs: a_scales first turns the
+// block scales of the step into (masked) FP16 multipliers.
+template <int PPT>
+struct AScales {
+  _Float16 s[PPT][2][2];
+};
+
+template <int PPT>
+__device__ __forceinline__ void a_scales(const AState<PPT>& A, const ARegs<PPT>& R, int k0, int K,
+                                         AScales<PPT>& S) {
+#pragma unroll
+  for (int q = 0; q < PPT; ++q)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const bool ok = A.ok[q] && (k0 + 64 * A.ag[q] + 32 * h) < K;
+      const uint32_t as = ok ? R.s[q][h] : 0u;
+      S.s[q][h][0] = e4m3_to_f16_div256(as);
+      S.s[q][h][1] = e4m3_to_f16_div256(as >> 8);
+    }
+}
+
+template <int THREADS, int MT, int MTA, int PPT>
+__device__ __forceinline__ void a_store_piece(const ARegs<PPT>& R, const AScales<PPT>& S, half8* __restrict__ lds,
+                                              int piece) {
+  const int q = piece >> 3;
+  const int h = (piece >> 2) & 1;
+  const int w = piece & 3;
+  const int pi = threadIdx.x + q * THREADS;
+  const bool in_chunk = (THREADS * PPT <= MT * 64) || pi < MT * 64;
+  const bool active = (MTA == MT) || (pi >> 6) < MTA;
+  if (in_chunk && active) {
+    const u32x4 c = R.c[q][h];
+    const uint32_t word = w == 0 ? c.x : w == 1 ? c.y : w == 2 ? c.z : c.w;
+    lds[(pi >> 6) * 8 * 64 + (4 * h + w) * 64 + (pi & 63)] = decode8_f16(word, S.s[q][h][w >> 1]);
   }
 }
 
@@ -249,13 +305,17 @@ __device__ __forceinline__ half8 b_frag(const BRegs& b, uint32_t scale4, int d) 
   return decode8_f16(word_of(b, d), e4m3_to_f16_div256(scale4 >> (8 * (d >> 1))));
 }
 
-// packed tile: contiguous, zero padded, streamed with non-temporal loads
-__device__ __forceinline__ void b_load_packed(const uint8_t* tile, BRegs& b) {
-  const int lane = threadIdx.x & 63;
-  b.c[0] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(tile + 16 * lane));
-  b.c[1] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(tile + 1024 + 16 * lane));
-  b.s = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(tile + 2048 + 4 * lane));
+// packed tile: contiguous, zero padded, streamed with non-temporal loads from
+// the expert's weight block (rb); tile_off is the tile's byte offset in the
+// block.  Past the block's end the loads give zeros.
+__device__ __forceinline__ void b_load_packed(rsrc_t rb, uint32_t tile_off, BRegs& b) {
+  const uint32_t lane = threadIdx.x & 63;
+  b.c[0] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rb, tile_off + 16u * lane, 0, kLoadNT));
+  b.c[1] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rb, tile_off + 1024u + 16u * lane, 0, kLoadNT));
+  b.s = __builtin_amdgcn_raw_buffer_load_b32(rb, tile_off + 2048u + 4u * lane, 0, kLoadNT);
 }
+
+__device__ __forceinline__ int clamp_k(int k, int K) { return min(k, K - 32); }
 
 // row-major B row (always a valid row): 32 code bytes and 4 scale bytes of the
 // lane's K range, each 32-K half clamped into the row; the caller zeroes the
@@ -299,7 +359,13 @@ __device__ __forceinline__ void epilogue_tile(const GemmParams& p, const float4v
 }
 
 // SwiGLU + NVFP4 re-quantisation of one 16-row tile: gate and up accumulators
-// of the same h column; a 16-column h block lives in the 16 lanes of a group.
+// of the same h column; a 16-column h block lives in the 16 lanes of a row,
+// lane (lr, lg) holding rows 4 lg + i.  The block scales of the 4 rows a lane
+// group holds are computed once: lane lr takes row 4 lg + (lr & 3), and the
+// results are broadcast back inside each quad.  The block scale follows the
+// quantiser exactly (two correctly rounded divisions); silu and the element
+// quotient use reciprocal-based divisions, whose ~2 ulp sit far inside the
+// rounding differences h already carries.
 __device__ __forceinline__ void epilogue_swiglu(const GemmParams& p, const float4v& gate_acc,
                                                 const float4v& up_acc, int prow0, int rows_left, int hc,
                                                 bool hc_ok, float gab) {
@@ -307,24 +373,32 @@ __device__ __forceinline__ void epilogue_swiglu(const GemmParams& p, const float
   const int lg = (threadIdx.x & 63) >> 4;
   const int I = p.N / 2;
   const float gh = p.out_g[0];
+  float h[4], am[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    h[i] = silu_fast(gate_acc[i] * gab) * (up_acc[i] * gab);
+    am[i] = row16_max(fabsf(h[i]));
+  }
+  const int q = lr & 3;
+  const float amq = q == 0 ? am[0] : q == 1 ? am[1] : q == 2 ? am[2] : am[3];
+  const uint32_t sq = f32_to_e4m3_sat((amq / 6.0f) / gh);
+  const float seq = e4m3_to_f32(sq) * gh;
+  uint32_t s[4];
+  float se[4];
+  s[0] = dpp_u32<0x00>(sq); se[0] = __uint_as_float(dpp_u32<0x00>(__float_as_uint(seq)));   // quad_perm [0,0,0,0]
+  s[1] = dpp_u32<0x55>(sq); se[1] = __uint_as_float(dpp_u32<0x55>(__float_as_uint(seq)));   // quad_perm [1,1,1,1]
+  s[2] = dpp_u32<0xAA>(sq); se[2] = __uint_as_float(dpp_u32<0xAA>(__float_as_uint(seq)));   // quad_perm [2,2,2,2]
+  s[3] = dpp_u32<0xFF>(sq); se[3] = __uint_as_float(dpp_u32<0xFF>(__float_as_uint(seq)));   // quad_perm [3,3,3,3]
+  if (lr < 4 && 4 * lg + lr < rows_left && hc_ok)
+    p.out_scales[static_cast<size_t>(prow0 + 4 * lg + lr) * (I / 16) + hc / 16] = static_cast<uint8_t>(sq);
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int m = 4 * lg + i;
-    const float h = silu_f32(gate_acc[i] * gab) * (up_acc[i] * gab);
-    float amax = fabsf(h);
-    amax = fmaxf(amax, __shfl_xor(amax, 1));
-    amax = fmaxf(amax, __shfl_xor(amax, 2));
-    amax = fmaxf(amax, __shfl_xor(amax, 4));
-    amax = fmaxf(amax, __shfl_xor(amax, 8));
-    const uint32_t s = f32_to_e4m3_sat((amax / 6.0f) / gh);
-    const float scale_eff = e4m3_to_f32(s) * gh;
-    const uint32_t code = encode_one(h, s, scale_eff);
-    const uint32_t other = __shfl_xor(code, 1);
-    if (m < rows_left && hc_ok) {
-      const size_t prow = static_cast<size_t>(prow0 + m);
-      if ((lr & 1) == 0) p.out_codes[prow * (I / 2) + hc / 2] = static_cast<uint8_t>(code | (other << 4));
-      if (lr == 0) p.out_scales[prow * (I / 16) + hc / 16] = static_cast<uint8_t>(s);
-    }
+    const float v = (s[i] != 0u && se[i] > 0.0f) ? __fdividef(fabsf(h[i]), se[i]) : 0.0f;
+    const uint32_t code = (s[i] != 0u) ? (f32_to_e2m1_mag(v) | ((__float_as_uint(h[i]) >> 31) << 3)) : 0u;
+    const uint32_t other = dpp_u32<kDppXor1>(code);
+    if (m < rows_left && hc_ok && (lr & 1) == 0)
+      p.out_codes[static_cast<size_t>(prow0 + m) * (I / 2) + hc / 2] = static_cast<uint8_t>(code | (other << 4));
   }
 }
 
@@ -332,95 +406,109 @@ __device__ __forceinline__ void epilogue_swiglu(const GemmParams& p, const float
 template <int WN, int PPT>
 struct KCtx {
   AState<PPT> A;
-  const uint8_t* b_code[WN];     // row-major: B row start; packed: first tile of the column tile
+  const uint8_t* b_code[WN];     // row-major: B row start
   const uint8_t* b_scale[WN];
+  rsrc_t rb;                     // packed: the expert's weight block
+  uint32_t b_tile0[WN];          // packed: byte offset of the column tile's first K step in the block
   bool bok[WN];
   int K;
   int nsteps;
 };
 
-template <int WN, int PPT>
-struct KRegs {
-  ARegs<PPT> a;
-  BRegs b[WN];
-};
-
 template <int WN, int PPT, bool PACKED>
-__device__ __forceinline__ void k_load(const KCtx<WN, PPT>& c, KRegs<WN, PPT>& R, int st) {
-  a_load(c.A, R.a, st * KSTEP, c.K);
+__device__ __forceinline__ void k_load_b(const KCtx<WN, PPT>& c, BRegs (&B)[WN], int st) {
   const int lg = (threadIdx.x & 63) >> 4;
 #pragma unroll
   for (int j = 0; j < WN; ++j) {
     if constexpr (PACKED)
-      b_load_packed(c.b_code[j] + static_cast<size_t>(min(st, c.nsteps - 1)) * PTILE, R.b[j]);
+      b_load_packed(c.rb, c.b_tile0[j] + static_cast<uint32_t>(min(st, c.nsteps - 1)) * PTILE, B[j]);
     else
-      b_load_rows(c.b_code[j], c.b_scale[j], lg, st * KSTEP, c.K, R.b[j]);
+      b_load_rows(c.b_code[j], c.b_scale[j], lg, st * KSTEP, c.K, B[j]);
   }
 }
 
+// One K step: the MFMAs of step st (A fragments from lds_cur, weights decoded
+// from registers), with the decode of step st+1's activation rows into
+// lds_nxt interleaved - both in one basic block, so the VALU work of the
+// decodes overlaps the matrix-core work - then the step's barrier.
 template <int NW, int WN, int MT, int MTA, int PPT, bool PACKED>
-__device__ __forceinline__ void k_consume(const KCtx<WN, PPT>& c, const KRegs<WN, PPT>& R, int st,
-                                          half8* __restrict__ lds, float4v (&acc)[MT][WN]) {
+__device__ __forceinline__ void k_step(const KCtx<WN, PPT>& c, const ARegs<PPT>& a_nxt, const BRegs (&B)[WN],
+                                       int st, const half8* __restrict__ lds_cur, half8* __restrict__ lds_nxt,
+                                       float4v (&acc)[MT][WN]) {
   const int lane = threadIdx.x & 63;
   const int lg = lane >> 4;
   const int k0 = st * KSTEP;
-  a_store<NW * 64, MT, MTA, PPT>(c.A, R.a, k0, c.K, lds);
   uint32_t bs[WN];
 #pragma unroll
   for (int j = 0; j < WN; ++j) {
     if constexpr (PACKED) {
-      bs[j] = (st < c.nsteps) ? R.b[j].s : 0u;     // packed tiles are zero padded past N and K
+      bs[j] = (st < c.nsteps) ? B[j].s : 0u;     // packed tiles are zero padded past N and K
     } else {
       const bool lo = c.bok[j] && (k0 + 64 * lg) < c.K;
       const bool hi = c.bok[j] && (k0 + 64 * lg + 32) < c.K;
-      bs[j] = (lo ? (R.b[j].s & 0xFFFFu) : 0u) | (hi ? (R.b[j].s & 0xFFFF0000u) : 0u);
+      bs[j] = (lo ? (B[j].s & 0xFFFFu) : 0u) | (hi ? (B[j].s & 0xFFFF0000u) : 0u);
     }
   }
-  __syncthreads();
+  AScales<PPT> as;
+  a_scales(c.A, a_nxt, k0 + KSTEP, c.K, as);
 #pragma unroll
   for (int s = 0; s < 8; ++s) {
     half8 af[MTA];
 #pragma unroll
-    for (int r = 0; r < MTA; ++r) af[r] = lds[(r * 8 + s) * 64 + lane];
+    for (int r = 0; r < MTA; ++r) af[r] = lds_cur[(r * 8 + s) * 64 + lane];
     half8 bf[WN];
 #pragma unroll
-    for (int j = 0; j < WN; ++j) bf[j] = b_frag(R.b[j], bs[j], s);
+    for (int j = 0; j < WN; ++j) bf[j] = b_frag(B[j], bs[j], s);
 #pragma unroll
     for (int r = 0; r < MTA; ++r)
 #pragma unroll
       for (int j = 0; j < WN; ++j)
         acc[r][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[r], bf[j], acc[r][j], 0, 0, 0);
+    // an eighth of the next step's activation decode rides behind these MFMAs
+#pragma unroll
+    for (int q = 0; q < PPT; ++q) a_store_piece<NW * 64, MT, MTA, PPT>(a_nxt, as, lds_nxt, 8 * q + s);
   }
+  __syncthreads();
 }
 
-// Software-pipelined K loop: two register sets alternate, so the loads of
-// step s+2 are in flight while step s computes (no register copies, which
-// would force a wait on the outstanding loads).  The body has no branches: a
-// step past K (odd step counts, and the prefetches after the last step) reads
-// valid clamped addresses and its data is masked to zero, which keeps the wait
-// counts exact.
+// Software-pipelined K loop.  Register sets alternate, so the loads of later
+// steps are in flight while a step computes, with no register copies (a copy
+// would force a wait on the outstanding loads): weights two steps ahead,
+// activation rows one to two steps ahead of their decode, which itself runs
+// one step ahead of the MFMAs (double-buffered LDS fragments).  The body has
+// no branches: a step past K (an odd step count, and the prefetches after the
+// last step) reads valid clamped addresses and its data is masked to zero,
+// which keeps the wait counts exact.
 template <int NW, int WN, int MT, int MTA, int PPT, bool PACKED>
 __device__ __forceinline__ void k_main_loop(const KCtx<WN, PPT>& c, half8* __restrict__ lds0,
                                             half8* __restrict__ lds1, float4v (&acc)[MT][WN]) {
-  KRegs<WN, PPT> R0, R1;
-  k_load<WN, PPT, PACKED>(c, R0, 0);
-  k_load<WN, PPT, PACKED>(c, R1, 1);
+  BRegs b0[WN], b1[WN];
+  ARegs<PPT> a0, a1;
+  a_load(c.A, a0, 0, c.K);
+  k_load_b<WN, PPT, PACKED>(c, b0, 0);
+  a_load(c.A, a1, KSTEP, c.K);
+  k_load_b<WN, PPT, PACKED>(c, b1, 1);
+  a_store<NW * 64, MT, MTA, PPT>(c.A, a0, 0, c.K, lds0);
+  __syncthreads();
+  a_load(c.A, a0, 2 * KSTEP, c.K);
   for (int st = 0; st < c.nsteps; st += 2) {
-    k_consume<NW, WN, MT, MTA, PPT, PACKED>(c, R0, st, lds0, acc);
-    k_load<WN, PPT, PACKED>(c, R0, st + 2);
-    k_consume<NW, WN, MT, MTA, PPT, PACKED>(c, R1, st + 1, lds1, acc);
-    k_load<WN, PPT, PACKED>(c, R1, st + 3);
+    k_step<NW, WN, MT, MTA, PPT, PACKED>(c, a1, b0, st, lds0, lds1, acc);
+    k_load_b<WN, PPT, PACKED>(c, b0, st + 2);
+    a_load(c.A, a1, (st + 3) * KSTEP, c.K);
+    k_step<NW, WN, MT, MTA, PPT, PACKED>(c, a0, b1, st + 1, lds1, lds0, acc);
+    k_load_b<WN, PPT, PACKED>(c, b1, st + 3);
+    a_load(c.A, a0, (st + 4) * KSTEP, c.K);
   }
 }
 
-template <int NW, int WN, int MT, int EPI, bool PACKED>
-__global__ __launch_bounds__(NW * 64) void k_gemm_streamk(const GemmParams p) {
+template <int NW, int WN, int MT, int EPI, bool PACKED, int MINB>
+__global__ __launch_bounds__(NW * 64, MINB) void k_gemm_streamk(const GemmParams p) {
   constexpr int THREADS = NW * 64;
   constexpr int MC = MT * 16;
   constexpr int BN = NW * WN * 16;
   constexpr int PPT = (MT * 64 + THREADS - 1) / THREADS;   // A (row, K group) pairs per thread
   static_assert(EPI != EPI_SWIGLU || (WN % 2) == 0, "SwiGLU pairs gate and up tiles");
-  static_assert(MT >= 1 && MT <= 4, "row tiles per chunk");
+  static_assert(MT == 1 || MT == 2 || MT == 3 || MT == 4 || MT == 6 || MT == 8, "row tiles per chunk");
   __shared__ half8 a_lds[2][MT * 8 * 64];   // double-buffered [row tile][sub-step][lane] fragments
   __shared__ int s_part[NW];
   __shared__ int s_work[2];
@@ -460,8 +548,11 @@ __global__ __launch_bounds__(NW * 64) void k_gemm_streamk(const GemmParams p) {
     }
     if constexpr (PACKED) {
       const int ntr = (N + 15) / 16;
-      const int rt = min(col0[j] / 16, ntr - 1);
-      c.b_code[j] = p.b_packed + (static_cast<size_t>(e) * ntr + rt) * c.nsteps * PTILE;
+      const uint32_t block = static_cast<uint32_t>(ntr) * c.nsteps * PTILE;
+      c.rb = make_rsrc(p.b_packed + static_cast<size_t>(e) * block, block);
+      // a column tile past N lies past the block: its loads give zeros
+      c.b_tile0[j] = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(col0[j] / 16)) * c.nsteps * PTILE;
+      c.b_code[j] = nullptr;
       c.b_scale[j] = nullptr;
     } else {
       const size_t brow = static_cast<size_t>(e) * N + (c.bok[j] ? col0[j] + lr : 0);
@@ -478,11 +569,15 @@ __global__ __launch_bounds__(NW * 64) void k_gemm_streamk(const GemmParams p) {
 #pragma unroll
     for (int j = 0; j < WN; ++j) acc[r][j] = float4v{0.f, 0.f, 0.f, 0.f};
 
+  half8* lds0 = a_lds[0];
+  half8* lds1 = a_lds[1];
   switch (mt_active) {
-    case 1: k_main_loop<NW, WN, MT, 1, PPT, PACKED>(c, a_lds[0], a_lds[1], acc); break;
-    case 2: if constexpr (MT >= 2) k_main_loop<NW, WN, MT, 2, PPT, PACKED>(c, a_lds[0], a_lds[1], acc); break;
-    case 3: if constexpr (MT >= 3) k_main_loop<NW, WN, MT, 3, PPT, PACKED>(c, a_lds[0], a_lds[1], acc); break;
-    default: if constexpr (MT >= 4) k_main_loop<NW, WN, MT, MT, PPT, PACKED>(c, a_lds[0], a_lds[1], acc); break;
+    case 1: k_main_loop<NW, WN, MT, 1, PPT, PACKED>(c, lds0, lds1, acc); break;
+    case 2: if constexpr (MT >= 2) k_main_loop<NW, WN, MT, 2, PPT, PACKED>(c, lds0, lds1, acc); break;
+    case 3: if constexpr (MT >= 3) k_main_loop<NW, WN, MT, 3, PPT, PACKED>(c, lds0, lds1, acc); break;
+    case 4: if constexpr (MT >= 4) k_main_loop<NW, WN, MT, 4, PPT, PACKED>(c, lds0, lds1, acc); break;
+    case 5: case 6: if constexpr (MT >= 6) k_main_loop<NW, WN, MT, 6, PPT, PACKED>(c, lds0, lds1, acc); break;
+    default: if constexpr (MT >= 8) k_main_loop<NW, WN, MT, MT, PPT, PACKED>(c, lds0, lds1, acc); break;
   }
 
   const int prow0 = row0 + m0;
@@ -554,16 +649,17 @@ __device__ __forceinline__ void store_unit(const GemmParams& p, const float4v (&
 
 template <int NW, int MT, int MTA, int UPW, int EPI>
 __device__ __forceinline__ void n_main_loop(const GemmParams& p, const half8* __restrict__ lds, float* stage,
-                                            const uint8_t* tiles, int u_first, int u_count, int ntr, int prow0,
+                                            rsrc_t rb, int u_first, int u_count, int ntr, int prow0,
                                             int rows, float gab) {
   const int lane = threadIdx.x & 63;
   const int lr = lane & 15;
   BRegs R0[UNIT], R1[UNIT];
   auto load_unit = [&](BRegs (&R)[UNIT], int i) {
-    const int ui = u_first + min(i, u_count - 1);
+    // tiles past the expert's block (the last unit's padding, prefetches past
+    // the wave's run) read zeros
+    const uint32_t ui = static_cast<uint32_t>(u_first + min(i, u_count - 1));   // re-read (cached), not new bytes
 #pragma unroll
-    for (int t = 0; t < UNIT; ++t)
-      b_load_packed(tiles + static_cast<size_t>(min(UNIT * ui + t, ntr - 1)) * PTILE, R[t]);
+    for (int t = 0; t < UNIT; ++t) b_load_packed(rb, (UNIT * ui + t) * PTILE, R[t]);
   };
   auto consume = [&](const BRegs (&R)[UNIT], int i) {
     float4v acc[MTA][UNIT];
@@ -643,15 +739,16 @@ __global__ __launch_bounds__(NW * 64) void k_gemm_streamn(const GemmParams p) {
   const int u_first = (ng * NW + wave) * UPW;
   const int u_count = min(UPW, nunits - u_first);
   if (u_count <= 0) return;
-  const uint8_t* tiles = p.b_packed + static_cast<size_t>(e) * ntr * PTILE;
+  const uint32_t block = static_cast<uint32_t>(ntr) * PTILE;    // K <= 256: one tile per 16 rows
+  const rsrc_t rb = make_rsrc(p.b_packed + static_cast<size_t>(e) * block, block);
   const float gab = p.a_g[0] * p.b_g[e];
   const int prow0 = row0 + m0;
   float* stage = stage_lds[wave];
   switch (mt_active) {
-    case 1: n_main_loop<NW, MT, 1, UPW, EPI>(p, a_lds, stage, tiles, u_first, u_count, ntr, prow0, rows, gab); break;
-    case 2: if constexpr (MT >= 2) n_main_loop<NW, MT, 2, UPW, EPI>(p, a_lds, stage, tiles, u_first, u_count, ntr, prow0, rows, gab); break;
-    case 3: if constexpr (MT >= 3) n_main_loop<NW, MT, 3, UPW, EPI>(p, a_lds, stage, tiles, u_first, u_count, ntr, prow0, rows, gab); break;
-    default: if constexpr (MT >= 4) n_main_loop<NW, MT, MT, UPW, EPI>(p, a_lds, stage, tiles, u_first, u_count, ntr, prow0, rows, gab); break;
+    case 1: n_main_loop<NW, MT, 1, UPW, EPI>(p, a_lds, stage, rb, u_first, u_count, ntr, prow0, rows, gab); break;
+    case 2: if constexpr (MT >= 2) n_main_loop<NW, MT, 2, UPW, EPI>(p, a_lds, stage, rb, u_first, u_count, ntr, prow0, rows, gab); break;
+    case 3: if constexpr (MT >= 3) n_main_loop<NW, MT, 3, UPW, EPI>(p, a_lds, stage, rb, u_first, u_count, ntr, prow0, rows, gab); break;
+    default: if constexpr (MT >= 4) n_main_loop<NW, MT, MT, UPW, EPI>(p, a_lds, stage, rb, u_first, u_count, ntr, prow0, rows, gab); break;
   }
 }
 
@@ -660,7 +757,7 @@ static hipError_t grid_check(int64_t blocks) {
   return blocks >= (int64_t(1) << 31) ? hipErrorInvalidConfiguration : hipSuccess;
 }
 
-template <int NW, int WN, int MT, int EPI, bool PACKED>
+template <int NW, int WN, int MT, int EPI, bool PACKED, int MINB = 1>
 static hipError_t launch_streamk(GemmParams prm, int64_t m_total, hipStream_t stream) {
   constexpr int BN = NW * WN * 16;
   constexpr int MC = MT * 16;
@@ -670,7 +767,7 @@ static hipError_t launch_streamk(GemmParams prm, int64_t m_total, hipStream_t st
   // sum over experts of ceil(Me / MC) <= m_total / MC + E
   const int64_t blocks = ((m_total + MC - 1) / MC + prm.E) * prm.n_tiles;
   if (grid_check(blocks) != hipSuccess) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((k_gemm_streamk<NW, WN, MT, EPI, PACKED>), dim3(static_cast<unsigned>(blocks)), dim3(NW * 64),
+  hipLaunchKernelGGL((k_gemm_streamk<NW, WN, MT, EPI, PACKED, MINB>), dim3(static_cast<unsigned>(blocks)), dim3(NW * 64),
                      0, stream, prm);
   return hipGetLastError();
 }
@@ -692,7 +789,13 @@ static hipError_t launch_k(const GemmParams& prm, int epilogue, int64_t m_total,
   switch (epilogue) {
     case EPI_F32: return launch_streamk<4, 2, 4, EPI_F32, PACKED>(prm, m_total, stream);
     case EPI_BF16: return launch_streamk<4, 2, 4, EPI_BF16, PACKED>(prm, m_total, stream);
-    case EPI_SWIGLU: return launch_streamk<4, 2, 4, EPI_SWIGLU, PACKED>(prm, m_total, stream);
+#ifndef GU_NW
+#define GU_NW 4
+#define GU_WN 2
+#define GU_MT 4
+#define GU_MINB 1
+#endif
+    case EPI_SWIGLU: return launch_streamk<GU_NW, GU_WN, GU_MT, EPI_SWIGLU, PACKED, GU_MINB>(prm, m_total, stream);
     case EPI_COMBINE: return launch_streamk<4, 2, 4, EPI_COMBINE, PACKED>(prm, m_total, stream);
     default: return hipErrorInvalidValue;
   }

@@ -143,6 +143,31 @@ __device__ __forceinline__ half8 decode8_f16(uint32_t w, _Float16 scale_div256) 
 // ------------------------------------------------------------------ misc
 __device__ __forceinline__ float silu_f32(float x) { return x / (1.0f + expf(-x)); }
 
+// silu with a reciprocal-based division (at most ~2 ulp from silu_f32); used
+// where the result is re-quantised from values that already differ from the
+// exact ones by rounding.
+__device__ __forceinline__ float silu_fast(float x) { return __fdividef(x, 1.0f + expf(-x)); }
+
+// ------------------------------------------------------------------ 16-lane rows
+// DPP lane exchanges inside each row of 16 lanes (no LDS round trip).
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+  return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), CTRL, 0xF, 0xF, false));
+}
+constexpr int kDppXor1 = 0xB1;         // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4E;         // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141;  // lane i <-> 7 - i within each 8-lane half
+constexpr int kDppMirror = 0x140;      // lane i <-> 15 - i within the row
+
+// maximum over the 16 lanes of the row, returned to every lane of the row
+__device__ __forceinline__ float row16_max(float v) {
+  v = fmaxf(v, __uint_as_float(dpp_u32<kDppXor1>(__float_as_uint(v))));
+  v = fmaxf(v, __uint_as_float(dpp_u32<kDppXor2>(__float_as_uint(v))));
+  v = fmaxf(v, __uint_as_float(dpp_u32<kDppHalfMirror>(__float_as_uint(v))));
+  v = fmaxf(v, __uint_as_float(dpp_u32<kDppMirror>(__float_as_uint(v))));
+  return v;
+}
+
 // The 8 XCDs of the chip take workgroups round-robin (workgroup i runs on XCD
 // i % 8).  Remap so that each XCD receives a contiguous range of tasks, which
 // keeps neighbouring tasks (same expert, same A rows) in one L2.
