@@ -113,12 +113,9 @@ int nvfp4_grouped_gemm(const nvfp4moe_gemm_args* a, void* stream) {
     return fail(NVFP4MOE_ERR_INVALID, "nvfp4_grouped_gemm: codes and packed tiles must be 16-byte, scales 2-byte aligned");
   if (a->m_total >= (int64_t(1) << 31) || a->a_rows_total >= (int64_t(1) << 31))
     return fail(NVFP4MOE_ERR_UNSUPPORTED, "nvfp4_grouped_gemm: more than 2^31 rows");
-  // the kernels address A, and each expert's packed weight block, with 32-bit
-  // byte offsets
+  // the kernels address A with 32-bit byte offsets
   if (a->a_rows_total * (int64_t(a->K) / 2) >= (int64_t(1) << 31))
     return fail(NVFP4MOE_ERR_UNSUPPORTED, "nvfp4_grouped_gemm: A codes of 2 GiB or more (a_rows_total * K / 2)");
-  if (a->b_packed && int64_t(a->N) * ((int64_t(a->K) + 255) / 256) * 144 >= (int64_t(1) << 31))
-    return fail(NVFP4MOE_ERR_UNSUPPORTED, "nvfp4_grouped_gemm: packed weight block of one expert of 2 GiB or more");
   if (static_cast<int64_t>(a->E) * a->N >= (int64_t(1) << 31))
     return fail(NVFP4MOE_ERR_UNSUPPORTED, "nvfp4_grouped_gemm: E*N >= 2^31");
   switch (a->epilogue) {

@@ -97,6 +97,43 @@ hipError_t launch_repack(const uint8_t* codes, const uint8_t* scales, int E, int
   return hipGetLastError();
 }
 
+// ------------------------------------------------------------------ task map
+// Number of row chunks over all experts (ceil(Me/MC) each), returned to every
+// thread of the workgroup.
+template <int THREADS, int MC>
+__device__ __forceinline__ int count_chunks(const GemmParams& p, int* s_part) {
+  const int tid = threadIdx.x;
+  constexpr int NWAVE = THREADS / 64;
+  int c = 0;
+  for (int e = tid; e < p.E; e += THREADS) {
+    const int a = min(max(p.offsets[e], 0), p.m_total);
+    const int b = min(max(p.offsets[e + 1], 0), p.m_total);
+    c += b > a ? (b - a + MC - 1) / MC : 0;
+  }
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) c += __shfl_xor(c, d);
+  if ((tid & 63) == 0) s_part[tid >> 6] = c;
+  __syncthreads();
+  int total = 0;
+#pragma unroll
+  for (int w = 0; w < NWAVE; ++w) total += s_part[w];
+  __syncthreads();     // s_part is reused by the caller
+  return total;
+}
+
+// The hardware hands workgroups to the 8 XCDs round-robin (workgroup i to XCD
+// i % 8).  Give each XCD a contiguous range of the n_real tasks that exist,
+// so neighbouring tasks (the column tiles of a chunk, the chunks of an expert)
+// share one L2 and every XCD gets an equal share; -1: no task for this
+// workgroup.  Needs a grid of at least 8 * ceil(n_real / 8) workgroups.
+__device__ __forceinline__ int xcd_task_of(int bid, int n_real) {
+  const int per = (n_real + 7) >> 3;
+  const int x = bid & 7;
+  const int j = bid >> 3;
+  const int t = x * per + j;
+  return (j < per && t < n_real) ? t : -1;
+}
+
 // ------------------------------------------------------------------ chunk map
 // Map this workgroup's row-chunk index to (expert, first row of the chunk).
 // Chunks are enumerated expert by expert: expert e owns ceil(Me/MC) chunks.
@@ -305,14 +342,14 @@ __device__ __forceinline__ half8 b_frag(const BRegs& b, uint32_t scale4, int d) 
   return decode8_f16(word_of(b, d), e4m3_to_f16_div256(scale4 >> (8 * (d >> 1))));
 }
 
-// packed tile: contiguous, zero padded, streamed with non-temporal loads from
-// the expert's weight block (rb); tile_off is the tile's byte offset in the
-// block.  Past the block's end the loads give zeros.
-__device__ __forceinline__ void b_load_packed(rsrc_t rb, uint32_t tile_off, BRegs& b) {
-  const uint32_t lane = threadIdx.x & 63;
-  b.c[0] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rb, tile_off + 16u * lane, 0, kLoadNT));
-  b.c[1] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rb, tile_off + 1024u + 16u * lane, 0, kLoadNT));
-  b.s = __builtin_amdgcn_raw_buffer_load_b32(rb, tile_off + 2048u + 4u * lane, 0, kLoadNT);
+// packed tile: contiguous, zero padded, streamed with non-temporal loads
+// (global loads: on gfx950 they keep more weight bytes in flight than buffer
+// loads of the same tiles)
+__device__ __forceinline__ void b_load_packed(const uint8_t* tile, BRegs& b) {
+  const int lane = threadIdx.x & 63;
+  b.c[0] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(tile + 16 * lane));
+  b.c[1] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(tile + 1024 + 16 * lane));
+  b.s = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(tile + 2048 + 4 * lane));
 }
 
 __device__ __forceinline__ int clamp_k(int k, int K) { return min(k, K - 32); }
@@ -406,10 +443,8 @@ __device__ __forceinline__ void epilogue_swiglu(const GemmParams& p, const float
 template <int WN, int PPT>
 struct KCtx {
   AState<PPT> A;
-  const uint8_t* b_code[WN];     // row-major: B row start
+  const uint8_t* b_code[WN];     // row-major: B row start; packed: first tile of the column tile
   const uint8_t* b_scale[WN];
-  rsrc_t rb;                     // packed: the expert's weight block
-  uint32_t b_tile0[WN];          // packed: byte offset of the column tile's first K step in the block
   bool bok[WN];
   int K;
   int nsteps;
@@ -421,7 +456,7 @@ __device__ __forceinline__ void k_load_b(const KCtx<WN, PPT>& c, BRegs (&B)[WN],
 #pragma unroll
   for (int j = 0; j < WN; ++j) {
     if constexpr (PACKED)
-      b_load_packed(c.rb, c.b_tile0[j] + static_cast<uint32_t>(min(st, c.nsteps - 1)) * PTILE, B[j]);
+      b_load_packed(c.b_code[j] + static_cast<size_t>(min(st, c.nsteps - 1)) * PTILE, B[j]);
     else
       b_load_rows(c.b_code[j], c.b_scale[j], lg, st * KSTEP, c.K, B[j]);
   }
@@ -517,7 +552,8 @@ __global__ __launch_bounds__(NW * 64, MINB) void k_gemm_streamk(const GemmParams
   const int wave = threadIdx.x >> 6;
   const int lr = lane & 15;
 
-  const int task = xcd_task(blockIdx.x, gridDim.x);
+  const int task = xcd_task_of(blockIdx.x, count_chunks<THREADS, MC>(p, s_part) * p.n_tiles);
+  if (task < 0) return;
   const int chunk = task / p.n_tiles;
   const int nt = task - chunk * p.n_tiles;
   int e, m0;
@@ -548,11 +584,8 @@ __global__ __launch_bounds__(NW * 64, MINB) void k_gemm_streamk(const GemmParams
     }
     if constexpr (PACKED) {
       const int ntr = (N + 15) / 16;
-      const uint32_t block = static_cast<uint32_t>(ntr) * c.nsteps * PTILE;
-      c.rb = make_rsrc(p.b_packed + static_cast<size_t>(e) * block, block);
-      // a column tile past N lies past the block: its loads give zeros
-      c.b_tile0[j] = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(col0[j] / 16)) * c.nsteps * PTILE;
-      c.b_code[j] = nullptr;
+      const int rt = min(col0[j] / 16, ntr - 1);
+      c.b_code[j] = p.b_packed + (static_cast<size_t>(e) * ntr + rt) * c.nsteps * PTILE;
       c.b_scale[j] = nullptr;
     } else {
       const size_t brow = static_cast<size_t>(e) * N + (c.bok[j] ? col0[j] + lr : 0);
@@ -649,17 +682,16 @@ __device__ __forceinline__ void store_unit(const GemmParams& p, const float4v (&
 
 template <int NW, int MT, int MTA, int UPW, int EPI>
 __device__ __forceinline__ void n_main_loop(const GemmParams& p, const half8* __restrict__ lds, float* stage,
-                                            rsrc_t rb, int u_first, int u_count, int ntr, int prow0,
+                                            const uint8_t* tiles, int u_first, int u_count, int ntr, int prow0,
                                             int rows, float gab) {
   const int lane = threadIdx.x & 63;
   const int lr = lane & 15;
   BRegs R0[UNIT], R1[UNIT];
   auto load_unit = [&](BRegs (&R)[UNIT], int i) {
-    // tiles past the expert's block (the last unit's padding, prefetches past
-    // the wave's run) read zeros
-    const uint32_t ui = static_cast<uint32_t>(u_first + min(i, u_count - 1));   // re-read (cached), not new bytes
+    const int ui = u_first + min(i, u_count - 1);     // prefetches past the run re-read (cached)
 #pragma unroll
-    for (int t = 0; t < UNIT; ++t) b_load_packed(rb, (UNIT * ui + t) * PTILE, R[t]);
+    for (int t = 0; t < UNIT; ++t)
+      b_load_packed(tiles + static_cast<size_t>(min(UNIT * ui + t, ntr - 1)) * PTILE, R[t]);
   };
   auto consume = [&](const BRegs (&R)[UNIT], int i) {
     float4v acc[MTA][UNIT];
@@ -716,7 +748,8 @@ __global__ __launch_bounds__(NW * 64) void k_gemm_streamn(const GemmParams p) {
   __shared__ int s_work[2];
 
   const int wave = threadIdx.x >> 6;
-  const int task = xcd_task(blockIdx.x, gridDim.x);
+  const int task = xcd_task_of(blockIdx.x, count_chunks<THREADS, MC>(p, s_part) * p.n_tiles);
+  if (task < 0) return;
   const int chunk = task / p.n_tiles;
   const int ng = task - chunk * p.n_tiles;
   int e, m0;
@@ -739,16 +772,15 @@ __global__ __launch_bounds__(NW * 64) void k_gemm_streamn(const GemmParams p) {
   const int u_first = (ng * NW + wave) * UPW;
   const int u_count = min(UPW, nunits - u_first);
   if (u_count <= 0) return;
-  const uint32_t block = static_cast<uint32_t>(ntr) * PTILE;    // K <= 256: one tile per 16 rows
-  const rsrc_t rb = make_rsrc(p.b_packed + static_cast<size_t>(e) * block, block);
+  const uint8_t* tiles = p.b_packed + static_cast<size_t>(e) * ntr * PTILE;
   const float gab = p.a_g[0] * p.b_g[e];
   const int prow0 = row0 + m0;
   float* stage = stage_lds[wave];
   switch (mt_active) {
-    case 1: n_main_loop<NW, MT, 1, UPW, EPI>(p, a_lds, stage, rb, u_first, u_count, ntr, prow0, rows, gab); break;
-    case 2: if constexpr (MT >= 2) n_main_loop<NW, MT, 2, UPW, EPI>(p, a_lds, stage, rb, u_first, u_count, ntr, prow0, rows, gab); break;
-    case 3: if constexpr (MT >= 3) n_main_loop<NW, MT, 3, UPW, EPI>(p, a_lds, stage, rb, u_first, u_count, ntr, prow0, rows, gab); break;
-    default: if constexpr (MT >= 4) n_main_loop<NW, MT, MT, UPW, EPI>(p, a_lds, stage, rb, u_first, u_count, ntr, prow0, rows, gab); break;
+    case 1: n_main_loop<NW, MT, 1, UPW, EPI>(p, a_lds, stage, tiles, u_first, u_count, ntr, prow0, rows, gab); break;
+    case 2: if constexpr (MT >= 2) n_main_loop<NW, MT, 2, UPW, EPI>(p, a_lds, stage, tiles, u_first, u_count, ntr, prow0, rows, gab); break;
+    case 3: if constexpr (MT >= 3) n_main_loop<NW, MT, 3, UPW, EPI>(p, a_lds, stage, tiles, u_first, u_count, ntr, prow0, rows, gab); break;
+    default: if constexpr (MT >= 4) n_main_loop<NW, MT, MT, UPW, EPI>(p, a_lds, stage, tiles, u_first, u_count, ntr, prow0, rows, gab); break;
   }
 }
 
@@ -764,8 +796,9 @@ static hipError_t launch_streamk(GemmParams prm, int64_t m_total, hipStream_t st
   const int cols = (EPI == EPI_SWIGLU) ? prm.N / 2 : prm.N;
   const int cols_per_tile = (EPI == EPI_SWIGLU) ? BN / 2 : BN;
   prm.n_tiles = (cols + cols_per_tile - 1) / cols_per_tile;
-  // sum over experts of ceil(Me / MC) <= m_total / MC + E
-  const int64_t blocks = ((m_total + MC - 1) / MC + prm.E) * prm.n_tiles;
+  // sum over experts of ceil(Me / MC) <= m_total / MC + E; a multiple of 8 for
+  // the XCD task map
+  const int64_t blocks = ((((m_total + MC - 1) / MC + prm.E) * prm.n_tiles) + 7) / 8 * 8;
   if (grid_check(blocks) != hipSuccess) return hipErrorInvalidConfiguration;
   hipLaunchKernelGGL((k_gemm_streamk<NW, WN, MT, EPI, PACKED, MINB>), dim3(static_cast<unsigned>(blocks)), dim3(NW * 64),
                      0, stream, prm);
@@ -777,7 +810,7 @@ static hipError_t launch_streamn(GemmParams prm, int64_t m_total, hipStream_t st
   constexpr int MC = MT * 16;
   const int nunits = ((prm.N + 15) / 16 + UNIT - 1) / UNIT;
   prm.n_tiles = (nunits + NW * UPW - 1) / (NW * UPW);     // column-unit groups per chunk
-  const int64_t blocks = ((m_total + MC - 1) / MC + prm.E) * prm.n_tiles;
+  const int64_t blocks = ((((m_total + MC - 1) / MC + prm.E) * prm.n_tiles) + 7) / 8 * 8;
   if (grid_check(blocks) != hipSuccess) return hipErrorInvalidConfiguration;
   hipLaunchKernelGGL((k_gemm_streamn<NW, MT, UPW, EPI>), dim3(static_cast<unsigned>(blocks)), dim3(NW * 64), 0,
                      stream, prm);

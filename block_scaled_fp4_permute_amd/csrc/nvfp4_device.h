@@ -168,12 +168,5 @@ __device__ __forceinline__ float row16_max(float v) {
   return v;
 }
 
-// The 8 XCDs of the chip take workgroups round-robin (workgroup i runs on XCD
-// i % 8).  Remap so that each XCD receives a contiguous range of tasks, which
-// keeps neighbouring tasks (same expert, same A rows) in one L2.
-__device__ __forceinline__ int xcd_task(int bid, int nblocks) {
-  if ((nblocks & 7) != 0) return bid;
-  return (bid & 7) * (nblocks >> 3) + (bid >> 3);
-}
 
 }  // namespace nvfp4

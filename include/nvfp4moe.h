@@ -154,8 +154,8 @@ int nvfp4_quantize(const void* x, int32_t x_dtype, int64_t rows, int64_t cols,
  * Implementations", section "Context: The Optimization Journey", is
  * NVFP4MOE_EPI_COMBINE_F32).  Rows p >= offsets[E] are not written.  Experts
  * with no rows read no weight bytes.  Size limits (NVFP4MOE_ERR_UNSUPPORTED
- * beyond them): A codes (a_rows_total * K / 2 bytes) and one expert's packed
- * weight block (N * ceil(K/256) * 144 bytes) below 2 GiB; fewer than 2^31 rows. */
+ * beyond them): A codes (a_rows_total * K / 2 bytes) below 2 GiB; fewer than
+ * 2^31 rows. */
 int nvfp4_grouped_gemm(const nvfp4moe_gemm_args* args, void* stream);
 
 /* ---------------------------------------------------------------- packed weights
