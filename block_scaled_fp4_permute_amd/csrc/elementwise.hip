@@ -45,19 +45,20 @@ __device__ __forceinline__ void block_max_store(float v, float* partial) {
   if (threadIdx.x == 0) partial[blockIdx.x] = fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
 }
 
-// per-tensor scale from the partial maxima (or the caller's scale)
+// per-tensor scale from the partial maxima (or the caller's scale).  All
+// threads of the workgroup read the partials with independent loads (one
+// round trip), then reduce through one LDS step.
 __device__ __forceinline__ float reduce_scale(const float* g_in, const float* partial, int nparts) {
   if (g_in) return *g_in;
-  __shared__ float s_g;
-  if (threadIdx.x < 64) {
-    float m = 0.0f;
-    for (int i = threadIdx.x; i < nparts; i += 64) m = fmaxf(m, partial[i]);
+  __shared__ float s_part[4];
+  float m = 0.0f;
+#pragma unroll 4
+  for (int i = threadIdx.x; i < nparts; i += 256) m = fmaxf(m, partial[i]);
 #pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
-    if (threadIdx.x == 0) s_g = global_scale_from_amax(m);
-  }
+  for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+  if ((threadIdx.x & 63) == 0) s_part[threadIdx.x >> 6] = m;
   __syncthreads();
-  return s_g;
+  return global_scale_from_amax(fmaxf(fmaxf(s_part[0], s_part[1]), fmaxf(s_part[2], s_part[3])));
 }
 
 static int amax_grid(int64_t nblocks) {

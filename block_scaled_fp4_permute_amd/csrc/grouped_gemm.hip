@@ -824,7 +824,7 @@ static hipError_t launch_k(const GemmParams& prm, int epilogue, int64_t m_total,
     case EPI_BF16: return launch_streamk<4, 2, 4, EPI_BF16, PACKED>(prm, m_total, stream);
 #ifndef GU_NW
 #define GU_NW 4
-#define GU_WN 2
+#define GU_WN 4
 #define GU_MT 4
 #define GU_MINB 1
 #endif
@@ -837,10 +837,13 @@ static hipError_t launch_k(const GemmParams& prm, int epilogue, int64_t m_total,
 hipError_t launch_grouped_gemm(const GemmParams& prm, int epilogue, int64_t m_total, int hint, hipStream_t stream) {
   (void)hint;
   if (prm.b_packed && prm.K <= KSTEP && epilogue != EPI_SWIGLU) {
+#ifndef DN_UPW
+#define DN_UPW 6
+#endif
     switch (epilogue) {
-      case EPI_F32: return launch_streamn<4, 4, 6, EPI_F32>(prm, m_total, stream);
-      case EPI_BF16: return launch_streamn<4, 4, 6, EPI_BF16>(prm, m_total, stream);
-      case EPI_COMBINE: return launch_streamn<4, 4, 6, EPI_COMBINE>(prm, m_total, stream);
+      case EPI_F32: return launch_streamn<4, 4, DN_UPW, EPI_F32>(prm, m_total, stream);
+      case EPI_BF16: return launch_streamn<4, 4, DN_UPW, EPI_BF16>(prm, m_total, stream);
+      case EPI_COMBINE: return launch_streamn<4, 4, DN_UPW, EPI_COMBINE>(prm, m_total, stream);
       default: return hipErrorInvalidValue;
     }
   }

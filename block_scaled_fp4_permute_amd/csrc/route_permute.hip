@@ -32,6 +32,38 @@ __device__ __forceinline__ bool better(float v, int id, float bv, int bid) {
   return v > bv || (v == bv && id < bid);
 }
 
+template <int CTRL>
+__device__ __forceinline__ void row_argmax_step(float& bv, int& bid) {
+  const float ov = __uint_as_float(dpp_u32<CTRL>(__float_as_uint(bv)));
+  const int oid = static_cast<int>(dpp_u32<CTRL>(static_cast<uint32_t>(bid)));
+  if (better(ov, oid, bv, bid)) {
+    bv = ov;
+    bid = oid;
+  }
+}
+
+// Best (value, id) of the wave, returned to every lane: DPP exchanges inside
+// each row of 16 lanes, then the 4 row winners read as scalars.
+__device__ __forceinline__ void wave_argmax(float& bv, int& bid) {
+  row_argmax_step<kDppXor1>(bv, bid);
+  row_argmax_step<kDppXor2>(bv, bid);
+  row_argmax_step<kDppHalfMirror>(bv, bid);
+  row_argmax_step<kDppMirror>(bv, bid);
+  float v = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(bv), 0));
+  int id = __builtin_amdgcn_readlane(bid, 0);
+#pragma unroll
+  for (int r = 1; r < 4; ++r) {
+    const float rv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(bv), 16 * r));
+    const int rid = __builtin_amdgcn_readlane(bid, 16 * r);
+    if (better(rv, rid, v, id)) {
+      v = rv;
+      id = rid;
+    }
+  }
+  bv = v;
+  bid = id;
+}
+
 // One wave per token.  For E <= 64 * CACHE the token's logits stay in
 // registers for all k rounds; larger E re-reads them (L1-resident) per round.
 template <int CACHE>
@@ -80,15 +112,7 @@ __global__ __launch_bounds__(256) void k_route(const float* __restrict__ logits,
         }
       }
     }
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-      const float ov = __shfl_xor(bv, off);
-      const int oid = __shfl_xor(bid, off);
-      if (better(ov, oid, bv, bid)) {
-        bv = ov;
-        bid = oid;
-      }
-    }
+    wave_argmax(bv, bid);
     if (bid < 0 || bid >= E) bid = 0;   // only reachable with non-finite logits
     last_v = bv;
     last_id = bid;
@@ -173,41 +197,82 @@ __global__ __launch_bounds__(kRankThreads) void k_chunk_rank(const int* __restri
 // ------------------------------------------------------------------ scan
 // One workgroup of 1024 threads.  chunk_hist [nchunks][E] becomes the base row
 // of each (chunk, expert): offsets[e] + number of earlier-chunk assignments.
-__global__ __launch_bounds__(1024) void k_scan(int* __restrict__ chunk_hist, int nchunks, int E,
-                                               int* __restrict__ counts, int* __restrict__ offsets) {
-  __shared__ int part[1024];
+// Thread t owns experts [t*per, t*per + per); a thread's chunk counts are read
+// with independent loads (batches of 16), so the latency is paid once per
+// batch rather than once per chunk.
+static constexpr int kScanBatch = 16;
+static constexpr int kMaxPer = 4;     // E <= 4096
+
+__device__ __forceinline__ void scan_chunks(int* __restrict__ chunk_hist, int nchunks, int E,
+                                            int* __restrict__ counts, int* __restrict__ offsets) {
+  __shared__ int wsum[16];
   const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
   const int per = (E + 1023) / 1024;
   const int e0 = tid * per;
+  int cnt[kMaxPer];
   int local = 0;
-  for (int e = e0; e < e0 + per && e < E; ++e) {
-    int s = 0;
-    for (int c = 0; c < nchunks; ++c) {
-      int* h = chunk_hist + static_cast<size_t>(c) * E + e;
-      const int v = *h;
-      *h = s;
-      s += v;
+#pragma unroll
+  for (int i = 0; i < kMaxPer; ++i) {
+    const int e = e0 + i;
+    cnt[i] = 0;
+    if (i < per && e < E) {
+      for (int c0 = 0; c0 < nchunks; c0 += kScanBatch) {
+        int v[kScanBatch];
+#pragma unroll
+        for (int j = 0; j < kScanBatch; ++j)
+          v[j] = (c0 + j < nchunks) ? chunk_hist[static_cast<size_t>(c0 + j) * E + e] : 0;
+#pragma unroll
+        for (int j = 0; j < kScanBatch; ++j) cnt[i] += v[j];
+      }
+      counts[e] = cnt[i];
+      local += cnt[i];
     }
-    counts[e] = s;
-    local += s;
   }
-  part[tid] = local;
+  // exclusive scan of the per-thread totals: wave scans, then the wave totals
+  int incl = local;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int v = __shfl_up(incl, d);
+    if (lane >= d) incl += v;
+  }
+  if (lane == 63) wsum[wave] = incl;
   __syncthreads();
-  // inclusive Hillis-Steele scan over 1024 partial sums
-  for (int off = 1; off < 1024; off <<= 1) {
-    const int v = tid >= off ? part[tid - off] : 0;
-    __syncthreads();
-    part[tid] += v;
-    __syncthreads();
+  int wbase = 0, total = 0;
+#pragma unroll
+  for (int w = 0; w < 16; ++w) {
+    const int v = wsum[w];
+    wbase += (w < wave) ? v : 0;
+    total += v;
   }
-  int run = tid ? part[tid - 1] : 0;
-  for (int e = e0; e < e0 + per && e < E; ++e) {
-    offsets[e] = run;
-    const int c = counts[e];
-    for (int ch = 0; ch < nchunks; ++ch) chunk_hist[static_cast<size_t>(ch) * E + e] += run;
-    run += c;
+  int run = wbase + incl - local;
+  if (tid == 0) offsets[E] = total;
+#pragma unroll
+  for (int i = 0; i < kMaxPer; ++i) {
+    const int e = e0 + i;
+    if (i < per && e < E) {
+      offsets[e] = run;
+      int s = run;
+      for (int c0 = 0; c0 < nchunks; c0 += kScanBatch) {
+        int v[kScanBatch];
+#pragma unroll
+        for (int j = 0; j < kScanBatch; ++j)
+          v[j] = (c0 + j < nchunks) ? chunk_hist[static_cast<size_t>(c0 + j) * E + e] : 0;
+#pragma unroll
+        for (int j = 0; j < kScanBatch; ++j) {
+          if (c0 + j < nchunks) chunk_hist[static_cast<size_t>(c0 + j) * E + e] = s;
+          s += v[j];
+        }
+      }
+      run += cnt[i];
+    }
   }
-  if (tid == 1023) offsets[E] = part[1023];
+}
+
+__global__ __launch_bounds__(1024) void k_scan(int* __restrict__ chunk_hist, int nchunks, int E,
+                                               int* __restrict__ counts, int* __restrict__ offsets) {
+  scan_chunks(chunk_hist, nchunks, E, counts, offsets);
 }
 
 // ------------------------------------------------------------------ scatter
@@ -240,38 +305,8 @@ __global__ __launch_bounds__(1024) void k_scan_scatter(int* __restrict__ chunk_h
                                                        int* __restrict__ perm_src_token,
                                                        int* __restrict__ perm_of_assignment,
                                                        float* __restrict__ perm_weight) {
-  __shared__ int part[1024];
   const int tid = threadIdx.x;
-  const int per = (E + 1023) / 1024;
-  const int e0 = tid * per;
-  int local = 0;
-  for (int e = e0; e < e0 + per && e < E; ++e) {
-    int s = 0;
-    for (int c = 0; c < nchunks; ++c) {
-      int* h = chunk_hist + static_cast<size_t>(c) * E + e;
-      const int v = *h;
-      *h = s;
-      s += v;
-    }
-    counts[e] = s;
-    local += s;
-  }
-  part[tid] = local;
-  __syncthreads();
-  for (int off = 1; off < 1024; off <<= 1) {
-    const int v = tid >= off ? part[tid - off] : 0;
-    __syncthreads();
-    part[tid] += v;
-    __syncthreads();
-  }
-  int run = tid ? part[tid - 1] : 0;
-  for (int e = e0; e < e0 + per && e < E; ++e) {
-    offsets[e] = run;
-    const int c = counts[e];
-    for (int ch = 0; ch < nchunks; ++ch) chunk_hist[static_cast<size_t>(ch) * E + e] += run;
-    run += c;
-  }
-  if (tid == 1023) offsets[E] = part[1023];
+  scan_chunks(chunk_hist, nchunks, E, counts, offsets);
   // the scatter reads chunk bases that other threads just wrote to global
   // memory: release them, then acquire (which also drops stale L1 lines) after
   // the barrier
