@@ -18,6 +18,8 @@
 //   k_scan         one workgroup: counts = sum of chunk histograms, offsets =
 //                  exclusive scan, and each chunk's base row per expert.
 //   k_scatter      one thread per assignment: row = chunk base + rank.
+// (A single-workgroup scan + scatter was slower than the two kernels even at
+// 2048 assignments: one workgroup scatters with too little parallelism.)
 // Atomics are used for nothing, so every output is deterministic.
 #include "nvfp4_internal.h"
 
@@ -293,36 +295,6 @@ __global__ __launch_bounds__(256) void k_scatter(const int* __restrict__ ids, co
   if (perm_weight) perm_weight[p] = topk_w[f];
 }
 
-// ------------------------------------------------------------------ scan + scatter, one workgroup
-// For up to kSmallScatter assignments the scan and the scatter run in one
-// 1024-thread workgroup (one launch instead of two).
-static constexpr int kSmallScatter = 2048;
-
-__global__ __launch_bounds__(1024) void k_scan_scatter(int* __restrict__ chunk_hist, int nchunks, int E,
-                                                       int* __restrict__ counts, int* __restrict__ offsets,
-                                                       const int* __restrict__ ids, const float* __restrict__ topk_w,
-                                                       const int* __restrict__ local_rank, int n_asg, int k,
-                                                       int* __restrict__ perm_src_token,
-                                                       int* __restrict__ perm_of_assignment,
-                                                       float* __restrict__ perm_weight) {
-  const int tid = threadIdx.x;
-  scan_chunks(chunk_hist, nchunks, E, counts, offsets);
-  // the scatter reads chunk bases that other threads just wrote to global
-  // memory: release them, then acquire (which also drops stale L1 lines) after
-  // the barrier
-  __threadfence();
-  __syncthreads();
-  __threadfence();
-  for (int f = tid; f < n_asg; f += 1024) {
-    const int e = min(max(ids[f], 0), E - 1);
-    int p = chunk_hist[static_cast<size_t>(f / kChunk) * E + e] + local_rank[f];
-    p = (p >= 0 && p < n_asg) ? p : 0;   // keeps a wrong rank inside the buffers
-    perm_src_token[p] = f / k;
-    perm_of_assignment[f] = p;
-    if (perm_weight) perm_weight[p] = topk_w[f];
-  }
-}
-
 // ------------------------------------------------------------------ host side
 size_t route_permute_ws_bytes(int T, int E, int k) {
   const size_t n = static_cast<size_t>(T) * k;
@@ -355,11 +327,6 @@ hipError_t launch_route_permute(const float* logits, int T, int E, int k, int* t
                      n, E, nbits, local_rank, chunk_hist);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
-  if (n <= kSmallScatter) {
-    hipLaunchKernelGGL(k_scan_scatter, dim3(1), dim3(1024), 0, stream, chunk_hist, nchunks, E, counts, offsets,
-                       topk_ids, topk_w, local_rank, n, k, perm_src_token, perm_of_assignment, perm_weight);
-    return hipGetLastError();
-  }
   hipLaunchKernelGGL(k_scan, dim3(1), dim3(1024), 0, stream, chunk_hist, nchunks, E, counts, offsets);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
