@@ -817,25 +817,38 @@ static hipError_t launch_streamn(GemmParams prm, int64_t m_total, hipStream_t st
   return hipGetLastError();
 }
 
-template <bool PACKED>
+// Two tile shapes for the stream-K kernel:
+//   decode  (few rows per expert): 4 waves, 64-row chunks; SwiGLU tiles of
+//           256 columns (waves of 2 gate + 2 up tiles), other epilogues 128;
+//   large-M (>= kLargeRows rows per expert): 8 waves, 128-row chunks, 256
+//           columns - each weight tile then serves twice the rows, which pays
+//           off once the MFMA work dominates.
+constexpr int kLargeRows = 128;
+
+template <bool PACKED, bool LARGE>
 static hipError_t launch_k(const GemmParams& prm, int epilogue, int64_t m_total, hipStream_t stream) {
   switch (epilogue) {
-    case EPI_F32: return launch_streamk<4, 2, 4, EPI_F32, PACKED>(prm, m_total, stream);
-    case EPI_BF16: return launch_streamk<4, 2, 4, EPI_BF16, PACKED>(prm, m_total, stream);
-#ifndef GU_NW
-#define GU_NW 4
-#define GU_WN 4
-#define GU_MT 4
-#define GU_MINB 1
-#endif
-    case EPI_SWIGLU: return launch_streamk<GU_NW, GU_WN, GU_MT, EPI_SWIGLU, PACKED, GU_MINB>(prm, m_total, stream);
-    case EPI_COMBINE: return launch_streamk<4, 2, 4, EPI_COMBINE, PACKED>(prm, m_total, stream);
+    case EPI_F32:
+      return LARGE ? launch_streamk<8, 2, 8, EPI_F32, PACKED>(prm, m_total, stream)
+                   : launch_streamk<4, 2, 4, EPI_F32, PACKED>(prm, m_total, stream);
+    case EPI_BF16:
+      return LARGE ? launch_streamk<8, 2, 8, EPI_BF16, PACKED>(prm, m_total, stream)
+                   : launch_streamk<4, 2, 4, EPI_BF16, PACKED>(prm, m_total, stream);
+    case EPI_SWIGLU:
+      return LARGE ? launch_streamk<8, 2, 8, EPI_SWIGLU, PACKED>(prm, m_total, stream)
+                   : launch_streamk<4, 4, 4, EPI_SWIGLU, PACKED>(prm, m_total, stream);
+    case EPI_COMBINE:
+      return LARGE ? launch_streamk<8, 2, 8, EPI_COMBINE, PACKED>(prm, m_total, stream)
+                   : launch_streamk<4, 2, 4, EPI_COMBINE, PACKED>(prm, m_total, stream);
     default: return hipErrorInvalidValue;
   }
 }
 
 hipError_t launch_grouped_gemm(const GemmParams& prm, int epilogue, int64_t m_total, int hint, hipStream_t stream) {
-  (void)hint;
+  // rows per expert: the caller's hint, else the average (the counts stay on
+  // the device)
+  const int64_t rows_per_expert = hint > 0 ? hint : m_total / prm.E;
+  const bool large = rows_per_expert >= kLargeRows;
   if (prm.b_packed && prm.K <= KSTEP && epilogue != EPI_SWIGLU) {
 #ifndef DN_UPW
 #define DN_UPW 6
@@ -847,7 +860,11 @@ hipError_t launch_grouped_gemm(const GemmParams& prm, int epilogue, int64_t m_to
       default: return hipErrorInvalidValue;
     }
   }
-  return prm.b_packed ? launch_k<true>(prm, epilogue, m_total, stream) : launch_k<false>(prm, epilogue, m_total, stream);
+  if (large)
+    return prm.b_packed ? launch_k<true, true>(prm, epilogue, m_total, stream)
+                        : launch_k<false, true>(prm, epilogue, m_total, stream);
+  return prm.b_packed ? launch_k<true, false>(prm, epilogue, m_total, stream)
+                      : launch_k<false, false>(prm, epilogue, m_total, stream);
 }
 
 }  // namespace nvfp4

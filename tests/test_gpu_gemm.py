@@ -97,6 +97,34 @@ def test_gemm_f32_random(case, gather, packed):
     assert_gemm_close(down(y)[:M], y_ref, absdot, what=f"case {case}")
 
 
+@pytest.mark.parametrize("hint", [1, 4096])
+@pytest.mark.parametrize("packed", [False, True])
+def test_gemm_decode_and_large_tile_shapes(hint, packed):
+    # the rows-per-expert hint picks the decode (64-row) or the large-M (128-row,
+    # 8-wave) tile; both must meet the oracle, with F32 and fused SwiGLU epilogues
+    rng = np.random.default_rng(hint + int(packed))
+    E, counts, N, K = 3, [150, 300, 7], 512, 1024
+    M = sum(counts)
+    a_codes, a_scales = _rand_nvfp4(rng, (400,), K)
+    b_codes, b_scales = _rand_nvfp4(rng, (E, N), K)
+    b_g = rng.uniform(0.001, 0.01, E).astype(np.float32)
+    a_rows = rng.integers(0, 400, M).astype(np.int32)
+    y, offsets = _run_gemm(a_codes, a_scales, 0.02, b_codes, b_scales, b_g, counts, a_rows, hint=hint,
+                           packed=packed)
+    y_ref, absdot = OM.grouped_gemm(a_codes, a_scales, 0.02, b_codes, b_scales, b_g, offsets, a_rows=a_rows)
+    assert_gemm_close(down(y)[:M], y_ref, absdot, what=f"hint {hint}")
+    h64 = OM.swiglu(y_ref)
+    g_h = np.float32(np.abs(h64.astype(np.float32)).max() / np.float32(2688))
+    a = m.NVFP4Tensor(up(a_codes), up(a_scales), up(np.array([0.02], np.float32)))
+    bc, bs = up(b_codes), up(b_scales)
+    hq = m.nvfp4_grouped_gemm(a, bc, bs, up(b_g), up(offsets), m_total=M, a_rows=up(a_rows),
+                              epilogue=m.EPI_SWIGLU_NVFP4, out_g=up(np.array([g_h], np.float32)),
+                              max_rows_per_expert_hint=hint, b_packed=m.nvfp4_weight_repack(bc, bs) if packed else None)
+    torch.cuda.synchronize()
+    check_requant(down(hq.codes), down(hq.scales), h64, g_h, _swiglu_tol(y_ref, absdot), max_flip_frac=0.02,
+                  what=f"fused swiglu hint {hint}")
+
+
 def test_gemm_bf16_epilogue_and_untouched_tail_rows():
     rng = np.random.default_rng(7)
     E, counts, N, K = 3, [9, 40, 2], 128, 256
