@@ -121,67 +121,138 @@ __device__ __forceinline__ int count_chunks(const GemmParams& p, int* s_part) {
   return total;
 }
 
-// The hardware hands workgroups to the 8 XCDs round-robin (workgroup i to XCD
-// i % 8).  Give each XCD a contiguous range of the n_real tasks that exist,
-// so neighbouring tasks (the column tiles of a chunk, the chunks of an expert)
-// share one L2 and every XCD gets an equal share; -1: no task for this
-// workgroup.  Needs a grid of at least 8 * ceil(n_real / 8) workgroups.
-__device__ __forceinline__ int xcd_task_of(int bid, int n_real) {
-  const int per = (n_real + 7) >> 3;
-  const int x = bid & 7;
-  const int j = bid >> 3;
-  const int t = x * per + j;
-  return (j < per && t < n_real) ? t : -1;
+// Block-wide exclusive prefix sum of one int per thread; every thread also
+// gets the block total.  s_tmp: one int per wave, reusable after return.
+template <int THREADS>
+__device__ __forceinline__ int block_excl_scan(int v, int* s_tmp, int& total) {
+  constexpr int NWAVE = THREADS / 64;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  int incl = v;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int u = __shfl_up(incl, d);
+    if (lane >= d) incl += u;
+  }
+  if (lane == 63) s_tmp[wave] = incl;
+  __syncthreads();
+  int before = 0;
+  total = 0;
+#pragma unroll
+  for (int w = 0; w < NWAVE; ++w) {
+    const int u = s_tmp[w];
+    before += (w < wave) ? u : 0;
+    total += u;
+  }
+  __syncthreads();
+  return before + incl - v;
 }
 
-// ------------------------------------------------------------------ chunk map
-// Map this workgroup's row-chunk index to (expert, first row of the chunk).
-// Chunks are enumerated expert by expert: expert e owns ceil(Me/MC) chunks.
-// Every thread takes part (block-wide scan of the per-expert chunk counts);
-// returns false when the index lies past the last chunk.
-template <int THREADS, int MC>
-__device__ __forceinline__ bool find_chunk(const GemmParams& p, int chunk, int& e_out, int& m0_out,
-                                           int* s_part, int* s_work) {
+__device__ __forceinline__ int overlap(int a0, int a1, int b0, int b1) { return max(0, min(a1, b1) - max(a0, b0)); }
+
+// ------------------------------------------------------------------ task map
+// A task is (row chunk, column tile).  Chunks are enumerated expert by expert
+// (expert e owns ceil(Me/MC) of them, all full but maybe the last) and tasks
+// chunk by chunk, so the tasks of an expert are contiguous.  The class of a
+// task is the number of live 16-row tiles of its chunk (1..MT); its cost grows
+// with the class.
+//
+// The hardware hands workgroups to the 8 XCDs round-robin (workgroup i to XCD
+// i % 8).  Each XCD gets an equal, contiguous range of the tasks that exist,
+// so the column tiles of a chunk and the chunks of an expert share one L2.
+// BY_CLASS: inside its range an XCD runs the tasks heaviest class first (task
+// order within a class): longest-first list scheduling, which keeps the full
+// chunks out of the last round of workgroups.  Otherwise in task order, so
+// that the chunks of an expert run side by side and share its weight tiles in
+// L2.  Every thread takes part; returns false (uniformly) when the workgroup
+// has no task.  Needs a grid of at least 8 * ceil(tasks / 8) workgroups and
+// s_work of at least MT + 4 ints.
+template <int THREADS, int MT, bool BY_CLASS>
+__device__ __forceinline__ bool find_task(const GemmParams& p, int* s_part, int* s_work, int& e_out, int& m0_out,
+                                          int& nt_out) {
+  constexpr int MC = MT * 16;
+  const int ntl = p.n_tiles;
+  const int n = count_chunks<THREADS, MC>(p, s_part) * ntl;
+  const int per = (n + 7) >> 3;
+  const int lo = (blockIdx.x & 7) * per;
+  const int hi = min(lo + per, n);
+  const int j = blockIdx.x >> 3;
+  if (lo + j >= hi) return false;
   const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  constexpr int NWAVE = THREADS / 64;
+  int* s_cnt = s_work + 2;   // tasks of class k in [lo, hi): s_cnt[k], k = 1..MT
+  if (tid <= MT) s_cnt[tid] = 0;
   if (tid == 0) s_work[0] = -1;
-  int base = 0;
-  for (int e0 = 0; e0 < p.E; e0 += THREADS) {
-    const int e = e0 + tid;
-    int c = 0;
+  __syncthreads();
+  // expert e: Me rows, c chunks from chunk cb; tasks [t0, t1) of the full
+  // chunks before the last, [t1, t2) of the last chunk (class cl)
+  auto expert_of = [&](int e, int& Me, int& c) {
+    Me = 0;
     if (e < p.E) {
       const int a = min(max(p.offsets[e], 0), p.m_total);
       const int b = min(max(p.offsets[e + 1], 0), p.m_total);
-      c = b > a ? (b - a + MC - 1) / MC : 0;
+      Me = max(b - a, 0);
     }
-    int incl = c;
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-      const int v = __shfl_up(incl, d);
-      if (lane >= d) incl += v;
-    }
-    if (lane == 63) s_part[wave] = incl;
-    __syncthreads();
-    int before = 0, total = 0;
-#pragma unroll
-    for (int w = 0; w < NWAVE; ++w) {
-      const int v = s_part[w];
-      before += (w < wave) ? v : 0;
-      total += v;
-    }
-    incl += before;
-    const int excl = incl - c;
-    if (c > 0 && chunk >= base + excl && chunk < base + incl) {
-      s_work[0] = e;
-      s_work[1] = (chunk - base - excl) * MC;
+    c = (Me + MC - 1) / MC;
+  };
+  int base = 0;
+  for (int e0 = 0; BY_CLASS && e0 < p.E && base * ntl < hi; e0 += THREADS) {
+    int Me, c, total;
+    expert_of(e0 + tid, Me, c);
+    const int cb = base + block_excl_scan<THREADS>(c, s_part, total);
+    if (c > 0) {
+      const int cl = (Me - (c - 1) * MC + 15) >> 4;
+      const int t1 = (cb + c - 1) * ntl;
+      const int nfull = overlap(cb * ntl, t1, lo, hi);
+      const int nlast = overlap(t1, t1 + ntl, lo, hi);
+      if (nfull) atomicAdd(&s_cnt[MT], nfull);
+      if (nlast) atomicAdd(&s_cnt[cl], nlast);
     }
     base += total;
-    __syncthreads();
   }
+  __syncthreads();
+  int k = MT, r = j;
+  while (BY_CLASS && k > 1 && r >= s_cnt[k]) r -= s_cnt[k--];
+  // the r-th task of class k in [lo, hi), in task order (without classes:
+  // task lo + j)
+  const int t_plain = lo + j;
+  base = 0;
+  int before = 0;
+  for (int e0 = 0; e0 < p.E && base * ntl < hi; e0 += THREADS) {
+    int Me, c, total;
+    expert_of(e0 + tid, Me, c);
+    const int cb = base + block_excl_scan<THREADS>(c, s_part, total);
+    int t = -1;
+    if constexpr (BY_CLASS) {
+      int t_lo = 0, v = 0, vtotal;
+      if (c > 0) {
+        const int cl = (Me - (c - 1) * MC + 15) >> 4;
+        const int t1 = (cb + c - 1) * ntl;
+        // class-k tasks of this expert form one interval
+        const int a0 = (k == MT) ? cb * ntl : t1;
+        const int a1 = (cl == k) ? t1 + ntl : t1;
+        if (a1 > a0) {
+          t_lo = max(a0, lo);
+          v = overlap(a0, a1, lo, hi);
+        }
+      }
+      const int vb = before + block_excl_scan<THREADS>(v, s_part + THREADS / 64, vtotal);
+      if (v > 0 && r >= vb && r < vb + v) t = t_lo + (r - vb);
+      before += vtotal;
+    } else {
+      if (c > 0 && t_plain >= cb * ntl && t_plain < (cb + c) * ntl) t = t_plain;
+    }
+    if (t >= 0) {
+      const int chunk = t / ntl;
+      s_work[0] = e0 + tid;
+      s_work[1] = (chunk - cb) * MC;
+      s_work[2 + MT + 1] = t - chunk * ntl;
+    }
+    base += total;
+  }
+  __syncthreads();
   e_out = s_work[0];
   m0_out = s_work[1];
+  nt_out = s_work[2 + MT + 1];
   return e_out >= 0;
 }
 
@@ -545,19 +616,15 @@ __global__ __launch_bounds__(NW * 64, MINB) void k_gemm_streamk(const GemmParams
   static_assert(EPI != EPI_SWIGLU || (WN % 2) == 0, "SwiGLU pairs gate and up tiles");
   static_assert(MT == 1 || MT == 2 || MT == 3 || MT == 4 || MT == 6 || MT == 8, "row tiles per chunk");
   __shared__ half8 a_lds[2][MT * 8 * 64];   // double-buffered [row tile][sub-step][lane] fragments
-  __shared__ int s_part[NW];
-  __shared__ int s_work[2];
+  __shared__ int s_part[2 * NW];
+  __shared__ int s_work[MT + 4];
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int lr = lane & 15;
 
-  const int task = xcd_task_of(blockIdx.x, count_chunks<THREADS, MC>(p, s_part) * p.n_tiles);
-  if (task < 0) return;
-  const int chunk = task / p.n_tiles;
-  const int nt = task - chunk * p.n_tiles;
-  int e, m0;
-  if (!find_chunk<THREADS, MC>(p, chunk, e, m0, s_part, s_work)) return;
+  int e, m0, nt;
+  if (!find_task<THREADS, MT, true>(p, s_part, s_work, e, m0, nt)) return;
   // data-dependent bounds are clamped so that inconsistent offsets can give
   // wrong rows but never an access outside the buffers
   const int row0 = min(max(p.offsets[e], 0), p.m_total);
@@ -744,16 +811,12 @@ __global__ __launch_bounds__(NW * 64) void k_gemm_streamn(const GemmParams p) {
   static_assert(UPW % 2 == 0, "units per wave come in pairs");
   __shared__ half8 a_lds[MT * 8 * 64];
   __shared__ float stage_lds[NW][16 * 68];   // per-wave output staging (row pitch 68 floats)
-  __shared__ int s_part[NW];
-  __shared__ int s_work[2];
+  __shared__ int s_part[2 * NW];
+  __shared__ int s_work[MT + 4];
 
   const int wave = threadIdx.x >> 6;
-  const int task = xcd_task_of(blockIdx.x, count_chunks<THREADS, MC>(p, s_part) * p.n_tiles);
-  if (task < 0) return;
-  const int chunk = task / p.n_tiles;
-  const int ng = task - chunk * p.n_tiles;
-  int e, m0;
-  if (!find_chunk<THREADS, MC>(p, chunk, e, m0, s_part, s_work)) return;
+  int e, m0, ng;
+  if (!find_task<THREADS, MT, false>(p, s_part, s_work, e, m0, ng)) return;
   const int row0 = min(max(p.offsets[e], 0), p.m_total);
   const int Me = min(max(p.offsets[e + 1], 0), p.m_total) - row0;
   const int rows = min(MC, Me - m0);
