@@ -90,9 +90,26 @@ __device__ __forceinline__ uint32_t encode_block16(const float (&x)[16], float g
   const float scale_eff = e4m3_to_f32(s) * g;
   uint32_t w[2] = {0u, 0u};
   if (s != 0u) {
+    // |x| / scale_eff rounded to nearest, from the correctly rounded
+    // reciprocal: q0 = a*y, r = a - q0*b (exact with an FMA), q = q0 + r*y.
+    // With y = RN(1/b) this gives RN(a/b) whenever nothing underflows or
+    // overflows (Markstein, IBM J. Res. Dev. 34(1), 1990).  The quotients it
+    // misses come from subnormal |x| and lie below 2^-50, far under the
+    // smallest E2M1 rounding boundary (0.25).  A reciprocal that overflows
+    // (b below 2^-128) takes true divisions.
+    const float y = 1.0f / scale_eff;
+    const bool via_rcp = scale_eff > 0.0f && y < __builtin_huge_valf();
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      const float v = scale_eff > 0.0f ? fabsf(x[i]) / scale_eff : 0.0f;
+      const float a = fabsf(x[i]);
+      float v;
+      if (via_rcp) {
+        const float q0 = a * y;
+        const float q = __builtin_fmaf(__builtin_fmaf(-q0, scale_eff, a), y, q0);
+        v = q0 < __builtin_huge_valf() ? q : q0;
+      } else {
+        v = scale_eff > 0.0f ? a / scale_eff : 0.0f;
+      }
       const uint32_t code = f32_to_e2m1_mag(v) | ((__float_as_uint(x[i]) >> 31) << 3);
       w[i >> 3] |= code << (4 * (i & 7));
     }

@@ -129,6 +129,34 @@ def test_quantize_e4m3_and_e2m1_decision_points():
     _quant_case(x, torch.float32, g=1.0)
 
 
+def test_quantize_quotients_next_to_e2m1_boundaries():
+    # a non-power-of-two per-tensor scale, so x / (s * g) is a rounded float32
+    # quotient; elements a few ulp either side of boundary * (s * g) make every
+    # E2M1 decision hang on the last bit of that quotient
+    from oracle import formats as F
+    g = np.float32(0.0371)
+    mids = (F.E2M1_MAGNITUDES[:-1] + F.E2M1_MAGNITUDES[1:]) / 2
+    rows = []
+    for sc in (8, 9, 30, 55, 56, 77, 100, 119, 126):          # E4M3 codes
+        sv = np.float32(F.e4m3_decode(np.array([sc], np.uint8))[0])
+        b = np.float32(sv * g)
+        for shift in (-2, -1, 1, 2):
+            r = np.zeros(16, np.float32)
+            r[0] = np.float32(np.float32(6.0) * b)               # block maximum: scale code sc
+            for i, mval in enumerate(mids):
+                v = np.float32(np.float32(mval) * b)
+                for _ in range(abs(shift)):
+                    v = np.nextafter(v, np.float32(np.inf if shift > 0 else 0), dtype=np.float32)
+                r[1 + 2 * i] = v
+                r[2 + 2 * i] = -np.nextafter(v, np.float32(0), dtype=np.float32)
+            rows.append(r)
+    x = np.array(rows, np.float32)
+    x = np.concatenate([x, x[::-1]], axis=1)
+    c, sc_codes, _ = OQ.quantize(x, g=g)
+    assert len(np.unique(OQ.unpack_codes(c))) >= 12          # the cases reach most codes
+    _quant_case(x, torch.float32, g=float(g))
+
+
 def test_quantize_config_activations_and_weights():
     c = workloads.CONFIGS[2]
     _quant_case(workloads.activations(c), torch.bfloat16)
