@@ -97,6 +97,43 @@ def test_gemm_f32_random(case, gather, packed):
     assert_gemm_close(down(y)[:M], y_ref, absdot, what=f"case {case}")
 
 
+@pytest.mark.parametrize("hint", [0, 4096])
+@pytest.mark.parametrize("packed", [False, True])
+def test_gemm_many_experts_task_map(hint, packed):
+    # more experts than threads in a work-group (the task map walks the
+    # experts in several block-wide passes), many empty experts, a few with
+    # several chunks; F32 (stream-K or stream-N) and fused SwiGLU (stream-K)
+    rng = np.random.default_rng(7 + hint + int(packed))
+    E, N, K = 600, 64, 512
+    counts = rng.integers(0, 40, E) * (rng.random(E) < 0.7)
+    counts[rng.choice(E, 6, replace=False)] = [150, 200, 64, 65, 129, 17]
+    counts = counts.astype(np.int64)
+    M = int(counts.sum())
+    print(f"many experts: E={E} M={M} hint={hint} packed={packed}", flush=True)
+    a_codes, a_scales = _rand_nvfp4(rng, (500,), K)
+    b_codes, b_scales = _rand_nvfp4(rng, (E, N), K)
+    b_g = rng.uniform(0.001, 0.01, E).astype(np.float32)
+    a_rows = rng.integers(0, 500, M).astype(np.int32)
+    for k_used in (K, 256):
+        ac, as_ = a_codes[:, :k_used // 2].copy(), a_scales[:, :k_used // 16].copy()
+        bc, bs = b_codes[:, :, :k_used // 2].copy(), b_scales[:, :, :k_used // 16].copy()
+        y, offsets = _run_gemm(ac, as_, 0.02, bc, bs, b_g, counts, a_rows, hint=hint, packed=packed)
+        y_ref, absdot = OM.grouped_gemm(ac, as_, 0.02, bc, bs, b_g, offsets, a_rows=a_rows)
+        assert_gemm_close(down(y)[:M], y_ref, absdot, what=f"K={k_used}")
+    y_ref, absdot = OM.grouped_gemm(a_codes, a_scales, 0.02, b_codes, b_scales, b_g, offsets, a_rows=a_rows)
+    h64 = OM.swiglu(y_ref)
+    g_h = np.float32(np.abs(h64.astype(np.float32)).max() / np.float32(2688))
+    a = m.NVFP4Tensor(up(a_codes), up(a_scales), up(np.array([0.02], np.float32)))
+    bct, bst = up(b_codes), up(b_scales)
+    hq = m.nvfp4_grouped_gemm(a, bct, bst, up(b_g), up(offsets), m_total=M, a_rows=up(a_rows),
+                              epilogue=m.EPI_SWIGLU_NVFP4, out_g=up(np.array([g_h], np.float32)),
+                              max_rows_per_expert_hint=hint,
+                              b_packed=m.nvfp4_weight_repack(bct, bst) if packed else None)
+    torch.cuda.synchronize()
+    check_requant(down(hq.codes), down(hq.scales), h64, g_h, _swiglu_tol(y_ref, absdot), max_flip_frac=0.02,
+                  what="many experts swiglu")
+
+
 @pytest.mark.parametrize("hint", [1, 4096])
 @pytest.mark.parametrize("packed", [False, True])
 def test_gemm_decode_and_large_tile_shapes(hint, packed):
