@@ -327,17 +327,18 @@ __device__ __forceinline__ void a_load(const AState<PPT>& A, ARegs<PPT>& R, int 
     }
 }
 
-// decode the thread's pairs of one K step into LDS (fragment slots of row tiles < MTA)
+// decode the thread's pairs of one K step into LDS
 template <int THREADS, int MT, int MTA, int PPT>
 __device__ __forceinline__ void a_store(const AState<PPT>& A, const ARegs<PPT>& R, int k0, int K,
                                         half8* __restrict__ lds) {
 #pragma unroll
   for (int q = 0; q < PPT; ++q) {
     const int pi = threadIdx.x + q * THREADS;
-    // compile-time true in the common shapes, so the store stays branch-free
+    // compile-time true in the common shapes, so the store stays branch-free;
+    // pairs of row tiles >= MTA decode into slots no MFMA reads (zeros: their
+    // rows do not exist) rather than branch around the store
     const bool in_chunk = (THREADS * PPT <= MT * 64) || pi < MT * 64;
-    const bool active = (MTA == MT) || (pi >> 6) < MTA;
-    if (in_chunk && active) {
+    if (in_chunk) {
       half8* dst = lds + (pi >> 6) * 8 * 64 + (pi & 63);
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
@@ -386,9 +387,9 @@ __device__ __forceinline__ void a_store_piece(const ARegs<PPT>& R, const AScales
   const int h = (piece >> 2) & 1;
   const int w = piece & 3;
   const int pi = threadIdx.x + q * THREADS;
+  // no branch on the live row tiles (see a_store): one basic block per K step
   const bool in_chunk = (THREADS * PPT <= MT * 64) || pi < MT * 64;
-  const bool active = (MTA == MT) || (pi >> 6) < MTA;
-  if (in_chunk && active) {
+  if (in_chunk) {
     const u32x4 c = R.c[q][h];
     const uint32_t word = w == 0 ? c.x : w == 1 ? c.y : w == 2 ? c.z : c.w;
     lds[(pi >> 6) * 8 * 64 + (4 * h + w) * 64 + (pi & 63)] = decode8_f16(word, S.s[q][h][w >> 1]);
@@ -413,15 +414,32 @@ __device__ __forceinline__ half8 b_frag(const BRegs& b, uint32_t scale4, int d) 
   return decode8_f16(word_of(b, d), e4m3_to_f16_div256(scale4 >> (8 * (d >> 1))));
 }
 
-// packed tile: contiguous, zero padded, streamed with non-temporal loads
-// (global loads: on gfx950 they keep more weight bytes in flight than buffer
-// loads of the same tiles)
+// packed tile: contiguous, zero padded, global loads (on gfx950 they keep
+// more weight bytes in flight than buffer loads of the same tiles).  NT:
+// non-temporal, for weights read once; otherwise cached, so that the row
+// chunks of one expert, running side by side on one XCD, share the tiles in
+// its L2.
+template <bool NT>
 __device__ __forceinline__ void b_load_packed(const uint8_t* tile, BRegs& b) {
   const int lane = threadIdx.x & 63;
-  b.c[0] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(tile + 16 * lane));
-  b.c[1] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(tile + 1024 + 16 * lane));
-  b.s = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(tile + 2048 + 4 * lane));
+  const u32x4* c = reinterpret_cast<const u32x4*>(tile + 16 * lane);
+  const u32x4* d = reinterpret_cast<const u32x4*>(tile + 1024 + 16 * lane);
+  const uint32_t* sc = reinterpret_cast<const uint32_t*>(tile + 2048 + 4 * lane);
+  if constexpr (NT) {
+    b.c[0] = __builtin_nontemporal_load(c);
+    b.c[1] = __builtin_nontemporal_load(d);
+    b.s = __builtin_nontemporal_load(sc);
+  } else {
+    b.c[0] = *c;
+    b.c[1] = *d;
+    b.s = *sc;
+  }
 }
+
+// How B is laid out and loaded (the PACKED template parameter)
+constexpr int kRowB = 0;          // row-major codes and scales
+constexpr int kPackedNT = 1;      // packed tiles, non-temporal loads
+constexpr int kPackedCached = 2;  // packed tiles, cached loads
 
 __device__ __forceinline__ int clamp_k(int k, int K) { return min(k, K - 32); }
 
@@ -521,13 +539,13 @@ struct KCtx {
   int nsteps;
 };
 
-template <int WN, int PPT, bool PACKED>
+template <int WN, int PPT, int PACKED>
 __device__ __forceinline__ void k_load_b(const KCtx<WN, PPT>& c, BRegs (&B)[WN], int st) {
   const int lg = (threadIdx.x & 63) >> 4;
 #pragma unroll
   for (int j = 0; j < WN; ++j) {
     if constexpr (PACKED)
-      b_load_packed(c.b_code[j] + static_cast<size_t>(min(st, c.nsteps - 1)) * PTILE, B[j]);
+      b_load_packed<PACKED == kPackedNT>(c.b_code[j] + static_cast<size_t>(min(st, c.nsteps - 1)) * PTILE, B[j]);
     else
       b_load_rows(c.b_code[j], c.b_scale[j], lg, st * KSTEP, c.K, B[j]);
   }
@@ -537,7 +555,7 @@ __device__ __forceinline__ void k_load_b(const KCtx<WN, PPT>& c, BRegs (&B)[WN],
 // from registers), with the decode of step st+1's activation rows into
 // lds_nxt interleaved - both in one basic block, so the VALU work of the
 // decodes overlaps the matrix-core work - then the step's barrier.
-template <int NW, int WN, int MT, int MTA, int PPT, bool PACKED>
+template <int NW, int WN, int MT, int MTA, int PPT, int PACKED>
 __device__ __forceinline__ void k_step(const KCtx<WN, PPT>& c, const ARegs<PPT>& a_nxt, const BRegs (&B)[WN],
                                        int st, const half8* __restrict__ lds_cur, half8* __restrict__ lds_nxt,
                                        float4v (&acc)[MT][WN]) {
@@ -585,7 +603,7 @@ __device__ __forceinline__ void k_step(const KCtx<WN, PPT>& c, const ARegs<PPT>&
 // no branches: a step past K (an odd step count, and the prefetches after the
 // last step) reads valid clamped addresses and its data is masked to zero,
 // which keeps the wait counts exact.
-template <int NW, int WN, int MT, int MTA, int PPT, bool PACKED>
+template <int NW, int WN, int MT, int MTA, int PPT, int PACKED>
 __device__ __forceinline__ void k_main_loop(const KCtx<WN, PPT>& c, half8* __restrict__ lds0,
                                             half8* __restrict__ lds1, float4v (&acc)[MT][WN]) {
   BRegs b0[WN], b1[WN];
@@ -607,7 +625,7 @@ __device__ __forceinline__ void k_main_loop(const KCtx<WN, PPT>& c, half8* __res
   }
 }
 
-template <int NW, int WN, int MT, int EPI, bool PACKED, int MINB>
+template <int NW, int WN, int MT, int EPI, int PACKED, int MINB>
 __global__ __launch_bounds__(NW * 64, MINB) void k_gemm_streamk(const GemmParams p) {
   constexpr int THREADS = NW * 64;
   constexpr int MC = MT * 16;
@@ -747,7 +765,7 @@ __device__ __forceinline__ void store_unit(const GemmParams& p, const float4v (&
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-template <int NW, int MT, int MTA, int UPW, int EPI>
+template <int NW, int MT, int MTA, int UPW, int EPI, int PACKED>
 __device__ __forceinline__ void n_main_loop(const GemmParams& p, const half8* __restrict__ lds, float* stage,
                                             const uint8_t* tiles, int u_first, int u_count, int ntr, int prow0,
                                             int rows, float gab) {
@@ -758,7 +776,7 @@ __device__ __forceinline__ void n_main_loop(const GemmParams& p, const half8* __
     const int ui = u_first + min(i, u_count - 1);     // prefetches past the run re-read (cached)
 #pragma unroll
     for (int t = 0; t < UNIT; ++t)
-      b_load_packed(tiles + static_cast<size_t>(min(UNIT * ui + t, ntr - 1)) * PTILE, R[t]);
+      b_load_packed<PACKED == kPackedNT>(tiles + static_cast<size_t>(min(UNIT * ui + t, ntr - 1)) * PTILE, R[t]);
   };
   auto consume = [&](const BRegs (&R)[UNIT], int i) {
     float4v acc[MTA][UNIT];
@@ -803,7 +821,7 @@ __device__ __forceinline__ void n_main_loop(const GemmParams& p, const half8* __
   }
 }
 
-template <int NW, int MT, int UPW, int EPI>
+template <int NW, int MT, int UPW, int EPI, int PACKED>
 __global__ __launch_bounds__(NW * 64) void k_gemm_streamn(const GemmParams p) {
   constexpr int THREADS = NW * 64;
   constexpr int MC = MT * 16;
@@ -840,10 +858,10 @@ __global__ __launch_bounds__(NW * 64) void k_gemm_streamn(const GemmParams p) {
   const int prow0 = row0 + m0;
   float* stage = stage_lds[wave];
   switch (mt_active) {
-    case 1: n_main_loop<NW, MT, 1, UPW, EPI>(p, a_lds, stage, tiles, u_first, u_count, ntr, prow0, rows, gab); break;
-    case 2: if constexpr (MT >= 2) n_main_loop<NW, MT, 2, UPW, EPI>(p, a_lds, stage, tiles, u_first, u_count, ntr, prow0, rows, gab); break;
-    case 3: if constexpr (MT >= 3) n_main_loop<NW, MT, 3, UPW, EPI>(p, a_lds, stage, tiles, u_first, u_count, ntr, prow0, rows, gab); break;
-    default: if constexpr (MT >= 4) n_main_loop<NW, MT, MT, UPW, EPI>(p, a_lds, stage, tiles, u_first, u_count, ntr, prow0, rows, gab); break;
+    case 1: n_main_loop<NW, MT, 1, UPW, EPI, PACKED>(p, a_lds, stage, tiles, u_first, u_count, ntr, prow0, rows, gab); break;
+    case 2: if constexpr (MT >= 2) n_main_loop<NW, MT, 2, UPW, EPI, PACKED>(p, a_lds, stage, tiles, u_first, u_count, ntr, prow0, rows, gab); break;
+    case 3: if constexpr (MT >= 3) n_main_loop<NW, MT, 3, UPW, EPI, PACKED>(p, a_lds, stage, tiles, u_first, u_count, ntr, prow0, rows, gab); break;
+    default: if constexpr (MT >= 4) n_main_loop<NW, MT, MT, UPW, EPI, PACKED>(p, a_lds, stage, tiles, u_first, u_count, ntr, prow0, rows, gab); break;
   }
 }
 
@@ -852,7 +870,7 @@ static hipError_t grid_check(int64_t blocks) {
   return blocks >= (int64_t(1) << 31) ? hipErrorInvalidConfiguration : hipSuccess;
 }
 
-template <int NW, int WN, int MT, int EPI, bool PACKED, int MINB = 1>
+template <int NW, int WN, int MT, int EPI, int PACKED, int MINB = 2>
 static hipError_t launch_streamk(GemmParams prm, int64_t m_total, hipStream_t stream) {
   constexpr int BN = NW * WN * 16;
   constexpr int MC = MT * 16;
@@ -868,14 +886,14 @@ static hipError_t launch_streamk(GemmParams prm, int64_t m_total, hipStream_t st
   return hipGetLastError();
 }
 
-template <int NW, int MT, int UPW, int EPI>
+template <int NW, int MT, int UPW, int EPI, int PACKED>
 static hipError_t launch_streamn(GemmParams prm, int64_t m_total, hipStream_t stream) {
   constexpr int MC = MT * 16;
   const int nunits = ((prm.N + 15) / 16 + UNIT - 1) / UNIT;
   prm.n_tiles = (nunits + NW * UPW - 1) / (NW * UPW);     // column-unit groups per chunk
   const int64_t blocks = ((((m_total + MC - 1) / MC + prm.E) * prm.n_tiles) + 7) / 8 * 8;
   if (grid_check(blocks) != hipSuccess) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((k_gemm_streamn<NW, MT, UPW, EPI>), dim3(static_cast<unsigned>(blocks)), dim3(NW * 64), 0,
+  hipLaunchKernelGGL((k_gemm_streamn<NW, MT, UPW, EPI, PACKED>), dim3(static_cast<unsigned>(blocks)), dim3(NW * 64), 0,
                      stream, prm);
   return hipGetLastError();
 }
@@ -888,7 +906,7 @@ static hipError_t launch_streamn(GemmParams prm, int64_t m_total, hipStream_t st
 //           off once the MFMA work dominates.
 constexpr int kLargeRows = 128;
 
-template <bool PACKED, bool LARGE>
+template <int PACKED, bool LARGE>
 static hipError_t launch_k(const GemmParams& prm, int epilogue, int64_t m_total, hipStream_t stream) {
   switch (epilogue) {
     case EPI_F32:
@@ -907,27 +925,50 @@ static hipError_t launch_k(const GemmParams& prm, int epilogue, int64_t m_total,
   }
 }
 
+// Weight loads are cached (not non-temporal) once the experts average a full
+// 64-row chunk: their row chunks then re-read the same tiles, side by side on
+// one XCD, and share them in its L2.  Config 2 (64 rows per expert on
+// average): HBM reads of gate_up 673 -> 609 MB and of down 364 -> 250 MB; the
+// combine then finds less of the down output in the last-level cache, but the
+// layer is still faster.  Experts of a few rows read their tiles once, and
+// non-temporal loads keep them from evicting anything.
+#ifndef CACHE_ROWS
+#define CACHE_ROWS 64
+#endif
+
 hipError_t launch_grouped_gemm(const GemmParams& prm, int epilogue, int64_t m_total, int hint, hipStream_t stream) {
   // rows per expert: the caller's hint, else the average (the counts stay on
   // the device)
   const int64_t rows_per_expert = hint > 0 ? hint : m_total / prm.E;
   const bool large = rows_per_expert >= kLargeRows;
   if (prm.b_packed && prm.K <= KSTEP && epilogue != EPI_SWIGLU) {
-#ifndef DN_UPW
-#define DN_UPW 6
-#endif
+    constexpr int UPW = 6;
+    const bool cached = rows_per_expert >= CACHE_ROWS;
     switch (epilogue) {
-      case EPI_F32: return launch_streamn<4, 4, DN_UPW, EPI_F32>(prm, m_total, stream);
-      case EPI_BF16: return launch_streamn<4, 4, DN_UPW, EPI_BF16>(prm, m_total, stream);
-      case EPI_COMBINE: return launch_streamn<4, 4, DN_UPW, EPI_COMBINE>(prm, m_total, stream);
+      case EPI_F32:
+        return cached ? launch_streamn<4, 4, UPW, EPI_F32, kPackedCached>(prm, m_total, stream)
+                      : launch_streamn<4, 4, UPW, EPI_F32, kPackedNT>(prm, m_total, stream);
+      case EPI_BF16:
+        return cached ? launch_streamn<4, 4, UPW, EPI_BF16, kPackedCached>(prm, m_total, stream)
+                      : launch_streamn<4, 4, UPW, EPI_BF16, kPackedNT>(prm, m_total, stream);
+      case EPI_COMBINE:
+        return cached ? launch_streamn<4, 4, UPW, EPI_COMBINE, kPackedCached>(prm, m_total, stream)
+                      : launch_streamn<4, 4, UPW, EPI_COMBINE, kPackedNT>(prm, m_total, stream);
       default: return hipErrorInvalidValue;
     }
   }
-  if (large)
-    return prm.b_packed ? launch_k<true, true>(prm, epilogue, m_total, stream)
-                        : launch_k<false, true>(prm, epilogue, m_total, stream);
-  return prm.b_packed ? launch_k<true, false>(prm, epilogue, m_total, stream)
-                      : launch_k<false, false>(prm, epilogue, m_total, stream);
+  const int mode = !prm.b_packed ? kRowB : rows_per_expert >= CACHE_ROWS ? kPackedCached : kPackedNT;
+  switch (mode) {
+    case kRowB:
+      return large ? launch_k<kRowB, true>(prm, epilogue, m_total, stream)
+                   : launch_k<kRowB, false>(prm, epilogue, m_total, stream);
+    case kPackedNT:
+      return large ? launch_k<kPackedNT, true>(prm, epilogue, m_total, stream)
+                   : launch_k<kPackedNT, false>(prm, epilogue, m_total, stream);
+    default:
+      return large ? launch_k<kPackedCached, true>(prm, epilogue, m_total, stream)
+                   : launch_k<kPackedCached, false>(prm, epilogue, m_total, stream);
+  }
 }
 
 }  // namespace nvfp4

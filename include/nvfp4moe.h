@@ -103,8 +103,9 @@ typedef struct nvfp4moe_gemm_args {
   const int32_t* row_token;   /* EPI_COMBINE_F32: device [m_total], values in [0, out_rows) */
   const float* row_weight;    /* EPI_COMBINE_F32: device [m_total] */
   int32_t max_rows_per_expert_hint;  /* rows per expert the caller expects (the pages' tune_max_num_tokens);
-                                        0: m_total / E.  Picks the tile shape only (>= 128: the large-M
-                                        tile), never the result beyond float32 summation order. */
+                                        0: m_total / E.  Picks the tile shape (>= 128: the large-M tile)
+                                        and the weight-load cache policy (>= 64: cached, else
+                                        non-temporal); never changes the result. */
   /* Optional: B in the packed tile layout written by nvfp4_weight_repack (16-byte
      aligned).  When set, b_codes / b_scales are not read (and may be NULL). */
   const uint8_t* b_packed;
