@@ -190,38 +190,56 @@ hipError_t launch_swiglu(const void* y, int dtype, int64_t M, int I, const float
 }
 
 // ------------------------------------------------------------------ combine
-// out[t, 8c .. 8c+8) = sum_j w[t, j] * y[row(t, j), 8c .. 8c+8)
+// out[t, 8c .. 8c+8) = sum_j w[t, j] * y[row(t, j), 8c .. 8c+8), summed in
+// order j = 0, 1, ...  The k rows of a token are fetched in batches of 8
+// independent loads (rows past k re-read the last one and are not added), so
+// a thread waits for one round trip per batch instead of one per row.
+template <int YT>
+__device__ __forceinline__ void load_row8(const void* y, int64_t row, int H, int c, float (&v)[8]) {
+  if constexpr (YT == 1) {
+    const uint4 q = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(y) + row * H)[c];
+    const uint32_t u[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      v[2 * m] = __uint_as_float(u[m] << 16);
+      v[2 * m + 1] = __uint_as_float(u[m] & 0xFFFF0000u);
+    }
+  } else {
+    const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(y) + row * H) + 2 * c;
+    const float4 a0 = p[0], a1 = p[1];
+    v[0] = a0.x; v[1] = a0.y; v[2] = a0.z; v[3] = a0.w;
+    v[4] = a1.x; v[5] = a1.y; v[6] = a1.z; v[7] = a1.w;
+  }
+}
+
 template <int YT, int OT>
 __global__ __launch_bounds__(256) void k_combine(const void* __restrict__ y, const int* __restrict__ perm,
                                                  const float* __restrict__ w, int T, int k, int H,
                                                  void* __restrict__ out) {
+  constexpr int B = 8;
   const int groups = H / 8;
   const int64_t i = blockIdx.x * 256ll + threadIdx.x;
   if (i >= static_cast<int64_t>(T) * groups) return;
   const int t = static_cast<int>(i / groups);
   const int c = static_cast<int>(i % groups);
   float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-  for (int j = 0; j < k; ++j) {
-    const int64_t a = static_cast<int64_t>(t) * k + j;
-    const int64_t row = perm ? perm[a] : a;
-    const float wt = w ? w[a] : 1.0f;
-    float v[8];
-    if constexpr (YT == 1) {
-      const uint4 q = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(y) + row * H)[c];
-      const uint32_t u[4] = {q.x, q.y, q.z, q.w};
+  for (int j0 = 0; j0 < k; j0 += B) {
+    int64_t rows[B];
+    float wt[B];
 #pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        v[2 * m] = __uint_as_float(u[m] << 16);
-        v[2 * m + 1] = __uint_as_float(u[m] & 0xFFFF0000u);
-      }
-    } else {
-      const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(y) + row * H) + 2 * c;
-      const float4 a0 = p[0], a1 = p[1];
-      v[0] = a0.x; v[1] = a0.y; v[2] = a0.z; v[3] = a0.w;
-      v[4] = a1.x; v[5] = a1.y; v[6] = a1.z; v[7] = a1.w;
+    for (int u = 0; u < B; ++u) {
+      const int64_t a = static_cast<int64_t>(t) * k + min(j0 + u, k - 1);
+      rows[u] = perm ? perm[a] : a;
+      wt[u] = w ? w[a] : 1.0f;
     }
+    float v[B][8];
 #pragma unroll
-    for (int m = 0; m < 8; ++m) acc[m] = fmaf(wt, v[m], acc[m]);
+    for (int u = 0; u < B; ++u) load_row8<YT>(y, rows[u], H, c, v[u]);
+#pragma unroll
+    for (int u = 0; u < B; ++u)
+      if (j0 + u < k)
+#pragma unroll
+        for (int m = 0; m < 8; ++m) acc[m] = fmaf(wt[u], v[u][m], acc[m]);
   }
   if constexpr (OT == 1) {
     uint4 q;

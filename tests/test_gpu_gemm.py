@@ -349,3 +349,27 @@ def test_config0_down_fused_combine_and_unfused_combine(packed):
     o = m.moe_unpermute_combine(up(y2), None, None, y2.shape[0], 1, out_dtype=torch.float32)
     torch.cuda.synchronize()
     assert np.array_equal(down(o), y2)
+
+
+@pytest.mark.parametrize("k", [1, 3, 8, 9, 17, 32])
+@pytest.mark.parametrize("ydt", [torch.float32, torch.bfloat16])
+def test_combine_any_k(k, ydt):
+    # the combine fetches a token's rows in batches of 8: k below, at and
+    # above a batch, and the largest k the router supports
+    rng = np.random.default_rng(50 + k)
+    T, H = 37, 272
+    M = T * k
+    y = rng.standard_normal((M, H)).astype(np.float32) * rng.uniform(0.1, 10, (M, 1)).astype(np.float32)
+    if ydt == torch.bfloat16:
+        y = workloads.to_bf16_values(y)
+    perm_of = rng.permutation(M).astype(np.int32)
+    w = rng.uniform(0, 1, (T, k)).astype(np.float32)
+    print(f"combine k={k} y={ydt}", flush=True)
+    ref64, _ = OM.combine(y, perm_of, w)
+    bound = k * 2.0 ** -23 * np.einsum("tj,tjh->th", np.abs(w.astype(np.float64)),
+                                        np.abs(y.astype(np.float64))[perm_of.reshape(T, k)]) + 1e-30
+    o16 = m.moe_unpermute_combine(up(y).to(ydt), up(perm_of), up(w), T, k)
+    o32 = m.moe_unpermute_combine(up(y).to(ydt), up(perm_of), up(w), T, k, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert np.all(np.abs(down(o32) - ref64) <= bound), "float32 out"
+    assert np.all(np.abs(bf16_to_f32(o16) - ref64) <= bound + 2.0 ** -8 * np.abs(ref64)), "bf16 out"
