@@ -925,13 +925,30 @@ static hipError_t launch_k(const GemmParams& prm, int epilogue, int64_t m_total,
   }
 }
 
+template <int UPW>
+static hipError_t launch_dn(const GemmParams& prm, int epilogue, bool cached, int64_t m_total, hipStream_t stream) {
+  switch (epilogue) {
+    case EPI_F32:
+      return cached ? launch_streamn<4, 4, UPW, EPI_F32, kPackedCached>(prm, m_total, stream)
+                    : launch_streamn<4, 4, UPW, EPI_F32, kPackedNT>(prm, m_total, stream);
+    case EPI_BF16:
+      return cached ? launch_streamn<4, 4, UPW, EPI_BF16, kPackedCached>(prm, m_total, stream)
+                    : launch_streamn<4, 4, UPW, EPI_BF16, kPackedNT>(prm, m_total, stream);
+    case EPI_COMBINE:
+      return cached ? launch_streamn<4, 4, UPW, EPI_COMBINE, kPackedCached>(prm, m_total, stream)
+                    : launch_streamn<4, 4, UPW, EPI_COMBINE, kPackedNT>(prm, m_total, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
 // Weight loads are cached (not non-temporal) once the experts average a full
 // 64-row chunk: their row chunks then re-read the same tiles, side by side on
-// one XCD, and share them in its L2.  Config 2 (64 rows per expert on
-// average): HBM reads of gate_up 673 -> 609 MB and of down 364 -> 250 MB; the
-// combine then finds less of the down output in the last-level cache, but the
-// layer is still faster.  Experts of a few rows read their tiles once, and
-// non-temporal loads keep them from evicting anything.
+// one XCD, and share them in its L2.  Decode MoE with T=2048, top-8 of 256
+// experts (64 rows per expert on average, Zipf-skewed): HBM reads of gate_up
+// 673 -> 609 MB and of down 364 -> 250 MB; the combine then finds less of
+// the down output in the last-level cache, but the layer is still faster.
+// Experts of a few rows read their tiles once, and non-temporal loads keep
+// them from evicting anything.
 #ifndef CACHE_ROWS
 #define CACHE_ROWS 64
 #endif
@@ -942,20 +959,12 @@ hipError_t launch_grouped_gemm(const GemmParams& prm, int epilogue, int64_t m_to
   const int64_t rows_per_expert = hint > 0 ? hint : m_total / prm.E;
   const bool large = rows_per_expert >= kLargeRows;
   if (prm.b_packed && prm.K <= KSTEP && epilogue != EPI_SWIGLU) {
-    constexpr int UPW = 6;
+    // units of 64 columns per wave: 8 at large M (T=16384 prefill, 512 rows
+    // per expert: down 586 -> 558 µs), 6 below (T=256 decode, 8 rows per
+    // expert: 57 µs against 60 with 8)
     const bool cached = rows_per_expert >= CACHE_ROWS;
-    switch (epilogue) {
-      case EPI_F32:
-        return cached ? launch_streamn<4, 4, UPW, EPI_F32, kPackedCached>(prm, m_total, stream)
-                      : launch_streamn<4, 4, UPW, EPI_F32, kPackedNT>(prm, m_total, stream);
-      case EPI_BF16:
-        return cached ? launch_streamn<4, 4, UPW, EPI_BF16, kPackedCached>(prm, m_total, stream)
-                      : launch_streamn<4, 4, UPW, EPI_BF16, kPackedNT>(prm, m_total, stream);
-      case EPI_COMBINE:
-        return cached ? launch_streamn<4, 4, UPW, EPI_COMBINE, kPackedCached>(prm, m_total, stream)
-                      : launch_streamn<4, 4, UPW, EPI_COMBINE, kPackedNT>(prm, m_total, stream);
-      default: return hipErrorInvalidValue;
-    }
+    return large ? launch_dn<8>(prm, epilogue, cached, m_total, stream)
+                 : launch_dn<6>(prm, epilogue, cached, m_total, stream);
   }
   const int mode = !prm.b_packed ? kRowB : rows_per_expert >= CACHE_ROWS ? kPackedCached : kPackedNT;
   switch (mode) {
