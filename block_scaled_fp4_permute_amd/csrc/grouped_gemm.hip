@@ -98,59 +98,6 @@ hipError_t launch_repack(const uint8_t* codes, const uint8_t* scales, int E, int
 }
 
 // ------------------------------------------------------------------ task map
-// Number of row chunks over all experts (ceil(Me/MC) each), returned to every
-// thread of the workgroup.
-template <int THREADS, int MC>
-__device__ __forceinline__ int count_chunks(const GemmParams& p, int* s_part) {
-  const int tid = threadIdx.x;
-  constexpr int NWAVE = THREADS / 64;
-  int c = 0;
-  for (int e = tid; e < p.E; e += THREADS) {
-    const int a = min(max(p.offsets[e], 0), p.m_total);
-    const int b = min(max(p.offsets[e + 1], 0), p.m_total);
-    c += b > a ? (b - a + MC - 1) / MC : 0;
-  }
-#pragma unroll
-  for (int d = 32; d >= 1; d >>= 1) c += __shfl_xor(c, d);
-  if ((tid & 63) == 0) s_part[tid >> 6] = c;
-  __syncthreads();
-  int total = 0;
-#pragma unroll
-  for (int w = 0; w < NWAVE; ++w) total += s_part[w];
-  __syncthreads();     // s_part is reused by the caller
-  return total;
-}
-
-// Block-wide exclusive prefix sum of one int per thread; every thread also
-// gets the block total.  s_tmp: one int per wave, reusable after return.
-template <int THREADS>
-__device__ __forceinline__ int block_excl_scan(int v, int* s_tmp, int& total) {
-  constexpr int NWAVE = THREADS / 64;
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  int incl = v;
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const int u = __shfl_up(incl, d);
-    if (lane >= d) incl += u;
-  }
-  if (lane == 63) s_tmp[wave] = incl;
-  __syncthreads();
-  int before = 0;
-  total = 0;
-#pragma unroll
-  for (int w = 0; w < NWAVE; ++w) {
-    const int u = s_tmp[w];
-    before += (w < wave) ? u : 0;
-    total += u;
-  }
-  __syncthreads();
-  return before + incl - v;
-}
-
-__device__ __forceinline__ int overlap(int a0, int a1, int b0, int b1) { return max(0, min(a1, b1) - max(a0, b0)); }
-
-// ------------------------------------------------------------------ task map
 // A task is (row chunk, column tile).  Chunks are enumerated expert by expert
 // (expert e owns ceil(Me/MC) of them, all full but maybe the last) and tasks
 // chunk by chunk, so the tasks of an expert are contiguous.  The class of a
@@ -164,96 +111,196 @@ __device__ __forceinline__ int overlap(int a0, int a1, int b0, int b1) { return 
 // order within a class): longest-first list scheduling, which keeps the full
 // chunks out of the last round of workgroups.  Otherwise in task order, so
 // that the chunks of an expert run side by side and share its weight tiles in
-// L2.  Every thread takes part; returns false (uniformly) when the workgroup
-// has no task.  Needs a grid of at least 8 * ceil(tasks / 8) workgroups and
-// s_work of at least MT + 4 ints.
-template <int THREADS, int MT, bool BY_CLASS>
-__device__ __forceinline__ bool find_task(const GemmParams& p, int* s_part, int* s_work, int& e_out, int& m0_out,
-                                          int& nt_out) {
+// L2.
+//
+// Every wave computes the map on its own, from one read of the expert offsets
+// (4 experts per lane) and wave shuffles only: no LDS and no barrier before a
+// workgroup's first loads.  Experts beyond 256 are taken in further groups of
+// 256.  Needs a grid of at least 8 * ceil(tasks / 8) workgroups.
+constexpr int kExpPerLane = 4;
+constexpr int kExpGroup = 64 * kExpPerLane;
+
+// rows of expert e (0 past the last expert); data-dependent bounds are clamped
+// so that inconsistent offsets give wrong rows, never an access out of bounds
+__device__ __forceinline__ int expert_rows(const GemmParams& p, int e) {
+  if (e >= p.E) return 0;
+  const int a = min(max(p.offsets[e], 0), p.m_total);
+  const int b = min(max(p.offsets[e + 1], 0), p.m_total);
+  return max(b - a, 0);
+}
+
+__device__ __forceinline__ int wave_sum(int v) {
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) v += __shfl_xor(v, d);
+  return v;
+}
+
+// exclusive prefix sum over the 64 lanes; total: the sum of all lanes
+__device__ __forceinline__ int wave_excl_scan(int v, int& total) {
+  const int lane = threadIdx.x & 63;
+  int incl = v;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int u = __shfl_up(incl, d);
+    if (lane >= d) incl += u;
+  }
+  total = __shfl(incl, 63);
+  return incl - v;
+}
+
+__device__ __forceinline__ int overlap(int a0, int a1, int b0, int b1) { return max(0, min(a1, b1) - max(a0, b0)); }
+
+// experts g0 + 4 lane + i of one group: rows, chunks, first chunk
+template <int MC>
+struct ExpGroup {
+  int Me[kExpPerLane];
+  int c[kExpPerLane];
+  int cb[kExpPerLane];
+  int total;            // chunks of the whole group
+};
+
+template <int MC>
+__device__ __forceinline__ void load_group(const GemmParams& p, int g0, int base, ExpGroup<MC>& G) {
+  const int lane = threadIdx.x & 63;
+  int sum = 0;
+#pragma unroll
+  for (int i = 0; i < kExpPerLane; ++i) {
+    G.Me[i] = expert_rows(p, g0 + kExpPerLane * lane + i);
+    G.c[i] = (G.Me[i] + MC - 1) / MC;
+    sum += G.c[i];
+  }
+  int run = base + wave_excl_scan(sum, G.total);
+#pragma unroll
+  for (int i = 0; i < kExpPerLane; ++i) {
+    G.cb[i] = run;
+    run += G.c[i];
+  }
+}
+
+// live 16-row tiles of the last chunk of an expert with Me rows in c chunks
+template <int MC>
+__device__ __forceinline__ int last_class(int Me, int c) { return (Me - (c - 1) * MC + 15) >> 4; }
+
+// (expert, first row of the chunk, column tile) of workgroup blockIdx.x;
+// false (uniformly) when it has no task
+template <int MT, bool BY_CLASS>
+__device__ __forceinline__ bool find_task(const GemmParams& p, int& e_out, int& m0_out, int& nt_out) {
   constexpr int MC = MT * 16;
   const int ntl = p.n_tiles;
-  const int n = count_chunks<THREADS, MC>(p, s_part) * ntl;
+  const int lane = threadIdx.x & 63;
+  ExpGroup<MC> G0;
+  load_group<MC>(p, 0, 0, G0);
+  int n_chunks = G0.total;
+  for (int g0 = kExpGroup; g0 < p.E; g0 += kExpGroup) {
+    ExpGroup<MC> G;
+    load_group<MC>(p, g0, n_chunks, G);
+    n_chunks += G.total;
+  }
+  const int n = n_chunks * ntl;
   const int per = (n + 7) >> 3;
   const int lo = (blockIdx.x & 7) * per;
   const int hi = min(lo + per, n);
   const int j = blockIdx.x >> 3;
   if (lo + j >= hi) return false;
-  const int tid = threadIdx.x;
-  int* s_cnt = s_work + 2;   // tasks of class k in [lo, hi): s_cnt[k], k = 1..MT
-  if (tid <= MT) s_cnt[tid] = 0;
-  if (tid == 0) s_work[0] = -1;
-  __syncthreads();
-  // expert e: Me rows, c chunks from chunk cb; tasks [t0, t1) of the full
-  // chunks before the last, [t1, t2) of the last chunk (class cl)
-  auto expert_of = [&](int e, int& Me, int& c) {
-    Me = 0;
-    if (e < p.E) {
-      const int a = min(max(p.offsets[e], 0), p.m_total);
-      const int b = min(max(p.offsets[e + 1], 0), p.m_total);
-      Me = max(b - a, 0);
-    }
-    c = (Me + MC - 1) / MC;
-  };
-  int base = 0;
-  for (int e0 = 0; BY_CLASS && e0 < p.E && base * ntl < hi; e0 += THREADS) {
-    int Me, c, total;
-    expert_of(e0 + tid, Me, c);
-    const int cb = base + block_excl_scan<THREADS>(c, s_part, total);
-    if (c > 0) {
-      const int cl = (Me - (c - 1) * MC + 15) >> 4;
-      const int t1 = (cb + c - 1) * ntl;
-      const int nfull = overlap(cb * ntl, t1, lo, hi);
-      const int nlast = overlap(t1, t1 + ntl, lo, hi);
-      if (nfull) atomicAdd(&s_cnt[MT], nfull);
-      if (nlast) atomicAdd(&s_cnt[cl], nlast);
-    }
-    base += total;
-  }
-  __syncthreads();
+
+  // the class k and rank r of this workgroup's task among the class-k tasks
+  // of [lo, hi)
   int k = MT, r = j;
-  while (BY_CLASS && k > 1 && r >= s_cnt[k]) r -= s_cnt[k--];
-  // the r-th task of class k in [lo, hi), in task order (without classes:
-  // task lo + j)
-  const int t_plain = lo + j;
-  base = 0;
-  int before = 0;
-  for (int e0 = 0; e0 < p.E && base * ntl < hi; e0 += THREADS) {
-    int Me, c, total;
-    expert_of(e0 + tid, Me, c);
-    const int cb = base + block_excl_scan<THREADS>(c, s_part, total);
-    int t = -1;
-    if constexpr (BY_CLASS) {
-      int t_lo = 0, v = 0, vtotal;
-      if (c > 0) {
-        const int cl = (Me - (c - 1) * MC + 15) >> 4;
-        const int t1 = (cb + c - 1) * ntl;
-        // class-k tasks of this expert form one interval
-        const int a0 = (k == MT) ? cb * ntl : t1;
-        const int a1 = (cl == k) ? t1 + ntl : t1;
-        if (a1 > a0) {
-          t_lo = max(a0, lo);
-          v = overlap(a0, a1, lo, hi);
+  if constexpr (BY_CLASS) {
+    int cnt[MT + 1];
+#pragma unroll
+    for (int q = 0; q <= MT; ++q) cnt[q] = 0;
+    int base = 0;
+    for (int g0 = 0; g0 < p.E && base * ntl < hi; g0 += kExpGroup) {
+      ExpGroup<MC> G;
+      if (g0 == 0) G = G0;
+      else load_group<MC>(p, g0, base, G);
+#pragma unroll
+      for (int i = 0; i < kExpPerLane; ++i) {
+        if (G.c[i] > 0) {
+          const int cl = last_class<MC>(G.Me[i], G.c[i]);
+          const int t1 = (G.cb[i] + G.c[i] - 1) * ntl;
+          cnt[MT] += overlap(G.cb[i] * ntl, t1, lo, hi);
+          const int nl = overlap(t1, t1 + ntl, lo, hi);
+#pragma unroll
+          for (int q = 1; q <= MT; ++q) cnt[q] += (q == cl) ? nl : 0;
         }
       }
-      const int vb = before + block_excl_scan<THREADS>(v, s_part + THREADS / 64, vtotal);
-      if (v > 0 && r >= vb && r < vb + v) t = t_lo + (r - vb);
+      base += G.total;
+    }
+#pragma unroll
+    for (int q = 1; q <= MT; ++q) cnt[q] = wave_sum(cnt[q]);
+#pragma unroll
+    for (int q = MT; q >= 2; --q) {
+      if (k == q && r >= cnt[q]) {
+        r -= cnt[q];
+        k = q - 1;
+      }
+    }
+  }
+
+  // find the r-th class-k task of [lo, hi) in task order (without classes:
+  // task lo + j); exactly one lane holds it
+  const int t_plain = lo + j;
+  int f_t = -1, f_e = 0, f_cb = 0;
+  int base = 0, before = 0;
+  for (int g0 = 0; g0 < p.E && base * ntl < hi; g0 += kExpGroup) {
+    ExpGroup<MC> G;
+    if (g0 == 0) G = G0;
+    else load_group<MC>(p, g0, base, G);
+    if constexpr (BY_CLASS) {
+      int v[kExpPerLane], tlo[kExpPerLane];
+      int vsum = 0;
+#pragma unroll
+      for (int i = 0; i < kExpPerLane; ++i) {
+        v[i] = 0;
+        tlo[i] = 0;
+        if (G.c[i] > 0) {
+          // the class-k tasks of one expert form one interval
+          const int cl = last_class<MC>(G.Me[i], G.c[i]);
+          const int t1 = (G.cb[i] + G.c[i] - 1) * ntl;
+          const int a0 = (k == MT) ? G.cb[i] * ntl : t1;
+          const int a1 = (cl == k) ? t1 + ntl : t1;
+          if (a1 > a0) {
+            tlo[i] = max(a0, lo);
+            v[i] = overlap(a0, a1, lo, hi);
+          }
+        }
+        vsum += v[i];
+      }
+      int vtotal;
+      int vb = before + wave_excl_scan(vsum, vtotal);
+#pragma unroll
+      for (int i = 0; i < kExpPerLane; ++i) {
+        if (v[i] > 0 && r >= vb && r < vb + v[i]) {
+          f_t = tlo[i] + (r - vb);
+          f_e = g0 + kExpPerLane * lane + i;
+          f_cb = G.cb[i];
+        }
+        vb += v[i];
+      }
       before += vtotal;
     } else {
-      if (c > 0 && t_plain >= cb * ntl && t_plain < (cb + c) * ntl) t = t_plain;
+#pragma unroll
+      for (int i = 0; i < kExpPerLane; ++i) {
+        if (G.c[i] > 0 && t_plain >= G.cb[i] * ntl && t_plain < (G.cb[i] + G.c[i]) * ntl) {
+          f_t = t_plain;
+          f_e = g0 + kExpPerLane * lane + i;
+          f_cb = G.cb[i];
+        }
+      }
     }
-    if (t >= 0) {
-      const int chunk = t / ntl;
-      s_work[0] = e0 + tid;
-      s_work[1] = (chunk - cb) * MC;
-      s_work[2 + MT + 1] = t - chunk * ntl;
-    }
-    base += total;
+    base += G.total;
   }
-  __syncthreads();
-  e_out = s_work[0];
-  m0_out = s_work[1];
-  nt_out = s_work[2 + MT + 1];
-  return e_out >= 0;
+  const uint64_t found = __ballot(f_t >= 0);
+  if (found == 0) return false;
+  const int src = __ffsll(static_cast<unsigned long long>(found)) - 1;
+  const int t = __shfl(f_t, src);
+  e_out = __shfl(f_e, src);
+  const int chunk = t / ntl;
+  m0_out = (chunk - __shfl(f_cb, src)) * MC;
+  nt_out = t - chunk * ntl;
+  return true;
 }
 
 // ------------------------------------------------------------------ A operand
@@ -634,15 +681,13 @@ __global__ __launch_bounds__(NW * 64, MINB) void k_gemm_streamk(const GemmParams
   static_assert(EPI != EPI_SWIGLU || (WN % 2) == 0, "SwiGLU pairs gate and up tiles");
   static_assert(MT == 1 || MT == 2 || MT == 3 || MT == 4 || MT == 6 || MT == 8, "row tiles per chunk");
   __shared__ half8 a_lds[2][MT * 8 * 64];   // double-buffered [row tile][sub-step][lane] fragments
-  __shared__ int s_part[2 * NW];
-  __shared__ int s_work[MT + 4];
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int lr = lane & 15;
 
   int e, m0, nt;
-  if (!find_task<THREADS, MT, true>(p, s_part, s_work, e, m0, nt)) return;
+  if (!find_task<MT, true>(p, e, m0, nt)) return;
   // data-dependent bounds are clamped so that inconsistent offsets can give
   // wrong rows but never an access outside the buffers
   const int row0 = min(max(p.offsets[e], 0), p.m_total);
@@ -829,12 +874,10 @@ __global__ __launch_bounds__(NW * 64) void k_gemm_streamn(const GemmParams p) {
   static_assert(UPW % 2 == 0, "units per wave come in pairs");
   __shared__ half8 a_lds[MT * 8 * 64];
   __shared__ float stage_lds[NW][16 * 68];   // per-wave output staging (row pitch 68 floats)
-  __shared__ int s_part[2 * NW];
-  __shared__ int s_work[MT + 4];
 
   const int wave = threadIdx.x >> 6;
   int e, m0, ng;
-  if (!find_task<THREADS, MT, false>(p, s_part, s_work, e, m0, ng)) return;
+  if (!find_task<MT, false>(p, e, m0, ng)) return;
   const int row0 = min(max(p.offsets[e], 0), p.m_total);
   const int Me = min(max(p.offsets[e + 1], 0), p.m_total) - row0;
   const int rows = min(MC, Me - m0);
