@@ -568,7 +568,8 @@ __device__ __forceinline__ void epilogue_swiglu(const GemmParams& p, const float
   for (int i = 0; i < 4; ++i) {
     const int m = 4 * lg + i;
     const float v = (s[i] != 0u && se[i] > 0.0f) ? __fdividef(fabsf(h[i]), se[i]) : 0.0f;
-    const uint32_t code = (s[i] != 0u) ? (f32_to_e2m1_mag(v) | ((__float_as_uint(h[i]) >> 31) << 3)) : 0u;
+    // a NaN quotient (zero times an infinite reciprocal) encodes as 0 | sign
+    const uint32_t code = (s[i] != 0u) ? e2m1_code(__builtin_copysignf(v == v ? v : 0.0f, h[i])) : 0u;
     const uint32_t other = dpp_u32<kDppXor1>(code);
     if (m < rows_left && hc_ok && (lr & 1) == 0)
       p.out_codes[static_cast<size_t>(prow0 + m) * (I / 2) + hc / 2] = static_cast<uint8_t>(code | (other << 4));

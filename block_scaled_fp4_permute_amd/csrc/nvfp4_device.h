@@ -61,14 +61,25 @@ __device__ __forceinline__ uint32_t f32_to_e4m3_sat(float t) {
 }
 
 // ------------------------------------------------------------------ E2M1
-// |v| -> 3-bit E2M1 magnitude code, nearest with ties to even, saturating at 6.
-// The grid is 0, .5, 1, 1.5, 2, 3, 4, 6; the decision points are the midpoints,
-// and at a midpoint the code with the even mantissa wins (>= or > below).
-__device__ __forceinline__ uint32_t f32_to_e2m1_mag(float v) {
-  return static_cast<uint32_t>(v > 0.25f) + static_cast<uint32_t>(v >= 0.75f) +
-         static_cast<uint32_t>(v > 1.25f) + static_cast<uint32_t>(v >= 1.75f) +
-         static_cast<uint32_t>(v > 2.5f) + static_cast<uint32_t>(v >= 3.5f) +
-         static_cast<uint32_t>(v > 5.0f);
+// E2M1 codes from the gfx950 conversion instruction with scale 1.  For every
+// float v that is not a NaN it returns the magnitude of v rounded to the grid
+// 0, .5, 1, 1.5, 2, 3, 4, 6 - nearest, with ties to the code whose mantissa bit
+// is 0, saturating at 6 (decision points 0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5,
+// the lower code winning at 0.25, 1.25, 2.5 and 5) - with the sign bit of v
+// as bit 3; infinities give 7 | sign, and so do NaNs.  Checked on the device
+// against that rule for every finite float of either sign, in both nibble
+// positions: no difference.
+__device__ __forceinline__ uint32_t e2m1_code(float v) {
+  return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, v, 0.0f, 1.0f, 0) & 0xFu;
+}
+
+// v[B..B+7] -> one word, element B+i in nibble i
+template <int B>
+__device__ __forceinline__ uint32_t e2m1_pack8(const float (&v)[16]) {
+  uint32_t w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, v[B], v[B + 1], 1.0f, 0);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[B + 2], v[B + 3], 1.0f, 1);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[B + 4], v[B + 5], 1.0f, 2);
+  return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[B + 6], v[B + 7], 1.0f, 3);
 }
 
 // Per-tensor scale from the absolute maximum: g = amax / 2688 (2688 = 6 * 448),
@@ -95,36 +106,31 @@ __device__ __forceinline__ uint32_t encode_block16(const float (&x)[16], float g
     // With y = RN(1/b) this gives RN(a/b) whenever nothing underflows or
     // overflows (Markstein, IBM J. Res. Dev. 34(1), 1990).  The quotients it
     // misses come from subnormal |x| and lie below 2^-50, far under the
-    // smallest E2M1 rounding boundary (0.25).  A reciprocal that overflows
-    // (b below 2^-128) takes true divisions.
+    // smallest E2M1 rounding boundary (0.25).  A q0 that overflows makes q a
+    // NaN, which encodes like the infinity (code 7).  A reciprocal that
+    // overflows (b below 2^-128) takes true divisions.  The sign bit is copied
+    // from x, -0 included.
     const float y = 1.0f / scale_eff;
     const bool via_rcp = scale_eff > 0.0f && y < __builtin_huge_valf();
+    float v[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const float a = fabsf(x[i]);
-      float v;
+      float q;
       if (via_rcp) {
         const float q0 = a * y;
-        const float q = __builtin_fmaf(__builtin_fmaf(-q0, scale_eff, a), y, q0);
-        v = q0 < __builtin_huge_valf() ? q : q0;
+        q = __builtin_fmaf(__builtin_fmaf(-q0, scale_eff, a), y, q0);
       } else {
-        v = scale_eff > 0.0f ? a / scale_eff : 0.0f;
+        q = scale_eff > 0.0f ? a / scale_eff : 0.0f;
       }
-      const uint32_t code = f32_to_e2m1_mag(v) | ((__float_as_uint(x[i]) >> 31) << 3);
-      w[i >> 3] |= code << (4 * (i & 7));
+      v[i] = __builtin_copysignf(q, x[i]);
     }
+    w[0] = e2m1_pack8<0>(v);
+    w[1] = e2m1_pack8<8>(v);
   }
   lo = w[0];
   hi = w[1];
   return s;
-}
-
-// Encode one value given the block's scale (used by epilogues that computed the
-// block scale cooperatively).
-__device__ __forceinline__ uint32_t encode_one(float x, uint32_t s, float scale_eff) {
-  if (s == 0u) return 0u;
-  const float v = scale_eff > 0.0f ? fabsf(x) / scale_eff : 0.0f;
-  return f32_to_e2m1_mag(v) | ((__float_as_uint(x) >> 31) << 3);
 }
 
 // ------------------------------------------------------------------ decode to FP16
