@@ -150,53 +150,90 @@ __device__ __forceinline__ int wave_excl_scan(int v, int& total) {
 
 __device__ __forceinline__ int overlap(int a0, int a1, int b0, int b1) { return max(0, min(a1, b1) - max(a0, b0)); }
 
-// experts g0 + 4 lane + i of one group: rows, chunks, first chunk
+// experts g0 + 4 lane + i of one group: rows, chunks, first task, tasks
 template <int MC>
 struct ExpGroup {
   int Me[kExpPerLane];
   int c[kExpPerLane];
-  int cb[kExpPerLane];
-  int total;            // chunks of the whole group
+  int tb[kExpPerLane];
+  int nt[kExpPerLane];
+  int total;            // tasks of the whole group
 };
-
-template <int MC>
-__device__ __forceinline__ void load_group(const GemmParams& p, int g0, int base, ExpGroup<MC>& G) {
-  const int lane = threadIdx.x & 63;
-  int sum = 0;
-#pragma unroll
-  for (int i = 0; i < kExpPerLane; ++i) {
-    G.Me[i] = expert_rows(p, g0 + kExpPerLane * lane + i);
-    G.c[i] = (G.Me[i] + MC - 1) / MC;
-    sum += G.c[i];
-  }
-  int run = base + wave_excl_scan(sum, G.total);
-#pragma unroll
-  for (int i = 0; i < kExpPerLane; ++i) {
-    G.cb[i] = run;
-    run += G.c[i];
-  }
-}
 
 // live 16-row tiles of the last chunk of an expert with Me rows in c chunks
 template <int MC>
 __device__ __forceinline__ int last_class(int Me, int c) { return (Me - (c - 1) * MC + 15) >> 4; }
 
-// (expert, first row of the chunk, column tile) of workgroup blockIdx.x;
-// false (uniformly) when it has no task
-template <int MT, bool BY_CLASS>
-__device__ __forceinline__ bool find_task(const GemmParams& p, int& e_out, int& m0_out, int& nt_out) {
+// column tasks of the last chunk of an expert: twice as many (half as wide)
+// when its class is at most `light`
+template <int MC>
+__device__ __forceinline__ int last_tasks(int Me, int c, int ntl, int light) {
+  return last_class<MC>(Me, c) <= light ? 2 * ntl : ntl;
+}
+
+// rows and chunks of the group's experts
+template <int MC>
+__device__ __forceinline__ void load_group(const GemmParams& p, int g0, ExpGroup<MC>& G) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int i = 0; i < kExpPerLane; ++i) {
+    G.Me[i] = expert_rows(p, g0 + kExpPerLane * lane + i);
+    G.c[i] = (G.Me[i] + MC - 1) / MC;
+  }
+}
+
+// tasks of the group's experts and their first task, from task `base` on
+template <int MC>
+__device__ __forceinline__ void assign_tasks(int ntl, int light, int base, ExpGroup<MC>& G) {
+  int sum = 0;
+#pragma unroll
+  for (int i = 0; i < kExpPerLane; ++i) {
+    G.nt[i] = G.c[i] > 0 ? (G.c[i] - 1) * ntl + last_tasks<MC>(G.Me[i], G.c[i], ntl, light) : 0;
+    sum += G.nt[i];
+  }
+  int run = base + wave_excl_scan(sum, G.total);
+#pragma unroll
+  for (int i = 0; i < kExpPerLane; ++i) {
+    G.tb[i] = run;
+    run += G.nt[i];
+  }
+}
+
+// (expert, first row of the chunk, column tile, narrow) of workgroup
+// blockIdx.x; false (uniformly) when it has no task.  A chunk has n_tiles
+// column tasks, or 2 * n_tiles half-width ("narrow") ones when it is the last
+// chunk of its expert and has at most LIGHT live row tiles (LIGHT = 0: never).
+// Light chunks split only when the whole-width tasks outnumber the resident
+// workgroups: the light tasks then run in a last round that would leave
+// workgroup slots empty; otherwise splitting only adds work.
+template <int MT, bool BY_CLASS, int LIGHT>
+__device__ __forceinline__ bool find_task(const GemmParams& p, int& e_out, int& m0_out, int& nt_out,
+                                          bool& narrow_out) {
   constexpr int MC = MT * 16;
+  static_assert(LIGHT < MT, "full chunks are never narrow");
   const int ntl = p.n_tiles;
   const int lane = threadIdx.x & 63;
   ExpGroup<MC> G0;
-  load_group<MC>(p, 0, 0, G0);
-  int n_chunks = G0.total;
+  load_group<MC>(p, 0, G0);
+  assign_tasks<MC>(ntl, 0, 0, G0);
+  int n = G0.total;
   for (int g0 = kExpGroup; g0 < p.E; g0 += kExpGroup) {
     ExpGroup<MC> G;
-    load_group<MC>(p, g0, n_chunks, G);
-    n_chunks += G.total;
+    load_group<MC>(p, g0, G);
+    assign_tasks<MC>(ntl, 0, n, G);
+    n += G.total;
   }
-  const int n = n_chunks * ntl;
+  const int light = (LIGHT > 0 && n > p.slots) ? LIGHT : 0;
+  if (light > 0) {
+    assign_tasks<MC>(ntl, light, 0, G0);
+    n = G0.total;
+    for (int g0 = kExpGroup; g0 < p.E; g0 += kExpGroup) {
+      ExpGroup<MC> G;
+      load_group<MC>(p, g0, G);
+      assign_tasks<MC>(ntl, light, n, G);
+      n += G.total;
+    }
+  }
   const int per = (n + 7) >> 3;
   const int lo = (blockIdx.x & 7) * per;
   const int hi = min(lo + per, n);
@@ -204,24 +241,29 @@ __device__ __forceinline__ bool find_task(const GemmParams& p, int& e_out, int& 
   if (lo + j >= hi) return false;
 
   // the class k and rank r of this workgroup's task among the class-k tasks
-  // of [lo, hi)
+  // of [lo, hi); the tasks of an expert's full chunks are class MT, those of
+  // its last chunk [t1, t1 + nl) have the class of that chunk
   int k = MT, r = j;
   if constexpr (BY_CLASS) {
     int cnt[MT + 1];
 #pragma unroll
     for (int q = 0; q <= MT; ++q) cnt[q] = 0;
     int base = 0;
-    for (int g0 = 0; g0 < p.E && base * ntl < hi; g0 += kExpGroup) {
+    for (int g0 = 0; g0 < p.E && base < hi; g0 += kExpGroup) {
       ExpGroup<MC> G;
-      if (g0 == 0) G = G0;
-      else load_group<MC>(p, g0, base, G);
+      if (g0 == 0) {
+        G = G0;
+      } else {
+        load_group<MC>(p, g0, G);
+        assign_tasks<MC>(ntl, light, base, G);
+      }
 #pragma unroll
       for (int i = 0; i < kExpPerLane; ++i) {
         if (G.c[i] > 0) {
           const int cl = last_class<MC>(G.Me[i], G.c[i]);
-          const int t1 = (G.cb[i] + G.c[i] - 1) * ntl;
-          cnt[MT] += overlap(G.cb[i] * ntl, t1, lo, hi);
-          const int nl = overlap(t1, t1 + ntl, lo, hi);
+          const int t1 = G.tb[i] + (G.c[i] - 1) * ntl;
+          cnt[MT] += overlap(G.tb[i], t1, lo, hi);
+          const int nl = overlap(t1, G.tb[i] + G.nt[i], lo, hi);
 #pragma unroll
           for (int q = 1; q <= MT; ++q) cnt[q] += (q == cl) ? nl : 0;
         }
@@ -242,12 +284,31 @@ __device__ __forceinline__ bool find_task(const GemmParams& p, int& e_out, int& 
   // find the r-th class-k task of [lo, hi) in task order (without classes:
   // task lo + j); exactly one lane holds it
   const int t_plain = lo + j;
-  int f_t = -1, f_e = 0, f_cb = 0;
+  int f_t = -1, f_e = 0, f_m0 = 0, f_nt = 0, f_narrow = 0;
+  auto take = [&](const ExpGroup<MC>& G, int i, int g0, int t) {
+    const int t1 = G.tb[i] + (G.c[i] - 1) * ntl;
+    f_t = t;
+    f_e = g0 + kExpPerLane * lane + i;
+    if (t < t1) {
+      const int q = (t - G.tb[i]) / ntl;
+      f_m0 = q * MC;
+      f_nt = t - G.tb[i] - q * ntl;
+      f_narrow = 0;
+    } else {
+      f_m0 = (G.c[i] - 1) * MC;
+      f_nt = t - t1;
+      f_narrow = (G.nt[i] - (t1 - G.tb[i])) > ntl ? 1 : 0;
+    }
+  };
   int base = 0, before = 0;
-  for (int g0 = 0; g0 < p.E && base * ntl < hi; g0 += kExpGroup) {
+  for (int g0 = 0; g0 < p.E && base < hi; g0 += kExpGroup) {
     ExpGroup<MC> G;
-    if (g0 == 0) G = G0;
-    else load_group<MC>(p, g0, base, G);
+    if (g0 == 0) {
+      G = G0;
+    } else {
+      load_group<MC>(p, g0, G);
+      assign_tasks<MC>(ntl, light, base, G);
+    }
     if constexpr (BY_CLASS) {
       int v[kExpPerLane], tlo[kExpPerLane];
       int vsum = 0;
@@ -258,9 +319,9 @@ __device__ __forceinline__ bool find_task(const GemmParams& p, int& e_out, int& 
         if (G.c[i] > 0) {
           // the class-k tasks of one expert form one interval
           const int cl = last_class<MC>(G.Me[i], G.c[i]);
-          const int t1 = (G.cb[i] + G.c[i] - 1) * ntl;
-          const int a0 = (k == MT) ? G.cb[i] * ntl : t1;
-          const int a1 = (cl == k) ? t1 + ntl : t1;
+          const int t1 = G.tb[i] + (G.c[i] - 1) * ntl;
+          const int a0 = (k == MT) ? G.tb[i] : t1;
+          const int a1 = (cl == k) ? G.tb[i] + G.nt[i] : t1;
           if (a1 > a0) {
             tlo[i] = max(a0, lo);
             v[i] = overlap(a0, a1, lo, hi);
@@ -272,34 +333,24 @@ __device__ __forceinline__ bool find_task(const GemmParams& p, int& e_out, int& 
       int vb = before + wave_excl_scan(vsum, vtotal);
 #pragma unroll
       for (int i = 0; i < kExpPerLane; ++i) {
-        if (v[i] > 0 && r >= vb && r < vb + v[i]) {
-          f_t = tlo[i] + (r - vb);
-          f_e = g0 + kExpPerLane * lane + i;
-          f_cb = G.cb[i];
-        }
+        if (v[i] > 0 && r >= vb && r < vb + v[i]) take(G, i, g0, tlo[i] + (r - vb));
         vb += v[i];
       }
       before += vtotal;
     } else {
 #pragma unroll
-      for (int i = 0; i < kExpPerLane; ++i) {
-        if (G.c[i] > 0 && t_plain >= G.cb[i] * ntl && t_plain < (G.cb[i] + G.c[i]) * ntl) {
-          f_t = t_plain;
-          f_e = g0 + kExpPerLane * lane + i;
-          f_cb = G.cb[i];
-        }
-      }
+      for (int i = 0; i < kExpPerLane; ++i)
+        if (G.nt[i] > 0 && t_plain >= G.tb[i] && t_plain < G.tb[i] + G.nt[i]) take(G, i, g0, t_plain);
     }
     base += G.total;
   }
   const uint64_t found = __ballot(f_t >= 0);
   if (found == 0) return false;
   const int src = __ffsll(static_cast<unsigned long long>(found)) - 1;
-  const int t = __shfl(f_t, src);
   e_out = __shfl(f_e, src);
-  const int chunk = t / ntl;
-  m0_out = (chunk - __shfl(f_cb, src)) * MC;
-  nt_out = t - chunk * ntl;
+  m0_out = __shfl(f_m0, src);
+  nt_out = __shfl(f_nt, src);
+  narrow_out = __shfl(f_narrow, src) != 0;
   return true;
 }
 
@@ -673,28 +724,27 @@ __device__ __forceinline__ void k_main_loop(const KCtx<WN, PPT>& c, half8* __res
   }
 }
 
-template <int NW, int WN, int MT, int EPI, int PACKED, int MINB>
-__global__ __launch_bounds__(NW * 64, MINB) void k_gemm_streamk(const GemmParams p) {
+// One task of the stream-K kernel: rows [m0, m0 + MC) of expert e, column
+// tile nt of width NW * WN * 16 (SwiGLU: half of them gate, half up).
+// MAXA: the most live row tiles the task can have.
+template <int NW, int WN, int MT, int MAXA, int EPI, int PACKED>
+__device__ __forceinline__ void streamk_task(const GemmParams& p, int e, int m0, int nt, half8* __restrict__ lds0,
+                                             half8* __restrict__ lds1) {
   constexpr int THREADS = NW * 64;
   constexpr int MC = MT * 16;
   constexpr int BN = NW * WN * 16;
   constexpr int PPT = (MT * 64 + THREADS - 1) / THREADS;   // A (row, K group) pairs per thread
   static_assert(EPI != EPI_SWIGLU || (WN % 2) == 0, "SwiGLU pairs gate and up tiles");
-  static_assert(MT == 1 || MT == 2 || MT == 3 || MT == 4 || MT == 6 || MT == 8, "row tiles per chunk");
-  __shared__ half8 a_lds[2][MT * 8 * 64];   // double-buffered [row tile][sub-step][lane] fragments
-
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int lr = lane & 15;
 
-  int e, m0, nt;
-  if (!find_task<MT, true>(p, e, m0, nt)) return;
   // data-dependent bounds are clamped so that inconsistent offsets can give
   // wrong rows but never an access outside the buffers
   const int row0 = min(max(p.offsets[e], 0), p.m_total);
   const int Me = min(max(p.offsets[e + 1], 0), p.m_total) - row0;
   const int rows = min(MC, Me - m0);      // valid rows of this chunk (>= 1)
-  const int mt_active = (rows + 15) >> 4;
+  const int mt_active = min((rows + 15) >> 4, MAXA);
 
   const int N = p.N;
   const int I = N / 2;
@@ -733,20 +783,18 @@ __global__ __launch_bounds__(NW * 64, MINB) void k_gemm_streamk(const GemmParams
 #pragma unroll
     for (int j = 0; j < WN; ++j) acc[r][j] = float4v{0.f, 0.f, 0.f, 0.f};
 
-  half8* lds0 = a_lds[0];
-  half8* lds1 = a_lds[1];
   switch (mt_active) {
     case 1: k_main_loop<NW, WN, MT, 1, PPT, PACKED>(c, lds0, lds1, acc); break;
-    case 2: if constexpr (MT >= 2) k_main_loop<NW, WN, MT, 2, PPT, PACKED>(c, lds0, lds1, acc); break;
-    case 3: if constexpr (MT >= 3) k_main_loop<NW, WN, MT, 3, PPT, PACKED>(c, lds0, lds1, acc); break;
-    case 4: if constexpr (MT >= 4) k_main_loop<NW, WN, MT, 4, PPT, PACKED>(c, lds0, lds1, acc); break;
-    case 5: case 6: if constexpr (MT >= 6) k_main_loop<NW, WN, MT, 6, PPT, PACKED>(c, lds0, lds1, acc); break;
-    default: if constexpr (MT >= 8) k_main_loop<NW, WN, MT, MT, PPT, PACKED>(c, lds0, lds1, acc); break;
+    case 2: if constexpr (MAXA >= 2) k_main_loop<NW, WN, MT, 2, PPT, PACKED>(c, lds0, lds1, acc); break;
+    case 3: if constexpr (MAXA >= 3) k_main_loop<NW, WN, MT, 3, PPT, PACKED>(c, lds0, lds1, acc); break;
+    case 4: if constexpr (MAXA >= 4) k_main_loop<NW, WN, MT, 4, PPT, PACKED>(c, lds0, lds1, acc); break;
+    case 5: case 6: if constexpr (MAXA >= 6) k_main_loop<NW, WN, MT, 6, PPT, PACKED>(c, lds0, lds1, acc); break;
+    default: if constexpr (MAXA >= 8) k_main_loop<NW, WN, MT, MT, PPT, PACKED>(c, lds0, lds1, acc); break;
   }
 
   const int prow0 = row0 + m0;
 #pragma unroll
-  for (int r = 0; r < MT; ++r) {
+  for (int r = 0; r < MAXA; ++r) {
     if (r >= mt_active) continue;
     if constexpr (EPI == EPI_SWIGLU) {
       constexpr int HALF = WN / 2;
@@ -760,6 +808,29 @@ __global__ __launch_bounds__(NW * 64, MINB) void k_gemm_streamk(const GemmParams
         epilogue_tile<EPI>(p, acc[r][j], prow0 + 16 * r, rows - 16 * r, col0[j] + lr, c.bok[j], gab);
     }
   }
+}
+
+// LIGHT > 0: the last chunk of an expert with at most LIGHT live row tiles
+// runs as twice as many tasks of half the width (WN / 2 tiles per wave).  Such
+// tasks are bound by the weight decode, which costs the same for 16 rows as
+// for 64; halving each one's columns spreads the light tail of the grid over
+// twice as many workgroups.  The sums are those of the wide tasks, element for
+// element.
+template <int NW, int WN, int MT, int EPI, int PACKED, int MINB, int LIGHT>
+__global__ __launch_bounds__(NW * 64, MINB) void k_gemm_streamk(const GemmParams p) {
+  static_assert(MT == 1 || MT == 2 || MT == 3 || MT == 4 || MT == 6 || MT == 8, "row tiles per chunk");
+  static_assert(LIGHT == 0 || (WN % 2) == 0, "narrow tasks halve the tiles per wave");
+  __shared__ half8 a_lds[2][MT * 8 * 64];   // double-buffered [row tile][sub-step][lane] fragments
+  int e, m0, nt;
+  bool narrow;
+  if (!find_task<MT, true, LIGHT>(p, e, m0, nt, narrow)) return;
+  if constexpr (LIGHT > 0) {
+    if (narrow) {
+      streamk_task<NW, WN / 2, MT, LIGHT, EPI, PACKED>(p, e, m0, nt, a_lds[0], a_lds[1]);
+      return;
+    }
+  }
+  streamk_task<NW, WN, MT, MT, EPI, PACKED>(p, e, m0, nt, a_lds[0], a_lds[1]);
 }
 
 // ================================================================== stream-N
@@ -878,7 +949,8 @@ __global__ __launch_bounds__(NW * 64) void k_gemm_streamn(const GemmParams p) {
 
   const int wave = threadIdx.x >> 6;
   int e, m0, ng;
-  if (!find_task<MT, false>(p, e, m0, ng)) return;
+  bool narrow;
+  if (!find_task<MT, false, 0>(p, e, m0, ng, narrow)) return;
   const int row0 = min(max(p.offsets[e], 0), p.m_total);
   const int Me = min(max(p.offsets[e + 1], 0), p.m_total) - row0;
   const int rows = min(MC, Me - m0);
@@ -910,23 +982,36 @@ __global__ __launch_bounds__(NW * 64) void k_gemm_streamn(const GemmParams p) {
 }
 
 // ------------------------------------------------------------------ launchers
+// compute units of the current device (the runtime's cached device
+// properties; 256, MI355X's count, if the query fails)
+static int compute_units() {
+  int dev = 0, v = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0)
+    return 256;
+  return v;
+}
+
 static hipError_t grid_check(int64_t blocks) {
   return blocks >= (int64_t(1) << 31) ? hipErrorInvalidConfiguration : hipSuccess;
 }
 
-template <int NW, int WN, int MT, int EPI, int PACKED, int MINB = 2>
+template <int NW, int WN, int MT, int EPI, int PACKED, int LIGHT, int MINB = 2>
 static hipError_t launch_streamk(GemmParams prm, int64_t m_total, hipStream_t stream) {
   constexpr int BN = NW * WN * 16;
   constexpr int MC = MT * 16;
   const int cols = (EPI == EPI_SWIGLU) ? prm.N / 2 : prm.N;
   const int cols_per_tile = (EPI == EPI_SWIGLU) ? BN / 2 : BN;
   prm.n_tiles = (cols + cols_per_tile - 1) / cols_per_tile;
-  // sum over experts of ceil(Me / MC) <= m_total / MC + E; a multiple of 8 for
-  // the XCD task map
-  const int64_t blocks = ((((m_total + MC - 1) / MC + prm.E) * prm.n_tiles) + 7) / 8 * 8;
+  // sum over experts of ceil(Me / MC) <= m_total / MC + E chunks, each of at
+  // most n_tiles tasks (2 * n_tiles when light chunks split); a multiple of 8
+  // for the XCD task map
+  const int64_t per_chunk = static_cast<int64_t>(prm.n_tiles) * (LIGHT > 0 ? 2 : 1);
+  prm.slots = MINB * compute_units();
+  const int64_t blocks = ((((m_total + MC - 1) / MC + prm.E) * per_chunk) + 7) / 8 * 8;
   if (grid_check(blocks) != hipSuccess) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((k_gemm_streamk<NW, WN, MT, EPI, PACKED, MINB>), dim3(static_cast<unsigned>(blocks)), dim3(NW * 64),
-                     0, stream, prm);
+  hipLaunchKernelGGL((k_gemm_streamk<NW, WN, MT, EPI, PACKED, MINB, LIGHT>), dim3(static_cast<unsigned>(blocks)),
+                     dim3(NW * 64), 0, stream, prm);
   return hipGetLastError();
 }
 
@@ -950,21 +1035,30 @@ static hipError_t launch_streamn(GemmParams prm, int64_t m_total, hipStream_t st
 //           off once the MFMA work dominates.
 constexpr int kLargeRows = 128;
 
+#ifndef LIGHT_CLASS
+#define LIGHT_CLASS 1
+#endif
+// decode tile, packed weights: last chunks of at most this many live row tiles split
+constexpr int kLightPacked = LIGHT_CLASS;
+
 template <int PACKED, bool LARGE>
 static hipError_t launch_k(const GemmParams& prm, int epilogue, int64_t m_total, hipStream_t stream) {
+  // row-major weights (not the streaming layout) keep whole-width tasks: the
+  // second task shape would make them spill registers
+  constexpr int kLight = PACKED == kRowB ? 0 : kLightPacked;
   switch (epilogue) {
     case EPI_F32:
-      return LARGE ? launch_streamk<8, 2, 8, EPI_F32, PACKED>(prm, m_total, stream)
-                   : launch_streamk<4, 2, 4, EPI_F32, PACKED>(prm, m_total, stream);
+      return LARGE ? launch_streamk<8, 2, 8, EPI_F32, PACKED, 0>(prm, m_total, stream)
+                   : launch_streamk<4, 2, 4, EPI_F32, PACKED, kLight>(prm, m_total, stream);
     case EPI_BF16:
-      return LARGE ? launch_streamk<8, 2, 8, EPI_BF16, PACKED>(prm, m_total, stream)
-                   : launch_streamk<4, 2, 4, EPI_BF16, PACKED>(prm, m_total, stream);
+      return LARGE ? launch_streamk<8, 2, 8, EPI_BF16, PACKED, 0>(prm, m_total, stream)
+                   : launch_streamk<4, 2, 4, EPI_BF16, PACKED, kLight>(prm, m_total, stream);
     case EPI_SWIGLU:
-      return LARGE ? launch_streamk<8, 2, 8, EPI_SWIGLU, PACKED>(prm, m_total, stream)
-                   : launch_streamk<4, 4, 4, EPI_SWIGLU, PACKED>(prm, m_total, stream);
+      return LARGE ? launch_streamk<8, 2, 8, EPI_SWIGLU, PACKED, 0>(prm, m_total, stream)
+                   : launch_streamk<4, 4, 4, EPI_SWIGLU, PACKED, kLight>(prm, m_total, stream);
     case EPI_COMBINE:
-      return LARGE ? launch_streamk<8, 2, 8, EPI_COMBINE, PACKED>(prm, m_total, stream)
-                   : launch_streamk<4, 2, 4, EPI_COMBINE, PACKED>(prm, m_total, stream);
+      return LARGE ? launch_streamk<8, 2, 8, EPI_COMBINE, PACKED, 0>(prm, m_total, stream)
+                   : launch_streamk<4, 2, 4, EPI_COMBINE, PACKED, kLight>(prm, m_total, stream);
     default: return hipErrorInvalidValue;
   }
 }

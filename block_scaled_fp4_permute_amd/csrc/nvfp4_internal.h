@@ -23,6 +23,7 @@ struct GemmParams {
   const int32_t* offsets;
   int E, N, K;
   int n_tiles;            // column tiles per expert (set by the launcher)
+  int slots;              // workgroups of the kernel resident at once (set by the launcher)
   int m_total;            // rows of the outputs indexed by GEMM row
   int a_rows_total;       // rows of A (bound for gathered row indices)
   int out_rows;           // rows of the combine accumulator
