@@ -162,6 +162,49 @@ def test_gemm_decode_and_large_tile_shapes(hint, packed):
                   what=f"fused swiglu hint {hint}")
 
 
+@pytest.mark.parametrize("epilogue", ["f32", "swiglu"])
+def test_gemm_light_chunks_split_into_narrow_tasks(epilogue):
+    # more whole-width tasks than resident workgroups, most experts with at
+    # most 16 rows: with packed weights those chunks run as twice as many
+    # half-width tasks; results must meet the oracle and equal, bit for bit,
+    # the row-major path (which never splits and sums in the same order)
+    rng = np.random.default_rng(11 + (epilogue == "swiglu"))
+    E, N, K = 300, 512, 512
+    counts = rng.integers(1, 17, E)
+    counts[rng.choice(E, 40, replace=False)] = rng.integers(17, 200, 40)
+    counts[rng.choice(E, 10, replace=False)] = 0
+    M = int(counts.sum())
+    print(f"light chunks: E={E} M={M} N={N} K={K} epilogue={epilogue}", flush=True)
+    a_codes, a_scales = _rand_nvfp4(rng, (700,), K)
+    b_codes, b_scales = _rand_nvfp4(rng, (E, N), K)
+    b_g = rng.uniform(0.001, 0.01, E).astype(np.float32)
+    a_rows = rng.integers(0, 700, M).astype(np.int32)
+    offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    y_ref, absdot = OM.grouped_gemm(a_codes, a_scales, 0.02, b_codes, b_scales, b_g, offsets, a_rows=a_rows)
+    if epilogue == "f32":
+        outs = []
+        for packed in (True, False):
+            y, _ = _run_gemm(a_codes, a_scales, 0.02, b_codes, b_scales, b_g, counts, a_rows, packed=packed)
+            outs.append(down(y)[:M])
+        assert_gemm_close(outs[0], y_ref, absdot, what="narrow tasks f32")
+        assert np.array_equal(outs[0].view(np.uint32), outs[1].view(np.uint32))
+    else:
+        h64 = OM.swiglu(y_ref)
+        g_h = np.float32(np.abs(h64.astype(np.float32)).max() / np.float32(2688))
+        a = m.NVFP4Tensor(up(a_codes), up(a_scales), up(np.array([0.02], np.float32)))
+        bc, bs = up(b_codes), up(b_scales)
+        outs = []
+        for packed in (True, False):
+            hq = m.nvfp4_grouped_gemm(a, bc, bs, up(b_g), up(offsets), m_total=M, a_rows=up(a_rows),
+                                      epilogue=m.EPI_SWIGLU_NVFP4, out_g=up(np.array([g_h], np.float32)),
+                                      b_packed=m.nvfp4_weight_repack(bc, bs) if packed else None)
+            torch.cuda.synchronize()
+            outs.append((down(hq.codes), down(hq.scales)))
+        check_requant(outs[0][0], outs[0][1], h64, g_h, _swiglu_tol(y_ref, absdot), max_flip_frac=0.02,
+                      what="narrow tasks swiglu")
+        assert np.array_equal(outs[0][0], outs[1][0]) and np.array_equal(outs[0][1], outs[1][1])
+
+
 def test_gemm_bf16_epilogue_and_untouched_tail_rows():
     rng = np.random.default_rng(7)
     E, counts, N, K = 3, [9, 40, 2], 128, 256
