@@ -494,6 +494,101 @@ __device__ __forceinline__ void a_store_piece(const ARegs<PPT>& R, const AScales
   }
 }
 
+// Activation staging policies of the stream-K loop.  APairs: every thread
+// stages PPT (row, K group) pairs, one row tile per wave - used whenever two
+// or more row tiles are live.  AOneTile: only row tile 0 is live (at most 16
+// rows); its 16 rows x 4 K groups x 4 word pairs are spread over 256 threads,
+// 2 code words (16 values) each, so no wave decodes rows that do not exist.
+// Both write the same LDS fragments for the live row tiles.
+template <int THREADS, int MT, int PPT>
+struct APairs {
+  using State = AState<PPT>;
+  using Regs = ARegs<PPT>;
+  using Scales = AScales<PPT>;
+  __device__ static void setup(const GemmParams& p, int row0, int m0, int rows, State& A) {
+    a_setup<THREADS, MT, PPT>(p, row0, m0, rows, A);
+  }
+  __device__ static void load(const State& A, Regs& R, int k0, int K) { a_load(A, R, k0, K); }
+  template <int MTA>
+  __device__ static void store(const State& A, const Regs& R, int k0, int K, half8* __restrict__ lds) {
+    a_store<THREADS, MT, MTA, PPT>(A, R, k0, K, lds);
+  }
+  __device__ static void scales(const State& A, const Regs& R, int k0, int K, Scales& S) { a_scales(A, R, k0, K, S); }
+  // the part of the decode that rides behind MFMA sub-step s (0..7)
+  template <int MTA>
+  __device__ static void piece(const State&, const Regs& R, const Scales& S, half8* __restrict__ lds, int s) {
+#pragma unroll
+    for (int q = 0; q < PPT; ++q) a_store_piece<THREADS, MT, MTA, PPT>(R, S, lds, 8 * q + s);
+  }
+};
+
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+template <int THREADS, int MT>
+struct AOneTile {
+  static_assert(THREADS >= 256, "one live row tile needs 256 threads");
+  struct State {
+    rsrc_t rc, rs;
+    uint32_t vc, vs;     // byte offsets of the thread's 8 code bytes / 1 scale byte in step 0
+    int kq;              // K offset of its 32-value half within a step
+    int slot;            // LDS slot of its first word
+    bool ok;
+  };
+  struct Regs {
+    u32x2 c;
+    uint32_t s;
+  };
+  struct Scales {
+    _Float16 s;
+  };
+  __device__ static bool active() { return THREADS == 256 || threadIdx.x < 256; }
+  __device__ static void setup(const GemmParams& p, int row0, int m0, int rows, State& A) {
+    const uint32_t krow = static_cast<uint32_t>(p.K) / 2;
+    const uint32_t srow = static_cast<uint32_t>(p.K) / 16;
+    A.rc = make_rsrc(p.a_codes, static_cast<uint32_t>(p.a_rows_total) * krow);
+    A.rs = make_rsrc(p.a_scales, static_cast<uint32_t>(p.a_rows_total) * srow);
+    const int t = threadIdx.x & 255;
+    const int pair = t & 63;            // row (pair & 15), K group (pair >> 4)
+    const int ar = pair & 15;
+    const int ag = pair >> 4;
+    const int h = (t >> 7) & 1;         // 32-value half of the K group
+    const int ws = (t >> 6) & 1;        // words 2 ws, 2 ws + 1 of the half
+    A.ok = active() && ar < rows;
+    int arow = row0 + m0 + (A.ok ? ar : 0);
+    if (p.a_rows) arow = p.a_rows[arow];
+    arow = (arow >= 0 && arow < p.a_rows_total) ? arow : 0;
+    A.vc = static_cast<uint32_t>(arow) * krow + 32u * ag + 16u * h + 8u * ws;
+    A.vs = static_cast<uint32_t>(arow) * srow + 4u * ag + 2u * h + ws;
+    A.kq = 64 * ag + 32 * h;
+    A.slot = (4 * h + 2 * ws) * 64 + pair;
+  }
+  __device__ static void load(const State& A, Regs& R, int k0, int K) {
+    // steps past K re-read the last step (cached) instead of fetching new bytes
+    const uint32_t kq = static_cast<uint32_t>(min(k0, ((K - 1) / KSTEP) * KSTEP));
+    R.c = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(A.rc, A.vc + kq / 2, 0, 0));
+    R.s = __builtin_amdgcn_raw_buffer_load_b8(A.rs, A.vs + kq / 16, 0, 0);
+  }
+  __device__ static void scales(const State& A, const Regs& R, int k0, int K, Scales& S) {
+    // a zero block scale zeroes a row that does not exist and a half past K
+    const bool ok = A.ok && (k0 + A.kq) < K;
+    S.s = e4m3_to_f16_div256(ok ? R.s : 0u);
+  }
+  template <int MTA>
+  __device__ static void store(const State& A, const Regs& R, int k0, int K, half8* __restrict__ lds) {
+    Scales S;
+    scales(A, R, k0, K, S);
+    if (active()) {
+      lds[A.slot] = decode8_f16(R.c.x, S.s);
+      lds[A.slot + 64] = decode8_f16(R.c.y, S.s);
+    }
+  }
+  // the two words ride behind MFMA sub-steps 0 and 4
+  template <int MTA>
+  __device__ static void piece(const State& A, const Regs& R, const Scales& S, half8* __restrict__ lds, int s) {
+    if ((s == 0 || s == 4) && active()) lds[A.slot + (s >> 2) * 64] = decode8_f16(s == 0 ? R.c.x : R.c.y, S.s);
+  }
+};
+
 // ------------------------------------------------------------------ B operand
 // One 16-column B tile of one K step, as held by a lane: 8 code dwords (dword
 // d covers the lane's K values [8d, 8d+8)) and the 4 scale bytes of its 64 K.
@@ -628,9 +723,9 @@ __device__ __forceinline__ void epilogue_swiglu(const GemmParams& p, const float
 }
 
 // ================================================================== stream-K
-template <int WN, int PPT>
+template <int WN, class AP>
 struct KCtx {
-  AState<PPT> A;
+  typename AP::State A;
   const uint8_t* b_code[WN];     // row-major: B row start; packed: first tile of the column tile
   const uint8_t* b_scale[WN];
   bool bok[WN];
@@ -638,8 +733,8 @@ struct KCtx {
   int nsteps;
 };
 
-template <int WN, int PPT, int PACKED>
-__device__ __forceinline__ void k_load_b(const KCtx<WN, PPT>& c, BRegs (&B)[WN], int st) {
+template <int WN, class AP, int PACKED>
+__device__ __forceinline__ void k_load_b(const KCtx<WN, AP>& c, BRegs (&B)[WN], int st) {
   const int lg = (threadIdx.x & 63) >> 4;
 #pragma unroll
   for (int j = 0; j < WN; ++j) {
@@ -654,8 +749,8 @@ __device__ __forceinline__ void k_load_b(const KCtx<WN, PPT>& c, BRegs (&B)[WN],
 // from registers), with the decode of step st+1's activation rows into
 // lds_nxt interleaved - both in one basic block, so the VALU work of the
 // decodes overlaps the matrix-core work - then the step's barrier.
-template <int NW, int WN, int MT, int MTA, int PPT, int PACKED>
-__device__ __forceinline__ void k_step(const KCtx<WN, PPT>& c, const ARegs<PPT>& a_nxt, const BRegs (&B)[WN],
+template <int NW, int WN, int MT, int MTA, class AP, int PACKED>
+__device__ __forceinline__ void k_step(const KCtx<WN, AP>& c, const typename AP::Regs& a_nxt, const BRegs (&B)[WN],
                                        int st, const half8* __restrict__ lds_cur, half8* __restrict__ lds_nxt,
                                        float4v (&acc)[MT][WN]) {
   const int lane = threadIdx.x & 63;
@@ -672,8 +767,8 @@ __device__ __forceinline__ void k_step(const KCtx<WN, PPT>& c, const ARegs<PPT>&
       bs[j] = (lo ? (B[j].s & 0xFFFFu) : 0u) | (hi ? (B[j].s & 0xFFFF0000u) : 0u);
     }
   }
-  AScales<PPT> as;
-  a_scales(c.A, a_nxt, k0 + KSTEP, c.K, as);
+  typename AP::Scales as;
+  AP::scales(c.A, a_nxt, k0 + KSTEP, c.K, as);
 #pragma unroll
   for (int s = 0; s < 8; ++s) {
     half8 af[MTA];
@@ -687,9 +782,8 @@ __device__ __forceinline__ void k_step(const KCtx<WN, PPT>& c, const ARegs<PPT>&
 #pragma unroll
       for (int j = 0; j < WN; ++j)
         acc[r][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[r], bf[j], acc[r][j], 0, 0, 0);
-    // an eighth of the next step's activation decode rides behind these MFMAs
-#pragma unroll
-    for (int q = 0; q < PPT; ++q) a_store_piece<NW * 64, MT, MTA, PPT>(a_nxt, as, lds_nxt, 8 * q + s);
+    // a share of the next step's activation decode rides behind these MFMAs
+    AP::template piece<MTA>(c.A, a_nxt, as, lds_nxt, s);
   }
   __syncthreads();
 }
@@ -702,26 +796,45 @@ __device__ __forceinline__ void k_step(const KCtx<WN, PPT>& c, const ARegs<PPT>&
 // no branches: a step past K (an odd step count, and the prefetches after the
 // last step) reads valid clamped addresses and its data is masked to zero,
 // which keeps the wait counts exact.
-template <int NW, int WN, int MT, int MTA, int PPT, int PACKED>
-__device__ __forceinline__ void k_main_loop(const KCtx<WN, PPT>& c, half8* __restrict__ lds0,
+template <int NW, int WN, int MT, int MTA, class AP, int PACKED>
+__device__ __forceinline__ void k_main_loop(const KCtx<WN, AP>& c, half8* __restrict__ lds0,
                                             half8* __restrict__ lds1, float4v (&acc)[MT][WN]) {
   BRegs b0[WN], b1[WN];
-  ARegs<PPT> a0, a1;
-  a_load(c.A, a0, 0, c.K);
-  k_load_b<WN, PPT, PACKED>(c, b0, 0);
-  a_load(c.A, a1, KSTEP, c.K);
-  k_load_b<WN, PPT, PACKED>(c, b1, 1);
-  a_store<NW * 64, MT, MTA, PPT>(c.A, a0, 0, c.K, lds0);
+  typename AP::Regs a0, a1;
+  AP::load(c.A, a0, 0, c.K);
+  k_load_b<WN, AP, PACKED>(c, b0, 0);
+  AP::load(c.A, a1, KSTEP, c.K);
+  k_load_b<WN, AP, PACKED>(c, b1, 1);
+  AP::template store<MTA>(c.A, a0, 0, c.K, lds0);
   __syncthreads();
-  a_load(c.A, a0, 2 * KSTEP, c.K);
+  AP::load(c.A, a0, 2 * KSTEP, c.K);
   for (int st = 0; st < c.nsteps; st += 2) {
-    k_step<NW, WN, MT, MTA, PPT, PACKED>(c, a1, b0, st, lds0, lds1, acc);
-    k_load_b<WN, PPT, PACKED>(c, b0, st + 2);
-    a_load(c.A, a1, (st + 3) * KSTEP, c.K);
-    k_step<NW, WN, MT, MTA, PPT, PACKED>(c, a0, b1, st + 1, lds1, lds0, acc);
-    k_load_b<WN, PPT, PACKED>(c, b1, st + 3);
-    a_load(c.A, a0, (st + 4) * KSTEP, c.K);
+    k_step<NW, WN, MT, MTA, AP, PACKED>(c, a1, b0, st, lds0, lds1, acc);
+    k_load_b<WN, AP, PACKED>(c, b0, st + 2);
+    AP::load(c.A, a1, (st + 3) * KSTEP, c.K);
+    k_step<NW, WN, MT, MTA, AP, PACKED>(c, a0, b1, st + 1, lds1, lds0, acc);
+    k_load_b<WN, AP, PACKED>(c, b1, st + 3);
+    AP::load(c.A, a0, (st + 4) * KSTEP, c.K);
   }
+}
+
+// The K loop of one task with activation staging policy AP: the weights part
+// of the context is copied from cb, the activation part set up here.
+template <int NW, int WN, int MT, int MTA, class AP, int PACKED, class CB>
+__device__ __forceinline__ void run_loop(const GemmParams& p, const CB& cb, int row0, int m0, int rows,
+                                         half8* __restrict__ lds0, half8* __restrict__ lds1,
+                                         float4v (&acc)[MT][WN]) {
+  KCtx<WN, AP> c;
+  c.K = cb.K;
+  c.nsteps = cb.nsteps;
+#pragma unroll
+  for (int j = 0; j < WN; ++j) {
+    c.b_code[j] = cb.b_code[j];
+    c.b_scale[j] = cb.b_scale[j];
+    c.bok[j] = cb.bok[j];
+  }
+  AP::setup(p, row0, m0, rows, c.A);
+  k_main_loop<NW, WN, MT, MTA, AP, PACKED>(c, lds0, lds1, acc);
 }
 
 // One task of the stream-K kernel: rows [m0, m0 + MC) of expert e, column
@@ -748,7 +861,7 @@ __device__ __forceinline__ void streamk_task(const GemmParams& p, int e, int m0,
 
   const int N = p.N;
   const int I = N / 2;
-  KCtx<WN, PPT> c;
+  KCtx<WN, APairs<THREADS, MT, PPT>> c;      // weights part; the activation part is set up per class below
   c.K = p.K;
   c.nsteps = (p.K + KSTEP - 1) / KSTEP;
   int col0[WN];     // first column of each 16-column tile of this wave
@@ -774,7 +887,6 @@ __device__ __forceinline__ void streamk_task(const GemmParams& p, int e, int m0,
       c.b_scale[j] = p.b_scales + brow * (static_cast<size_t>(p.K) / 16);
     }
   }
-  a_setup<THREADS, MT, PPT>(p, row0, m0, rows, c.A);
   const float gab = p.a_g[0] * p.b_g[e];
 
   float4v acc[MT][WN];
@@ -784,12 +896,18 @@ __device__ __forceinline__ void streamk_task(const GemmParams& p, int e, int m0,
     for (int j = 0; j < WN; ++j) acc[r][j] = float4v{0.f, 0.f, 0.f, 0.f};
 
   switch (mt_active) {
-    case 1: k_main_loop<NW, WN, MT, 1, PPT, PACKED>(c, lds0, lds1, acc); break;
-    case 2: if constexpr (MAXA >= 2) k_main_loop<NW, WN, MT, 2, PPT, PACKED>(c, lds0, lds1, acc); break;
-    case 3: if constexpr (MAXA >= 3) k_main_loop<NW, WN, MT, 3, PPT, PACKED>(c, lds0, lds1, acc); break;
-    case 4: if constexpr (MAXA >= 4) k_main_loop<NW, WN, MT, 4, PPT, PACKED>(c, lds0, lds1, acc); break;
-    case 5: case 6: if constexpr (MAXA >= 6) k_main_loop<NW, WN, MT, 6, PPT, PACKED>(c, lds0, lds1, acc); break;
-    default: if constexpr (MAXA >= 8) k_main_loop<NW, WN, MT, MT, PPT, PACKED>(c, lds0, lds1, acc); break;
+    case 1:
+      if constexpr (THREADS >= 256) {
+        run_loop<NW, WN, MT, 1, AOneTile<THREADS, MT>, PACKED>(p, c, row0, m0, rows, lds0, lds1, acc);
+      } else {
+        run_loop<NW, WN, MT, 1, APairs<THREADS, MT, PPT>, PACKED>(p, c, row0, m0, rows, lds0, lds1, acc);
+      }
+      break;
+    case 2: if constexpr (MAXA >= 2) run_loop<NW, WN, MT, 2, APairs<THREADS, MT, PPT>, PACKED>(p, c, row0, m0, rows, lds0, lds1, acc); break;
+    case 3: if constexpr (MAXA >= 3) run_loop<NW, WN, MT, 3, APairs<THREADS, MT, PPT>, PACKED>(p, c, row0, m0, rows, lds0, lds1, acc); break;
+    case 4: if constexpr (MAXA >= 4) run_loop<NW, WN, MT, 4, APairs<THREADS, MT, PPT>, PACKED>(p, c, row0, m0, rows, lds0, lds1, acc); break;
+    case 5: case 6: if constexpr (MAXA >= 6) run_loop<NW, WN, MT, 6, APairs<THREADS, MT, PPT>, PACKED>(p, c, row0, m0, rows, lds0, lds1, acc); break;
+    default: if constexpr (MAXA >= 8) run_loop<NW, WN, MT, MT, APairs<THREADS, MT, PPT>, PACKED>(p, c, row0, m0, rows, lds0, lds1, acc); break;
   }
 
   const int prow0 = row0 + m0;
