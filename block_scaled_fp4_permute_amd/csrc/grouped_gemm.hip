@@ -723,9 +723,9 @@ __device__ __forceinline__ void epilogue_swiglu(const GemmParams& p, const float
 }
 
 // ================================================================== stream-K
-template <int WN, class AP>
-struct KCtx {
-  typename AP::State A;
+// weights part of a task's context
+template <int WN>
+struct BCtx {
   const uint8_t* b_code[WN];     // row-major: B row start; packed: first tile of the column tile
   const uint8_t* b_scale[WN];
   bool bok[WN];
@@ -733,8 +733,14 @@ struct KCtx {
   int nsteps;
 };
 
-template <int WN, class AP, int PACKED>
-__device__ __forceinline__ void k_load_b(const KCtx<WN, AP>& c, BRegs (&B)[WN], int st) {
+// the whole context: weights, and the activation rows as staged by policy AP
+template <int WN, class AP>
+struct KCtx : BCtx<WN> {
+  typename AP::State A;
+};
+
+template <int WN, int PACKED>
+__device__ __forceinline__ void k_load_b(const BCtx<WN>& c, BRegs (&B)[WN], int st) {
   const int lg = (threadIdx.x & 63) >> 4;
 #pragma unroll
   for (int j = 0; j < WN; ++j) {
@@ -802,37 +808,30 @@ __device__ __forceinline__ void k_main_loop(const KCtx<WN, AP>& c, half8* __rest
   BRegs b0[WN], b1[WN];
   typename AP::Regs a0, a1;
   AP::load(c.A, a0, 0, c.K);
-  k_load_b<WN, AP, PACKED>(c, b0, 0);
+  k_load_b<WN, PACKED>(c, b0, 0);
   AP::load(c.A, a1, KSTEP, c.K);
-  k_load_b<WN, AP, PACKED>(c, b1, 1);
+  k_load_b<WN, PACKED>(c, b1, 1);
   AP::template store<MTA>(c.A, a0, 0, c.K, lds0);
   __syncthreads();
   AP::load(c.A, a0, 2 * KSTEP, c.K);
   for (int st = 0; st < c.nsteps; st += 2) {
     k_step<NW, WN, MT, MTA, AP, PACKED>(c, a1, b0, st, lds0, lds1, acc);
-    k_load_b<WN, AP, PACKED>(c, b0, st + 2);
+    k_load_b<WN, PACKED>(c, b0, st + 2);
     AP::load(c.A, a1, (st + 3) * KSTEP, c.K);
     k_step<NW, WN, MT, MTA, AP, PACKED>(c, a0, b1, st + 1, lds1, lds0, acc);
-    k_load_b<WN, AP, PACKED>(c, b1, st + 3);
+    k_load_b<WN, PACKED>(c, b1, st + 3);
     AP::load(c.A, a0, (st + 4) * KSTEP, c.K);
   }
 }
 
 // The K loop of one task with activation staging policy AP: the weights part
-// of the context is copied from cb, the activation part set up here.
-template <int NW, int WN, int MT, int MTA, class AP, int PACKED, class CB>
-__device__ __forceinline__ void run_loop(const GemmParams& p, const CB& cb, int row0, int m0, int rows,
+// of the context comes from cb, the activation part is set up here.
+template <int NW, int WN, int MT, int MTA, class AP, int PACKED>
+__device__ __forceinline__ void run_loop(const GemmParams& p, const BCtx<WN>& cb, int row0, int m0, int rows,
                                          half8* __restrict__ lds0, half8* __restrict__ lds1,
                                          float4v (&acc)[MT][WN]) {
   KCtx<WN, AP> c;
-  c.K = cb.K;
-  c.nsteps = cb.nsteps;
-#pragma unroll
-  for (int j = 0; j < WN; ++j) {
-    c.b_code[j] = cb.b_code[j];
-    c.b_scale[j] = cb.b_scale[j];
-    c.bok[j] = cb.bok[j];
-  }
+  static_cast<BCtx<WN>&>(c) = cb;
   AP::setup(p, row0, m0, rows, c.A);
   k_main_loop<NW, WN, MT, MTA, AP, PACKED>(c, lds0, lds1, acc);
 }
@@ -861,7 +860,7 @@ __device__ __forceinline__ void streamk_task(const GemmParams& p, int e, int m0,
 
   const int N = p.N;
   const int I = N / 2;
-  KCtx<WN, APairs<THREADS, MT, PPT>> c;      // weights part; the activation part is set up per class below
+  BCtx<WN> c;      // weights part; the activation staging is set up per class below
   c.K = p.K;
   c.nsteps = (p.K + KSTEP - 1) / KSTEP;
   int col0[WN];     // first column of each 16-column tile of this wave
