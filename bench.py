@@ -1,8 +1,9 @@
 #!/usr/bin/env python3
 """Benchmark of the NVFP4 MoE layer on one MI355X.
 
-One step = one forward of the whole hot path on one batch: route + permute,
-NVFP4 quantisation of the activations, gate_up grouped GEMM with the fused
+One step = one forward of the whole hot path on one batch: route + permute and
+NVFP4 quantisation of the activations (one call whose kernels share launches),
+gate_up grouped GEMM with the fused
 SwiGLU + re-quantisation, down grouped GEMM (bf16 rows), weighted gather
 combine to bf16 token order.  Default workload: the decode MoE at
 16-64 tokens per expert (T=2048, H=6144, I=256, E=256, top-8, Zipf-skewed
@@ -202,7 +203,8 @@ def main():
     # ---- timed region: exactly K steps.  Two events per step bracket the
     # gate_up launch on the launch stream (its live average duration); the
     # step time is the first event to the last.
-    names = ["route_permute", "quantize_x", "gate_up_swiglu",
+    # routing and the quantisation of x share launches (one call): one stage
+    names = ["route_permute+quantize_x", None, "gate_up_swiglu",
              "down" if args.combine == "gather" else "down_scatter_add",
              "combine" if args.combine == "gather" else "to_bf16"]
 
@@ -227,7 +229,7 @@ def main():
     for i in range(args.steps):
         layer.forward(logits, x, copies[i % 2], g_h, marks=marks[i])
     torch.cuda.synchronize()
-    stage_ms = {n: float(np.mean([m[j].elapsed_time(m[j + 1]) for m in marks])) for j, n in enumerate(names)}
+    stage_ms = {n: float(np.mean([m[j].elapsed_time(m[j + 1]) for m in marks])) for j, n in enumerate(names) if n}
 
     touched = int((counts > 0).sum())
     gu_bytes_e = 2 * I * H * 9 // 16

@@ -8,7 +8,8 @@ eager-PyTorch fallback, and importing a function whose library is missing
 raises.
 
 C entry points (include/nvfp4moe.h): moe_route_permute, nvfp4_quantize,
-nvfp4_grouped_gemm, moe_swiglu, moe_unpermute_combine.
+nvfp4_grouped_gemm, moe_swiglu, moe_unpermute_combine, and moe_route_quantize
+(routing and activation quantisation in shared launches).
 """
 from __future__ import annotations
 
@@ -67,6 +68,10 @@ _SIGNATURES = {
     "moe_unpermute_combine": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p,
                                              ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p,
                                              ctypes.c_int32, ctypes.c_void_p]),
+    "moe_route_quantize_workspace_size": (ctypes.c_size_t, [ctypes.c_int32] * 3),
+    "moe_route_quantize": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32]
+                           + [ctypes.c_void_p] * 7 + [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64]
+                           + [ctypes.c_void_p] * 4 + [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
     "nvfp4moe_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "nvfp4moe_last_error_detail": (ctypes.c_char_p, []),
     "nvfp4moe_version": (ctypes.c_int, []),
@@ -203,6 +208,39 @@ def nvfp4_weight_repack(codes, scales, out=None, stream=None):
     _check(lib().nvfp4_weight_repack(codes.data_ptr(), scales.data_ptr(), E, N, 2 * K2, out.data_ptr(),
                                      out.numel(), _stream(stream)))
     return out
+
+
+# ------------------------------------------------------------------ route + quantise
+def moe_route_quantize(logits, k: int, x, g=None, out: Routing | None = None, xq: NVFP4Tensor | None = None,
+                       workspace=None, stream=None) -> tuple[Routing, NVFP4Tensor]:
+    """moe_route_permute(logits, k) and nvfp4_quantize(x, g) in one call whose
+    kernels share launches; the outputs are those of the two calls."""
+    import torch
+    _need(logits, torch.float32, "logits")
+    _need(x, x.dtype, "x")
+    T, E = logits.shape
+    if x.dim() != 2 or x.shape[0] != T:
+        raise ValueError("x must be [T, cols] with the logits' T rows")
+    cols = x.shape[1]
+    dev = logits.device
+    if out is None:
+        i32 = dict(dtype=torch.int32, device=dev)
+        out = Routing(torch.empty((T, k), **i32), torch.empty((T, k), dtype=torch.float32, device=dev),
+                      torch.empty(E, **i32), torch.empty(E + 1, **i32), torch.empty(T * k, **i32),
+                      torch.empty(T * k, **i32), torch.empty(T * k, dtype=torch.float32, device=dev))
+    if xq is None:
+        xq = NVFP4Tensor(torch.empty((T, cols // 2), dtype=torch.uint8, device=dev),
+                         torch.empty((T, cols // 16), dtype=torch.uint8, device=dev),
+                         torch.empty(1, dtype=torch.float32, device=dev))
+    nbytes = lib().moe_route_quantize_workspace_size(T, E, k)
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=dev)
+    _check(lib().moe_route_quantize(
+        logits.data_ptr(), T, E, k, out.topk_ids.data_ptr(), out.topk_w.data_ptr(), out.counts.data_ptr(),
+        out.offsets.data_ptr(), out.perm_src_token.data_ptr(), out.perm_of_assignment.data_ptr(),
+        _ptr(out.perm_weight), x.data_ptr(), _dtype_code(x), cols, _ptr(g), _ptr(xq.g), xq.codes.data_ptr(),
+        xq.scales.data_ptr(), workspace.data_ptr(), workspace.numel(), _stream(stream)))
+    return out, xq
 
 
 # ---------------------------------------------------------------------------- gemm

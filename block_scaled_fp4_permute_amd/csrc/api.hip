@@ -97,6 +97,48 @@ int nvfp4_quantize(const void* x, int32_t x_dtype, int64_t rows, int64_t cols, c
                     "nvfp4_quantize");
 }
 
+// ------------------------------------------------------------------ route + quantise
+size_t moe_route_quantize_workspace_size(int32_t T, int32_t E, int32_t k) {
+  if (T <= 0 || E <= 0 || k <= 0) return 0;
+  return nvfp4::route_quantize_ws_bytes(T, E, k);
+}
+
+int moe_route_quantize(const float* logits, int32_t T, int32_t E, int32_t k, int32_t* topk_ids, float* topk_w,
+                       int32_t* counts, int32_t* offsets, int32_t* perm_src_token, int32_t* perm_of_assignment,
+                       float* perm_weight, const void* x, int32_t x_dtype, int64_t cols, const float* g_in,
+                       float* g_out, uint8_t* codes, uint8_t* scales, void* workspace, size_t workspace_bytes,
+                       void* stream) {
+  if (!logits || !topk_ids || !topk_w || !counts || !offsets || !perm_src_token || !perm_of_assignment)
+    return fail(NVFP4MOE_ERR_INVALID, "moe_route_quantize: null routing pointer argument");
+  if (!x || !codes || !scales) return fail(NVFP4MOE_ERR_INVALID, "moe_route_quantize: null x, codes or scales");
+  if (T <= 0 || E <= 0 || k <= 0) return fail(NVFP4MOE_ERR_INVALID, "moe_route_quantize: T, E, k must be > 0");
+  if (k > E) return fail(NVFP4MOE_ERR_INVALID, "moe_route_quantize: k=%d > E=%d", k, E);
+  if (k > 32) return fail(NVFP4MOE_ERR_UNSUPPORTED, "moe_route_quantize: k=%d > 32", k);
+  if (E > 4096) return fail(NVFP4MOE_ERR_UNSUPPORTED, "moe_route_quantize: E=%d > 4096", E);
+  if (static_cast<int64_t>(T) * k >= (int64_t(1) << 30))
+    return fail(NVFP4MOE_ERR_UNSUPPORTED, "moe_route_quantize: T*k >= 2^30");
+  if (x_dtype != NVFP4MOE_F32 && x_dtype != NVFP4MOE_BF16)
+    return fail(NVFP4MOE_ERR_INVALID, "moe_route_quantize: x_dtype %d", x_dtype);
+  if (cols <= 0 || cols % 32 != 0)
+    return fail(NVFP4MOE_ERR_INVALID, "moe_route_quantize: cols=%lld must be a positive multiple of 32", (long long)cols);
+  if (static_cast<int64_t>(T) * (cols / 16) >= (int64_t(1) << 40))
+    return fail(NVFP4MOE_ERR_UNSUPPORTED, "moe_route_quantize: tensor too large");
+  // the encoder's workgroups are indexed after the ranks' in one grid
+  if ((static_cast<int64_t>(T) * (cols / 16) + 255) / 256 + (static_cast<int64_t>(T) * k + 1023) / 1024 >=
+      (int64_t(1) << 31))
+    return fail(NVFP4MOE_ERR_UNSUPPORTED, "moe_route_quantize: grid too large");
+  if (!aligned(x, 16) || !aligned(codes, 8))
+    return fail(NVFP4MOE_ERR_INVALID, "moe_route_quantize: misaligned x or codes");
+  const size_t need = nvfp4::route_quantize_ws_bytes(T, E, k);
+  if (!workspace || workspace_bytes < need)
+    return fail(NVFP4MOE_ERR_WORKSPACE, "moe_route_quantize: workspace %zu < %zu bytes", workspace_bytes, need);
+  if (!aligned(workspace, 16)) return fail(NVFP4MOE_ERR_INVALID, "moe_route_quantize: workspace not 16-byte aligned");
+  return hip_status(nvfp4::launch_route_quantize(logits, T, E, k, topk_ids, topk_w, counts, offsets, perm_src_token,
+                                                 perm_of_assignment, perm_weight, x, x_dtype, cols, g_in, g_out,
+                                                 codes, scales, workspace, static_cast<hipStream_t>(stream)),
+                    "moe_route_quantize");
+}
+
 // ------------------------------------------------------------------ grouped GEMM
 int nvfp4_grouped_gemm(const nvfp4moe_gemm_args* a, void* stream) {
   if (!a) return fail(NVFP4MOE_ERR_INVALID, "nvfp4_grouped_gemm: args is NULL");

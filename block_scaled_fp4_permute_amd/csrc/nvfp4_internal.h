@@ -39,6 +39,11 @@ size_t route_permute_ws_bytes(int T, int E, int k);
 hipError_t launch_route_permute(const float* logits, int T, int E, int k, int* topk_ids, float* topk_w,
                                 int* counts, int* offsets, int* perm_src_token, int* perm_of_assignment,
                                 float* perm_weight, void* ws, hipStream_t stream);
+size_t route_quantize_ws_bytes(int T, int E, int k);
+hipError_t launch_route_quantize(const float* logits, int T, int E, int k, int* topk_ids, float* topk_w,
+                                 int* counts, int* offsets, int* perm_src_token, int* perm_of_assignment,
+                                 float* perm_weight, const void* x, int dtype, int64_t cols, const float* g_in,
+                                 float* g_out, uint8_t* codes, uint8_t* scales, void* ws, hipStream_t stream);
 hipError_t launch_quantize(const void* x, int dtype, int64_t rows, int64_t cols, const float* g_in, float* g_out,
                            uint8_t* codes, uint8_t* scales, void* ws, hipStream_t stream);
 hipError_t launch_swiglu(const void* y, int dtype, int64_t M, int I, const float* g_in, float* g_out,

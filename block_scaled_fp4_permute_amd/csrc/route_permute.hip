@@ -21,7 +21,7 @@
 // (A single-workgroup scan + scatter was slower than the two kernels even at
 // 2048 assignments: one workgroup scatters with too little parallelism.)
 // Atomics are used for nothing, so every output is deterministic.
-#include "nvfp4_internal.h"
+#include "quantize_impl.h"
 
 namespace nvfp4 {
 
@@ -69,10 +69,10 @@ __device__ __forceinline__ void wave_argmax(float& bv, int& bid) {
 // One wave per token.  For E <= 64 * CACHE the token's logits stay in
 // registers for all k rounds; larger E re-reads them (L1-resident) per round.
 template <int CACHE>
-__global__ __launch_bounds__(256) void k_route(const float* __restrict__ logits, int T, int E, int k,
-                                               int* __restrict__ topk_ids, float* __restrict__ topk_w) {
+__device__ __forceinline__ void route_body(const float* __restrict__ logits, int T, int E, int k,
+                                           int* __restrict__ topk_ids, float* __restrict__ topk_w, int blk) {
   const int lane = threadIdx.x & 63;
-  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int t = blk * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
   const float* row = logits + static_cast<size_t>(t) * E;
   float cache[CACHE > 0 ? CACHE : 1];
@@ -136,20 +136,26 @@ __global__ __launch_bounds__(256) void k_route(const float* __restrict__ logits,
   }
 }
 
+template <int CACHE>
+__global__ __launch_bounds__(256) void k_route(const float* __restrict__ logits, int T, int E, int k,
+                                               int* __restrict__ topk_ids, float* __restrict__ topk_w) {
+  route_body<CACHE>(logits, T, E, k, topk_ids, topk_w, blockIdx.x);
+}
+
 // ------------------------------------------------------------------ stable ranks
 __device__ __forceinline__ uint64_t ballot64(bool p) { return __ballot(p); }
 
-__global__ __launch_bounds__(kRankThreads) void k_chunk_rank(const int* __restrict__ ids, int n_asg, int E,
-                                                             int nbits, int* __restrict__ local_rank,
-                                                             int* __restrict__ chunk_hist) {
-  extern __shared__ int cnt_sh[];  // [4][E]
+// chunk `blk`; cnt_sh: 4 E ints of LDS
+__device__ __forceinline__ void chunk_rank_body(const int* __restrict__ ids, int n_asg, int E, int nbits,
+                                                int* __restrict__ local_rank, int* __restrict__ chunk_hist,
+                                                int* cnt_sh, int blk) {
   const int wave = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
   for (int i = threadIdx.x; i < 4 * E; i += kRankThreads) cnt_sh[i] = 0;
   __syncthreads();
 
   int* cnt = cnt_sh + wave * E;
-  const int base = blockIdx.x * kChunk + wave * (kChunk / 4);
+  const int base = blk * kChunk + wave * (kChunk / 4);
   const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
   int xs[kChunk / 4 / 64];
 #pragma unroll
@@ -186,7 +192,7 @@ __global__ __launch_bounds__(kRankThreads) void k_chunk_rank(const int* __restri
       cnt_sh[w * E + e] = s;
       s += c;
     }
-    chunk_hist[static_cast<size_t>(blockIdx.x) * E + e] = s;
+    chunk_hist[static_cast<size_t>(blk) * E + e] = s;
   }
   __syncthreads();
 #pragma unroll
@@ -194,6 +200,49 @@ __global__ __launch_bounds__(kRankThreads) void k_chunk_rank(const int* __restri
     const int f = base + s * 64 + lane;
     if (f < n_asg && xs[s] < E) local_rank[f] += cnt_sh[wave * E + xs[s]];
   }
+}
+
+__global__ __launch_bounds__(kRankThreads) void k_chunk_rank(const int* __restrict__ ids, int n_asg, int E,
+                                                             int nbits, int* __restrict__ local_rank,
+                                                             int* __restrict__ chunk_hist) {
+  extern __shared__ int cnt_sh[];  // [4][E]
+  chunk_rank_body(ids, n_asg, E, nbits, local_rank, chunk_hist, cnt_sh, blockIdx.x);
+}
+
+// ------------------------------------------------------------------ routing paired with quantisation
+// Routing and the activation quantisation read different inputs, and each of
+// their kernels is short and leaves most of the GPU idle.  Two launches run
+// them side by side, split by workgroup index (the branch is uniform per
+// workgroup, so the barriers inside each body stay valid): the router's
+// workgroups with the amax partials, then the chunk ranks with the encoder.
+// The router's and the ranks' workgroups come first: they head the longer
+// dependency chain.
+template <int CACHE, int DT>
+__global__ __launch_bounds__(256) void k_route_amax(const float* __restrict__ logits, int T, int E, int k,
+                                                    int* __restrict__ topk_ids, float* __restrict__ topk_w,
+                                                    int n_route, const void* __restrict__ x, int64_t nblocks16,
+                                                    float* __restrict__ partial, int n_amax) {
+  if (static_cast<int>(blockIdx.x) < n_route)
+    route_body<CACHE>(logits, T, E, k, topk_ids, topk_w, blockIdx.x);
+  else
+    amax_body<DT>(x, nblocks16, partial, blockIdx.x - n_route, n_amax);
+}
+
+template <int DT>
+__global__ __launch_bounds__(kRankThreads) void k_rank_quantize(const int* __restrict__ ids, int n_asg, int E,
+                                                                int nbits, int* __restrict__ local_rank,
+                                                                int* __restrict__ chunk_hist, int nchunks,
+                                                                const void* __restrict__ x, int64_t nblocks16,
+                                                                const float* __restrict__ g_in,
+                                                                const float* __restrict__ partial, int nparts,
+                                                                float* __restrict__ g_out,
+                                                                uint8_t* __restrict__ codes,
+                                                                uint8_t* __restrict__ scales) {
+  extern __shared__ int cnt_sh[];  // [4][E], used by the rank workgroups
+  if (static_cast<int>(blockIdx.x) < nchunks)
+    chunk_rank_body(ids, n_asg, E, nbits, local_rank, chunk_hist, cnt_sh, blockIdx.x);
+  else
+    quantize_body<DT>(x, nblocks16, g_in, partial, nparts, g_out, codes, scales, blockIdx.x - nchunks);
 }
 
 // ------------------------------------------------------------------ scan
@@ -325,6 +374,64 @@ hipError_t launch_route_permute(const float* logits, int T, int E, int k, int* t
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL(k_chunk_rank, dim3(nchunks), dim3(kRankThreads), 4 * E * sizeof(int), stream, topk_ids,
                      n, E, nbits, local_rank, chunk_hist);
+  err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL(k_scan, dim3(1), dim3(1024), 0, stream, chunk_hist, nchunks, E, counts, offsets);
+  err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL(k_scatter, dim3((n + 255) / 256), dim3(256), 0, stream, topk_ids, topk_w, local_rank,
+                     chunk_hist, n, E, k, perm_src_token, perm_of_assignment, perm_weight);
+  return hipGetLastError();
+}
+
+size_t route_quantize_ws_bytes(int T, int E, int k) {
+  return route_permute_ws_bytes(T, E, k) + kAmaxBlocks * sizeof(float);
+}
+
+template <int CACHE, int DT>
+static void launch_route_amax(const float* logits, int T, int E, int k, int* topk_ids, float* topk_w, int n_route,
+                              const void* x, int64_t nb16, float* partial, int n_amax, hipStream_t stream) {
+  hipLaunchKernelGGL((k_route_amax<CACHE, DT>), dim3(n_route + n_amax), dim3(256), 0, stream, logits, T, E, k,
+                     topk_ids, topk_w, n_route, x, nb16, partial, n_amax);
+}
+
+hipError_t launch_route_quantize(const float* logits, int T, int E, int k, int* topk_ids, float* topk_w,
+                                 int* counts, int* offsets, int* perm_src_token, int* perm_of_assignment,
+                                 float* perm_weight, const void* x, int dtype, int64_t cols, const float* g_in,
+                                 float* g_out, uint8_t* codes, uint8_t* scales, void* ws, hipStream_t stream) {
+  const int n = T * k;
+  const int nchunks = (n + kChunk - 1) / kChunk;
+  int* local_rank = static_cast<int*>(ws);
+  int* chunk_hist = reinterpret_cast<int*>(static_cast<char*>(ws) +
+                                           ((static_cast<size_t>(n) * sizeof(int) + 255) & ~size_t(255)));
+  float* partial = reinterpret_cast<float*>(static_cast<char*>(ws) + route_permute_ws_bytes(T, E, k));
+  int nbits = 0;
+  while ((1 << nbits) <= E) ++nbits;
+  const int64_t nb16 = static_cast<int64_t>(T) * (cols / 16);
+  const int n_route = (T + 3) / 4;
+  // with a caller-given scale there is nothing to reduce: no amax workgroups
+  const int n_amax = g_in ? 0 : amax_grid(nb16);
+  const int nparts = n_amax;
+  if (dtype == 1) {
+    if (E <= 256) launch_route_amax<4, 1>(logits, T, E, k, topk_ids, topk_w, n_route, x, nb16, partial, n_amax, stream);
+    else if (E <= 1024) launch_route_amax<16, 1>(logits, T, E, k, topk_ids, topk_w, n_route, x, nb16, partial, n_amax, stream);
+    else launch_route_amax<0, 1>(logits, T, E, k, topk_ids, topk_w, n_route, x, nb16, partial, n_amax, stream);
+  } else {
+    if (E <= 256) launch_route_amax<4, 0>(logits, T, E, k, topk_ids, topk_w, n_route, x, nb16, partial, n_amax, stream);
+    else if (E <= 1024) launch_route_amax<16, 0>(logits, T, E, k, topk_ids, topk_w, n_route, x, nb16, partial, n_amax, stream);
+    else launch_route_amax<0, 0>(logits, T, E, k, topk_ids, topk_w, n_route, x, nb16, partial, n_amax, stream);
+  }
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  const int n_quant = static_cast<int>((nb16 + 255) / 256);
+  if (dtype == 1)
+    hipLaunchKernelGGL(k_rank_quantize<1>, dim3(nchunks + n_quant), dim3(kRankThreads), 4 * E * sizeof(int), stream,
+                       topk_ids, n, E, nbits, local_rank, chunk_hist, nchunks, x, nb16, g_in, partial, nparts, g_out,
+                       codes, scales);
+  else
+    hipLaunchKernelGGL(k_rank_quantize<0>, dim3(nchunks + n_quant), dim3(kRankThreads), 4 * E * sizeof(int), stream,
+                       topk_ids, n, E, nbits, local_rank, chunk_hist, nchunks, x, nb16, g_in, partial, nparts, g_out,
+                       codes, scales);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL(k_scan, dim3(1), dim3(1024), 0, stream, chunk_hist, nchunks, E, counts, offsets);

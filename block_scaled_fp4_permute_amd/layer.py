@@ -24,8 +24,8 @@ from dataclasses import dataclass
 import torch
 
 from . import (BF16, EPI_BF16, EPI_COMBINE_F32, EPI_F32, EPI_SWIGLU_NVFP4, F32, NVFP4Tensor, Routing, lib,
-               moe_route_permute, moe_swiglu, moe_unpermute_combine, nvfp4_grouped_gemm, nvfp4_quantize,
-               nvfp4_weight_repack)
+               moe_route_permute, moe_route_quantize, moe_swiglu, moe_unpermute_combine, nvfp4_grouped_gemm,
+               nvfp4_quantize, nvfp4_weight_repack)
 
 
 @dataclass
@@ -98,7 +98,7 @@ class MoELayer:
         self.routing = Routing(torch.empty((T, k), **i32), torch.empty((T, k), **f32), torch.empty(E, **i32),
                                torch.empty(E + 1, **i32), torch.empty(M, **i32), torch.empty(M, **i32),
                                torch.empty(M, **f32))
-        self.route_ws = torch.empty(max(16, lib().moe_route_permute_workspace_size(T, E, k)), **u8)
+        self.route_ws = torch.empty(max(16, lib().moe_route_quantize_workspace_size(T, E, k)), **u8)
         self.small_ws = torch.empty(lib().nvfp4_quantize_workspace_size(), **u8)
         self.xq = NVFP4Tensor(torch.empty((T, H // 2), **u8), torch.empty((T, H // 16), **u8),
                               torch.empty(1, **f32))
@@ -114,8 +114,10 @@ class MoELayer:
     def forward(self, logits: torch.Tensor, x: torch.Tensor, w: ExpertWeights, g_h: torch.Tensor,
                 stream=None, marks=None) -> torch.Tensor:
         """One layer step.  ``marks``: optional list of 6 torch.cuda.Event (or None
-        entries) recorded before routing and after each stage (route+permute,
-        quantise x, gate_up, down, to-bf16/combine) on the launch stream."""
+        entries) recorded on the launch stream before routing and after each
+        stage: route+permute and the quantisation of x (one call whose kernels
+        share launches; marks 1 and 2 both follow it), gate_up, down,
+        to-bf16/combine."""
         T, k, M = self.T, self.k, self.T * self.k
         hq = NVFP4Tensor(self.hq.codes, self.hq.scales, g_h)
 
@@ -124,9 +126,8 @@ class MoELayer:
                 marks[i].record(stream)
 
         mark(0)
-        r = moe_route_permute(logits, k, out=self.routing, workspace=self.route_ws, stream=stream)
+        r, _ = moe_route_quantize(logits, k, x, out=self.routing, xq=self.xq, workspace=self.route_ws, stream=stream)
         mark(1)
-        nvfp4_quantize(x, out=self.xq, workspace=self.small_ws, stream=stream)
         mark(2)
         if self.swiglu == "fused":
             nvfp4_grouped_gemm(self.xq, w.gu_codes, w.gu_scales, w.gu_g, r.offsets, m_total=M,

@@ -145,6 +145,22 @@ int nvfp4_quantize(const void* x, int32_t x_dtype, int64_t rows, int64_t cols,
                    const float* g_in, float* g_out, uint8_t* codes, uint8_t* scales,
                    void* workspace, size_t workspace_bytes, void* stream);
 
+/* ---------------------------------------------------------------- route + quantise
+ * moe_route_permute and nvfp4_quantize of the layer's activations in one
+ * call, with the same arguments and the same, bit-identical outputs (x has
+ * T rows).  The two steps read different inputs; their kernels share launches,
+ * so their short launches overlap instead of running one after another.
+ * workspace: moe_route_quantize_workspace_size(T, E, k) bytes, 16-byte
+ * aligned, caller-owned (the routing scratch followed by the quantiser's amax
+ * partials).  Errors as for the two calls. */
+size_t moe_route_quantize_workspace_size(int32_t T, int32_t E, int32_t k);
+int moe_route_quantize(const float* logits, int32_t T, int32_t E, int32_t k,
+                       int32_t* topk_ids, float* topk_w, int32_t* counts, int32_t* offsets,
+                       int32_t* perm_src_token, int32_t* perm_of_assignment, float* perm_weight,
+                       const void* x, int32_t x_dtype, int64_t cols, const float* g_in, float* g_out,
+                       uint8_t* codes, uint8_t* scales,
+                       void* workspace, size_t workspace_bytes, void* stream);
+
 /* ---------------------------------------------------------------- grouped GEMM
  * For expert e and GEMM row p in [offsets[e], offsets[e+1]) with A row
  * r = a_rows ? a_rows[p] : p:

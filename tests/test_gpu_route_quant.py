@@ -162,3 +162,48 @@ def test_quantize_config_activations_and_weights():
     _quant_case(workloads.activations(c), torch.bfloat16)
     _quant_case(workloads.gate_up_weight(c, 3), torch.float32)
     _quant_case(workloads.down_weight(c, 200), torch.float32)
+
+
+# ------------------------------------------------------------------ route + quantise in one call
+def _route_quantize_case(logits, x, k, dtype, g=None):
+    T, E = logits.shape
+    print(f"route+quantise case T={T} E={E} k={k} cols={x.shape[1]} {dtype} g={g}", flush=True)
+    xt = (bf16_up(x) if dtype == torch.bfloat16 else up(x.astype(np.float32)))
+    gt = None if g is None else up(np.array([g], np.float32))
+    r, xq = m.moe_route_quantize(up(logits), k, xt, g=gt)
+    torch.cuda.synchronize()
+    # the separate calls, themselves checked against the oracle
+    r2 = _route_case(logits, k)
+    xq2 = m.nvfp4_quantize(xt, g=gt)
+    torch.cuda.synchronize()
+    for name in ("topk_ids", "topk_w", "counts", "offsets", "perm_src_token", "perm_of_assignment", "perm_weight"):
+        assert np.array_equal(down(getattr(r, name)).view(np.uint32), down(getattr(r2, name)).view(np.uint32)), name
+    assert np.array_equal(down(xq.codes), down(xq2.codes))
+    assert np.array_equal(down(xq.scales), down(xq2.scales))
+    assert down(xq.g)[0] == down(xq2.g)[0]
+    # and the oracle's quantisation of the same values (a sample of rows for
+    # the large configs, with the oracle's per-tensor scale of the whole tensor)
+    x32 = x.astype(np.float32)
+    gg = OQ.global_scale(x32) if g is None else np.float32(g)
+    rows = np.arange(T) if T <= 2048 else np.unique(np.random.default_rng(T).integers(0, T, 256))
+    c, s, gq = OQ.quantize(x32[rows], g=gg)
+    assert down(xq.g)[0] == gg == gq
+    assert np.array_equal(down(xq.scales)[rows], s)
+    assert np.array_equal(down(xq.codes)[rows], c)
+
+
+@pytest.mark.parametrize("cfg", [0, 1, 2, 3])
+def test_route_quantize_configs(cfg):
+    c = workloads.CONFIGS[cfg]
+    _route_quantize_case(workloads.logits(c), workloads.activations(c), c.k, torch.bfloat16)
+
+
+@pytest.mark.parametrize("T,E,k,cols,dt,g", [(1, 1, 1, 32, "bf16", None), (5, 7, 7, 96, "f32", None),
+                                             (129, 64, 3, 256, "bf16", 0.01), (3, 4096, 32, 64, "bf16", None),
+                                             (1000, 300, 1, 160, "f32", 0.5)])
+def test_route_quantize_shapes(T, E, k, cols, dt, g):
+    rng = np.random.default_rng(T * 3 + E + cols)
+    logits = rng.standard_normal((T, E)).astype(np.float32)
+    x = rng.standard_normal((T, cols)) * 2
+    x = workloads.to_bf16_values(x.astype(np.float32)) if dt == "bf16" else x.astype(np.float32)
+    _route_quantize_case(logits, x, k, torch.bfloat16 if dt == "bf16" else torch.float32, g)
