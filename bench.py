@@ -40,7 +40,8 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", type=int, default=2, help="workload index (0..3); 2 is the reported one")
+    ap.add_argument("--workload", type=int, default=2,
+                    help="workload index: 0..3 MoE layers (2 is the reported one), 4 the dense 8192^3 GEMM")
     ap.add_argument("--swiglu", choices=["fused", "separate"], default="fused",
                     help="SwiGLU + requant in the gate_up epilogue, or a separate call")
     ap.add_argument("--combine", choices=["gather", "atomic"], default="gather",
@@ -143,6 +144,58 @@ def cpu_baseline(cfg, logits_np, x_np, w_gu_dev, w_dn_dev, g_h, budget_s=15.0, p
                       f"stopped after {budget_s:g} s"}
 
 
+def dense_gemm(cfg, args):
+    """The single dense NVFP4 GEMM (E=1, no routing, bf16 out): A [M, K] and
+    B [N, K] drawn N(0, 1) on the GPU, quantised to NVFP4 (B repacked) untimed;
+    K steps of the GEMM alone, timed with events on the launch stream.  A
+    secondary measurement of the MFMA-bound regime; not the reported metric."""
+    import numpy as np
+    import torch
+
+    from block_scaled_fp4_permute_amd import EPI_BF16, lib, nvfp4_grouped_gemm, nvfp4_quantize, nvfp4_weight_repack
+
+    lib()
+    dev = torch.device("cuda:0")
+    M, N, K = cfg.T, cfg.H, cfg.I
+    a32, b32 = workloads_mod().torch_dense_operands(cfg, dev)
+    aq = nvfp4_quantize(a32)
+    bq = nvfp4_quantize(b32)
+    del a32, b32
+    b_codes, b_scales = bq.codes.view(1, N, K // 2), bq.scales.view(1, N, K // 16)
+    packed = nvfp4_weight_repack(b_codes, b_scales)
+    offsets = torch.tensor([0, M], dtype=torch.int32, device=dev)
+    out = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+
+    def run():
+        nvfp4_grouped_gemm(aq, b_codes, b_scales, bq.g, offsets, m_total=M, epilogue=EPI_BF16, out=out,
+                           max_rows_per_expert_hint=M, b_packed=packed)
+
+    for _ in range(args.warmup):
+        run()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    for s_, e_ in evs:
+        s_.record()
+        run()
+        e_.record()
+    torch.cuda.synchronize()
+    ms = float(np.mean([s_.elapsed_time(e_) for s_, e_ in evs]))
+    tflops = 2.0 * M * N * K / (ms * 1e-3) / 1e12
+    print(json.dumps({
+        "metric": "dense NVFP4 GEMM TFLOP/s (secondary: the MFMA-bound regime)", "value": round(tflops, 1),
+        "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+        "higher_is_better": True, "vs_baseline": None, "dtype": "nvfp4 operands, f16 mfma, f32 accumulate",
+        "data": "synthetic", "config": {"workload": f"dense_gemm_M{M}_N{N}_K{K}", "out": "bf16"},
+        "roofline": {"kernel": "nvfp4 grouped GEMM, large-M tile", "bound": "mfma", "achieved": round(tflops, 1),
+                     "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(tflops / MFMA_F16_PEAK_TFLOPS, 4),
+                     "traffic": None}}), flush=True)
+
+
+def workloads_mod():
+    import workloads
+    return workloads
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -166,7 +219,9 @@ def main():
     lib()
     dev = torch.device("cuda:0")
     cfg = workloads.CONFIGS[args.workload]
-    assert not cfg.dense, "the layer benchmark runs an MoE workload"
+    if cfg.dense:
+        dense_gemm(cfg, args)
+        return
     T, H, I, E, k = cfg.T, cfg.H, cfg.I, cfg.E, cfg.k
 
     logits_np = workloads.logits(cfg)
@@ -243,7 +298,7 @@ def main():
     # gate_up weights + the NVFP4 activations read once + the NVFP4 h written.
     gu_alg = touched * gu_bytes_e + T * H * 9 // 16 + T * k * I * 9 // 16
     achieved = gu_alg / (gu_ms * 1e-3) / 1e9
-    wl_name = f"decode_moe_T{T}_H{H}_I{I}_E{E}_top{k}_{cfg.routing}"
+    wl_name = f"{'decode' if T <= 2048 else 'prefill'}_moe_T{T}_H{H}_I{I}_E{E}_top{k}_{cfg.routing}"
     traffic = measured_traffic("gate_up_swiglu", wl_name) if args.swiglu == "fused" else None
 
     res = {
