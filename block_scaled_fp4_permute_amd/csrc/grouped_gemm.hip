@@ -43,6 +43,7 @@
 // gfx950, and no masks in the kernel.
 #include "nvfp4_internal.h"
 
+
 namespace nvfp4 {
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
@@ -495,11 +496,12 @@ __device__ __forceinline__ void a_store_piece(const ARegs<PPT>& R, const AScales
 }
 
 // Activation staging policies of the stream-K loop.  APairs: every thread
-// stages PPT (row, K group) pairs, one row tile per wave - used whenever two
-// or more row tiles are live.  AOneTile: only row tile 0 is live (at most 16
+// stages PPT (row, K group) pairs, one row tile per wave - used when three or
+// more row tiles are live.  AOneTile: only row tile 0 is live (at most 16
 // rows); its 16 rows x 4 K groups x 4 word pairs are spread over 256 threads,
 // 2 code words (16 values) each, so no wave decodes rows that do not exist.
-// Both write the same LDS fragments for the live row tiles.
+// ATwoTiles (below the B operand helpers' types): row tiles 0 and 1 live.
+// All write the same LDS fragments for the live row tiles.
 template <int THREADS, int MT, int PPT>
 struct APairs {
   using State = AState<PPT>;
@@ -586,6 +588,82 @@ struct AOneTile {
   template <int MTA>
   __device__ static void piece(const State& A, const Regs& R, const Scales& S, half8* __restrict__ lds, int s) {
     if ((s == 0 || s == 4) && active()) lds[A.slot + (s >> 2) * 64] = decode8_f16(s == 0 ? R.c.x : R.c.y, S.s);
+  }
+};
+
+// ATwoTiles: row tiles 0 and 1 live (17 to 32 rows): their 128 (row, K
+// group) pairs x 2 halves are spread over 256 threads, 4 code words each, so
+// no wave decodes rows that do not exist (one row tile per wave would leave
+// waves 2 and 3 decoding dead rows while waves 0 and 1 decode 8 words each).
+template <int THREADS, int MT>
+struct ATwoTiles {
+  static_assert(THREADS >= 256, "two live row tiles need 256 threads");
+  struct State {
+    rsrc_t rc, rs;
+    uint32_t vc, vs;
+    int kq;
+    int slot;
+    bool ok;
+  };
+  struct Regs {
+    u32x4 c;
+    uint32_t s;
+  };
+  struct Scales {
+    _Float16 s[2];
+  };
+  __device__ static bool active() { return THREADS == 256 || threadIdx.x < 256; }
+  __device__ static void setup(const GemmParams& p, int row0, int m0, int rows, State& A) {
+    const uint32_t krow = static_cast<uint32_t>(p.K) / 2;
+    const uint32_t srow = static_cast<uint32_t>(p.K) / 16;
+    A.rc = make_rsrc(p.a_codes, static_cast<uint32_t>(p.a_rows_total) * krow);
+    A.rs = make_rsrc(p.a_scales, static_cast<uint32_t>(p.a_rows_total) * srow);
+    const int t = threadIdx.x & 255;
+    const int pi = t & 127;             // pair: row (pi & 15) + 16 (pi >> 6), K group (pi >> 4) & 3
+    const int h = t >> 7;               // 32-value half of the K group
+    const int ag = (pi >> 4) & 3;
+    const int ar = (pi & 15) + 16 * (pi >> 6);
+    A.ok = active() && ar < rows;
+    int arow = row0 + m0 + (A.ok ? ar : 0);
+    if (p.a_rows) arow = p.a_rows[arow];
+    arow = (arow >= 0 && arow < p.a_rows_total) ? arow : 0;
+    A.vc = static_cast<uint32_t>(arow) * krow + 32u * ag + 16u * h;
+    A.vs = static_cast<uint32_t>(arow) * srow + 4u * ag + 2u * h;
+    A.kq = 64 * ag + 32 * h;
+    A.slot = (pi >> 6) * 8 * 64 + (4 * h) * 64 + (pi & 63);
+  }
+  __device__ static void load(const State& A, Regs& R, int k0, int K) {
+    // steps past K re-read the last step (cached) instead of fetching new bytes
+    const uint32_t kq = static_cast<uint32_t>(min(k0, ((K - 1) / KSTEP) * KSTEP));
+    R.c = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(A.rc, A.vc + kq / 2, 0, 0));
+    R.s = __builtin_amdgcn_raw_buffer_load_b16(A.rs, A.vs + kq / 16, 0, 0);
+  }
+  __device__ static void scales(const State& A, const Regs& R, int k0, int K, Scales& S) {
+    // a zero block scale zeroes a row that does not exist and a half past K
+    const bool ok = A.ok && (k0 + A.kq) < K;
+    const uint32_t as = ok ? R.s : 0u;
+    S.s[0] = e4m3_to_f16_div256(as);
+    S.s[1] = e4m3_to_f16_div256(as >> 8);
+  }
+  template <int MTA>
+  __device__ static void store(const State& A, const Regs& R, int k0, int K, half8* __restrict__ lds) {
+    Scales S;
+    scales(A, R, k0, K, S);
+    if (active()) {
+      lds[A.slot] = decode8_f16(R.c.x, S.s[0]);
+      lds[A.slot + 64] = decode8_f16(R.c.y, S.s[0]);
+      lds[A.slot + 128] = decode8_f16(R.c.z, S.s[1]);
+      lds[A.slot + 192] = decode8_f16(R.c.w, S.s[1]);
+    }
+  }
+  // the four words ride behind MFMA sub-steps 0, 2, 4, 6
+  template <int MTA>
+  __device__ static void piece(const State& A, const Regs& R, const Scales& S, half8* __restrict__ lds, int s) {
+    if ((s & 1) == 0 && active()) {
+      const int w = s >> 1;
+      const uint32_t word = w == 0 ? R.c.x : w == 1 ? R.c.y : w == 2 ? R.c.z : R.c.w;
+      lds[A.slot + w * 64] = decode8_f16(word, S.s[w >> 1]);
+    }
   }
 };
 
@@ -902,7 +980,15 @@ __device__ __forceinline__ void streamk_task(const GemmParams& p, int e, int m0,
         run_loop<NW, WN, MT, 1, APairs<THREADS, MT, PPT>, PACKED>(p, c, row0, m0, rows, lds0, lds1, acc);
       }
       break;
-    case 2: if constexpr (MAXA >= 2) run_loop<NW, WN, MT, 2, APairs<THREADS, MT, PPT>, PACKED>(p, c, row0, m0, rows, lds0, lds1, acc); break;
+    case 2:
+      if constexpr (MAXA >= 2) {
+        if constexpr (THREADS >= 256) {
+          run_loop<NW, WN, MT, 2, ATwoTiles<THREADS, MT>, PACKED>(p, c, row0, m0, rows, lds0, lds1, acc);
+        } else {
+          run_loop<NW, WN, MT, 2, APairs<THREADS, MT, PPT>, PACKED>(p, c, row0, m0, rows, lds0, lds1, acc);
+        }
+      }
+      break;
     case 3: if constexpr (MAXA >= 3) run_loop<NW, WN, MT, 3, APairs<THREADS, MT, PPT>, PACKED>(p, c, row0, m0, rows, lds0, lds1, acc); break;
     case 4: if constexpr (MAXA >= 4) run_loop<NW, WN, MT, 4, APairs<THREADS, MT, PPT>, PACKED>(p, c, row0, m0, rows, lds0, lds1, acc); break;
     case 5: case 6: if constexpr (MAXA >= 6) run_loop<NW, WN, MT, 6, APairs<THREADS, MT, PPT>, PACKED>(p, c, row0, m0, rows, lds0, lds1, acc); break;
