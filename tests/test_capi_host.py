@@ -68,6 +68,32 @@ def test_route_validation():
     assert L.moe_route_permute_workspace_size(256, 256, 8) >= 256 * 8 * 4 + 2 * 256 * 4
 
 
+def _route_quantize(logits=FAKE, T=16, E=8, k=2, x=FAKE, x_dtype=m.BF16, cols=64, codes=FAKE, ws=FAKE,
+                    ws_bytes=1 << 20):
+    L = m.lib()
+    return L.moe_route_quantize(logits, T, E, k, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, x, x_dtype, cols, None,
+                                None, codes, FAKE, ws, ws_bytes, None)
+
+
+def test_route_quantize_validation():
+    # every check runs before any launch: no GPU needed
+    L = m.lib()
+    assert _route_quantize(logits=None) == m.ERR_INVALID
+    assert _route_quantize(x=None) == m.ERR_INVALID
+    assert _route_quantize(T=0) == m.ERR_INVALID
+    assert _route_quantize(k=9, E=8) == m.ERR_INVALID
+    assert _route_quantize(k=33, E=64) == m.ERR_UNSUPPORTED
+    assert _route_quantize(cols=48) == m.ERR_INVALID
+    assert b"cols=48" in L.nvfp4moe_last_error_detail()
+    assert _route_quantize(x_dtype=7) == m.ERR_INVALID
+    assert _route_quantize(x=FAKE + 8) == m.ERR_INVALID          # x not 16-byte aligned
+    assert _route_quantize(ws_bytes=4) == m.ERR_WORKSPACE
+    assert _route_quantize(ws=None) == m.ERR_WORKSPACE
+    need = L.moe_route_quantize_workspace_size(256, 256, 8)
+    assert need == L.moe_route_permute_workspace_size(256, 256, 8) + 1024 * 4
+    assert L.moe_route_quantize_workspace_size(0, 256, 8) == 0
+
+
 def test_quantize_validation():
     L = m.lib()
     q = L.nvfp4_quantize
