@@ -27,12 +27,16 @@ def _frac_e4m3(c):
     return Fraction(F.e4m3_value(int(c)))
 
 
-def _exact(a_codes, a_scales, a_g, b_codes, b_scales, b_g, offsets, a_rows):
-    """Exact rational value of every output, from the definition (nested loops)."""
+def _exact(a_codes, a_scales, a_g, b_codes, b_scales, b_g, offsets, a_rows, want_abs=False):
+    """Exact rational value of every output, from the definition (nested loops).
+    With want_abs, also the exact sum_k |a^_k b^_k| g_a g_b[e] of every output
+    (the scale of the error bound), from the same loops with each product's
+    magnitude."""
     E, N, K2 = b_codes.shape
     K = 2 * K2
     M = int(offsets[-1])
     out = [[None] * N for _ in range(M)]
+    mag = [[None] * N for _ in range(M)]
     ua = unpack_codes(a_codes)
     ub = unpack_codes(b_codes)
     for e in range(E):
@@ -40,14 +44,22 @@ def _exact(a_codes, a_scales, a_g, b_codes, b_scales, b_g, offsets, a_rows):
             r = int(a_rows[p]) if a_rows is not None else p
             for n in range(N):
                 acc = Fraction(0)
+                acc_abs = Fraction(0)
                 for kb in range(K // 16):
                     part = Fraction(0)
+                    part_abs = Fraction(0)
                     for i in range(16):
                         kk = 16 * kb + i
-                        part += _frac_e2m1(ua[r, kk]) * _frac_e2m1(ub[e, n, kk])
-                    acc += _frac_e4m3(a_scales[r, kb]) * _frac_e4m3(b_scales[e, n, kb]) * part
-                out[p][n] = acc * Fraction(float(np.float32(a_g))) * Fraction(float(np.float32(b_g[e])))
-    return out
+                        prod = _frac_e2m1(ua[r, kk]) * _frac_e2m1(ub[e, n, kk])
+                        part += prod
+                        part_abs += abs(prod)
+                    s = _frac_e4m3(a_scales[r, kb]) * _frac_e4m3(b_scales[e, n, kb])
+                    acc += s * part
+                    acc_abs += s * part_abs
+                g = Fraction(float(np.float32(a_g))) * Fraction(float(np.float32(b_g[e])))
+                out[p][n] = acc * g
+                mag[p][n] = acc_abs * g
+    return (out, mag) if want_abs else out
 
 
 @pytest.mark.parametrize("seed", [0, 1, 2])
@@ -62,12 +74,15 @@ def test_grouped_gemm_equals_exact_rational(seed):
     a_g = np.float32(0.37)
     b_g = np.array([1.5, 0.25, 0.0078125 * 3], np.float32)
     y, absdot = grouped_gemm(a_codes, a_scales, a_g, b_codes, b_scales, b_g, offsets, a_rows=a_rows)
-    ex = _exact(a_codes, a_scales, a_g, b_codes, b_scales, b_g, offsets, a_rows)
+    ex, ex_abs = _exact(a_codes, a_scales, a_g, b_codes, b_scales, b_g, offsets, a_rows, want_abs=True)
     for p in range(offsets[-1]):
         for n in range(N):
             want = np.float32(float(ex[p][n]))          # correctly rounded
             got = y[p, n]
             assert abs(float(got) - float(ex[p][n])) <= abs(float(want)) * 2 ** -23 + 1e-30, (p, n)
+            # the tolerance scale sum|a^ b^| is pinned from both sides: exact
+            # up to float64 rounding of the per-tensor scale product
+            assert abs(Fraction(float(absdot[p, n])) - ex_abs[p][n]) <= ex_abs[p][n] * Fraction(1, 2 ** 50), (p, n)
     assert np.all(absdot >= np.abs(y) * (1 - 1e-6))
 
 

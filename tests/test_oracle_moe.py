@@ -168,3 +168,68 @@ def test_zipf_recipe_spread():
     ids, w = M.route(workloads.logits(cfg), cfg.k)
     c = np.bincount(ids.reshape(-1), minlength=cfg.E)
     assert c.min() >= 2 and 150 <= c.max() <= 300 and 20 <= np.median(c) <= 50
+
+
+def _token_by_token_layer(logits, x, wgu_q, wdn_q, k, g_h):
+    """The routed layer written token by token with plain loops, from the
+    layer's definition rather than from the permuted grouped form: for each
+    token t and each of its k experts e_j (the route's ids, in order),
+        y1 = g_x g_gu[e] * (x^[t] . w^_gu[e, n])           (rounded to float32)
+        h  = silu(y1[:I]) * y1[I:]                          (rounded to float32)
+        y2 = g_h g_dn[e] * (h^ . w^_dn[e, n])               (rounded to float32)
+        out[t] = sum_j w[t, j] * y2_j                       (float64)
+    where ^ marks dequantised NVFP4 values (x and h quantised with their
+    per-tensor scales).  No permutation, offsets or gathered rows appear."""
+    T, E = logits.shape
+    ids, w = M.route(logits, k)
+    xc, xs, xg = quantize(x)
+    gc, gs, gg = wgu_q
+    dc, ds, dg = wdn_q
+    I = gc.shape[1] // 2
+    H = dc.shape[1]
+    out = np.zeros((T, H))
+    for t in range(T):
+        xt = dequantize(xc[t:t + 1], xs[t:t + 1], 1.0)[0]
+        for j in range(k):
+            e = int(ids[t, j])
+            wg = dequantize(gc[e], gs[e], 1.0)
+            y1 = np.empty(2 * I, np.float32)
+            for n in range(2 * I):
+                y1[n] = np.float32(float(np.dot(xt, wg[n])) * (float(xg) * float(gg[e])))
+            h = np.empty(I, np.float32)
+            for i in range(I):
+                gate = float(y1[i])
+                h[i] = np.float32(gate / (1.0 + np.exp(-gate)) * float(y1[I + i]))
+            hc, hs, _ = quantize(h[None], g=g_h)
+            ht = dequantize(hc, hs, 1.0)[0]
+            wd = dequantize(dc[e], ds[e], 1.0)
+            for n in range(H):
+                y2 = np.float32(float(np.dot(ht, wd[n])) * (float(np.float32(g_h)) * float(dg[e])))
+                out[t, n] += float(w[t, j]) * float(y2)
+    return out
+
+
+def _routed_case():
+    rng = np.random.default_rng(77)
+    T, H, I, E, k = 11, 64, 32, 6, 3
+    x = workloads.to_bf16_values(rng.standard_normal((T, H)).astype(np.float32))
+    logits = rng.standard_normal((T, E)).astype(np.float32)
+    wgu = M.quantize_experts([(rng.standard_normal((2 * I, H)) * 0.1).astype(np.float32) for _ in range(E)])
+    wdn = M.quantize_experts([(rng.standard_normal((H, I)) * 0.1).astype(np.float32) for _ in range(E)])
+    return logits, x, wgu, wdn, k
+
+
+def test_layer_routed_matches_token_by_token_definition():
+    # several experts, k > 1, uneven expert loads: the permuted, grouped form
+    # of moe_layer (offsets, gathered rows, perm_of_assignment in the combine)
+    # must equal the token-by-token definition element by element.  Every
+    # float64 sum of dequantised products here is exact (multiples of 2^-20
+    # below 2^33 for K <= 1024), so y1 and y2 round identically on both sides
+    # and the requantised h codes agree exactly; only the float64 combine
+    # order may differ.
+    logits, x, wgu, wdn, k = _routed_case()
+    ref = M.moe_layer(logits, x, wgu, wdn, k, g_h=np.float32(0.001))
+    counts = ref["counts"]
+    assert (counts > 0).sum() >= 4 and counts.max() > counts.min()      # a routed case, not E=1
+    want = _token_by_token_layer(logits, x, wgu, wdn, k, np.float32(0.001))
+    np.testing.assert_allclose(ref["out64"], want, rtol=1e-12, atol=1e-12 * np.abs(want).max())

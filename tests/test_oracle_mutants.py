@@ -142,6 +142,54 @@ def test_mutant_e4m3_truncating_encoder(monkeypatch):
     assert _fails(TF.test_e4m3_encode_matches_torch_rne)
 
 
+def test_mutant_absdot_doubled(monkeypatch):
+    # a looser error-bound scale would widen every GEMM tolerance unnoticed
+    def bad(*a, **kw):
+        y, absdot = ORIG_GEMM(*a, **kw)
+        return y, absdot * 2
+    monkeypatch.setattr(TG, "grouped_gemm", bad)
+    assert _fails(TG.test_grouped_gemm_equals_exact_rational, 0)
+
+
+def test_mutant_absdot_per_tensor_scales_twice(monkeypatch):
+    def bad(a_codes, a_scales, a_g, b_codes, b_scales, b_g, offsets, a_rows=None, want_absdot=True):
+        y, absdot = ORIG_GEMM(a_codes, a_scales, a_g, b_codes, b_scales, b_g, offsets, a_rows=a_rows,
+                              want_absdot=want_absdot)
+        gb = np.repeat(np.asarray(b_g, np.float64), np.diff(np.asarray(offsets, np.int64)))
+        return y, absdot * float(np.float32(a_g)) * gb[:, None]
+    monkeypatch.setattr(TG, "grouped_gemm", bad)
+    assert _fails(TG.test_grouped_gemm_equals_exact_rational, 1)
+
+
+def test_mutant_layer_swaps_permutation_maps(monkeypatch):
+    # the gather of gate_up and the combine read the two maps of the
+    # permutation; handing each the other's map must break the routed pin
+    def bad(topk_ids, topk_w, E):
+        counts, offsets, src, perm_of, pw = ORIG_PERMUTE(topk_ids, topk_w, E)
+        return counts, offsets, perm_of // topk_ids.shape[1], src * topk_ids.shape[1], pw
+    monkeypatch.setattr(M, "permute", bad)
+    assert _fails(TM.test_layer_routed_matches_token_by_token_definition)
+
+
+def test_mutant_layer_gathers_assignment_not_token(monkeypatch):
+    # perm_src_token holding the flat assignment index instead of its token
+    def bad(topk_ids, topk_w, E):
+        T, k = topk_ids.shape
+        counts, offsets, src, perm_of, pw = ORIG_PERMUTE(topk_ids, topk_w, E)
+        order = np.argsort(topk_ids.reshape(-1), kind="stable")
+        return counts, offsets, (order % T).astype(np.int32), perm_of, pw
+    monkeypatch.setattr(M, "permute", bad)
+    assert _fails(TM.test_layer_routed_matches_token_by_token_definition)
+
+
+def test_mutant_layer_combine_ignores_permutation(monkeypatch):
+    def bad(y2, perm_of_assignment, topk_w):
+        return ORIG_COMBINE(y2, np.arange(len(perm_of_assignment), dtype=np.int32), topk_w)
+    monkeypatch.setattr(M, "combine", bad)
+    assert _fails(TM.test_layer_routed_matches_token_by_token_definition)
+
+
 ORIG_GEMM = M.grouped_gemm
 ORIG_ROUTE = M.route
 ORIG_COMBINE = M.combine
+ORIG_PERMUTE = M.permute
