@@ -48,6 +48,9 @@ def parse():
                     help="bf16 down output + gather combine, or float32 atomic scatter-add epilogue")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="time budget of the CPU-oracle sample")
+    ap.add_argument("--oracle-only", action="store_true",
+                    help="time only the CPU oracle on the workload (no GPU) and print one JSON line")
+    ap.add_argument("--oracle-threads", type=int, default=0, help="BLAS threads of the oracle (0: all)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB 5 times (to scale HBM byte counters)")
     return ap.parse_args()
@@ -86,7 +89,21 @@ def measured_traffic(kernel: str, workload: str):
     return ent.get("bytes_per_launch")
 
 
-def cpu_baseline(cfg, logits_np, x_np, w_gu_dev, w_dn_dev, g_h, budget_s=15.0, pool=8):
+def host_cpu():
+    """Host CPU model (from /proc/cpuinfo, as lscpu reports it) and logical CPU count."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:  # pragma: no cover
+        pass
+    return {"host_cpus": os.cpu_count(), "cpu_model": model}
+
+
+def cpu_baseline(cfg, logits_np, x_np, expert_weights, g_h, budget_s=15.0, pool=8, threads=None):
     """The CPU oracle, as it stands, on a bounded sample of the same workload.
 
     Timed: whole layer steps, repeated - routing, permutation and activation
@@ -99,16 +116,26 @@ def cpu_baseline(cfg, logits_np, x_np, w_gu_dev, w_dn_dev, g_h, budget_s=15.0, p
     computes with pool[e % pool] (same shapes, so the same arithmetic volume).
     Returns the throughput in the benchmark's unit: weight bytes of the experts
     done per second."""
+    import contextlib
+
     import numpy as np
     from oracle import moe as OM
     from oracle import quant as OQ
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    except Exception:  # pragma: no cover
-        threads = 1
-    wq = [(OQ.quantize(w_gu_dev[e].float().cpu().numpy()), OQ.quantize(w_dn_dev[e].float().cpu().numpy()))
-          for e in range(min(pool, cfg.E))]
+    from threadpoolctl import threadpool_info, threadpool_limits
+    wq = [tuple(OQ.quantize(w) for w in expert_weights(e)) for e in range(min(pool, cfg.E))]
+    limit = threadpool_limits(limits=threads) if threads else contextlib.nullcontext()
+    with limit:
+        used = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+        res = _cpu_baseline_timed(cfg, logits_np, x_np, wq, g_h, budget_s)
+    res["cores"] = int(used)
+    res.update(host_cpu())
+    return res
+
+
+def _cpu_baseline_timed(cfg, logits_np, x_np, wq, g_h, budget_s):
+    import numpy as np
+    from oracle import moe as OM
+    from oracle import quant as OQ
     done = rows_done = passes = 0
     n_touched = 0
     t0 = time.perf_counter()
@@ -135,7 +162,7 @@ def cpu_baseline(cfg, logits_np, x_np, w_gu_dev, w_dn_dev, g_h, budget_s=15.0, p
         passes += 1
     dt = time.perf_counter() - t0
     per_expert = 3 * cfg.I * cfg.H * 9 // 16
-    return {"value": round(done * per_expert / dt / 1e9, 6), "unit": "GB/s", "cores": int(threads),
+    return {"value": round(done * per_expert / dt / 1e9, 6), "unit": "GB/s",
             "kind": "oracle", "seconds": round(dt, 3),
             "sample": f"{passes} pass(es) of the layer step, {done} expert GEMM pairs in all ({n_touched} touched "
                       f"experts per step; {rows_done} routed rows; weights from a pool of {len(wq)} "
@@ -191,6 +218,22 @@ def dense_gemm(cfg, args):
                      "traffic": None}}), flush=True)
 
 
+def oracle_only(args):
+    """The CPU oracle alone on a MoE workload (weights drawn on the host from
+    the seeded recipe; g_h from the workload's static calibration), with a
+    chosen number of BLAS threads: the single- and all-thread oracle timings."""
+    import numpy as np
+
+    wl = workloads_mod()
+    cfg = wl.CONFIGS[args.workload]
+    g_h = float(np.float32(np.float32(wl.H_CALIBRATION_AMAX[cfg.index]) / np.float32(2688.0)))
+    res = cpu_baseline(cfg, wl.logits(cfg), wl.activations(cfg),
+                       lambda e: (wl.gate_up_weight(cfg, e), wl.down_weight(cfg, e)), g_h,
+                       budget_s=args.cpu_seconds, pool=min(8, cfg.E), threads=args.oracle_threads or None)
+    print(json.dumps({"oracle_only": True, "workload": cfg.name, "T": cfg.T, "H": cfg.H, "I": cfg.I, "E": cfg.E,
+                      "top_k": cfg.k, "threads_requested": args.oracle_threads or "all", **res}), flush=True)
+
+
 def workloads_mod():
     import workloads
     return workloads
@@ -206,6 +249,9 @@ def main():
 
     if args.copy_calibration:
         copy_calibration(args.copy_calibration)
+        return
+    if args.oracle_only:
+        oracle_only(args)
         return
 
     import numpy as np
@@ -334,7 +380,9 @@ def main():
     }
     if not args.no_cpu_baseline:
         gh = float(g_h.cpu().numpy()[0])
-        res["cpu_baseline"] = cpu_baseline(cfg, logits_np, x_np, w_gu0, w_dn0, gh, budget_s=args.cpu_seconds)
+        res["cpu_baseline"] = cpu_baseline(
+            cfg, logits_np, x_np, lambda e: (w_gu0[e].float().cpu().numpy(), w_dn0[e].float().cpu().numpy()), gh,
+            budget_s=args.cpu_seconds)
     print(json.dumps(res), flush=True)
 
 

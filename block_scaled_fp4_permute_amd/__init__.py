@@ -268,18 +268,50 @@ def nvfp4_grouped_gemm(a: NVFP4Tensor, b_codes, b_scales, b_g, offsets, *, m_tot
     _need(offsets, torch.int32, "offsets")
     if a.codes.shape[1] != K2 or tuple(b_scales.shape) != (E, N, K // 16):
         raise ValueError("operand shapes disagree")
+    a_rows_total = a.codes.shape[0]
+    if tuple(a.scales.shape) != (a_rows_total, K // 16):
+        raise ValueError(f"a.scales: expected [{a_rows_total}, {K // 16}], got {list(a.scales.shape)}")
+    if a.g.numel() < 1 or b_g.numel() < E:
+        raise ValueError("a.g needs 1 and b_g needs E float32 values")
+    if offsets.numel() < E + 1:
+        raise ValueError(f"offsets: {offsets.numel()} values, expected E+1 = {E + 1}")
     if a_rows is not None:
         _need(a_rows, torch.int32, "a_rows")
+        if a_rows.numel() < m_total:
+            raise ValueError(f"a_rows: {a_rows.numel()} values, expected m_total = {m_total}")
     dev = b_codes.device
     I = N // 2
-    if epilogue in (EPI_F32, EPI_BF16) and out is None:
-        out = torch.empty((m_total, N), dtype=torch.float32 if epilogue == EPI_F32 else torch.bfloat16, device=dev)
-    if epilogue == EPI_SWIGLU_NVFP4 and out_codes is None:
-        out_codes = torch.empty((m_total, I // 2), dtype=torch.uint8, device=dev)
-        out_scales = torch.empty((m_total, I // 16), dtype=torch.uint8, device=dev)
+    if epilogue in (EPI_F32, EPI_BF16):
+        want = torch.float32 if epilogue == EPI_F32 else torch.bfloat16
+        if out is None:
+            out = torch.empty((m_total, N), dtype=want, device=dev)
+        else:
+            _need(out, want, "out")
+            if tuple(out.shape) != (m_total, N):
+                raise ValueError(f"out: expected [{m_total}, {N}], got {list(out.shape)}")
+    if epilogue == EPI_SWIGLU_NVFP4:
+        if out_g is None:
+            raise ValueError("EPI_SWIGLU_NVFP4 needs out_g (the per-tensor scale of h)")
+        _need(out_g, torch.float32, "out_g")
+        if out_codes is None:
+            out_codes = torch.empty((m_total, I // 2), dtype=torch.uint8, device=dev)
+            out_scales = torch.empty((m_total, I // 16), dtype=torch.uint8, device=dev)
+        _need(out_codes, torch.uint8, "out_codes")
+        _need(out_scales, torch.uint8, "out_scales")
+        if tuple(out_codes.shape) != (m_total, I // 2) or tuple(out_scales.shape) != (m_total, I // 16):
+            raise ValueError(f"out_codes/out_scales: expected [{m_total}, {I // 2}] and [{m_total}, {I // 16}]")
+    if epilogue == EPI_COMBINE_F32:
+        if out is None or row_token is None or row_weight is None:
+            raise ValueError("EPI_COMBINE_F32 needs out, row_token and row_weight")
+        _need(out, torch.float32, "out")
+        _need(row_token, torch.int32, "row_token")
+        _need(row_weight, torch.float32, "row_weight")
+        if tuple(out.shape) != (out_rows, N) or row_token.numel() < m_total or row_weight.numel() < m_total:
+            raise ValueError(f"combine epilogue: out must be [out_rows={out_rows}, {N}], row_token and row_weight "
+                             f"at least m_total = {m_total} long")
     args = GemmArgs(
         a_codes=a.codes.data_ptr(), a_scales=a.scales.data_ptr(), a_g=a.g.data_ptr(), a_rows=_ptr(a_rows),
-        a_rows_total=a.codes.shape[0],
+        a_rows_total=a_rows_total,
         b_codes=None if b_packed is not None else b_codes.data_ptr(),
         b_scales=None if b_packed is not None else b_scales.data_ptr(), b_packed=_ptr(b_packed),
         b_g=b_g.data_ptr(), offsets=offsets.data_ptr(), E=E, N=N, K=K, m_total=m_total, epilogue=epilogue,
@@ -320,15 +352,24 @@ def moe_unpermute_combine(y, perm_of_assignment, topk_w, T: int, k: int, out=Non
     H = y.shape[1]
     if out is None:
         out = torch.empty((T, H), dtype=out_dtype or torch.bfloat16, device=y.device)
+    if tuple(out.shape) != (T, H):
+        raise ValueError(f"out: expected [{T}, {H}], got {list(out.shape)}")
+    _need(out, out.dtype, "out")
     if perm_of_assignment is not None:
         _need(perm_of_assignment, torch.int32, "perm_of_assignment")
+        if perm_of_assignment.numel() < T * k:
+            raise ValueError(f"perm_of_assignment: {perm_of_assignment.numel()} values, expected T*k = {T * k}")
+    elif y.shape[0] < T * k:
+        raise ValueError(f"y has {y.shape[0]} rows, fewer than T*k = {T * k} (and no perm_of_assignment)")
     if topk_w is not None:
         _need(topk_w, torch.float32, "topk_w")
+        if topk_w.numel() < T * k:
+            raise ValueError(f"topk_w: {topk_w.numel()} values, expected T*k = {T * k}")
     _check(lib().moe_unpermute_combine(y.data_ptr(), _dtype_code(y), _ptr(perm_of_assignment), _ptr(topk_w),
                                        T, k, H, out.data_ptr(), _dtype_code(out), _stream(stream)))
     return out
 
 
-__all__ = ["lib", "moe_route_permute", "nvfp4_quantize", "nvfp4_grouped_gemm", "moe_swiglu", "nvfp4_weight_repack",
+__all__ = ["lib", "moe_route_permute", "moe_route_quantize", "nvfp4_quantize", "nvfp4_grouped_gemm", "moe_swiglu", "nvfp4_weight_repack",
            "moe_unpermute_combine", "NVFP4Tensor", "Routing", "GemmArgs", "NVFP4MoEError",
            "F32", "BF16", "EPI_F32", "EPI_BF16", "EPI_SWIGLU_NVFP4", "EPI_COMBINE_F32"]

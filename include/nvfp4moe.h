@@ -135,6 +135,10 @@ int moe_route_permute(const float* logits, int32_t T, int32_t E, int32_t k,
                       void* workspace, size_t workspace_bytes, void* stream);
 
 /* ---------------------------------------------------------------- quantise
+ * The NVFP4 encoding of an operand (e2m1 values with one ue4m3 scale per 16
+ * along the reduction axis: "From Empirical Limits ...", section "Section 1:
+ * CUTLASS Kernels - The Foundation"; the quantiser rule is the reading given
+ * at the top of this file).
  * x [rows, cols] (bf16 or float32, finite) -> NVFP4 codes/scales as described
  * above.  g_in (device, nullable): a caller-supplied per-tensor scale; NULL
  * computes g = amax/2688 (1 if the tensor is zero) on the device.  g_out
@@ -194,6 +198,12 @@ int nvfp4_weight_repack(const uint8_t* codes, const uint8_t* scales, int32_t E, 
                         uint8_t* packed, size_t packed_bytes, void* stream);
 
 /* ---------------------------------------------------------------- SwiGLU (unfused)
+ * The activation between the two expert GEMMs, re-quantised to NVFP4 so that
+ * the down GEMM runs on e2m1 operands too (the e2m1 x e2m1 block-scaled MMA of
+ * "From Empirical Limits ...", section "Section 1: CUTLASS Kernels - The
+ * Foundation"; the same step fused into the gate_up epilogue is
+ * NVFP4MOE_EPI_SWIGLU_NVFP4, the kind of epilogue fusion that section "Key
+ * Findings and Their Impact" of that page weighs more when bandwidth is tight).
  * gate_up [M, 2I] (float32 or bf16) -> h = silu(gate) * up, gate = columns
  * [0, I), up = [I, 2I), quantised to NVFP4 codes [M, I/2], scales [M, I/16].
  * g_in (nullable): per-tensor scale of h; NULL computes amax(h)/2688 on the
@@ -210,6 +220,9 @@ int moe_swiglu(const void* gate_up, int32_t dtype, int64_t M, int32_t I,
  * [T, H] float32 or bf16 (nearest even); float32 accumulation in j order.
  * perm_of_assignment NULL means row t*k + j; topk_w NULL means weight 1, so
  * (perm NULL, w NULL, k = 1) converts a float32 accumulator to bf16.
+ * Every perm_of_assignment entry must lie in [0, rows of y): the kernel reads
+ * the rows it names without a bounds check (the routing calls produce such
+ * entries).  Without perm_of_assignment, y needs at least T*k rows.
  * H % 8 == 0. */
 int moe_unpermute_combine(const void* y, int32_t y_dtype, const int32_t* perm_of_assignment,
                           const float* topk_w, int32_t T, int32_t k, int32_t H,

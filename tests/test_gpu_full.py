@@ -1,8 +1,14 @@
 """Full-size parity at the workloads' real shapes, in the launch configuration
-the benchmark times (MoELayer, fused epilogues), checked on sampled outputs
-that the oracle computes row by row; plus the dense 8192^3 GEMM on sampled
-entries.  Both sides start from the same seeded raw inputs (logits, bf16
-activations, float32 weights) and run their own chains."""
+the benchmark times (MoELayer, fused epilogues), checked end to end on sampled
+tokens that the oracle computes row by row; plus the dense 8192^3 GEMM on
+sampled entries.  Both sides start from the same seeded raw inputs (logits,
+bf16 activations, float32 weights) and run their own chains.
+
+End to end, the GPU's h can differ from the oracle's where a requantisation
+input lies next to a decision point (the gate_up sums differ by rounding).
+Each such h value is first checked to be a valid rounding (check_requant),
+and the output tolerance then carries the exact bound of that choice's effect
+on the down GEMM, |delta h| * |w_dn|; every output element is compared."""
 import numpy as np
 import pytest
 import torch
@@ -50,7 +56,7 @@ def test_full_layer_sampled_tokens(cfg_index, mode):
     g_x = OQ.global_scale(x)
     assert down(layer.xq.g)[0] == g_x
     rng = np.random.default_rng(cfg_index)
-    tokens = rng.choice(T, size=4, replace=False)
+    tokens = rng.choice(T, size=8, replace=False)
     experts = sorted(set(ids[tokens].reshape(-1).tolist()))
     wq_ref = {}
     for e in experts:
@@ -58,13 +64,11 @@ def test_full_layer_sampled_tokens(cfg_index, mode):
         assert np.array_equal(down(wq.gu_codes[e]), wq_ref[e][0][0]), "gate_up weight codes"
         assert np.array_equal(down(wq.dn_scales[e]), wq_ref[e][1][1]), "down weight scales"
     h_codes_gpu, h_scales_gpu = down(layer.hq.codes), down(layer.hq.scales)
-    flipped_tokens = 0
     for t in tokens:
         xc, xs, _ = OQ.quantize(x[t:t + 1], g=g_x)
         acc = np.zeros(H)
         tol = np.zeros(H)
         absterm = np.zeros(H)
-        flips = 0
         for j in range(k):
             e = int(ids[t, j])
             p = int(perm_of[t * k + j])
@@ -74,24 +78,26 @@ def test_full_layer_sampled_tokens(cfg_index, mode):
             tol_y = 1e-3 * ad1 + 1e-6
             uu, gg_ = y1[:, I:].astype(np.float64), y1[:, :I].astype(np.float64)
             tol_h = 1.1 * tol_y[:, :I] * np.abs(uu) + np.abs(OM.silu(gg_)) * tol_y[:, I:] + 2.0 ** -20 * np.abs(h64) + 1e-7
-            ns, nc = check_requant(h_codes_gpu[p:p + 1], h_scales_gpu[p:p + 1], h64, g_h, tol_h, max_flip_frac=0.05,
-                                   what=f"h row of token {t} slot {j}")
-            flips += ns + nc
+            # every differing h code or block scale must be a valid rounding of a
+            # value within the propagated gate_up tolerance (next to a decision point)
+            check_requant(h_codes_gpu[p:p + 1], h_scales_gpu[p:p + 1], h64, g_h, tol_h, max_flip_frac=1.0,
+                          what=f"h row of token {t} slot {j}")
             hc, hs, _ = OQ.quantize(h64.astype(np.float32), g=g_h)
             y2, ad2 = OM.grouped_gemm(hc, hs, g_h, dc[None], ds[None], np.array([dg]), np.array([0, 1]))
+            # a flipped h value is one of the two valid roundings; its effect on
+            # the down GEMM is bounded by |delta h| * |w_dn| (both rounding
+            # candidates, so either choice of the GPU passes, nothing else does)
+            dh = np.abs(OQ.dequantize(h_codes_gpu[p:p + 1], h_scales_gpu[p:p + 1], g_h)
+                        - OQ.dequantize(hc, hs, g_h))[0]
+            flip_tol = (np.abs(OQ.dequantize_unscaled(dc, ds)) @ dh) * float(dg) if dh.any() else 0.0
             acc += float(w[t, j]) * y2[0].astype(np.float64)
-            tol += abs(float(w[t, j])) * (1e-3 * ad2[0] + 1e-6)
-            absterm += abs(float(w[t, j])) * np.abs(y2[0].astype(np.float64))
-        tol += 2.0 ** -8 * np.abs(acc) + 1e-6
+            tol += abs(float(w[t, j])) * (1e-3 * ad2[0] + 1e-6 + 1.001 * flip_tol)
+            absterm += abs(float(w[t, j])) * (np.abs(y2[0].astype(np.float64)) + flip_tol)
+        tol = tol * (1 + 2.0 ** -8) + 2.0 ** -8 * np.abs(acc) + 1e-6     # bf16 rounding of the output
         if not fused:
             tol += 2.0 ** -8 * absterm            # the bf16 rounding of each y2 row before the combine
         err = np.abs(out[t] - acc)
-        if flips == 0:
-            assert np.all(err <= tol), f"token {t}: max err {err.max()} (tol there {tol[np.argmax(err)]})"
-        else:
-            flipped_tokens += 1
-            assert np.linalg.norm(out[t] - acc) <= 0.05 * np.linalg.norm(acc), f"token {t} with {flips} flips"
-    assert flipped_tokens <= 2
+        assert np.all(err <= tol), f"token {t}: max err {err.max()} (tol there {tol[np.argmax(err)]})"
 
 
 def test_full_dense_gemm_8192_sampled():
@@ -102,7 +108,10 @@ def test_full_dense_gemm_8192_sampled():
     aq = m.nvfp4_quantize(a)
     bq = m.nvfp4_quantize(b)
     offsets = torch.tensor([0, M_], dtype=torch.int32, device=DEV)
-    y = m.nvfp4_grouped_gemm(aq, bq.codes[None], bq.scales[None], bq.g, offsets, m_total=M_, epilogue=m.EPI_BF16)
+    # the instance the dense benchmark times: packed weights, large-M tile (hint = M)
+    packed = m.nvfp4_weight_repack(bq.codes[None], bq.scales[None])
+    y = m.nvfp4_grouped_gemm(aq, bq.codes[None], bq.scales[None], bq.g, offsets, m_total=M_, epilogue=m.EPI_BF16,
+                             max_rows_per_expert_hint=M_, b_packed=packed)
     torch.cuda.synchronize()
     a_np, b_np = a.cpu().numpy(), b.cpu().numpy()
     g_a, g_b = OQ.global_scale(a_np), OQ.global_scale(b_np)

@@ -80,9 +80,12 @@ GEMM_CASES = [
 @pytest.mark.parametrize("case", range(len(GEMM_CASES)))
 @pytest.mark.parametrize("gather", [False, True])
 @pytest.mark.parametrize("packed", [False, True])
-def test_gemm_f32_random(case, gather, packed):
+@pytest.mark.parametrize("epi", ["f32", "bf16"])
+def test_gemm_f32_random(case, gather, packed, epi):
+    # with packed weights and K <= 256 the launcher picks the stream-N kernel
+    # (whose bf16 rows leave through its LDS-staged store), otherwise stream-K
     E, counts, N, K, rows_a, hint = GEMM_CASES[case]
-    print(f"gemm case {case} gather={gather} packed={packed} E={E} N={N} K={K}", flush=True)
+    print(f"gemm case {case} gather={gather} packed={packed} epi={epi} E={E} N={N} K={K}", flush=True)
     rng = np.random.default_rng(100 + case)
     a_codes, a_scales = _rand_nvfp4(rng, (rows_a,), K)
     b_codes, b_scales = _rand_nvfp4(rng, (E, N), K)
@@ -92,9 +95,11 @@ def test_gemm_f32_random(case, gather, packed):
     a_rows = rng.integers(0, rows_a, M).astype(np.int32) if gather else None
     if not gather:
         a_codes, a_scales = a_codes[:max(M, 1)], a_scales[:max(M, 1)]
-    y, offsets = _run_gemm(a_codes, a_scales, a_g, b_codes, b_scales, b_g, counts, a_rows, hint=hint, packed=packed)
+    y, offsets = _run_gemm(a_codes, a_scales, a_g, b_codes, b_scales, b_g, counts, a_rows, hint=hint, packed=packed,
+                           epilogue=m.EPI_F32 if epi == "f32" else m.EPI_BF16)
     y_ref, absdot = OM.grouped_gemm(a_codes, a_scales, a_g, b_codes, b_scales, b_g, offsets, a_rows=a_rows)
-    assert_gemm_close(down(y)[:M], y_ref, absdot, what=f"case {case}")
+    got = down(y)[:M] if epi == "f32" else bf16_to_f32(y)[:M]
+    assert_gemm_close(got, y_ref, absdot, bf16_out=epi == "bf16", what=f"case {case} {epi}")
 
 
 @pytest.mark.parametrize("hint", [0, 4096])

@@ -7,7 +7,7 @@ oracle and the GPU path receive exactly the arrays produced here.
 Every stream is ``numpy.random.default_rng(SeedSequence([2026, cfg, stream, ...]))``
 with streams 0 = router logits, 1 = expert popularity ranks, 2 = activations,
 3 = gate_up weights (one sub-stream per expert), 4 = down weights (one per
-expert), 5/6 = dense A/B.  Activations are drawn in float32 and rounded to
+expert), 5/6 = dense A/B, 7 = NVFP4 operand bytes drawn directly.  Activations are drawn in float32 and rounded to
 bfloat16 (round to nearest even, by torch), because the layer's input is a
 bfloat16 tensor; the float32 copy returned here holds the same values.
 
@@ -147,6 +147,24 @@ def torch_dense_operands(cfg: MoEConfig, device):
     a = torch.randn((cfg.T, cfg.I), generator=gen, device=device, dtype=torch.float32)
     b = torch.randn((cfg.H, cfg.I), generator=gen, device=device, dtype=torch.float32)
     return a, b
+
+
+def nvfp4_codes(cfg: MoEConfig, stream: int, shape_rows: tuple, K: int, scale_lo: int = 0x60,
+                scale_hi: int = 0x7F, const_scale: int | None = None):
+    """Random NVFP4 operand bytes: codes uint8 [*shape_rows, K/2] uniform over all
+    256 byte values (two 4-bit codes each) and block-scale bytes uint8
+    [*shape_rows, K/16] uniform in [scale_lo, scale_hi) (E4M3 codes; the default
+    range 0x60..0x7E is where block scales of quantised Gaussian weights land,
+    about 64..448), or all equal to ``const_scale``.  Raw input bytes, drawn
+    from stream ``stream`` (7 = GEMM operands given directly as codes); no
+    arithmetic of the method is involved."""
+    g = rng(cfg.index, 7, stream)
+    codes = g.integers(0, 256, tuple(shape_rows) + (K // 2,), dtype=np.uint8)
+    if const_scale is None:
+        scales = g.integers(scale_lo, scale_hi, tuple(shape_rows) + (K // 16,), dtype=np.uint8)
+    else:
+        scales = np.full(tuple(shape_rows) + (K // 16,), const_scale, np.uint8)
+    return codes, scales
 
 
 # Static calibration of the intermediate's per-tensor scale: an expected
