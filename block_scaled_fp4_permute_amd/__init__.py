@@ -72,6 +72,10 @@ _SIGNATURES = {
     "moe_route_quantize": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32]
                            + [ctypes.c_void_p] * 7 + [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64]
                            + [ctypes.c_void_p] * 4 + [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
+    "moe_route_quantize_noalloc_max_workspace": (ctypes.c_size_t, []),
+    "moe_route_quantize_noalloc": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32]
+                                   + [ctypes.c_void_p] * 7 + [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64]
+                                   + [ctypes.c_void_p] * 4 + [ctypes.c_void_p]),
     "nvfp4moe_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "nvfp4moe_last_error_detail": (ctypes.c_char_p, []),
     "nvfp4moe_version": (ctypes.c_int, []),
@@ -243,6 +247,28 @@ def moe_route_quantize(logits, k: int, x, g=None, out: Routing | None = None, xq
     return out, xq
 
 
+def moe_route_quantize_noalloc(logits, k: int, x, out: Routing, xq: NVFP4Tensor, g=None, stream=None):
+    """moe_route_quantize with the library's per-device scratch instead of a
+    workspace: allocates nothing (outputs are the caller's ``out`` and ``xq``)."""
+    import torch
+    _need(logits, torch.float32, "logits")
+    _need(x, x.dtype, "x")
+    T, E = logits.shape
+    if x.dim() != 2 or x.shape[0] != T:
+        raise ValueError("x must be [T, cols] with the logits' T rows")
+    cols = x.shape[1]
+    if tuple(out.topk_ids.shape) != (T, k) or out.perm_src_token.numel() < T * k or out.offsets.numel() < E + 1:
+        raise ValueError("routing outputs do not match T, E, k")
+    if tuple(xq.codes.shape) != (T, cols // 2) or tuple(xq.scales.shape) != (T, cols // 16):
+        raise ValueError("xq does not match x")
+    _check(lib().moe_route_quantize_noalloc(
+        logits.data_ptr(), T, E, k, out.topk_ids.data_ptr(), out.topk_w.data_ptr(), out.counts.data_ptr(),
+        out.offsets.data_ptr(), out.perm_src_token.data_ptr(), out.perm_of_assignment.data_ptr(),
+        _ptr(out.perm_weight), x.data_ptr(), _dtype_code(x), cols, _ptr(g), _ptr(xq.g), xq.codes.data_ptr(),
+        xq.scales.data_ptr(), _stream(stream)))
+    return out, xq
+
+
 # ---------------------------------------------------------------------------- gemm
 def nvfp4_grouped_gemm(a: NVFP4Tensor, b_codes, b_scales, b_g, offsets, *, m_total: int, a_rows=None,
                        epilogue: int = EPI_F32, out=None, out_rows: int = 0, out_codes=None,
@@ -370,6 +396,6 @@ def moe_unpermute_combine(y, perm_of_assignment, topk_w, T: int, k: int, out=Non
     return out
 
 
-__all__ = ["lib", "moe_route_permute", "moe_route_quantize", "nvfp4_quantize", "nvfp4_grouped_gemm", "moe_swiglu", "nvfp4_weight_repack",
+__all__ = ["lib", "moe_route_permute", "moe_route_quantize", "moe_route_quantize_noalloc", "nvfp4_quantize", "nvfp4_grouped_gemm", "moe_swiglu", "nvfp4_weight_repack",
            "moe_unpermute_combine", "NVFP4Tensor", "Routing", "GemmArgs", "NVFP4MoEError",
            "F32", "BF16", "EPI_F32", "EPI_BF16", "EPI_SWIGLU_NVFP4", "EPI_COMBINE_F32"]

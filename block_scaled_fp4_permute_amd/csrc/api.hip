@@ -3,6 +3,8 @@
 #include <stdio.h>
 #include <stdarg.h>
 
+#include <mutex>
+
 #include "../../include/nvfp4moe.h"
 #include "nvfp4_internal.h"
 
@@ -31,6 +33,63 @@ int hip_status(hipError_t err, const char* what) {
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
 constexpr size_t kSmallWs = 4096;   // 1024 partial maxima of the amax reduction
+
+// Argument checks of the route + quantise calls (everything but the workspace).
+int check_route_quantize(const char* fn, const float* logits, int32_t T, int32_t E, int32_t k,
+                         const int32_t* topk_ids, const float* topk_w, const int32_t* counts, const int32_t* offsets,
+                         const int32_t* perm_src_token, const int32_t* perm_of_assignment, const void* x,
+                         int32_t x_dtype, int64_t cols, const uint8_t* codes, const uint8_t* scales) {
+  if (!logits || !topk_ids || !topk_w || !counts || !offsets || !perm_src_token || !perm_of_assignment)
+    return fail(NVFP4MOE_ERR_INVALID, "%s: null routing pointer argument", fn);
+  if (!x || !codes || !scales) return fail(NVFP4MOE_ERR_INVALID, "%s: null x, codes or scales", fn);
+  if (T <= 0 || E <= 0 || k <= 0) return fail(NVFP4MOE_ERR_INVALID, "%s: T, E, k must be > 0", fn);
+  if (k > E) return fail(NVFP4MOE_ERR_INVALID, "%s: k=%d > E=%d", fn, k, E);
+  if (k > 32) return fail(NVFP4MOE_ERR_UNSUPPORTED, "%s: k=%d > 32", fn, k);
+  if (E > 4096) return fail(NVFP4MOE_ERR_UNSUPPORTED, "%s: E=%d > 4096", fn, E);
+  if (static_cast<int64_t>(T) * k >= (int64_t(1) << 30)) return fail(NVFP4MOE_ERR_UNSUPPORTED, "%s: T*k >= 2^30", fn);
+  if (x_dtype != NVFP4MOE_F32 && x_dtype != NVFP4MOE_BF16)
+    return fail(NVFP4MOE_ERR_INVALID, "%s: x_dtype %d", fn, x_dtype);
+  if (cols <= 0 || cols % 32 != 0)
+    return fail(NVFP4MOE_ERR_INVALID, "%s: cols=%lld must be a positive multiple of 32", fn, (long long)cols);
+  if (static_cast<int64_t>(T) * (cols / 16) >= (int64_t(1) << 40))
+    return fail(NVFP4MOE_ERR_UNSUPPORTED, "%s: tensor too large", fn);
+  // the encoder's workgroups are indexed after the ranks' in one grid
+  if ((static_cast<int64_t>(T) * (cols / 16) + 255) / 256 + (static_cast<int64_t>(T) * k + 1023) / 1024 >=
+      (int64_t(1) << 31))
+    return fail(NVFP4MOE_ERR_UNSUPPORTED, "%s: grid too large", fn);
+  if (!aligned(x, 16) || !aligned(codes, 8)) return fail(NVFP4MOE_ERR_INVALID, "%s: misaligned x or codes", fn);
+  return NVFP4MOE_OK;
+}
+
+// ------------------------------------------------------------------ scratch of the no-allocation entry point
+// One fixed block of device memory per GPU, held until the process ends,
+// shared by every call of moe_route_quantize_noalloc on that GPU.  In host
+// code `scratch` names a host-side stand-in, not a device address: kernels
+// get the device address that hipGetSymbolAddress returns for the current
+// device, looked up once per device and kept.
+constexpr size_t kScratchBytes = size_t(4) << 20;
+__device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+int device_scratch(void** out) {
+  int dev = -1;
+  hipError_t err = hipGetDevice(&dev);
+  if (err != hipSuccess) return fail(NVFP4MOE_ERR_HIP, "scratch: hipGetDevice: %s", hipGetErrorString(err));
+  if (dev < 0 || dev >= kMaxDevices) return fail(NVFP4MOE_ERR_UNSUPPORTED, "scratch: device %d beyond %d", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (err != hipSuccess || !p)
+      return fail(NVFP4MOE_ERR_HIP, "scratch: hipGetSymbolAddress on device %d: %s", dev, hipGetErrorString(err));
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return NVFP4MOE_OK;
+}
 
 }  // namespace
 
@@ -108,27 +167,9 @@ int moe_route_quantize(const float* logits, int32_t T, int32_t E, int32_t k, int
                        float* perm_weight, const void* x, int32_t x_dtype, int64_t cols, const float* g_in,
                        float* g_out, uint8_t* codes, uint8_t* scales, void* workspace, size_t workspace_bytes,
                        void* stream) {
-  if (!logits || !topk_ids || !topk_w || !counts || !offsets || !perm_src_token || !perm_of_assignment)
-    return fail(NVFP4MOE_ERR_INVALID, "moe_route_quantize: null routing pointer argument");
-  if (!x || !codes || !scales) return fail(NVFP4MOE_ERR_INVALID, "moe_route_quantize: null x, codes or scales");
-  if (T <= 0 || E <= 0 || k <= 0) return fail(NVFP4MOE_ERR_INVALID, "moe_route_quantize: T, E, k must be > 0");
-  if (k > E) return fail(NVFP4MOE_ERR_INVALID, "moe_route_quantize: k=%d > E=%d", k, E);
-  if (k > 32) return fail(NVFP4MOE_ERR_UNSUPPORTED, "moe_route_quantize: k=%d > 32", k);
-  if (E > 4096) return fail(NVFP4MOE_ERR_UNSUPPORTED, "moe_route_quantize: E=%d > 4096", E);
-  if (static_cast<int64_t>(T) * k >= (int64_t(1) << 30))
-    return fail(NVFP4MOE_ERR_UNSUPPORTED, "moe_route_quantize: T*k >= 2^30");
-  if (x_dtype != NVFP4MOE_F32 && x_dtype != NVFP4MOE_BF16)
-    return fail(NVFP4MOE_ERR_INVALID, "moe_route_quantize: x_dtype %d", x_dtype);
-  if (cols <= 0 || cols % 32 != 0)
-    return fail(NVFP4MOE_ERR_INVALID, "moe_route_quantize: cols=%lld must be a positive multiple of 32", (long long)cols);
-  if (static_cast<int64_t>(T) * (cols / 16) >= (int64_t(1) << 40))
-    return fail(NVFP4MOE_ERR_UNSUPPORTED, "moe_route_quantize: tensor too large");
-  // the encoder's workgroups are indexed after the ranks' in one grid
-  if ((static_cast<int64_t>(T) * (cols / 16) + 255) / 256 + (static_cast<int64_t>(T) * k + 1023) / 1024 >=
-      (int64_t(1) << 31))
-    return fail(NVFP4MOE_ERR_UNSUPPORTED, "moe_route_quantize: grid too large");
-  if (!aligned(x, 16) || !aligned(codes, 8))
-    return fail(NVFP4MOE_ERR_INVALID, "moe_route_quantize: misaligned x or codes");
+  const int bad = check_route_quantize("moe_route_quantize", logits, T, E, k, topk_ids, topk_w, counts, offsets,
+                                       perm_src_token, perm_of_assignment, x, x_dtype, cols, codes, scales);
+  if (bad != NVFP4MOE_OK) return bad;
   const size_t need = nvfp4::route_quantize_ws_bytes(T, E, k);
   if (!workspace || workspace_bytes < need)
     return fail(NVFP4MOE_ERR_WORKSPACE, "moe_route_quantize: workspace %zu < %zu bytes", workspace_bytes, need);
@@ -137,6 +178,33 @@ int moe_route_quantize(const float* logits, int32_t T, int32_t E, int32_t k, int
                                                  perm_of_assignment, perm_weight, x, x_dtype, cols, g_in, g_out,
                                                  codes, scales, workspace, static_cast<hipStream_t>(stream)),
                     "moe_route_quantize");
+}
+
+size_t moe_route_quantize_noalloc_max_workspace(void) { return kScratchBytes; }
+
+int moe_route_quantize_noalloc(const float* logits, int32_t T, int32_t E, int32_t k, int32_t* topk_ids,
+                               float* topk_w, int32_t* counts, int32_t* offsets, int32_t* perm_src_token,
+                               int32_t* perm_of_assignment, float* perm_weight, const void* x, int32_t x_dtype,
+                               int64_t cols, const float* g_in, float* g_out, uint8_t* codes, uint8_t* scales,
+                               void* stream) {
+  const int bad = check_route_quantize("moe_route_quantize_noalloc", logits, T, E, k, topk_ids, topk_w, counts,
+                                       offsets, perm_src_token, perm_of_assignment, x, x_dtype, cols, codes, scales);
+  if (bad != NVFP4MOE_OK) return bad;
+  const size_t need = nvfp4::route_quantize_ws_bytes(T, E, k);
+  if (need > kScratchBytes)
+    return fail(NVFP4MOE_ERR_UNSUPPORTED,
+                "moe_route_quantize_noalloc: T=%d, E=%d, k=%d need %zu bytes of scratch, more than the %zu the "
+                "library holds per device (use moe_route_quantize with a workspace)",
+                T, E, k, need, kScratchBytes);
+  void* ws = nullptr;
+  const int st = device_scratch(&ws);
+  if (st != NVFP4MOE_OK) return st;
+  // every scratch word the kernels read is written earlier in the same call:
+  // nothing needs clearing between calls
+  return hip_status(nvfp4::launch_route_quantize(logits, T, E, k, topk_ids, topk_w, counts, offsets, perm_src_token,
+                                                 perm_of_assignment, perm_weight, x, x_dtype, cols, g_in, g_out,
+                                                 codes, scales, ws, static_cast<hipStream_t>(stream)),
+                    "moe_route_quantize_noalloc");
 }
 
 // ------------------------------------------------------------------ grouped GEMM

@@ -165,6 +165,27 @@ int moe_route_quantize(const float* logits, int32_t T, int32_t E, int32_t k,
                        uint8_t* codes, uint8_t* scales,
                        void* workspace, size_t workspace_bytes, void* stream);
 
+/* ---------------------------------------------------------------- route + quantise, no allocation
+ * For callers that cannot allocate device memory or pass a workspace: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  Same arguments, kernels and bit-identical outputs as
+ * moe_route_quantize, minus the workspace: the scratch comes from one fixed
+ * block of device memory that the library holds on each GPU it runs on until
+ * the process ends (moe_route_quantize_noalloc_max_workspace() bytes, 4 MiB).
+ * A call whose moe_route_quantize_workspace_size(T, E, k) exceeds that block
+ * returns NVFP4MOE_ERR_UNSUPPORTED (about T*k <= 900k at E = 256).  Nothing is
+ * allocated: the device address of the block is looked up once per device, on
+ * the first call with that device current.  Every call on one GPU shares the
+ * block, so calls that overlap on one GPU (concurrent streams, or threads)
+ * race and must be serialised by the caller.  Other errors as for
+ * moe_route_quantize. */
+size_t moe_route_quantize_noalloc_max_workspace(void);
+int moe_route_quantize_noalloc(const float* logits, int32_t T, int32_t E, int32_t k,
+                               int32_t* topk_ids, float* topk_w, int32_t* counts, int32_t* offsets,
+                               int32_t* perm_src_token, int32_t* perm_of_assignment, float* perm_weight,
+                               const void* x, int32_t x_dtype, int64_t cols, const float* g_in, float* g_out,
+                               uint8_t* codes, uint8_t* scales, void* stream);
+
 /* ---------------------------------------------------------------- grouped GEMM
  * For expert e and GEMM row p in [offsets[e], offsets[e+1]) with A row
  * r = a_rows ? a_rows[p] : p:

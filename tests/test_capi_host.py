@@ -178,3 +178,24 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     with pytest.raises(ImportError):
         m.lib()
 
+
+def test_route_quantize_noalloc_validation():
+    # the no-allocation variant checks the same arguments, and rejects a
+    # problem whose scratch exceeds the library's fixed per-device block,
+    # all before touching a device
+    L = m.lib()
+    cap = L.moe_route_quantize_noalloc_max_workspace()
+    assert cap == 4 << 20
+
+    def call(logits=FAKE, T=16, E=8, k=2, cols=64, x=FAKE):
+        return L.moe_route_quantize_noalloc(logits, T, E, k, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, x, m.BF16,
+                                            cols, None, None, FAKE, FAKE, None)
+    assert call(logits=None) == m.ERR_INVALID
+    assert call(k=9, E=8) == m.ERR_INVALID
+    assert call(cols=48) == m.ERR_INVALID
+    assert call(x=FAKE + 8) == m.ERR_INVALID
+    T_big = 200_000
+    assert L.moe_route_quantize_workspace_size(T_big, 256, 8) > cap
+    assert call(T=T_big, E=256, k=8) == m.ERR_UNSUPPORTED
+    assert b"scratch" in L.nvfp4moe_last_error_detail()
+    assert L.moe_route_quantize_workspace_size(16384, 256, 8) <= cap      # the prefill workload fits
