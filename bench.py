@@ -4,8 +4,9 @@
 One step = one forward of the whole hot path on one batch: route + permute and
 NVFP4 quantisation of the activations (one call whose kernels share launches),
 gate_up grouped GEMM with the fused
-SwiGLU + re-quantisation, down grouped GEMM (bf16 rows), weighted gather
-combine to bf16 token order.  Default workload: the decode MoE at
+SwiGLU + re-quantisation and down grouped GEMM (bf16 rows) through
+moe_expert_ffn (one persistent launch at 32-127 rows per expert, the default
+workload's 64), weighted gather combine to bf16 token order.  Default workload: the decode MoE at
 16-64 tokens per expert (T=2048, H=6144, I=256, E=256, top-8, Zipf-skewed
 routing), seeded synthetic inputs, weights drawn N(0, 0.02) and quantised to
 NVFP4 on the GPU and repacked into the streaming tile layout (untimed).  Two
@@ -42,6 +43,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", type=int, default=2,
                     help="workload index: 0..3 MoE layers (2 is the reported one), 4 the dense 8192^3 GEMM")
+    ap.add_argument("--ffn", choices=["one_launch", "two_launch"], default="one_launch",
+                    help="gate_up + down through moe_expert_ffn (one persistent launch at decode sizes) or the two "
+                         "grouped-GEMM calls")
     ap.add_argument("--swiglu", choices=["fused", "separate"], default="fused",
                     help="SwiGLU + requant in the gate_up epilogue, or a separate call")
     ap.add_argument("--combine", choices=["gather", "atomic"], default="gather",
@@ -69,7 +73,7 @@ def copy_calibration(mib: int):
 
 def gemm_source_hash() -> str:
     h = hashlib.sha256()
-    for f in ("grouped_gemm.hip", "nvfp4_device.h"):
+    for f in ("grouped_gemm.hip", "gemm_device.h", "moe_ffn.hip", "nvfp4_device.h"):
         with open(os.path.join(ROOT, "block_scaled_fp4_permute_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -296,7 +300,11 @@ def main():
     del y1
     torch.cuda.synchronize()
 
-    layer = MoELayer(T, H, I, E, k, dev, swiglu=args.swiglu, combine=args.combine)
+    layer = MoELayer(T, H, I, E, k, dev, swiglu=args.swiglu, combine=args.combine, ffn=args.ffn)
+    one_call = layer.ffn == "one_launch"
+    # moe_expert_ffn's tile table: one persistent launch from 32 to 127 rows
+    # per expert, the two grouped-GEMM launches outside that range
+    one_launch = one_call and 32 <= (T * k) // E < 128
     for i in range(args.warmup):
         layer.forward(logits, x, copies[i % 2], g_h)
     torch.cuda.synchronize()
@@ -305,9 +313,13 @@ def main():
     # gate_up launch on the launch stream (its live average duration); the
     # step time is the first event to the last.
     # routing and the quantisation of x share launches (one call): one stage
-    names = ["route_permute+quantize_x", None, "gate_up_swiglu",
-             "down" if args.combine == "gather" else "down_scatter_add",
-             "combine" if args.combine == "gather" else "to_bf16"]
+    if one_call:
+        names = ["route_permute+quantize_x", None,
+                 "expert_ffn_one_launch" if one_launch else "expert_ffn_two_launches", None, "combine"]
+    else:
+        names = ["route_permute+quantize_x", None, "gate_up_swiglu",
+                 "down" if args.combine == "gather" else "down_scatter_add",
+                 "combine" if args.combine == "gather" else "to_bf16"]
 
     def ev():
         return torch.cuda.Event(enable_timing=True)
@@ -340,12 +352,18 @@ def main():
     gbs = weight_bytes / (ms_per_step * 1e-3) / 1e9
     tflops = flops / (ms_per_step * 1e-3) / 1e12
 
-    # dominant kernel: gate_up GEMM.  Algorithmic bytes per launch = touched
-    # gate_up weights + the NVFP4 activations read once + the NVFP4 h written.
+    # dominant kernel.  Algorithmic bytes per launch: gate_up = touched gate_up
+    # weights + the NVFP4 activations read once + the NVFP4 h written; down =
+    # touched down weights + h read + the bf16 rows written.  The one-launch
+    # FFN kernel does both; its bracket also holds the small planning kernel
+    # launched with it (so the rate is, if anything, understated).
     gu_alg = touched * gu_bytes_e + T * H * 9 // 16 + T * k * I * 9 // 16
-    achieved = gu_alg / (gu_ms * 1e-3) / 1e9
+    dn_alg = touched * dn_bytes_e + T * k * I * 9 // 16 + T * k * H * 2
+    alg = gu_alg + dn_alg if one_call else gu_alg
+    achieved = alg / (gu_ms * 1e-3) / 1e9
     wl_name = f"{'decode' if T <= 2048 else 'prefill'}_moe_T{T}_H{H}_I{I}_E{E}_top{k}_{cfg.routing}"
-    traffic = measured_traffic("gate_up_swiglu", wl_name) if args.swiglu == "fused" else None
+    tkey = "expert_ffn_one_launch" if one_launch else "expert_ffn_two_launches" if one_call else "gate_up_swiglu"
+    traffic = measured_traffic(tkey, wl_name) if args.swiglu == "fused" else None
 
     res = {
         "metric": "NVFP4 MoE grouped-GEMM TFLOPS & weight GB/s at 16-64 tok/expert, 1 MI355X",
@@ -362,7 +380,7 @@ def main():
         "dtype": "nvfp4 operands, f16 mfma, f32 accumulate",
         "data": "synthetic",
         "tflops": round(tflops, 3),
-        "gemm_weight_gbs": round(weight_bytes / ((stage_ms[names[2]] + stage_ms[names[3]]) * 1e-3) / 1e9, 2),
+        "gemm_weight_gbs": round(weight_bytes / (sum(stage_ms[n] for n in names[2:4] if n) * 1e-3) / 1e9, 2),
         "tflops_frac_f16_peak": round(tflops / MFMA_F16_PEAK_TFLOPS, 4),
         "weight_bytes": weight_bytes,
         "layer_flops": flops,
@@ -370,12 +388,15 @@ def main():
         "tokens_per_expert": {"min": int(counts.min()), "median": float(np.median(counts)),
                               "max": int(counts.max()), "touched_experts": touched},
         "config": {"workload": wl_name, "T": T, "H": H, "I": I, "E": E, "top_k": k, "routing": cfg.routing,
-                   "swiglu": args.swiglu, "combine": args.combine, "weight_layout": "packed tiles",
+                   "ffn": layer.ffn, "swiglu": args.swiglu, "combine": args.combine, "weight_layout": "packed tiles",
                    "weight_copies": 2},
-        "roofline": {"kernel": "nvfp4 grouped GEMM gate_up + SwiGLU/requant epilogue", "bound": "hbm",
-                     "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+        "roofline": {"kernel": ("k_moe_ffn: gate_up + SwiGLU/requant + down grouped GEMMs, one persistent launch"
+                                if one_launch else
+                                "moe_expert_ffn: gate_up + SwiGLU/requant and down grouped GEMMs, two launches"
+                                if one_call else "nvfp4 grouped GEMM gate_up + SwiGLU/requant epilogue"),
+                     "bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                     "alg_bytes_per_launch": gu_alg, "avg_launch_ms": round(gu_ms, 5)},
+                     "alg_bytes_per_launch": alg, "avg_launch_ms": round(gu_ms, 5)},
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:

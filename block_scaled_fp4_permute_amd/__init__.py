@@ -8,8 +8,10 @@ eager-PyTorch fallback, and importing a function whose library is missing
 raises.
 
 C entry points (include/nvfp4moe.h): moe_route_permute, nvfp4_quantize,
-nvfp4_grouped_gemm, moe_swiglu, moe_unpermute_combine, and moe_route_quantize
-(routing and activation quantisation in shared launches).
+nvfp4_grouped_gemm, moe_swiglu, moe_unpermute_combine, moe_route_quantize
+(routing and activation quantisation in shared launches) and moe_expert_ffn
+(gate_up + SwiGLU requant + down for all experts, one persistent launch at
+decode sizes).
 """
 from __future__ import annotations
 
@@ -30,6 +32,19 @@ class NVFP4MoEError(RuntimeError):
         super().__init__(f"nvfp4moe status {status}: {detail}")
         self.status = status
         self.detail = detail
+
+
+class FfnArgs(ctypes.Structure):
+    """Mirror of nvfp4moe_ffn_args."""
+    _fields_ = [
+        ("x_codes", ctypes.c_void_p), ("x_scales", ctypes.c_void_p), ("x_g", ctypes.c_void_p),
+        ("x_rows", ctypes.c_int64), ("perm_src_token", ctypes.c_void_p), ("offsets", ctypes.c_void_p),
+        ("E", ctypes.c_int32), ("H", ctypes.c_int32), ("I", ctypes.c_int32), ("m_total", ctypes.c_int64),
+        ("w_gu_packed", ctypes.c_void_p), ("g_gu", ctypes.c_void_p),
+        ("w_dn_packed", ctypes.c_void_p), ("g_dn", ctypes.c_void_p), ("g_h", ctypes.c_void_p),
+        ("h_codes", ctypes.c_void_p), ("h_scales", ctypes.c_void_p), ("y", ctypes.c_void_p),
+        ("max_rows_per_expert_hint", ctypes.c_int32),
+    ]
 
 
 class GemmArgs(ctypes.Structure):
@@ -76,6 +91,9 @@ _SIGNATURES = {
     "moe_route_quantize_noalloc": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32]
                                    + [ctypes.c_void_p] * 7 + [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64]
                                    + [ctypes.c_void_p] * 4 + [ctypes.c_void_p]),
+    "moe_expert_ffn_workspace_size": (ctypes.c_size_t, [ctypes.c_int32, ctypes.c_int64, ctypes.c_int32,
+                                                        ctypes.c_int32]),
+    "moe_expert_ffn": (ctypes.c_int, [ctypes.POINTER(FfnArgs), ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
     "nvfp4moe_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "nvfp4moe_last_error_detail": (ctypes.c_char_p, []),
     "nvfp4moe_version": (ctypes.c_int, []),
@@ -350,6 +368,60 @@ def nvfp4_grouped_gemm(a: NVFP4Tensor, b_codes, b_scales, b_g, offsets, *, m_tot
     return out
 
 
+# ---------------------------------------------------------------------- expert FFN
+def moe_expert_ffn_workspace(E: int, m_total: int, H: int, I: int, device):
+    import torch
+    n = lib().moe_expert_ffn_workspace_size(E, m_total, H, I)
+    return torch.empty(max(n, 256), dtype=torch.uint8, device=device)
+
+
+def moe_expert_ffn(xq: NVFP4Tensor, perm_src_token, offsets, w_gu_packed, g_gu, w_dn_packed, g_dn, g_h, *, H: int,
+                   I: int, m_total: int, h: NVFP4Tensor | None = None, y=None, workspace=None,
+                   max_rows_per_expert_hint: int = 0, stream=None):
+    """gate_up + SwiGLU/requant + down for all experts (see include/nvfp4moe.h):
+    returns (h NVFP4Tensor [m_total, I], y bf16 [m_total, H])."""
+    import torch
+    E = offsets.numel() - 1
+    dev = offsets.device
+    _need(xq.codes, torch.uint8, "x codes")
+    _need(xq.scales, torch.uint8, "x scales")
+    if tuple(xq.codes.shape[1:]) != (H // 2,) or tuple(xq.scales.shape) != (xq.codes.shape[0], H // 16):
+        raise ValueError("x codes/scales do not match H")
+    _need(perm_src_token, torch.int32, "perm_src_token")
+    _need(offsets, torch.int32, "offsets")
+    if perm_src_token.numel() < m_total:
+        raise ValueError("perm_src_token shorter than m_total")
+    for t, name, n in ((w_gu_packed, "w_gu_packed", lib().nvfp4_weight_packed_size(E, 2 * I, H)),
+                       (w_dn_packed, "w_dn_packed", lib().nvfp4_weight_packed_size(E, H, I))):
+        _need(t, torch.uint8, name)
+        if t.numel() < n:
+            raise ValueError(f"{name}: {t.numel()} bytes, the packed size is {n}")
+    for t, name, n in ((g_gu, "g_gu", E), (g_dn, "g_dn", E), (g_h, "g_h", 1)):
+        _need(t, torch.float32, name)
+        if t.numel() < n:
+            raise ValueError(f"{name}: needs {n} values")
+    if h is None:
+        h = NVFP4Tensor(torch.empty((m_total, I // 2), dtype=torch.uint8, device=dev),
+                        torch.empty((m_total, I // 16), dtype=torch.uint8, device=dev), g_h)
+    if tuple(h.codes.shape) != (m_total, I // 2) or tuple(h.scales.shape) != (m_total, I // 16):
+        raise ValueError("h codes/scales must be [m_total, I/2] and [m_total, I/16]")
+    if y is None:
+        y = torch.empty((m_total, H), dtype=torch.bfloat16, device=dev)
+    _need(y, torch.bfloat16, "y")
+    if tuple(y.shape) != (m_total, H):
+        raise ValueError("y must be bf16 [m_total, H]")
+    if workspace is None:
+        workspace = moe_expert_ffn_workspace(E, m_total, H, I, dev)
+    args = FfnArgs(x_codes=xq.codes.data_ptr(), x_scales=xq.scales.data_ptr(), x_g=xq.g.data_ptr(),
+                   x_rows=xq.codes.shape[0], perm_src_token=perm_src_token.data_ptr(), offsets=offsets.data_ptr(),
+                   E=E, H=H, I=I, m_total=m_total, w_gu_packed=w_gu_packed.data_ptr(), g_gu=g_gu.data_ptr(),
+                   w_dn_packed=w_dn_packed.data_ptr(), g_dn=g_dn.data_ptr(), g_h=g_h.data_ptr(),
+                   h_codes=h.codes.data_ptr(), h_scales=h.scales.data_ptr(), y=y.data_ptr(),
+                   max_rows_per_expert_hint=max_rows_per_expert_hint)
+    _check(lib().moe_expert_ffn(ctypes.byref(args), workspace.data_ptr(), workspace.numel(), _stream(stream)))
+    return NVFP4Tensor(h.codes, h.scales, g_h), y
+
+
 # -------------------------------------------------------------------------- swiglu
 def moe_swiglu(gate_up, g=None, out: NVFP4Tensor | None = None, workspace=None, stream=None) -> NVFP4Tensor:
     """gate_up float32/bf16 [M, 2I] -> NVFP4 h = silu(gate) * up."""
@@ -397,5 +469,5 @@ def moe_unpermute_combine(y, perm_of_assignment, topk_w, T: int, k: int, out=Non
 
 
 __all__ = ["lib", "moe_route_permute", "moe_route_quantize", "moe_route_quantize_noalloc", "nvfp4_quantize", "nvfp4_grouped_gemm", "moe_swiglu", "nvfp4_weight_repack",
-           "moe_unpermute_combine", "NVFP4Tensor", "Routing", "GemmArgs", "NVFP4MoEError",
+           "moe_unpermute_combine", "moe_expert_ffn", "moe_expert_ffn_workspace", "NVFP4Tensor", "Routing", "GemmArgs", "NVFP4MoEError",
            "F32", "BF16", "EPI_F32", "EPI_BF16", "EPI_SWIGLU_NVFP4", "EPI_COMBINE_F32"]

@@ -274,6 +274,92 @@ int nvfp4_grouped_gemm(const nvfp4moe_gemm_args* a, void* stream) {
                     "nvfp4_grouped_gemm");
 }
 
+// ------------------------------------------------------------------ expert FFN
+// The tile table of moe_expert_ffn by rows per expert (measured on MI355X,
+// T tokens x top-8 of 256 experts, H = 6144, I = 256):
+//   < 32    two launches, decode tile: at 8 rows per expert (T = 256) gate_up
+//           fills every workgroup slot in one round, so there is no tail for
+//           down tasks to fill (one launch 157 us, two launches 140 us)
+//   32..127 one persistent launch, decode tile: at 64 rows per expert (Zipf
+//           T = 2048) down tasks fill gate_up's light last round (266 us
+//           against 283 us for the two launches)
+//   >= 128  two launches, large-M tile (the MFMA-bound regime)
+static constexpr int kFfnMinRows = 32;
+static constexpr int kFfnLargeRows = 128;
+static constexpr int kFfnSpinLimit = 1 << 20; // about a second of waiting for one chunk's h rows
+
+size_t moe_expert_ffn_workspace_size(int32_t E, int64_t m_total, int32_t H, int32_t I) {
+  if (E <= 0 || m_total < 0 || H <= 0 || I <= 0) return 0;
+  return nvfp4::moe_ffn_ws_bytes(E, m_total, H, I);
+}
+
+int moe_expert_ffn(const nvfp4moe_ffn_args* a, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!a) return fail(NVFP4MOE_ERR_INVALID, "moe_expert_ffn: args is NULL");
+  if (!a->x_codes || !a->x_scales || !a->x_g || !a->perm_src_token || !a->offsets || !a->w_gu_packed ||
+      !a->g_gu || !a->w_dn_packed || !a->g_dn || !a->g_h || !a->h_codes || !a->h_scales || !a->y)
+    return fail(NVFP4MOE_ERR_INVALID, "moe_expert_ffn: null pointer argument");
+  if (a->E <= 0 || a->H <= 0 || a->I <= 0 || a->m_total < 0 || a->x_rows <= 0)
+    return fail(NVFP4MOE_ERR_INVALID, "moe_expert_ffn: E, H, I, x_rows must be > 0 and m_total >= 0");
+  if (a->H % 32 != 0 || a->I % 16 != 0)
+    return fail(NVFP4MOE_ERR_INVALID, "moe_expert_ffn: H=%d must be a multiple of 32 and I=%d of 16", a->H, a->I);
+  if (a->I % 32 != 0 || a->I > 256)
+    return fail(NVFP4MOE_ERR_UNSUPPORTED, "moe_expert_ffn: I=%d: the down GEMM runs one K step (I <= 256, I %% 32 == 0)",
+                a->I);
+  if (!aligned(a->x_codes, 16) || !aligned(a->x_scales, 2) || !aligned(a->w_gu_packed, 16) ||
+      !aligned(a->w_dn_packed, 16) || !aligned(a->h_codes, 16) || !aligned(a->h_scales, 2) || !aligned(a->y, 16))
+    return fail(NVFP4MOE_ERR_INVALID, "moe_expert_ffn: misaligned pointer");
+  if (a->m_total >= (int64_t(1) << 31) || a->x_rows >= (int64_t(1) << 31) ||
+      a->x_rows * (int64_t(a->H) / 2) >= (int64_t(1) << 31) || a->m_total * (int64_t(a->I) / 2) >= (int64_t(1) << 31))
+    return fail(NVFP4MOE_ERR_UNSUPPORTED, "moe_expert_ffn: operands of 2 GiB or more");
+  if (static_cast<int64_t>(a->E) * a->H >= (int64_t(1) << 31))
+    return fail(NVFP4MOE_ERR_UNSUPPORTED, "moe_expert_ffn: E*H >= 2^31");
+  if (a->E > 4096) return fail(NVFP4MOE_ERR_UNSUPPORTED, "moe_expert_ffn: E=%d > 4096", a->E);
+  const size_t need = nvfp4::moe_ffn_ws_bytes(a->E, a->m_total, a->H, a->I);
+  if (!workspace || workspace_bytes < need)
+    return fail(NVFP4MOE_ERR_WORKSPACE, "moe_expert_ffn: workspace %zu < %zu bytes", workspace_bytes, need);
+  if (!aligned(workspace, 256)) return fail(NVFP4MOE_ERR_INVALID, "moe_expert_ffn: workspace not 256-byte aligned");
+  if (a->m_total == 0) return ok();
+  nvfp4::GemmParams gu{};
+  gu.a_codes = a->x_codes;
+  gu.a_scales = a->x_scales;
+  gu.a_g = a->x_g;
+  gu.a_rows = a->perm_src_token;
+  gu.b_packed = a->w_gu_packed;
+  gu.b_g = a->g_gu;
+  gu.offsets = a->offsets;
+  gu.E = a->E;
+  gu.N = 2 * a->I;
+  gu.K = a->H;
+  gu.m_total = static_cast<int>(a->m_total);
+  gu.a_rows_total = static_cast<int>(a->x_rows);
+  gu.out_codes = a->h_codes;
+  gu.out_scales = a->h_scales;
+  gu.out_g = a->g_h;
+  nvfp4::GemmParams dn{};
+  dn.a_codes = a->h_codes;
+  dn.a_scales = a->h_scales;
+  dn.a_g = a->g_h;
+  dn.b_packed = a->w_dn_packed;
+  dn.b_g = a->g_dn;
+  dn.offsets = a->offsets;
+  dn.E = a->E;
+  dn.N = a->H;
+  dn.K = a->I;
+  dn.m_total = static_cast<int>(a->m_total);
+  dn.a_rows_total = static_cast<int>(a->m_total);
+  dn.out = a->y;
+  const int64_t rows_per_expert = a->max_rows_per_expert_hint > 0 ? a->max_rows_per_expert_hint : a->m_total / a->E;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (rows_per_expert < kFfnMinRows || rows_per_expert >= kFfnLargeRows) {
+    hipError_t err = nvfp4::launch_grouped_gemm(gu, nvfp4::EPI_SWIGLU, a->m_total, a->max_rows_per_expert_hint, s);
+    if (err != hipSuccess) return hip_status(err, "moe_expert_ffn (gate_up)");
+    return hip_status(nvfp4::launch_grouped_gemm(dn, nvfp4::EPI_BF16, a->m_total, a->max_rows_per_expert_hint, s),
+                      "moe_expert_ffn (down)");
+  }
+  return hip_status(nvfp4::launch_moe_ffn(gu, dn, a->m_total, rows_per_expert >= 64, workspace, kFfnSpinLimit, s),
+                    "moe_expert_ffn");
+}
+
 // ------------------------------------------------------------------ packed weights
 size_t nvfp4_weight_packed_size(int32_t E, int32_t N, int32_t K) {
   if (E <= 0 || N <= 0 || K <= 0) return 0;

@@ -4,8 +4,13 @@ route + permute -> quantise x -> gate_up grouped GEMM (rows gathered by token)
 -> SwiGLU + NVFP4 re-quantisation -> down grouped GEMM -> weighted combine back
 to token order, bfloat16 out.
 
-Two independent choices:
-  swiglu="fused"   (default) the gate_up GEMM epilogue computes SwiGLU and
+Choices:
+  ffn="one_launch" (default) gate_up + SwiGLU/requant + down through
+                   moe_expert_ffn: one persistent launch at decode sizes (down
+                   tasks start as soon as their chunk's h rows exist), the two
+                   grouped-GEMM launches from 128 rows per expert on;
+  ffn="two_launch" the two grouped-GEMM calls, with the choices below;
+  swiglu="fused"   (two_launch) the gate_up GEMM epilogue computes SwiGLU and
                    writes NVFP4 h directly;
   swiglu="separate" float32 gate_up output, then moe_swiglu;
   combine="gather" (default) the down GEMM writes bf16 rows, then
@@ -24,8 +29,8 @@ from dataclasses import dataclass
 import torch
 
 from . import (BF16, EPI_BF16, EPI_COMBINE_F32, EPI_F32, EPI_SWIGLU_NVFP4, F32, NVFP4Tensor, Routing, lib,
-               moe_route_permute, moe_route_quantize, moe_swiglu, moe_unpermute_combine, nvfp4_grouped_gemm,
-               nvfp4_quantize, nvfp4_weight_repack)
+               moe_expert_ffn, moe_expert_ffn_workspace, moe_route_permute, moe_route_quantize, moe_swiglu,
+               moe_unpermute_combine, nvfp4_grouped_gemm, nvfp4_quantize, nvfp4_weight_repack)
 
 
 @dataclass
@@ -86,10 +91,13 @@ class MoELayer:
     """Preallocated NVFP4 MoE layer for T tokens."""
 
     def __init__(self, T: int, H: int, I: int, E: int, k: int, device, swiglu: str = "fused",
-                 combine: str = "gather"):
+                 combine: str = "gather", ffn: str = "one_launch"):
         assert swiglu in ("fused", "separate") and combine in ("gather", "atomic")
+        assert ffn in ("one_launch", "two_launch")
+        if ffn == "one_launch" and (swiglu, combine) != ("fused", "gather"):
+            ffn = "two_launch"     # the one-launch FFN has the fused SwiGLU and bf16 rows
         self.T, self.H, self.I, self.E, self.k = T, H, I, E, k
-        self.swiglu, self.combine = swiglu, combine
+        self.swiglu, self.combine, self.ffn = swiglu, combine, ffn
         dev = torch.device(device)
         i32 = dict(dtype=torch.int32, device=dev)
         f32 = dict(dtype=torch.float32, device=dev)
@@ -110,6 +118,8 @@ class MoELayer:
             self.acc = torch.empty((T, H), **f32)
         else:
             self.y2 = torch.empty((M, H), dtype=torch.bfloat16, device=dev)
+        if self.ffn == "one_launch":
+            self.ffn_ws = moe_expert_ffn_workspace(E, M, H, I, dev)
 
     def forward(self, logits: torch.Tensor, x: torch.Tensor, w: ExpertWeights, g_h: torch.Tensor,
                 stream=None, marks=None) -> torch.Tensor:
@@ -117,7 +127,8 @@ class MoELayer:
         entries) recorded on the launch stream before routing and after each
         stage: route+permute and the quantisation of x (one call whose kernels
         share launches; marks 1 and 2 both follow it), gate_up, down,
-        to-bf16/combine."""
+        to-bf16/combine.  With the one-launch FFN, marks 3 and 4 both follow
+        the gate_up + down call."""
         T, k, M = self.T, self.k, self.T * self.k
         hq = NVFP4Tensor(self.hq.codes, self.hq.scales, g_h)
 
@@ -129,6 +140,14 @@ class MoELayer:
         r, _ = moe_route_quantize(logits, k, x, out=self.routing, xq=self.xq, workspace=self.route_ws, stream=stream)
         mark(1)
         mark(2)
+        if self.ffn == "one_launch" and w.gu_packed is not None and w.dn_packed is not None:
+            moe_expert_ffn(self.xq, r.perm_src_token, r.offsets, w.gu_packed, w.gu_g, w.dn_packed, w.dn_g, g_h,
+                           H=self.H, I=self.I, m_total=M, h=hq, y=self.y2, workspace=self.ffn_ws, stream=stream)
+            mark(3)
+            mark(4)
+            moe_unpermute_combine(self.y2, r.perm_of_assignment, r.topk_w, T, k, out=self.out, stream=stream)
+            mark(5)
+            return self.out
         if self.swiglu == "fused":
             nvfp4_grouped_gemm(self.xq, w.gu_codes, w.gu_scales, w.gu_g, r.offsets, m_total=M,
                                a_rows=r.perm_src_token, epilogue=EPI_SWIGLU_NVFP4, out_codes=self.hq.codes,

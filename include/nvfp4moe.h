@@ -202,6 +202,66 @@ int moe_route_quantize_noalloc(const float* logits, int32_t T, int32_t E, int32_
  * 2^31 rows. */
 int nvfp4_grouped_gemm(const nvfp4moe_gemm_args* args, void* stream);
 
+/* ---------------------------------------------------------------- expert FFN in one call
+ * gate_up grouped GEMM + SwiGLU + NVFP4 requantisation of h, then the down
+ * grouped GEMM, for all experts: the two nvfp4_grouped_gemm calls of the
+ * layer (EPI_SWIGLU_NVFP4 on gathered x rows, then EPI_BF16 on h), with the
+ * same results bit for bit.  From 32 to 127 rows per expert (the hint, else
+ * m_total / E) both run in ONE persistent launch whose down tasks start as soon
+ * as the gate_up tasks of their row chunk are done, filling the slots the light
+ * chunks leave free ("From Empirical Limits ...", section "Sections 5-6:
+ * Algorithmic Techniques": adaptive grid sizing; section "Key Findings and
+ * Their Impact": fusion; "Discovering SM120-Specific CUTLASS MoE Kernels",
+ * section "The Discovery": a min-latency kernel for small batches, tuned to the
+ * expected tokens).  The tile table, by rows per expert (measured):
+ *   < 32       two launches, decode tile, non-temporal weight loads (gate_up
+ *              fills every slot in one round: no tail to fill)
+ *   32 .. 63   one launch, decode tile, non-temporal weight loads
+ *   64 .. 127  one launch, decode tile, cached weight loads
+ *   >= 128     two launches, large-M tile, cached weight loads (MFMA-bound)
+ * Arguments (device pointers):
+ *   x_codes/x_scales/x_g   NVFP4 activations [x_rows, H/2], [x_rows, H/16], g
+ *   perm_src_token         [m_total]: x row of GEMM row p (moe_route_permute)
+ *   offsets                [E+1] expert offsets (moe_route_permute)
+ *   w_gu_packed, g_gu      gate_up weights [E, 2I, H] repacked by
+ *                          nvfp4_weight_repack, per-expert scales [E]
+ *   w_dn_packed, g_dn      down weights [E, H, I] repacked, scales [E]
+ *   g_h                    per-tensor scale of h (1 float)
+ *   h_codes, h_scales      (out) h [m_total, I/2], [m_total, I/16]
+ *   y                      (out) bf16 [m_total, H], the down rows (then
+ *                          moe_unpermute_combine)
+ * I % 32 == 0, I <= 256 (one K step of the down GEMM), H % 32 == 0, E <= 4096.
+ * workspace: moe_expert_ffn_workspace_size(E, m_total, H, I) bytes, 256-byte
+ * aligned, caller-owned; it holds the task lists and chunk counters, which the
+ * call rewrites (a planning kernel, no memset).  Its first 64 int32 words are a
+ * header; word 8 is nonzero after a launch in which a down task stopped waiting
+ * for its h rows past a bounded spin (a fault of the scheduling, never expected:
+ * the results of that launch are then invalid).  Calls sharing a workspace must
+ * not overlap. */
+typedef struct nvfp4moe_ffn_args {
+  const uint8_t* x_codes;
+  const uint8_t* x_scales;
+  const float* x_g;
+  int64_t x_rows;
+  const int32_t* perm_src_token;
+  const int32_t* offsets;
+  int32_t E;
+  int32_t H;
+  int32_t I;
+  int64_t m_total;
+  const uint8_t* w_gu_packed;
+  const float* g_gu;
+  const uint8_t* w_dn_packed;
+  const float* g_dn;
+  const float* g_h;
+  uint8_t* h_codes;
+  uint8_t* h_scales;
+  void* y;
+  int32_t max_rows_per_expert_hint;
+} nvfp4moe_ffn_args;
+size_t moe_expert_ffn_workspace_size(int32_t E, int64_t m_total, int32_t H, int32_t I);
+int moe_expert_ffn(const nvfp4moe_ffn_args* args, void* workspace, size_t workspace_bytes, void* stream);
+
 /* ---------------------------------------------------------------- packed weights
  * Weights are static, so they can be repacked once into a tile layout that the
  * grouped GEMM streams with fully contiguous, non-temporal loads: tile

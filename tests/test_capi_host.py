@@ -199,3 +199,34 @@ def test_route_quantize_noalloc_validation():
     assert call(T=T_big, E=256, k=8) == m.ERR_UNSUPPORTED
     assert b"scratch" in L.nvfp4moe_last_error_detail()
     assert L.moe_route_quantize_workspace_size(16384, 256, 8) <= cap      # the prefill workload fits
+
+
+def _ffn_args(**over):
+    a = m.FfnArgs(x_codes=FAKE, x_scales=FAKE, x_g=FAKE, x_rows=64, perm_src_token=FAKE, offsets=FAKE, E=8, H=512,
+                  I=256, m_total=128, w_gu_packed=FAKE, g_gu=FAKE, w_dn_packed=FAKE, g_dn=FAKE, g_h=FAKE,
+                  h_codes=FAKE, h_scales=FAKE, y=FAKE, max_rows_per_expert_hint=0)
+    for k_, v in over.items():
+        setattr(a, k_, v)
+    return a
+
+
+def test_expert_ffn_validation():
+    L = m.lib()
+    need = L.moe_expert_ffn_workspace_size(8, 128, 512, 256)
+    assert need > 0 and L.moe_expert_ffn_workspace_size(0, 128, 512, 256) == 0
+
+    def call(ws=FAKE, ws_bytes=None, **over):
+        return L.moe_expert_ffn(ctypes.byref(_ffn_args(**over)), ws, need if ws_bytes is None else ws_bytes, None)
+    assert L.moe_expert_ffn(None, FAKE, need, None) == m.ERR_INVALID
+    assert call(x_codes=None) == m.ERR_INVALID
+    assert call(y=None) == m.ERR_INVALID
+    assert call(E=0) == m.ERR_INVALID
+    assert call(H=500) == m.ERR_INVALID
+    assert call(I=24) == m.ERR_INVALID
+    assert call(I=512) == m.ERR_UNSUPPORTED          # down GEMM is one K step
+    assert call(E=5000) == m.ERR_UNSUPPORTED
+    assert call(x_codes=FAKE_MIS) == m.ERR_INVALID
+    assert call(ws_bytes=need - 1) == m.ERR_WORKSPACE
+    assert call(ws=None) == m.ERR_WORKSPACE
+    assert call(ws=FAKE + 16) == m.ERR_INVALID         # workspace must be 256-byte aligned
+    assert call(m_total=0) == m.OK                     # nothing to do, nothing enqueued
