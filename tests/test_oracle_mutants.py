@@ -193,3 +193,49 @@ ORIG_GEMM = M.grouped_gemm
 ORIG_ROUTE = M.route
 ORIG_COMBINE = M.combine
 ORIG_PERMUTE = M.permute
+
+
+# ------------------------------------------------------------------ MXFP4 oracle
+import oracle.mx as MXO
+import tests.test_oracle_mx as TMX
+
+
+def test_mutant_mx_exponent_off_by_one(monkeypatch):
+    orig = MXO.mx_shared_exponent
+    monkeypatch.setattr(MXO, "mx_shared_exponent", lambda a: np.clip(orig(a) + 1, -127, 127))
+    assert _fails(TMX.test_worked_block_by_hand)
+
+
+def test_mutant_mx_e8m0_bias(monkeypatch):
+    monkeypatch.setattr(MXO, "E8M0_BIAS", 128)
+    assert _fails(TMX.test_e8m0_closed_form_and_library)
+
+
+def test_mutant_mx_ties_away_from_zero(monkeypatch):
+    def bad(v):
+        v = np.minimum(np.asarray(v, np.float64), 6.0)
+        d = np.abs(v[..., None] - F.E2M1_MAGNITUDES)
+        return (7 - np.argmin(d[..., ::-1], axis=-1)).astype(np.uint8)
+    monkeypatch.setattr(MXO, "e2m1_encode_magnitude", bad)
+    assert _fails(TMX.test_worked_block_by_hand)
+
+
+def test_mutant_mx_gemm_drops_b_block_scale(monkeypatch):
+    orig = MXO.mx_dequantize
+
+    def bad(codes, scales):
+        return orig(codes, np.full_like(scales, 127) if codes.ndim == 2 and codes.shape[0] == 5 else scales)
+    monkeypatch.setattr(MXO, "mx_dequantize", bad)
+    assert _fails(TMX.test_mx_gemm_equals_exact_rational, 0)
+
+
+def test_mutant_mx_zero_block_keeps_sign(monkeypatch):
+    orig = MXO.mx_quantize
+
+    def bad(x):
+        codes, scales = orig(x)
+        q = Q.unpack_codes(codes)
+        q[np.signbit(np.asarray(x, np.float32)) & (np.asarray(x) == 0)] |= 8
+        return Q.pack_codes(q), scales
+    monkeypatch.setattr(MXO, "mx_quantize", bad)
+    assert _fails(TMX.test_quantiser_invariants)
