@@ -34,6 +34,8 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense FP16/BF16 MFMA, published
+MFMA_FP8_PEAK_TFLOPS = 5000.0  # MI355X dense FP8 MFMA, published
+MFMA_FP4_PEAK_TFLOPS = 10100.0  # MI355X dense FP4/FP6 MFMA, published
 
 
 def parse():
@@ -46,6 +48,9 @@ def parse():
     ap.add_argument("--ffn", choices=["one_launch", "two_launch"], default="one_launch",
                     help="gate_up + down through moe_expert_ffn (one persistent launch at decode sizes) or the two "
                          "grouped-GEMM calls")
+    ap.add_argument("--format", choices=["nvfp4", "mxfp4"], default="nvfp4",
+                    help="number format: NVFP4 (the reported one) or the MXFP4 variant (E8M0 scale per 32, "
+                         "gfx950's block-scaled FP4 MFMA)")
     ap.add_argument("--swiglu", choices=["fused", "separate"], default="fused",
                     help="SwiGLU + requant in the gate_up epilogue, or a separate call")
     ap.add_argument("--combine", choices=["gather", "atomic"], default="gather",
@@ -238,6 +243,111 @@ def oracle_only(args):
                       "top_k": cfg.k, "threads_requested": args.oracle_threads or "all", **res}), flush=True)
 
 
+def mx_bench(cfg, args):
+    """The MXFP4 variant (secondary measurements, not the reported metric):
+    the MoE layer step on the MoE workloads (route + permute, MXFP4 quantise
+    of x, gate_up with fused SwiGLU + MXFP4 requant, down, combine), or the
+    dense GEMM.  Roofline of the gate_up kernel against HBM (MoE) or of the
+    GEMM against the dense FP4 MFMA peak (dense)."""
+    import numpy as np
+    import torch
+
+    from block_scaled_fp4_permute_amd import EPI_BF16, lib, mxfp4_grouped_gemm, mxfp4_quantize
+    from block_scaled_fp4_permute_amd.layer import MXMoELayer, quantize_expert_weights_mx
+
+    lib()
+    dev = torch.device("cuda:0")
+    wl = workloads_mod()
+
+    def ev():
+        return torch.cuda.Event(enable_timing=True)
+
+    if cfg.dense:
+        M, N, K = cfg.T, cfg.H, cfg.I
+        a32, b32 = wl.torch_dense_operands(cfg, dev)
+        aq, bq = mxfp4_quantize(a32), mxfp4_quantize(b32)
+        del a32, b32
+        from block_scaled_fp4_permute_amd import MXFP4Tensor
+        from block_scaled_fp4_permute_amd import mxfp4_weight_repack
+        b3 = MXFP4Tensor(bq.codes.view(1, N, K // 2), bq.scales.view(1, N, K // 32))
+        b3p = mxfp4_weight_repack(b3)
+        offsets = torch.tensor([0, M], dtype=torch.int32, device=dev)
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+
+        def run():
+            mxfp4_grouped_gemm(aq, b3, offsets, m_total=M, epilogue=EPI_BF16, out=out, max_rows_per_expert_hint=M,
+                               b_packed=b3p)
+        for _ in range(args.warmup):
+            run()
+        torch.cuda.synchronize()
+        t0, t1 = ev(), ev()
+        t0.record()
+        for _ in range(args.steps):
+            run()
+        t1.record()
+        torch.cuda.synchronize()
+        ms = t0.elapsed_time(t1) / args.steps
+        tflops = 2.0 * M * N * K / (ms * 1e-3) / 1e12
+        print(json.dumps({
+            "metric": "dense MXFP4 GEMM TFLOP/s (secondary: gfx950 block-scaled FP4 MFMA)", "value": round(tflops, 1),
+            "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+            "higher_is_better": True, "vs_baseline": None, "dtype": "mxfp4 operands, fp4 scaled mfma, f32 accumulate",
+            "data": "synthetic", "config": {"workload": f"dense_gemm_M{M}_N{N}_K{K}", "format": "mxfp4", "out": "bf16"},
+            "roofline": {"kernel": "k_mx_gemm", "bound": "mfma", "achieved": round(tflops, 1),
+                         "peak": MFMA_FP4_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(tflops / MFMA_FP4_PEAK_TFLOPS, 4),
+                         "traffic": None}}), flush=True)
+        return
+
+    T, H, I, E, k = cfg.T, cfg.H, cfg.I, cfg.E, cfg.k
+    logits = torch.from_numpy(wl.logits(cfg)).to(dev)
+    x = torch.from_numpy(wl.activations(cfg)).to(dev).to(torch.bfloat16)
+    copies = []
+    for c in range(2):
+        w_gu, w_dn = wl.torch_expert_weights(cfg, dev, copy=c)
+        copies.append(quantize_expert_weights_mx(w_gu, w_dn))
+        del w_gu, w_dn
+    layer = MXMoELayer(T, H, I, E, k, dev)
+    for i in range(args.warmup):
+        layer.forward(logits, x, copies[i % 2])
+    torch.cuda.synchronize()
+    counts = layer.routing.counts.cpu().numpy()
+    t_start, t_end = ev(), ev()
+    gu_marks = [[None, None, ev(), ev(), None, None] for _ in range(args.steps)]
+    t_start.record()
+    for i in range(args.steps):
+        layer.forward(logits, x, copies[i % 2], marks=gu_marks[i])
+    t_end.record()
+    torch.cuda.synchronize()
+    ms = t_start.elapsed_time(t_end) / args.steps
+    gu_ms = float(np.mean([m_[2].elapsed_time(m_[3]) for m_ in gu_marks]))
+    marks = [[ev() for _ in range(6)] for _ in range(args.steps)]
+    for i in range(args.steps):
+        layer.forward(logits, x, copies[i % 2], marks=marks[i])
+    torch.cuda.synchronize()
+    names = ["route_permute", "quantize_x", "gate_up_swiglu", "down", "combine"]
+    stage_ms = {n: round(float(np.mean([m_[j].elapsed_time(m_[j + 1]) for m_ in marks])), 5)
+                for j, n in enumerate(names)}
+    touched = int((counts > 0).sum())
+    bpe = 17 / 32                         # bytes per element: 4-bit code + one byte per 32
+    gu_w = 2 * I * H * bpe
+    dn_w = H * I * bpe
+    weight_bytes = touched * (gu_w + dn_w)
+    gu_alg = touched * gu_w + T * H * bpe + T * k * I * bpe
+    print(json.dumps({
+        "metric": "MXFP4 MoE layer weight GB/s (secondary: the block format gfx950's scaled FP4 MFMA takes natively)",
+        "value": round(weight_bytes / (ms * 1e-3) / 1e9, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True, "vs_baseline": None,
+        "dtype": "mxfp4 operands, fp4 scaled mfma, f32 accumulate", "data": "synthetic",
+        "tflops": round(2.0 * T * k * 3 * I * H / (ms * 1e-3) / 1e12, 3), "weight_bytes": int(weight_bytes),
+        "stage_ms": stage_ms,
+        "config": {"workload": f"{'decode' if T <= 2048 else 'prefill'}_moe_T{T}_H{H}_I{I}_E{E}_top{k}_{cfg.routing}",
+                   "format": "mxfp4", "weight_copies": 2},
+        "roofline": {"kernel": "k_mx_gemm gate_up + SwiGLU/MXFP4 requant epilogue", "bound": "hbm",
+                     "achieved": round(gu_alg / (gu_ms * 1e-3) / 1e9, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gu_alg / (gu_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4), "traffic": None,
+                     "alg_bytes_per_launch": int(gu_alg), "avg_launch_ms": round(gu_ms, 5)}}), flush=True)
+
+
 def workloads_mod():
     import workloads
     return workloads
@@ -269,6 +379,9 @@ def main():
     lib()
     dev = torch.device("cuda:0")
     cfg = workloads.CONFIGS[args.workload]
+    if args.format == "mxfp4":
+        mx_bench(cfg, args)
+        return
     if cfg.dense:
         dense_gemm(cfg, args)
         return

@@ -94,6 +94,12 @@ _SIGNATURES = {
     "moe_expert_ffn_workspace_size": (ctypes.c_size_t, [ctypes.c_int32, ctypes.c_int64, ctypes.c_int32,
                                                         ctypes.c_int32]),
     "moe_expert_ffn": (ctypes.c_int, [ctypes.POINTER(FfnArgs), ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
+    "mxfp4_quantize": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_int64,
+                                      ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]),
+    "mxfp4_grouped_gemm": (ctypes.c_int, [ctypes.POINTER(GemmArgs), ctypes.c_void_p]),
+    "mxfp4_weight_packed_size": (ctypes.c_size_t, [ctypes.c_int32] * 3),
+    "mxfp4_weight_repack": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
+                                           ctypes.c_int32, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
     "nvfp4moe_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "nvfp4moe_last_error_detail": (ctypes.c_char_p, []),
     "nvfp4moe_version": (ctypes.c_int, []),
@@ -422,6 +428,111 @@ def moe_expert_ffn(xq: NVFP4Tensor, perm_src_token, offsets, w_gu_packed, g_gu, 
     return NVFP4Tensor(h.codes, h.scales, g_h), y
 
 
+# --------------------------------------------------------------------------- MXFP4
+@dataclass
+class MXFP4Tensor:
+    codes: "object"     # uint8 [rows, cols/2]
+    scales: "object"    # uint8 [rows, cols/32], E8M0
+
+
+def mxfp4_quantize(x, out: MXFP4Tensor | None = None, stream=None) -> MXFP4Tensor:
+    """x bf16/float32 [rows, cols] (or [..., cols]) -> MXFP4Tensor (E8M0 scale per 32 values)."""
+    import torch
+    _need(x, x.dtype, "x")
+    cols = x.shape[-1]
+    rows = x.numel() // cols
+    dev = x.device
+    if out is None:
+        out = MXFP4Tensor(torch.empty(x.shape[:-1] + (cols // 2,), dtype=torch.uint8, device=dev),
+                          torch.empty(x.shape[:-1] + (cols // 32,), dtype=torch.uint8, device=dev))
+    if out.codes.numel() != rows * (cols // 2) or out.scales.numel() != rows * (cols // 32):
+        raise ValueError("out codes/scales do not match x")
+    _need(out.codes, torch.uint8, "out.codes")
+    _need(out.scales, torch.uint8, "out.scales")
+    _check(lib().mxfp4_quantize(x.data_ptr(), _dtype_code(x), rows, cols, out.codes.data_ptr(), out.scales.data_ptr(),
+                                _stream(stream)))
+    return out
+
+
+def mxfp4_weight_repack(b: MXFP4Tensor, out=None, stream=None):
+    """MXFP4 weights codes [E, N, K/2], scales [E, N, K/32] -> packed tiles
+    (uint8 tensor) for mxfp4_grouped_gemm(b_packed=...)."""
+    import torch
+    _need(b.codes, torch.uint8, "codes")
+    _need(b.scales, torch.uint8, "scales")
+    E, N, K2 = b.codes.shape
+    nbytes = lib().mxfp4_weight_packed_size(E, N, 2 * K2)
+    if out is None:
+        out = torch.empty(nbytes, dtype=torch.uint8, device=b.codes.device)
+    _check(lib().mxfp4_weight_repack(b.codes.data_ptr(), b.scales.data_ptr(), E, N, 2 * K2, out.data_ptr(),
+                                     out.numel(), _stream(stream)))
+    return out
+
+
+def mxfp4_grouped_gemm(a: MXFP4Tensor, b: MXFP4Tensor, offsets, *, m_total: int, a_rows=None, epilogue: int = EPI_F32,
+                       out=None, out_codes=None, out_scales=None, a_g=None, b_g=None,
+                       max_rows_per_expert_hint: int = 0, b_packed=None, stream=None):
+    """Grouped MXFP4 GEMM (see include/nvfp4moe.h): a [rows, K], b [E, N, K]
+    (codes/scales), offsets int32 [E+1].  Epilogues F32, BF16, or
+    EPI_SWIGLU_NVFP4 read as SwiGLU + MXFP4 requantisation (returns an
+    MXFP4Tensor of h).  a_g / b_g: optional float32 multipliers (1 / E values)."""
+    import torch
+    E, N, K2 = b.codes.shape
+    K = 2 * K2
+    dev = b.codes.device
+    for t, name in ((a.codes, "a.codes"), (a.scales, "a.scales")):
+        _need(t, torch.uint8, name)
+    if b_packed is None:
+        _need(b.codes, torch.uint8, "b.codes")
+        _need(b.scales, torch.uint8, "b.scales")
+    else:
+        _need(b_packed, torch.uint8, "b_packed")
+        if b_packed.numel() < lib().mxfp4_weight_packed_size(E, N, K):
+            raise ValueError("b_packed is smaller than the packed size of [E, N, K]")
+    _need(offsets, torch.int32, "offsets")
+    rows_a = a.codes.shape[0]
+    if tuple(a.codes.shape) != (rows_a, K2) or tuple(a.scales.shape) != (rows_a, K // 32) \
+            or tuple(b.scales.shape) != (E, N, K // 32):
+        raise ValueError("operand shapes disagree")
+    if offsets.numel() < E + 1:
+        raise ValueError("offsets needs E+1 values")
+    if a_rows is not None:
+        _need(a_rows, torch.int32, "a_rows")
+        if a_rows.numel() < m_total:
+            raise ValueError("a_rows shorter than m_total")
+    if a_g is None:
+        a_g = torch.ones(1, dtype=torch.float32, device=dev)
+    if b_g is None:
+        b_g = torch.ones(E, dtype=torch.float32, device=dev)
+    _need(a_g, torch.float32, "a_g")
+    _need(b_g, torch.float32, "b_g")
+    I = N // 2
+    if epilogue in (EPI_F32, EPI_BF16):
+        want = torch.float32 if epilogue == EPI_F32 else torch.bfloat16
+        if out is None:
+            out = torch.empty((m_total, N), dtype=want, device=dev)
+        _need(out, want, "out")
+        if tuple(out.shape) != (m_total, N):
+            raise ValueError("out must be [m_total, N]")
+    elif epilogue == EPI_SWIGLU_NVFP4:
+        if out_codes is None:
+            out_codes = torch.empty((m_total, I // 2), dtype=torch.uint8, device=dev)
+            out_scales = torch.empty((m_total, I // 32), dtype=torch.uint8, device=dev)
+        if tuple(out_codes.shape) != (m_total, I // 2) or tuple(out_scales.shape) != (m_total, I // 32):
+            raise ValueError("out_codes/out_scales must be [m_total, I/2] and [m_total, I/32]")
+    args = GemmArgs(a_codes=a.codes.data_ptr(), a_scales=a.scales.data_ptr(), a_g=a_g.data_ptr(), a_rows=_ptr(a_rows),
+                    a_rows_total=rows_a, b_codes=None if b_packed is not None else b.codes.data_ptr(),
+                    b_scales=None if b_packed is not None else b.scales.data_ptr(), b_packed=_ptr(b_packed),
+                    b_g=b_g.data_ptr(), offsets=offsets.data_ptr(), E=E, N=N, K=K, m_total=m_total,
+                    epilogue=epilogue, out=_ptr(out), out_rows=0, out_codes=_ptr(out_codes),
+                    out_scales=_ptr(out_scales), out_g=None, row_token=None, row_weight=None,
+                    max_rows_per_expert_hint=max_rows_per_expert_hint)
+    _check(lib().mxfp4_grouped_gemm(ctypes.byref(args), _stream(stream)))
+    if epilogue == EPI_SWIGLU_NVFP4:
+        return MXFP4Tensor(out_codes, out_scales)
+    return out
+
+
 # -------------------------------------------------------------------------- swiglu
 def moe_swiglu(gate_up, g=None, out: NVFP4Tensor | None = None, workspace=None, stream=None) -> NVFP4Tensor:
     """gate_up float32/bf16 [M, 2I] -> NVFP4 h = silu(gate) * up."""
@@ -469,5 +580,6 @@ def moe_unpermute_combine(y, perm_of_assignment, topk_w, T: int, k: int, out=Non
 
 
 __all__ = ["lib", "moe_route_permute", "moe_route_quantize", "moe_route_quantize_noalloc", "nvfp4_quantize", "nvfp4_grouped_gemm", "moe_swiglu", "nvfp4_weight_repack",
-           "moe_unpermute_combine", "moe_expert_ffn", "moe_expert_ffn_workspace", "NVFP4Tensor", "Routing", "GemmArgs", "NVFP4MoEError",
+           "moe_unpermute_combine", "moe_expert_ffn", "moe_expert_ffn_workspace", "mxfp4_quantize",
+           "mxfp4_grouped_gemm", "mxfp4_weight_repack", "MXFP4Tensor", "NVFP4Tensor", "Routing", "GemmArgs", "NVFP4MoEError",
            "F32", "BF16", "EPI_F32", "EPI_BF16", "EPI_SWIGLU_NVFP4", "EPI_COMBINE_F32"]

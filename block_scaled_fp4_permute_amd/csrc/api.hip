@@ -360,6 +360,99 @@ int moe_expert_ffn(const nvfp4moe_ffn_args* a, void* workspace, size_t workspace
                     "moe_expert_ffn");
 }
 
+// ------------------------------------------------------------------ MXFP4
+int mxfp4_quantize(const void* x, int32_t x_dtype, int64_t rows, int64_t cols, uint8_t* codes, uint8_t* scales,
+                   void* stream) {
+  if (!x || !codes || !scales) return fail(NVFP4MOE_ERR_INVALID, "mxfp4_quantize: null pointer argument");
+  if (x_dtype != NVFP4MOE_F32 && x_dtype != NVFP4MOE_BF16)
+    return fail(NVFP4MOE_ERR_INVALID, "mxfp4_quantize: x_dtype %d", x_dtype);
+  if (rows <= 0 || cols <= 0 || cols % 32 != 0)
+    return fail(NVFP4MOE_ERR_INVALID, "mxfp4_quantize: rows > 0 and cols a positive multiple of 32 needed");
+  if (rows * (cols / 32) >= (int64_t(1) << 38)) return fail(NVFP4MOE_ERR_UNSUPPORTED, "mxfp4_quantize: tensor too large");
+  if (!aligned(x, 16) || !aligned(codes, 16))
+    return fail(NVFP4MOE_ERR_INVALID, "mxfp4_quantize: x and codes must be 16-byte aligned");
+  return hip_status(nvfp4::launch_mx_quantize(x, x_dtype, rows, cols, codes, scales, static_cast<hipStream_t>(stream)),
+                    "mxfp4_quantize");
+}
+
+int mxfp4_grouped_gemm(const nvfp4moe_gemm_args* a, void* stream) {
+  if (!a) return fail(NVFP4MOE_ERR_INVALID, "mxfp4_grouped_gemm: args is NULL");
+  if (!a->a_codes || !a->a_scales || !a->a_g || !a->b_g || !a->offsets)
+    return fail(NVFP4MOE_ERR_INVALID, "mxfp4_grouped_gemm: null operand pointer");
+  if (!a->b_packed && (!a->b_codes || !a->b_scales))
+    return fail(NVFP4MOE_ERR_INVALID, "mxfp4_grouped_gemm: B needs b_codes and b_scales, or b_packed");
+  if (a->E <= 0 || a->N <= 0 || a->K <= 0 || a->m_total < 0 || a->a_rows_total <= 0)
+    return fail(NVFP4MOE_ERR_INVALID, "mxfp4_grouped_gemm: E, N, K, a_rows_total must be > 0 and m_total >= 0");
+  if (a->K % 32 != 0) return fail(NVFP4MOE_ERR_INVALID, "mxfp4_grouped_gemm: K=%d not a multiple of 32", a->K);
+  if (a->N % 16 != 0) return fail(NVFP4MOE_ERR_INVALID, "mxfp4_grouped_gemm: N=%d not a multiple of 16", a->N);
+  if (!aligned(a->a_codes, 16) || !aligned(a->a_scales, 2) || !aligned(a->b_packed, 16) ||
+      (!a->b_packed && (!aligned(a->b_codes, 16) || !aligned(a->b_scales, 2))))
+    return fail(NVFP4MOE_ERR_INVALID, "mxfp4_grouped_gemm: codes and packed tiles must be 16-byte, scales 2-byte aligned");
+  if (nvfp4::mx_packed_weight_bytes(1, a->N, a->K) >= (size_t(1) << 31))
+    return fail(NVFP4MOE_ERR_UNSUPPORTED, "mxfp4_grouped_gemm: one expert's weights of 2 GiB or more");
+  if (a->m_total >= (int64_t(1) << 31) || a->a_rows_total * (int64_t(a->K) / 2) >= (int64_t(1) << 31))
+    return fail(NVFP4MOE_ERR_UNSUPPORTED, "mxfp4_grouped_gemm: A codes of 2 GiB or more");
+  if (static_cast<int64_t>(a->E) * a->N >= (int64_t(1) << 31) ||
+      static_cast<int64_t>(a->N) * (a->K / 2) >= (int64_t(1) << 31))
+    return fail(NVFP4MOE_ERR_UNSUPPORTED, "mxfp4_grouped_gemm: E*N or one expert's B codes (N*K/2) >= 2^31");
+  switch (a->epilogue) {
+    case NVFP4MOE_EPI_F32:
+    case NVFP4MOE_EPI_BF16:
+      if (!a->out && a->m_total > 0) return fail(NVFP4MOE_ERR_INVALID, "mxfp4_grouped_gemm: out is NULL");
+      break;
+    case NVFP4MOE_EPI_SWIGLU_NVFP4:
+      if (a->N % 64 != 0) return fail(NVFP4MOE_ERR_INVALID, "mxfp4_grouped_gemm: SwiGLU needs N = 2I with I %% 32 == 0");
+      if (!a->out_codes || !a->out_scales)
+        return fail(NVFP4MOE_ERR_INVALID, "mxfp4_grouped_gemm: SwiGLU needs out_codes, out_scales");
+      break;
+    default:
+      return fail(NVFP4MOE_ERR_UNSUPPORTED, "mxfp4_grouped_gemm: epilogue %d (F32, BF16 or SwiGLU)", a->epilogue);
+  }
+  if (a->m_total == 0) return ok();
+  nvfp4::GemmParams prm{};
+  prm.a_codes = a->a_codes;
+  prm.a_scales = a->a_scales;
+  prm.a_g = a->a_g;
+  prm.a_rows = a->a_rows;
+  prm.b_codes = a->b_codes;
+  prm.b_scales = a->b_scales;
+  prm.b_packed = a->b_packed;
+  prm.b_g = a->b_g;
+  prm.offsets = a->offsets;
+  prm.E = a->E;
+  prm.N = a->N;
+  prm.K = a->K;
+  prm.m_total = static_cast<int>(a->m_total);
+  prm.a_rows_total = static_cast<int>(a->a_rows_total);
+  prm.out = a->out;
+  prm.out_codes = a->out_codes;
+  prm.out_scales = a->out_scales;
+  return hip_status(nvfp4::launch_mx_gemm(prm, a->epilogue, a->m_total, a->max_rows_per_expert_hint,
+                                          static_cast<hipStream_t>(stream)),
+                    "mxfp4_grouped_gemm");
+}
+
+size_t mxfp4_weight_packed_size(int32_t E, int32_t N, int32_t K) {
+  if (E <= 0 || N <= 0 || K <= 0) return 0;
+  return nvfp4::mx_packed_weight_bytes(E, N, K);
+}
+
+int mxfp4_weight_repack(const uint8_t* codes, const uint8_t* scales, int32_t E, int32_t N, int32_t K,
+                        uint8_t* packed, size_t packed_bytes, void* stream) {
+  if (!codes || !scales || !packed) return fail(NVFP4MOE_ERR_INVALID, "mxfp4_weight_repack: null pointer argument");
+  if (E <= 0 || N <= 0 || K <= 0) return fail(NVFP4MOE_ERR_INVALID, "mxfp4_weight_repack: E, N, K must be > 0");
+  if (K % 32 != 0) return fail(NVFP4MOE_ERR_INVALID, "mxfp4_weight_repack: K=%d not a multiple of 32", K);
+  if (!aligned(codes, 16) || !aligned(packed, 16))
+    return fail(NVFP4MOE_ERR_INVALID, "mxfp4_weight_repack: codes and packed must be 16-byte aligned");
+  if (static_cast<int64_t>(E) * N >= (int64_t(1) << 31))
+    return fail(NVFP4MOE_ERR_UNSUPPORTED, "mxfp4_weight_repack: E*N >= 2^31");
+  const size_t need = nvfp4::mx_packed_weight_bytes(E, N, K);
+  if (packed_bytes < need)
+    return fail(NVFP4MOE_ERR_WORKSPACE, "mxfp4_weight_repack: packed buffer %zu < %zu bytes", packed_bytes, need);
+  return hip_status(nvfp4::launch_mx_repack(codes, scales, E, N, K, packed, static_cast<hipStream_t>(stream)),
+                    "mxfp4_weight_repack");
+}
+
 // ------------------------------------------------------------------ packed weights
 size_t nvfp4_weight_packed_size(int32_t E, int32_t N, int32_t K) {
   if (E <= 0 || N <= 0 || K <= 0) return 0;

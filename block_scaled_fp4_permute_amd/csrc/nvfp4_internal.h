@@ -54,6 +54,12 @@ size_t packed_weight_bytes(int E, int N, int K);
 hipError_t launch_repack(const uint8_t* codes, const uint8_t* scales, int E, int N, int K, uint8_t* packed,
                          hipStream_t stream);
 hipError_t launch_grouped_gemm(const GemmParams& prm, int epilogue, int64_t m_total, int hint, hipStream_t stream);
+hipError_t launch_mx_quantize(const void* x, int dtype, int64_t rows, int64_t cols, uint8_t* codes,
+                              uint8_t* scales, hipStream_t stream);
+hipError_t launch_mx_gemm(const GemmParams& prm, int epilogue, int64_t m_total, int hint, hipStream_t stream);
+size_t mx_packed_weight_bytes(int E, int N, int K);
+hipError_t launch_mx_repack(const uint8_t* codes, const uint8_t* scales, int E, int N, int K, uint8_t* packed,
+                            hipStream_t stream);
 size_t moe_ffn_ws_bytes(int E, int64_t m_total, int H, int I);
 hipError_t launch_moe_ffn(GemmParams gu, GemmParams dn, int64_t m_total, bool cached, void* ws, int spin_limit,
                           hipStream_t stream);

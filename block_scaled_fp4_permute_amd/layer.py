@@ -172,3 +172,84 @@ class MoELayer:
             moe_unpermute_combine(self.y2, r.perm_of_assignment, r.topk_w, T, k, out=self.out, stream=stream)
         mark(5)
         return self.out
+
+
+# ------------------------------------------------------------------ MXFP4 variant
+@dataclass
+class MXExpertWeights:
+    """Per-expert MXFP4 weights (E8M0 scale per 32 along K, no per-tensor scale):
+    gate_up codes [E, 2I, H/2], scales [E, 2I, H/32]; down [E, H, I/2], [E, H, I/32]."""
+    gu: "object"
+    dn: "object"
+    gu_packed: "object" = None     # streaming tiles from mxfp4_weight_repack
+    dn_packed: "object" = None
+
+    def pack(self) -> "MXExpertWeights":
+        from . import mxfp4_weight_repack
+        self.gu_packed = mxfp4_weight_repack(self.gu)
+        self.dn_packed = mxfp4_weight_repack(self.dn)
+        return self
+
+    @property
+    def E(self):
+        return self.gu.codes.shape[0]
+
+    def nbytes(self) -> int:
+        return sum(t.numel() for t in (self.gu.codes, self.gu.scales, self.dn.codes, self.dn.scales))
+
+
+def quantize_expert_weights_mx(w_gu: torch.Tensor, w_dn: torch.Tensor) -> MXExpertWeights:
+    """Quantise float32/bf16 weights [E, 2I, H] and [E, H, I] to MXFP4 on the GPU."""
+    from . import mxfp4_quantize
+    return MXExpertWeights(mxfp4_quantize(w_gu.contiguous()), mxfp4_quantize(w_dn.contiguous())).pack()
+
+
+class MXMoELayer:
+    """Preallocated MXFP4 MoE layer for T tokens: route + permute, MXFP4
+    quantisation of x, gate_up grouped GEMM with the fused SwiGLU + MXFP4
+    requantisation, down grouped GEMM (bf16 rows), weighted gather combine."""
+
+    def __init__(self, T: int, H: int, I: int, E: int, k: int, device):
+        from . import MXFP4Tensor
+        self.T, self.H, self.I, self.E, self.k = T, H, I, E, k
+        dev = torch.device(device)
+        i32 = dict(dtype=torch.int32, device=dev)
+        f32 = dict(dtype=torch.float32, device=dev)
+        u8 = dict(dtype=torch.uint8, device=dev)
+        M = T * k
+        self.routing = Routing(torch.empty((T, k), **i32), torch.empty((T, k), **f32), torch.empty(E, **i32),
+                               torch.empty(E + 1, **i32), torch.empty(M, **i32), torch.empty(M, **i32),
+                               torch.empty(M, **f32))
+        self.route_ws = torch.empty(max(16, lib().moe_route_permute_workspace_size(T, E, k)), **u8)
+        self.xq = MXFP4Tensor(torch.empty((T, H // 2), **u8), torch.empty((T, H // 32), **u8))
+        self.hq = MXFP4Tensor(torch.empty((M, I // 2), **u8), torch.empty((M, I // 32), **u8))
+        self.y2 = torch.empty((M, H), dtype=torch.bfloat16, device=dev)
+        self.out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+        self.ones = torch.ones(max(E, 1), **f32)
+
+    def forward(self, logits: torch.Tensor, x: torch.Tensor, w: MXExpertWeights, stream=None,
+                marks=None) -> torch.Tensor:
+        """One layer step; ``marks``: optional 6 events (as MoELayer.forward:
+        route, quantise x, gate_up, down, combine)."""
+        from . import mxfp4_grouped_gemm, mxfp4_quantize
+        T, k, M = self.T, self.k, self.T * self.k
+
+        def mark(i):
+            if marks is not None and marks[i] is not None:
+                marks[i].record(stream)
+
+        mark(0)
+        r = moe_route_permute(logits, k, out=self.routing, workspace=self.route_ws, stream=stream)
+        mark(1)
+        mxfp4_quantize(x, out=self.xq, stream=stream)
+        mark(2)
+        mxfp4_grouped_gemm(self.xq, w.gu, r.offsets, m_total=M, a_rows=r.perm_src_token, epilogue=EPI_SWIGLU_NVFP4,
+                           out_codes=self.hq.codes, out_scales=self.hq.scales, a_g=self.ones[:1], b_g=self.ones,
+                           b_packed=w.gu_packed, stream=stream)
+        mark(3)
+        mxfp4_grouped_gemm(self.hq, w.dn, r.offsets, m_total=M, epilogue=EPI_BF16, out=self.y2, a_g=self.ones[:1],
+                           b_g=self.ones, b_packed=w.dn_packed, stream=stream)
+        mark(4)
+        moe_unpermute_combine(self.y2, r.perm_of_assignment, r.topk_w, T, k, out=self.out, stream=stream)
+        mark(5)
+        return self.out

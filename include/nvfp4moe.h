@@ -262,6 +262,39 @@ typedef struct nvfp4moe_ffn_args {
 size_t moe_expert_ffn_workspace_size(int32_t E, int64_t m_total, int32_t H, int32_t I);
 int moe_expert_ffn(const nvfp4moe_ffn_args* args, void* workspace, size_t workspace_bytes, void* stream);
 
+/* ---------------------------------------------------------------- MXFP4 variant
+ * The MXFP4 format: E2M1 values with one E8M0 scale (a power of two, code c =
+ * 2^(c-127)) per 32 consecutive values along the reduction axis and no
+ * per-tensor scale (the OCP MX format; the pages list an MXFP4 grouped GEMM
+ * with 128x128x128 tiles among the kernels they survey: "From Empirical Limits
+ * ...", section "Sections 2-4: Framework and Community Landscape").  It maps
+ * onto gfx950's block-scaled MFMA with no decode in registers.
+ *   codes  uint8 [rows, cols/2]   as NVFP4 (element 2i in the low nibble of byte i)
+ *   scales uint8 [rows, cols/32]  E8M0 codes
+ * Quantiser: X = floor(log2(absmax_block)) - 2 clamped to [-127, 127], scale
+ * code X + 127, code = E2M1 nearest-even of x / 2^X (exact), saturating at 6,
+ * sign copied from x; an all-zero block gets scale code 0 and codes 0.
+ * x: bf16 or float32 [rows, cols], finite, 16-byte aligned, cols % 32 == 0. */
+int mxfp4_quantize(const void* x, int32_t x_dtype, int64_t rows, int64_t cols, uint8_t* codes, uint8_t* scales,
+                   void* stream);
+/* Grouped MXFP4 GEMM with the nvfp4_grouped_gemm argument struct, read as:
+ *   y[p, n] = a_g * b_g[e] * sum_k A^[r, k] B^[e, n, k]   (A^, B^ dequantised MX values)
+ * a_scales [a_rows_total, K/32], b_scales [E, N, K/32] (E8M0); a_g, b_g are
+ * float32 multipliers (pass 1.0 for plain MX tensors); b_packed: optional B in
+ * the layout written by mxfp4_weight_repack (then b_codes/b_scales are not read).  Epilogues: EPI_F32, EPI_BF16, and EPI_SWIGLU_NVFP4
+ * read as SwiGLU + MXFP4 requantisation of h: out_codes [m_total, I/2],
+ * out_scales [m_total, I/32] (out_g unused; I % 32 == 0).  EPI_COMBINE_F32 is
+ * NVFP4MOE_ERR_UNSUPPORTED.  K % 32 == 0.  FP32 accumulation of exact
+ * E2M1 x E2M1 x 2^k products; other limits as for nvfp4_grouped_gemm. */
+int mxfp4_grouped_gemm(const nvfp4moe_gemm_args* args, void* stream);
+/* MXFP4 weights [E, N, K] repacked once into streaming tiles of 16 rows x 256
+ * K (2176 bytes: each lane's 32 code bytes and 2 scale bytes, in the order the
+ * kernel's lanes read them; zero codes past N and K).  Private layout, pure
+ * data movement.  K % 32 == 0; 16-byte aligned codes and packed. */
+size_t mxfp4_weight_packed_size(int32_t E, int32_t N, int32_t K);
+int mxfp4_weight_repack(const uint8_t* codes, const uint8_t* scales, int32_t E, int32_t N, int32_t K,
+                        uint8_t* packed, size_t packed_bytes, void* stream);
+
 /* ---------------------------------------------------------------- packed weights
  * Weights are static, so they can be repacked once into a tile layout that the
  * grouped GEMM streams with fully contiguous, non-temporal loads: tile

@@ -124,3 +124,65 @@ def check_requant(codes_gpu, scales_gpu, x_ref, g, tol_abs, max_flip_frac=1e-3, 
     if flips > max_flip_frac * x32.size:
         raise AssertionError(f"{what}: {nsflip} scale flips and {ncflip} code flips in {x32.size} elements")
     return nsflip, ncflip
+
+
+def check_requant_mx(codes_gpu, scales_gpu, x_ref, tol_abs, max_flip_frac=1e-3, what="mx requant"):
+    """GPU MXFP4 codes of a value the GPU computed itself (within tol_abs of
+    the oracle's x_ref per element) against the oracle's MXFP4 encoding of x_ref.
+
+    * a block's E8M0 scale may differ by one code, and only where the oracle's
+      block absmax lies within the block's tolerance of the power of two
+      between the two exponents; such blocks are checked by the error bound of
+      the GPU's own encoding;
+    * an element code may differ by one magnitude step, and only where the
+      oracle's |x| / 2^X lies within tol of the E2M1 decision point between them;
+    * at most max_flip_frac of the elements may differ.
+    Returns (scale flips, code flips)."""
+    from oracle import mx as MXO
+    x32 = np.asarray(x_ref, np.float64).astype(np.float32)
+    rows, cols = x32.shape
+    tol_abs = np.broadcast_to(np.asarray(tol_abs, np.float64), x32.shape)
+    c_ref, s_ref = MXO.mx_quantize(x32)
+    s_gpu = np.asarray(scales_gpu, np.uint8).reshape(rows, cols // 32)
+    c_gpu = unpack_codes(np.asarray(codes_gpu, np.uint8).reshape(rows, cols // 2))
+    c_ref = unpack_codes(c_ref)
+    sdiff = s_gpu != s_ref
+    nsflip = int(sdiff.sum())
+    if nsflip:
+        blk = np.abs(x32.astype(np.float64)).reshape(rows, -1, 32)
+        amax = blk.max(axis=2)
+        tol_blk = tol_abs.reshape(rows, -1, 32).max(axis=2) + amax * 2.0 ** -22
+        hi = np.maximum(s_gpu, s_ref).astype(np.int64) - 127 + 2        # the power of two between
+        adjacent = np.abs(s_gpu.astype(np.int64) - s_ref.astype(np.int64)) == 1
+        near = np.abs(amax - np.exp2(hi.astype(np.float64))) <= tol_blk
+        bad = sdiff & ~(adjacent & near)
+        if bad.any():
+            i = tuple(np.argwhere(bad)[0])
+            raise AssertionError(f"{what}: block scale {i} gpu {s_gpu[i]} ref {s_ref[i]} amax {amax[i]} tol {tol_blk[i]}")
+        sv = np.repeat(np.exp2(s_gpu.astype(np.float64) - 127), 32, axis=1)
+        deq = F.e2m1_decode(c_gpu) * sv
+        v = np.abs(x32.astype(np.float64)) / sv
+        hi2 = np.clip(np.searchsorted(F.E2M1_MAGNITUDES, v), 1, 7)
+        gap = F.E2M1_MAGNITUDES[hi2] - F.E2M1_MAGNITUDES[hi2 - 1]
+        bound = np.where(v > 6, np.abs(x32) - 6 * sv, 0.5 * gap * sv) + tol_abs + 1e-30
+        fb = np.repeat(sdiff, 32, axis=1)
+        if np.any((np.abs(deq - x32) > bound * (1 + 1e-6))[fb]):
+            raise AssertionError(f"{what}: codes of a flipped-scale block exceed the quantisation bound")
+    same = np.repeat(~sdiff, 32, axis=1)
+    cdiff = (c_gpu != c_ref) & same
+    ncflip = int(cdiff.sum())
+    if ncflip:
+        sv = np.repeat(np.exp2(s_ref.astype(np.float64) - 127), 32, axis=1)
+        v = np.abs(x32.astype(np.float64)) / sv
+        tol_v = tol_abs / sv + v * 2.0 ** -22
+        mg, mr = (c_gpu & 7).astype(np.int64), (c_ref & 7).astype(np.int64)
+        sign_ok = ((c_gpu & 8) == (c_ref & 8)) | ((mg == 0) & (mr == 0) & (np.abs(x32) <= tol_abs))
+        mid = E2M1_MIDPOINTS[np.clip(np.minimum(mg, mr), 0, 6)]
+        near = (mg == mr) | (np.abs(v - mid) <= tol_v)
+        bad = cdiff & ~(sign_ok & (np.abs(mg - mr) <= 1) & near)
+        if bad.any():
+            i = tuple(np.argwhere(bad)[0])
+            raise AssertionError(f"{what}: code {i} gpu {c_gpu[i]:#x} ref {c_ref[i]:#x} v {v[i]} tol {tol_v[i]}")
+    if nsflip * 32 + ncflip > max_flip_frac * x32.size:
+        raise AssertionError(f"{what}: {nsflip} scale flips and {ncflip} code flips in {x32.size} elements")
+    return nsflip, ncflip

@@ -150,20 +150,21 @@ def torch_dense_operands(cfg: MoEConfig, device):
 
 
 def nvfp4_codes(cfg: MoEConfig, stream: int, shape_rows: tuple, K: int, scale_lo: int = 0x60,
-                scale_hi: int = 0x7F, const_scale: int | None = None):
-    """Random NVFP4 operand bytes: codes uint8 [*shape_rows, K/2] uniform over all
+                scale_hi: int = 0x7F, const_scale: int | None = None, block: int = 16):
+    """Random FP4 operand bytes: codes uint8 [*shape_rows, K/2] uniform over all
     256 byte values (two 4-bit codes each) and block-scale bytes uint8
-    [*shape_rows, K/16] uniform in [scale_lo, scale_hi) (E4M3 codes; the default
-    range 0x60..0x7E is where block scales of quantised Gaussian weights land,
-    about 64..448), or all equal to ``const_scale``.  Raw input bytes, drawn
-    from stream ``stream`` (7 = GEMM operands given directly as codes); no
-    arithmetic of the method is involved."""
+    [*shape_rows, K/block] uniform in [scale_lo, scale_hi) (for NVFP4, E4M3
+    codes with 16-value blocks: the default range 0x60..0x7E is where block
+    scales of quantised Gaussian weights land, about 64..448; for MXFP4, E8M0
+    codes with block=32), or all equal to ``const_scale``.  Raw input bytes,
+    drawn from stream ``stream`` (7 = GEMM operands given directly as codes);
+    no arithmetic of the method is involved."""
     g = rng(cfg.index, 7, stream)
     codes = g.integers(0, 256, tuple(shape_rows) + (K // 2,), dtype=np.uint8)
     if const_scale is None:
-        scales = g.integers(scale_lo, scale_hi, tuple(shape_rows) + (K // 16,), dtype=np.uint8)
+        scales = g.integers(scale_lo, scale_hi, tuple(shape_rows) + (K // block,), dtype=np.uint8)
     else:
-        scales = np.full(tuple(shape_rows) + (K // 16,), const_scale, np.uint8)
+        scales = np.full(tuple(shape_rows) + (K // block,), const_scale, np.uint8)
     return codes, scales
 
 
