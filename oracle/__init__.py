@@ -12,13 +12,15 @@ Modules:
   moe      route, permute, grouped GEMM, SwiGLU, combine, whole layer
   mx       MXFP4 (E2M1 with an E8M0 scale per 32): quantise, dequantise,
            grouped GEMM, SwiGLU requantisation
+  fp8      FP8 E4M3 with float32 block scales (1 x 128 activations,
+           128 x 128 weights): quantise, dequantise, grouped GEMM
 
 Parity status: every function is pinned by tests/test_oracle_*.py against
 closed forms, library routines (torch.float8_e4m3fn and float8_e8m0fnu, numpy
 sorting, scipy's expit/softmax), exact rational brute force and invariants.  The Zipf-skewed
 routing recipe has no pin from the pages (it is a synthetic input recipe).
 """
-from . import formats, quant, moe, mx  # noqa: F401
+from . import formats, quant, moe, mx, fp8  # noqa: F401
 from .quant import quantize, dequantize, dequantize_unscaled, pack_codes, unpack_codes  # noqa: F401
 from .moe import (route, permute, grouped_gemm, grouped_gemm_blockwise, swiglu,  # noqa: F401
                   swiglu_quantize, combine, moe_layer, quantize_experts)

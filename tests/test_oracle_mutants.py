@@ -239,3 +239,44 @@ def test_mutant_mx_zero_block_keeps_sign(monkeypatch):
         return Q.pack_codes(q), scales
     monkeypatch.setattr(MXO, "mx_quantize", bad)
     assert _fails(TMX.test_quantiser_invariants)
+
+
+# ------------------------------------------------------------------ FP8 block-scaled oracle
+import oracle.fp8 as P8
+import tests.test_oracle_fp8 as TP8
+
+
+def test_mutant_fp8_scale_constant(monkeypatch):
+    monkeypatch.setattr(P8, "F32_448", np.float32(240.0))       # the E4M3 max of another FP8 variant
+    assert _fails(TP8.test_worked_block_by_hand)
+
+
+def test_mutant_fp8_truncating_encoder(monkeypatch):
+    def bad(t):
+        t = np.minimum(np.asarray(t, np.float64), 448.0)
+        return (np.searchsorted(F.E4M3_POS, t, side="right") - 1).astype(np.uint8)
+    monkeypatch.setattr(P8, "e4m3_encode_satfinite", bad)
+    assert _fails(TP8.test_encoder_matches_torch_float8_cast)
+
+
+def test_mutant_fp8_weight_scale_per_row(monkeypatch):
+    # the weight scale indexed by output row instead of by its 128-row block
+    orig = P8.fp8_dequantize
+
+    def bad(codes, scales, block_rows=1):
+        if block_rows != 128:
+            return orig(codes, scales, block_rows)
+        sc = np.asarray(scales)
+        idx = np.minimum(np.arange(np.asarray(codes).shape[-2]), sc.shape[-2] - 1)
+        return orig(codes, sc[..., idx, :], 1)
+    monkeypatch.setattr(P8, "fp8_dequantize", bad)
+    assert _fails(TP8.test_fp8_gemm_equals_exact_rational)
+
+
+def test_mutant_fp8_gemm_drops_activation_scale(monkeypatch):
+    orig = P8.fp8_dequantize
+
+    def bad(codes, scales, block_rows=1):
+        return orig(codes, np.ones_like(scales) if block_rows == 1 else scales, block_rows)
+    monkeypatch.setattr(P8, "fp8_dequantize", bad)
+    assert _fails(TP8.test_fp8_gemm_equals_exact_rational)
