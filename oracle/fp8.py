@@ -22,8 +22,14 @@ this module takes the plainest blockwise reading:
 
 GEMM, per expert:
     y[p, n] = sum_kb sa[r, kb] * sb[e, n // 128, kb] * sum_{k in kb} qa[r, k] qb[e, n, k]
-Every product of two dequantised values is exact in float64; the sum runs in
-float64 (numpy matmul as the summation primitive) and is rounded to float32 once.
+computed as written: each block's sum of code products is exact in float64
+(a product of two E4M3 values has at most 8 significant bits and lies in
+[2^-18, 2^17], so 128 of them sum exactly), the product of the two float32
+scales is exact (48 bits), each scaled block term is rounded once, the terms
+sum in float64 (numpy matmul as the summation primitive for the block sums)
+and the result is rounded to float32 once.  (A product of two dequantised
+values, E4M3 * float32 scale on each side, can need 56 bits and would not be
+exact in float64.)
 """
 from __future__ import annotations
 
@@ -63,11 +69,16 @@ def fp8_quantize(x: np.ndarray, block_rows: int = 1):
     return (mag | sign).astype(np.uint8), s
 
 
+def fp8_row_scales(scales: np.ndarray, block_rows: int, rows: int) -> np.ndarray:
+    """The scale of each row and 128-value block: [..., rows, cols/128] (row i
+    takes its row block i // block_rows), float64."""
+    return np.repeat(np.asarray(scales, np.float64), block_rows, axis=-2)[..., :rows, :]
+
+
 def fp8_dequantize(codes: np.ndarray, scales: np.ndarray, block_rows: int = 1) -> np.ndarray:
     """E4M3(q) * s, float64 (exact)."""
     codes = np.asarray(codes)
-    rows = codes.shape[-2]
-    s = np.repeat(np.repeat(np.asarray(scales, np.float64), block_rows, axis=-2)[..., :rows, :], FP8_BLOCK, axis=-1)
+    s = np.repeat(fp8_row_scales(scales, block_rows, codes.shape[-2]), FP8_BLOCK, axis=-1)
     return e4m3_decode(codes) * s
 
 
@@ -77,6 +88,7 @@ def fp8_grouped_gemm(a_codes, a_scales, b_codes, b_scales, offsets, a_rows=None,
     blocks).  Rows p in [offsets[e], offsets[e+1]) use expert e and A row
     a_rows[p] (or p).  Returns (y float32 [M, N], absdot = sum_k |a^ b^|)."""
     E, N, K = b_codes.shape
+    nkb = K // FP8_BLOCK
     offsets = np.asarray(offsets, dtype=np.int64)
     M = int(offsets[-1])
     y = np.zeros((M, N), dtype=np.float32)
@@ -86,9 +98,19 @@ def fp8_grouped_gemm(a_codes, a_scales, b_codes, b_scales, offsets, a_rows=None,
         if p1 == p0:
             continue
         rows = np.arange(p0, p1) if a_rows is None else np.asarray(a_rows)[p0:p1]
-        a_hat = fp8_dequantize(a_codes[rows], a_scales[rows], 1)
-        b_hat = fp8_dequantize(b_codes[e], b_scales[e], FP8_BLOCK)
-        y[p0:p1] = (a_hat @ b_hat.T).astype(np.float32)
+        qa = e4m3_decode(a_codes[rows])                                   # float64, exact
+        qb = e4m3_decode(b_codes[e])
+        sa = fp8_row_scales(np.asarray(a_scales)[rows], 1, len(rows))     # [m, nkb]
+        sb = fp8_row_scales(b_scales[e], FP8_BLOCK, N)                     # [N, nkb]
+        acc = np.zeros((p1 - p0, N))
+        accm = np.zeros((p1 - p0, N)) if want_absdot else None
+        for kb in range(nkb):
+            blk = slice(kb * FP8_BLOCK, (kb + 1) * FP8_BLOCK)
+            s = sa[:, kb:kb + 1] * sb[None, :, kb]                         # exact: 24 x 24 bits
+            acc += (qa[:, blk] @ qb[:, blk].T) * s                         # exact block sum, one rounding
+            if want_absdot:
+                accm += (np.abs(qa[:, blk]) @ np.abs(qb[:, blk]).T) * s
+        y[p0:p1] = acc.astype(np.float32)
         if want_absdot:
-            absdot[p0:p1] = np.abs(a_hat) @ np.abs(b_hat).T
+            absdot[p0:p1] = accm
     return y, absdot

@@ -104,6 +104,36 @@ def test_fp8_gemm_equals_exact_rational():
             assert abs(Fraction(float(absdot[p, n])) - accm) <= accm * Fraction(1, 2 ** 50)
 
 
+def test_fp8_gemm_single_block_terms_correctly_rounded():
+    # one nonzero 128-block, arbitrary float32 scales: each output is one exact
+    # block term, so the oracle must return its float32 rounding (up to a
+    # double rounding through float64) and exactly 0 where the code products
+    # cancel.  Rows 0-1 against weight rows 0-1 cancel exactly with terms of
+    # different size: 1.875 * 1.875 - 1.75 * 2 - 0.125 * 0.125 = 0, where the
+    # first term times the scales needs more than float64's 53 bits
+    rng = np.random.default_rng(6)
+    M, N, K = 6, 20, 384
+    ac = np.zeros((M, K), np.uint8)
+    bc = np.zeros((1, N, K), np.uint8)
+    ac[:, 128:256] = _rand_fp8(rng, (M, 128))
+    bc[0, :, 128:256] = _rand_fp8(rng, (N, 128))
+    ac[0:2, 128:256] = 0
+    bc[0, 0:2, 128:256] = 0
+    ac[0:2, 128:131] = [0x3F, 0x3E, 0x20]                       # 1.875, 1.75, 0.125
+    bc[0, 0:2, 128:131] = [0x3F, 0xC0, 0xA0]                    # 1.875, -2, -0.125
+    as_ = rng.uniform(0.1, 10, (M, K // 128)).astype(np.float32)
+    bs = rng.uniform(0.1, 10, (1, 1, K // 128)).astype(np.float32)
+    y, _ = P.fp8_grouped_gemm(ac, as_, bc, bs, np.array([0, M]))
+    for p in range(M):
+        for n in range(N):
+            part = sum(Fraction(F.e4m3_value(int(ac[p, k]))) * Fraction(F.e4m3_value(int(bc[0, n, k])))
+                       for k in range(128, 256))
+            exact = part * Fraction(float(as_[p, 1])) * Fraction(float(bs[0, 0, 1]))
+            if p < 2 and n < 2:
+                assert exact == 0 and y[p, n] == 0
+            assert abs(Fraction(float(y[p, n])) - exact) <= abs(exact) * Fraction(1, 2 ** 24) * (1 + Fraction(1, 2 ** 27))
+
+
 def test_fp8_gemm_dense_is_matmul_and_approximates_full_precision():
     rng = np.random.default_rng(4)
     A = rng.standard_normal((20, 256)).astype(np.float32)

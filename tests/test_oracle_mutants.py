@@ -261,22 +261,39 @@ def test_mutant_fp8_truncating_encoder(monkeypatch):
 
 def test_mutant_fp8_weight_scale_per_row(monkeypatch):
     # the weight scale indexed by output row instead of by its 128-row block
-    orig = P8.fp8_dequantize
+    orig = P8.fp8_row_scales
 
-    def bad(codes, scales, block_rows=1):
+    def bad(scales, block_rows, rows):
         if block_rows != 128:
-            return orig(codes, scales, block_rows)
+            return orig(scales, block_rows, rows)
         sc = np.asarray(scales)
-        idx = np.minimum(np.arange(np.asarray(codes).shape[-2]), sc.shape[-2] - 1)
-        return orig(codes, sc[..., idx, :], 1)
-    monkeypatch.setattr(P8, "fp8_dequantize", bad)
+        idx = np.minimum(np.arange(rows), sc.shape[-2] - 1)
+        return orig(sc[..., idx, :], 1, rows)
+    monkeypatch.setattr(P8, "fp8_row_scales", bad)
     assert _fails(TP8.test_fp8_gemm_equals_exact_rational)
 
 
 def test_mutant_fp8_gemm_drops_activation_scale(monkeypatch):
-    orig = P8.fp8_dequantize
+    orig = P8.fp8_row_scales
 
-    def bad(codes, scales, block_rows=1):
-        return orig(codes, np.ones_like(scales) if block_rows == 1 else scales, block_rows)
-    monkeypatch.setattr(P8, "fp8_dequantize", bad)
+    def bad(scales, block_rows, rows):
+        return orig(np.ones_like(scales) if block_rows == 1 else scales, block_rows, rows)
+    monkeypatch.setattr(P8, "fp8_row_scales", bad)
     assert _fails(TP8.test_fp8_gemm_equals_exact_rational)
+
+
+def test_mutant_fp8_gemm_scales_dequantised_operands(monkeypatch):
+    # products of the dequantised values (E4M3 x float32 scale on each side)
+    # instead of scaled exact block sums: rounding where the code products cancel
+    def bad(a_codes, a_scales, b_codes, b_scales, offsets, a_rows=None, want_absdot=True):
+        E, N, K = b_codes.shape
+        offsets = np.asarray(offsets, np.int64)
+        y = np.zeros((int(offsets[-1]), N), np.float32)
+        for e in range(E):
+            p0, p1 = int(offsets[e]), int(offsets[e + 1])
+            rows = np.arange(p0, p1) if a_rows is None else np.asarray(a_rows)[p0:p1]
+            y[p0:p1] = (P8.fp8_dequantize(a_codes[rows], a_scales[rows], 1)
+                        @ P8.fp8_dequantize(b_codes[e], b_scales[e], 128).T).astype(np.float32)
+        return y, np.zeros_like(y, np.float64)
+    monkeypatch.setattr(P8, "fp8_grouped_gemm", bad)
+    assert _fails(TP8.test_fp8_gemm_single_block_terms_correctly_rounded)
