@@ -48,9 +48,10 @@ def parse():
     ap.add_argument("--ffn", choices=["one_launch", "two_launch"], default="one_launch",
                     help="gate_up + down through moe_expert_ffn (one persistent launch at decode sizes) or the two "
                          "grouped-GEMM calls")
-    ap.add_argument("--format", choices=["nvfp4", "mxfp4"], default="nvfp4",
-                    help="number format: NVFP4 (the reported one) or the MXFP4 variant (E8M0 scale per 32, "
-                         "gfx950's block-scaled FP4 MFMA)")
+    ap.add_argument("--format", choices=["nvfp4", "mxfp4", "fp8"], default="nvfp4",
+                    help="number format: NVFP4 (the reported one), the MXFP4 variant (E8M0 scale per 32, "
+                         "gfx950's block-scaled FP4 MFMA) or the FP8 block-scaled grouped GEMMs (E4M3, float32 "
+                         "scales per 1x128 / 128x128 block)")
     ap.add_argument("--swiglu", choices=["fused", "separate"], default="fused",
                     help="SwiGLU + requant in the gate_up epilogue, or a separate call")
     ap.add_argument("--combine", choices=["gather", "atomic"], default="gather",
@@ -348,6 +349,118 @@ def mx_bench(cfg, args):
                      "alg_bytes_per_launch": int(gu_alg), "avg_launch_ms": round(gu_ms, 5)}}), flush=True)
 
 
+def fp8_bench(cfg, args):
+    """The FP8 block-scaled grouped GEMMs (secondary measurements, not the
+    reported metric).  MoE workloads: the gate_up GEMM over the routed rows
+    (A gathered by the permutation, bf16 out) and the down GEMM (bf16 out) on
+    FP8 activations, weights quantised with 128 x 128 blocks and repacked
+    (untimed), two weight copies alternating; roofline of gate_up against HBM.
+    Dense workload: the GEMM against the dense FP8 MFMA peak."""
+    import numpy as np
+    import torch
+
+    from block_scaled_fp4_permute_amd import (EPI_BF16, fp8_grouped_gemm, fp8_quantize, fp8_weight_repack, lib,
+                                              moe_route_permute)
+
+    lib()
+    dev = torch.device("cuda:0")
+    wl = workloads_mod()
+
+    def ev():
+        return torch.cuda.Event(enable_timing=True)
+
+    def timed(run, steps):
+        for i in range(args.warmup):
+            run(i)
+        torch.cuda.synchronize()
+        t0, t1 = ev(), ev()
+        t0.record()
+        for i in range(steps):
+            run(i)
+        t1.record()
+        torch.cuda.synchronize()
+        return t0.elapsed_time(t1) / steps
+
+    if cfg.dense:
+        M, N, K = cfg.T, cfg.H, cfg.I
+        a32, b32 = wl.torch_dense_operands(cfg, dev)
+        aq, bq = fp8_quantize(a32, 1), fp8_quantize(b32.view(1, N, K), 128)
+        del a32, b32
+        bp = fp8_weight_repack(bq.codes)
+        offsets = torch.tensor([0, M], dtype=torch.int32, device=dev)
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        ms = timed(lambda i: fp8_grouped_gemm(aq, bp, bq.scales, offsets, N=N, m_total=M, epilogue=EPI_BF16, out=out,
+                                              max_rows_per_expert_hint=M), args.steps)
+        tflops = 2.0 * M * N * K / (ms * 1e-3) / 1e12
+        print(json.dumps({
+            "metric": "dense FP8 block-scaled GEMM TFLOP/s (secondary: gfx950 FP8 MFMA)", "value": round(tflops, 1),
+            "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+            "higher_is_better": True, "vs_baseline": None,
+            "dtype": "e4m3 operands, f32 block scales, fp8 mfma, f32 accumulate", "data": "synthetic",
+            "config": {"workload": f"dense_gemm_M{M}_N{N}_K{K}", "format": "fp8_block128", "out": "bf16"},
+            "roofline": {"kernel": "k_fp8_gemm", "bound": "mfma", "achieved": round(tflops, 1),
+                         "peak": MFMA_FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(tflops / MFMA_FP8_PEAK_TFLOPS, 4), "traffic": None}}), flush=True)
+        return
+
+    T, H, I, E, k = cfg.T, cfg.H, cfg.I, cfg.E, cfg.k
+    M = T * k
+    logits = torch.from_numpy(wl.logits(cfg)).to(dev)
+    x = torch.from_numpy(wl.activations(cfg)).to(dev).to(torch.bfloat16)
+    r = moe_route_permute(logits, k)
+    xq = fp8_quantize(x, 1)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(11)
+    hq = fp8_quantize(torch.randn((M, I), generator=gen, device=dev), 1)
+    copies = []
+    for c in range(2):
+        w_gu, w_dn = wl.torch_expert_weights(cfg, dev, copy=c)
+        gq, dq = fp8_quantize(w_gu, 128), fp8_quantize(w_dn, 128)
+        del w_gu, w_dn
+        copies.append((fp8_weight_repack(gq.codes), gq.scales, fp8_weight_repack(dq.codes), dq.scales))
+        del gq, dq
+    y1 = torch.empty((M, 2 * I), dtype=torch.bfloat16, device=dev)
+    y2 = torch.empty((M, H), dtype=torch.bfloat16, device=dev)
+    hint = M // E
+
+    def gate_up(i):
+        gp, gs, _, _ = copies[i % 2]
+        fp8_grouped_gemm(xq, gp, gs, r.offsets, N=2 * I, m_total=M, a_rows=r.perm_src_token, epilogue=EPI_BF16,
+                         out=y1, max_rows_per_expert_hint=hint)
+
+    def down(i):
+        _, _, dp, ds = copies[i % 2]
+        fp8_grouped_gemm(hq, dp, ds, r.offsets, N=H, m_total=M, epilogue=EPI_BF16, out=y2,
+                         max_rows_per_expert_hint=hint)
+
+    def both(i):
+        gate_up(i)
+        down(i)
+
+    ms = timed(both, args.steps)
+    gu_ms = timed(gate_up, args.steps)
+    dn_ms = timed(down, args.steps)
+    counts = r.counts.cpu().numpy()
+    touched = int((counts > 0).sum())
+    gu_w = 2 * I * H * (1 + 4 / (128 * 128))        # E4M3 codes + one float32 per 128 x 128 block
+    dn_w = H * I * (1 + 4 / (128 * 128))
+    weight_bytes = touched * (gu_w + dn_w)
+    gu_alg = touched * gu_w + T * H * (1 + 4 / 128) + M * 2 * I * 2
+    print(json.dumps({
+        "metric": "FP8 block-scaled grouped GEMM pair weight GB/s (secondary: gate_up + down of the MoE workload)",
+        "value": round(weight_bytes / (ms * 1e-3) / 1e9, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True, "vs_baseline": None,
+        "dtype": "e4m3 operands, f32 block scales, fp8 mfma, f32 accumulate", "data": "synthetic",
+        "tflops": round(2.0 * M * 3 * I * H / (ms * 1e-3) / 1e12, 3), "weight_bytes": int(weight_bytes),
+        "stage_ms": {"gate_up": round(gu_ms, 5), "down": round(dn_ms, 5)},
+        "config": {"workload": f"{'decode' if T <= 2048 else 'prefill'}_moe_T{T}_H{H}_I{I}_E{E}_top{k}_{cfg.routing}",
+                   "format": "fp8_block128", "weight_copies": 2},
+        "roofline": {"kernel": "k_fp8_gemm gate_up", "bound": "hbm",
+                     "achieved": round(gu_alg / (gu_ms * 1e-3) / 1e9, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gu_alg / (gu_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4), "traffic": None,
+                     "alg_bytes_per_launch": int(gu_alg), "avg_launch_ms": round(gu_ms, 5)}}), flush=True)
+
+
 def workloads_mod():
     import workloads
     return workloads
@@ -379,6 +492,9 @@ def main():
     lib()
     dev = torch.device("cuda:0")
     cfg = workloads.CONFIGS[args.workload]
+    if args.format == "fp8":
+        fp8_bench(cfg, args)
+        return
     if args.format == "mxfp4":
         mx_bench(cfg, args)
         return

@@ -64,6 +64,17 @@ class GemmArgs(ctypes.Structure):
     ]
 
 
+class Fp8GemmArgs(ctypes.Structure):
+    """Mirror of nvfp4moe_fp8_gemm_args."""
+    _fields_ = [
+        ("a_codes", ctypes.c_void_p), ("a_scales", ctypes.c_void_p), ("a_rows", ctypes.c_void_p),
+        ("a_rows_total", ctypes.c_int64), ("b_packed", ctypes.c_void_p), ("b_scales", ctypes.c_void_p),
+        ("offsets", ctypes.c_void_p), ("E", ctypes.c_int32), ("N", ctypes.c_int32), ("K", ctypes.c_int32),
+        ("m_total", ctypes.c_int64), ("epilogue", ctypes.c_int32), ("out", ctypes.c_void_p),
+        ("max_rows_per_expert_hint", ctypes.c_int32),
+    ]
+
+
 _lib = None
 
 _SIGNATURES = {
@@ -100,6 +111,12 @@ _SIGNATURES = {
     "mxfp4_weight_packed_size": (ctypes.c_size_t, [ctypes.c_int32] * 3),
     "mxfp4_weight_repack": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
                                            ctypes.c_int32, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
+    "fp8_quantize": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+                                    ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]),
+    "fp8_weight_packed_size": (ctypes.c_size_t, [ctypes.c_int32] * 3),
+    "fp8_weight_repack": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                         ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
+    "fp8_grouped_gemm": (ctypes.c_int, [ctypes.POINTER(Fp8GemmArgs), ctypes.c_void_p]),
     "nvfp4moe_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "nvfp4moe_last_error_detail": (ctypes.c_char_p, []),
     "nvfp4moe_version": (ctypes.c_int, []),
@@ -533,6 +550,98 @@ def mxfp4_grouped_gemm(a: MXFP4Tensor, b: MXFP4Tensor, offsets, *, m_total: int,
     return out
 
 
+# --------------------------------------------------------------------------- FP8
+FP8_BLOCK = 128
+
+
+@dataclass
+class FP8Tensor:
+    codes: "object"     # uint8 [..., rows, cols], E4M3 bytes
+    scales: "object"    # float32 [..., ceil(rows/block_rows), cols/128]
+    block_rows: int     # 1 (activations) or 128 (weights)
+
+
+def fp8_quantize(x, block_rows: int = 1, out: FP8Tensor | None = None, stream=None) -> FP8Tensor:
+    """x bf16/float32 [rows, cols] (block_rows 1) or [batch, rows, cols]
+    (block_rows 128: one scale per 128 x 128 tile of each matrix) -> FP8Tensor."""
+    import torch
+    _need(x, x.dtype, "x")
+    cols = x.shape[-1]
+    if block_rows == 1:
+        batch, rows = 1, x.numel() // cols
+        sshape = x.shape[:-1] + (cols // FP8_BLOCK,)
+    else:
+        rows = x.shape[-2]
+        batch = x.numel() // (rows * cols)
+        sshape = x.shape[:-2] + ((rows + FP8_BLOCK - 1) // FP8_BLOCK, cols // FP8_BLOCK)
+    dev = x.device
+    if out is None:
+        out = FP8Tensor(torch.empty(x.shape, dtype=torch.uint8, device=dev),
+                        torch.empty(sshape, dtype=torch.float32, device=dev), block_rows)
+    if out.codes.numel() != x.numel() or tuple(out.scales.shape) != tuple(sshape):
+        raise ValueError("out codes/scales do not match x")
+    _need(out.codes, torch.uint8, "out.codes")
+    _need(out.scales, torch.float32, "out.scales")
+    _check(lib().fp8_quantize(x.data_ptr(), _dtype_code(x), batch, rows, cols, block_rows, out.codes.data_ptr(),
+                              out.scales.data_ptr(), _stream(stream)))
+    return out
+
+
+def fp8_weight_repack(codes, out=None, stream=None):
+    """FP8 weight codes [E, N, K] -> packed tiles (uint8 tensor) for fp8_grouped_gemm."""
+    import torch
+    _need(codes, torch.uint8, "codes")
+    E, N, K = codes.shape
+    nbytes = lib().fp8_weight_packed_size(E, N, K)
+    if out is None:
+        out = torch.empty(nbytes, dtype=torch.uint8, device=codes.device)
+    _check(lib().fp8_weight_repack(codes.data_ptr(), E, N, K, out.data_ptr(), out.numel(), _stream(stream)))
+    return out
+
+
+def fp8_grouped_gemm(a: FP8Tensor, b_packed, b_scales, offsets, *, N: int, m_total: int, a_rows=None,
+                     epilogue: int = EPI_F32, out=None, max_rows_per_expert_hint: int = 0, stream=None):
+    """Grouped FP8 GEMM (see include/nvfp4moe.h): a [rows, K] (1 x 128 blocks),
+    b_packed from fp8_weight_repack, b_scales float32 [E, ceil(N/128), K/128],
+    offsets int32 [E+1].  Epilogues F32 or BF16."""
+    import torch
+    rows_a, K = a.codes.shape
+    E = b_scales.shape[0]
+    dev = a.codes.device
+    if a.block_rows != 1:
+        raise ValueError("A must be quantised with 1 x 128 blocks")
+    _need(a.codes, torch.uint8, "a.codes")
+    _need(a.scales, torch.float32, "a.scales")
+    _need(b_packed, torch.uint8, "b_packed")
+    _need(b_scales, torch.float32, "b_scales")
+    _need(offsets, torch.int32, "offsets")
+    if tuple(a.scales.shape) != (rows_a, K // FP8_BLOCK) or \
+            tuple(b_scales.shape) != (E, (N + FP8_BLOCK - 1) // FP8_BLOCK, K // FP8_BLOCK):
+        raise ValueError("operand shapes disagree")
+    if b_packed.numel() < lib().fp8_weight_packed_size(E, N, K):
+        raise ValueError("b_packed is smaller than the packed size of [E, N, K]")
+    if offsets.numel() < E + 1:
+        raise ValueError("offsets needs E+1 values")
+    if a_rows is not None:
+        _need(a_rows, torch.int32, "a_rows")
+        if a_rows.numel() < m_total:
+            raise ValueError("a_rows shorter than m_total")
+    if epilogue not in (EPI_F32, EPI_BF16):
+        raise ValueError("fp8_grouped_gemm: epilogue F32 or BF16")
+    want = torch.float32 if epilogue == EPI_F32 else torch.bfloat16
+    if out is None:
+        out = torch.empty((m_total, N), dtype=want, device=dev)
+    _need(out, want, "out")
+    if tuple(out.shape) != (m_total, N):
+        raise ValueError("out must be [m_total, N]")
+    args = Fp8GemmArgs(a_codes=a.codes.data_ptr(), a_scales=a.scales.data_ptr(), a_rows=_ptr(a_rows),
+                       a_rows_total=rows_a, b_packed=b_packed.data_ptr(), b_scales=b_scales.data_ptr(),
+                       offsets=offsets.data_ptr(), E=E, N=N, K=K, m_total=m_total, epilogue=epilogue,
+                       out=out.data_ptr(), max_rows_per_expert_hint=max_rows_per_expert_hint)
+    _check(lib().fp8_grouped_gemm(ctypes.byref(args), _stream(stream)))
+    return out
+
+
 # -------------------------------------------------------------------------- swiglu
 def moe_swiglu(gate_up, g=None, out: NVFP4Tensor | None = None, workspace=None, stream=None) -> NVFP4Tensor:
     """gate_up float32/bf16 [M, 2I] -> NVFP4 h = silu(gate) * up."""
@@ -581,5 +690,6 @@ def moe_unpermute_combine(y, perm_of_assignment, topk_w, T: int, k: int, out=Non
 
 __all__ = ["lib", "moe_route_permute", "moe_route_quantize", "moe_route_quantize_noalloc", "nvfp4_quantize", "nvfp4_grouped_gemm", "moe_swiglu", "nvfp4_weight_repack",
            "moe_unpermute_combine", "moe_expert_ffn", "moe_expert_ffn_workspace", "mxfp4_quantize",
-           "mxfp4_grouped_gemm", "mxfp4_weight_repack", "MXFP4Tensor", "NVFP4Tensor", "Routing", "GemmArgs", "NVFP4MoEError",
+           "mxfp4_grouped_gemm", "mxfp4_weight_repack", "MXFP4Tensor", "fp8_quantize", "fp8_weight_repack",
+           "fp8_grouped_gemm", "FP8Tensor", "Fp8GemmArgs", "NVFP4Tensor", "Routing", "GemmArgs", "NVFP4MoEError",
            "F32", "BF16", "EPI_F32", "EPI_BF16", "EPI_SWIGLU_NVFP4", "EPI_COMBINE_F32"]

@@ -453,6 +453,84 @@ int mxfp4_weight_repack(const uint8_t* codes, const uint8_t* scales, int32_t E, 
                     "mxfp4_weight_repack");
 }
 
+// ------------------------------------------------------------------ FP8 block-scaled
+int fp8_quantize(const void* x, int32_t x_dtype, int64_t batch, int64_t rows, int64_t cols, int32_t block_rows,
+                 uint8_t* codes, float* scales, void* stream) {
+  if (!x || !codes || !scales) return fail(NVFP4MOE_ERR_INVALID, "fp8_quantize: null pointer argument");
+  if (x_dtype != NVFP4MOE_F32 && x_dtype != NVFP4MOE_BF16)
+    return fail(NVFP4MOE_ERR_INVALID, "fp8_quantize: x_dtype %d", x_dtype);
+  if (batch <= 0 || rows <= 0 || cols <= 0 || cols % 128 != 0)
+    return fail(NVFP4MOE_ERR_INVALID, "fp8_quantize: batch, rows > 0 and cols a positive multiple of 128 needed");
+  if (block_rows != 1 && block_rows != 128)
+    return fail(NVFP4MOE_ERR_INVALID, "fp8_quantize: block_rows %d (1 or 128)", block_rows);
+  if (block_rows == 128 && (batch > 65535 || rows > 65535ll * 128 || cols / 128 >= (int64_t(1) << 31)))
+    return fail(NVFP4MOE_ERR_UNSUPPORTED, "fp8_quantize: batch > 65535 or rows > 8388480");
+  if (batch * rows * (cols / 128) >= (int64_t(1) << 38))
+    return fail(NVFP4MOE_ERR_UNSUPPORTED, "fp8_quantize: tensor too large");
+  if (!aligned(x, 16) || !aligned(codes, 16) || !aligned(scales, 4))
+    return fail(NVFP4MOE_ERR_INVALID, "fp8_quantize: x and codes must be 16-byte, scales 4-byte aligned");
+  return hip_status(nvfp4::launch_fp8_quantize(x, x_dtype, batch, rows, cols, block_rows, codes, scales,
+                                               static_cast<hipStream_t>(stream)),
+                    "fp8_quantize");
+}
+
+size_t fp8_weight_packed_size(int32_t E, int32_t N, int32_t K) {
+  if (E <= 0 || N <= 0 || K <= 0) return 0;
+  return nvfp4::fp8_packed_weight_bytes(E, N, K);
+}
+
+int fp8_weight_repack(const uint8_t* codes, int32_t E, int32_t N, int32_t K, uint8_t* packed, size_t packed_bytes,
+                      void* stream) {
+  if (!codes || !packed) return fail(NVFP4MOE_ERR_INVALID, "fp8_weight_repack: null pointer argument");
+  if (E <= 0 || N <= 0 || K <= 0) return fail(NVFP4MOE_ERR_INVALID, "fp8_weight_repack: E, N, K must be > 0");
+  if (K % 128 != 0 || N % 16 != 0)
+    return fail(NVFP4MOE_ERR_INVALID, "fp8_weight_repack: K=%d must be a multiple of 128, N=%d of 16", K, N);
+  if (!aligned(codes, 16) || !aligned(packed, 16))
+    return fail(NVFP4MOE_ERR_INVALID, "fp8_weight_repack: codes and packed must be 16-byte aligned");
+  if (static_cast<int64_t>(E) * (N / 16) * (K / 128) * 64 >= (int64_t(1) << 40))
+    return fail(NVFP4MOE_ERR_UNSUPPORTED, "fp8_weight_repack: weights too large");
+  const size_t need = nvfp4::fp8_packed_weight_bytes(E, N, K);
+  if (packed_bytes < need)
+    return fail(NVFP4MOE_ERR_WORKSPACE, "fp8_weight_repack: packed buffer %zu < %zu bytes", packed_bytes, need);
+  return hip_status(nvfp4::launch_fp8_repack(codes, E, N, K, packed, static_cast<hipStream_t>(stream)),
+                    "fp8_weight_repack");
+}
+
+int fp8_grouped_gemm(const nvfp4moe_fp8_gemm_args* a, void* stream) {
+  if (!a) return fail(NVFP4MOE_ERR_INVALID, "fp8_grouped_gemm: args is NULL");
+  if (!a->a_codes || !a->a_scales || !a->b_packed || !a->b_scales || !a->offsets)
+    return fail(NVFP4MOE_ERR_INVALID, "fp8_grouped_gemm: null operand pointer");
+  if (a->E <= 0 || a->N <= 0 || a->K <= 0 || a->m_total < 0 || a->a_rows_total <= 0)
+    return fail(NVFP4MOE_ERR_INVALID, "fp8_grouped_gemm: E, N, K, a_rows_total must be > 0 and m_total >= 0");
+  if (a->K % 128 != 0) return fail(NVFP4MOE_ERR_INVALID, "fp8_grouped_gemm: K=%d not a multiple of 128", a->K);
+  if (a->N % 16 != 0) return fail(NVFP4MOE_ERR_INVALID, "fp8_grouped_gemm: N=%d not a multiple of 16", a->N);
+  if (!aligned(a->a_codes, 16) || !aligned(a->a_scales, 4) || !aligned(a->b_packed, 16) || !aligned(a->b_scales, 4))
+    return fail(NVFP4MOE_ERR_INVALID, "fp8_grouped_gemm: codes and packed tiles must be 16-byte, scales 4-byte aligned");
+  if (a->E > 4096) return fail(NVFP4MOE_ERR_UNSUPPORTED, "fp8_grouped_gemm: E > 4096");
+  if (a->m_total >= (int64_t(1) << 31) || a->a_rows_total * int64_t(a->K) >= (int64_t(1) << 31))
+    return fail(NVFP4MOE_ERR_UNSUPPORTED, "fp8_grouped_gemm: A codes of 2 GiB or more");
+  if (a->epilogue != NVFP4MOE_EPI_F32 && a->epilogue != NVFP4MOE_EPI_BF16)
+    return fail(NVFP4MOE_ERR_UNSUPPORTED, "fp8_grouped_gemm: epilogue %d (F32 or BF16)", a->epilogue);
+  if (!a->out && a->m_total > 0) return fail(NVFP4MOE_ERR_INVALID, "fp8_grouped_gemm: out is NULL");
+  if (a->m_total == 0) return ok();
+  nvfp4::Fp8Params prm{};
+  prm.a_codes = a->a_codes;
+  prm.a_scales = a->a_scales;
+  prm.a_rows = a->a_rows;
+  prm.b_packed = a->b_packed;
+  prm.b_scales = a->b_scales;
+  prm.offsets = a->offsets;
+  prm.E = a->E;
+  prm.N = a->N;
+  prm.K = a->K;
+  prm.m_total = static_cast<int>(a->m_total);
+  prm.a_rows_total = static_cast<int>(a->a_rows_total);
+  prm.out = a->out;
+  return hip_status(nvfp4::launch_fp8_gemm(prm, a->epilogue, a->m_total, a->max_rows_per_expert_hint,
+                                           static_cast<hipStream_t>(stream)),
+                    "fp8_grouped_gemm");
+}
+
 // ------------------------------------------------------------------ packed weights
 size_t nvfp4_weight_packed_size(int32_t E, int32_t N, int32_t K) {
   if (E <= 0 || N <= 0 || K <= 0) return 0;

@@ -1,0 +1,431 @@
+// FP8 block-scaled variant for gfx950: E4M3 operands with float32 scales per
+// 128-value block along K (one per row for activations, one per 128 x 128
+// tile for weights) - the FP8 grouped GEMM the pages name next to the FP4
+// ones ("From Empirical Limits to Research-Driven Optimization", section
+// "Sections 2-4: Framework and Community Landscape"), with the blockwise
+// scaling of the FP8 collective they search for ("The Critical Search:
+// Uncovering SM120 CUTLASS Collective Implementations", section "Output
+// Knowledge Created").
+//
+//   fp8_quantize  s = absmax_block / 448 (1 for a zero block), q = E4M3
+//                 nearest-even of |x| / s (correctly rounded float32 quotient),
+//                 saturating, sign copied
+//   fp8 gemm      per 128-value K step, one v_mfma_scale_f32_16x16x128_f8f6f4
+//                 (E4M3 operands, unit E8M0 scales) per 16 x 16 tile gives the
+//                 block's partial sum, and the float32 block scales enter as
+//                 acc += partial * (sa[row] * sb[tile]) (four FMAs a lane)
+//
+// Operand mapping: a K step is 128 values; lane l = 16 g + r holds values
+// [32 g, 32 g + 32) of its row (8 dwords), the layout of the 16x16x128 FP8
+// instruction.  Weights are read from packed tiles (fp8_weight_repack): tile
+// (e, 16-row tile rt, step st) is 2048 bytes, lane l's first 16 bytes at
+// [16 l, 16 l + 16) and the next 16 at [1024 + 16 l, +16).
+#include "gemm_device.h"
+
+namespace nvfp4 {
+
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+constexpr int kFp8Block = 128;
+constexpr int kFp8Tile = 2048;
+constexpr int kFp8FmtE4M3 = 0;         // operand format code of E4M3 in the scaled MFMA
+constexpr int kE8M0One = 127;          // E8M0 code of 2^0
+
+__device__ __forceinline__ uint32_t fp8_encode(float x, float s) {
+  const float v = fabsf(x) / s;                       // correctly rounded float32 quotient
+  return f32_to_e4m3_sat(v) | (__float_as_uint(x) >> 31 << 7);
+}
+
+// ------------------------------------------------------------------ quantise, 1 x 128 blocks
+// One wave per block (a lane holds 2 values), four blocks per workgroup.
+template <int DT>
+__global__ __launch_bounds__(256) void k_fp8_quant_rows(const void* __restrict__ x, int64_t nblocks,
+                                                        uint8_t* __restrict__ codes, float* __restrict__ scales) {
+  const int64_t b = blockIdx.x * 4ll + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (b >= nblocks) return;
+  float v0, v1;
+  if constexpr (DT == 1) {
+    const uint32_t w = reinterpret_cast<const uint32_t*>(static_cast<const uint16_t*>(x) + b * kFp8Block)[lane];
+    v0 = __uint_as_float(w << 16);
+    v1 = __uint_as_float(w & 0xFFFF0000u);
+  } else {
+    const float2 w = reinterpret_cast<const float2*>(static_cast<const float*>(x) + b * kFp8Block)[lane];
+    v0 = w.x;
+    v1 = w.y;
+  }
+  float m = fmaxf(fabsf(v0), fabsf(v1));
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) m = fmaxf(m, __shfl_xor(m, d));
+  const float s = m > 0.0f ? m / 448.0f : 1.0f;
+  const uint32_t c = fp8_encode(v0, s) | (fp8_encode(v1, s) << 8);
+  reinterpret_cast<uint16_t*>(codes + b * kFp8Block)[lane] = static_cast<uint16_t>(c);
+  if (lane == 0) scales[b] = s;
+}
+
+// ------------------------------------------------------------------ quantise, 128 x 128 blocks
+// One workgroup per block of matrix blockIdx.z: thread t takes row t / 2 of
+// the block, 64 values (half t % 2); rows past the matrix count as zeros.
+template <int DT>
+__global__ __launch_bounds__(256) void k_fp8_quant_tiles(const void* __restrict__ x_all, int64_t rows, int64_t cols,
+                                                         uint8_t* __restrict__ codes_all,
+                                                         float* __restrict__ scales_all) {
+  __shared__ float s_max[4];
+  const int64_t rb = blockIdx.y, cb = blockIdx.x, z = blockIdx.z;
+  const int64_t nrb = gridDim.y;
+  const void* x = static_cast<const uint8_t*>(x_all) + z * rows * cols * (DT == 1 ? 2 : 4);
+  uint8_t* codes = codes_all + z * rows * cols;
+  float* scales = scales_all + z * nrb * (cols / kFp8Block);
+  const int t = threadIdx.x;
+  const int64_t r = rb * kFp8Block + (t >> 1);
+  const int64_t c0 = cb * kFp8Block + 64 * (t & 1);
+  const bool row_ok = r < rows;
+  float v[64];
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    if constexpr (DT == 1) {
+      uint4 w = make_uint4(0u, 0u, 0u, 0u);
+      if (row_ok) w = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(x) + r * cols + c0)[q];
+      const uint32_t u[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        v[8 * q + 2 * i] = __uint_as_float(u[i] << 16);
+        v[8 * q + 2 * i + 1] = __uint_as_float(u[i] & 0xFFFF0000u);
+      }
+    } else {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        float4 w = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (row_ok) w = reinterpret_cast<const float4*>(static_cast<const float*>(x) + r * cols + c0)[2 * q + h];
+        v[8 * q + 4 * h] = w.x; v[8 * q + 4 * h + 1] = w.y; v[8 * q + 4 * h + 2] = w.z; v[8 * q + 4 * h + 3] = w.w;
+      }
+    }
+  }
+  float m = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 64; ++i) m = fmaxf(m, fabsf(v[i]));
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) m = fmaxf(m, __shfl_xor(m, d));
+  if ((t & 63) == 0) s_max[t >> 6] = m;
+  __syncthreads();
+  m = fmaxf(fmaxf(s_max[0], s_max[1]), fmaxf(s_max[2], s_max[3]));
+  const float s = m > 0.0f ? m / 448.0f : 1.0f;
+  if (t == 0) scales[rb * (cols / kFp8Block) + cb] = s;
+  if (!row_ok) return;
+  uint4* dst = reinterpret_cast<uint4*>(codes + r * cols + c0);
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    uint32_t w[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int e = 16 * q + 4 * i;
+      w[i] = fp8_encode(v[e], s) | (fp8_encode(v[e + 1], s) << 8) | (fp8_encode(v[e + 2], s) << 16) |
+             (fp8_encode(v[e + 3], s) << 24);
+    }
+    dst[q] = make_uint4(w[0], w[1], w[2], w[3]);
+  }
+}
+
+hipError_t launch_fp8_quantize(const void* x, int dtype, int64_t batch, int64_t rows, int64_t cols, int block_rows,
+                               uint8_t* codes, float* scales, hipStream_t stream) {
+  if (block_rows == 1) {
+    const int64_t nb = batch * rows * (cols / kFp8Block);
+    const dim3 grid(static_cast<unsigned>((nb + 3) / 4));
+    if (dtype == 1)
+      hipLaunchKernelGGL(k_fp8_quant_rows<1>, grid, dim3(256), 0, stream, x, nb, codes, scales);
+    else
+      hipLaunchKernelGGL(k_fp8_quant_rows<0>, grid, dim3(256), 0, stream, x, nb, codes, scales);
+  } else {
+    const dim3 grid(static_cast<unsigned>(cols / kFp8Block), static_cast<unsigned>((rows + kFp8Block - 1) / kFp8Block),
+                    static_cast<unsigned>(batch));
+    if (dtype == 1)
+      hipLaunchKernelGGL(k_fp8_quant_tiles<1>, grid, dim3(256), 0, stream, x, rows, cols, codes, scales);
+    else
+      hipLaunchKernelGGL(k_fp8_quant_tiles<0>, grid, dim3(256), 0, stream, x, rows, cols, codes, scales);
+  }
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------------ packed weights
+size_t fp8_packed_weight_bytes(int E, int N, int K) {
+  return static_cast<size_t>(E) * ((N + 15) / 16) * ((K + kFp8Block - 1) / kFp8Block) * kFp8Tile;
+}
+
+__global__ __launch_bounds__(256) void k_fp8_repack(const uint8_t* __restrict__ codes, int E, int N, int K,
+                                                    uint8_t* __restrict__ packed, int64_t total_tiles) {
+  const int64_t t = blockIdx.x * 256ll + threadIdx.x;
+  const int64_t tile = t >> 6;
+  const int lane = static_cast<int>(t & 63);
+  if (tile >= total_tiles) return;
+  const int nst = (K + kFp8Block - 1) / kFp8Block;
+  const int ntr = (N + 15) / 16;
+  const int st = static_cast<int>(tile % nst);
+  const int rt = static_cast<int>((tile / nst) % ntr);
+  const int e = static_cast<int>(tile / (static_cast<int64_t>(nst) * ntr));
+  const int n = 16 * rt + (lane & 15);
+  const int g = lane >> 4;
+  uint8_t* dst = packed + tile * kFp8Tile;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int k = kFp8Block * st + 32 * g + 16 * h;
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (n < N && k < K) v = *reinterpret_cast<const u32x4*>(codes + (static_cast<size_t>(e) * N + n) * K + k);
+    *reinterpret_cast<u32x4*>(dst + 1024 * h + 16 * lane) = v;
+  }
+}
+
+hipError_t launch_fp8_repack(const uint8_t* codes, int E, int N, int K, uint8_t* packed, hipStream_t stream) {
+  const int64_t tiles = static_cast<int64_t>(E) * ((N + 15) / 16) * ((K + kFp8Block - 1) / kFp8Block);
+  hipLaunchKernelGGL(k_fp8_repack, dim3(static_cast<unsigned>((tiles * 64 + 255) / 256)), dim3(256), 0, stream, codes,
+                     E, N, K, packed, tiles);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------------ GEMM
+
+constexpr int kFp8RowLds = 144;     // A row pitch in LDS: 128 code bytes + 16 of padding
+
+// A staging: thread t stages (row t / 4, quarter t % 4: 32 code bytes) of the
+// chunk's 64 rows for one step, and threads t < 64 the row's block scale;
+// rows that do not exist stage zero codes.
+struct Fp8AStage {
+  rsrc_t rc, rs;
+  uint32_t vc, vs;
+  bool row_ok;
+  int q;
+};
+
+__device__ __forceinline__ void fp8a_setup(const Fp8Params& p, int row0, int m0, int rows, Fp8AStage& S) {
+  const int t = threadIdx.x;
+  const uint32_t krow = static_cast<uint32_t>(p.K), srow = static_cast<uint32_t>(p.K / kFp8Block);
+  S.rc = make_rsrc(p.a_codes, static_cast<uint32_t>(p.a_rows_total) * krow);
+  S.rs = make_rsrc(p.a_scales, static_cast<uint32_t>(p.a_rows_total) * srow * 4u);
+  const int ar = t >> 2;
+  S.q = t & 3;
+  S.row_ok = ar < rows;
+  int arow = row0 + m0 + (S.row_ok ? ar : 0);
+  if (p.a_rows) arow = p.a_rows[arow];
+  arow = (arow >= 0 && arow < p.a_rows_total) ? arow : 0;
+  S.vc = static_cast<uint32_t>(arow) * krow + 32u * S.q;
+  const int sr = t & 63;       // every thread stages a scale: t, t + 64, ... the same row's
+  int srow_i = row0 + m0 + (sr < rows ? sr : 0);
+  if (p.a_rows) srow_i = p.a_rows[srow_i];
+  srow_i = (srow_i >= 0 && srow_i < p.a_rows_total) ? srow_i : 0;
+  S.vs = static_cast<uint32_t>(srow_i) * srow * 4u;
+}
+
+struct Fp8ARegs {
+  u32x4 c[2];
+  float s;
+};
+
+__device__ __forceinline__ void fp8a_load(const Fp8AStage& S, Fp8ARegs& R, int st, int nsteps) {
+  const int s = min(st, nsteps - 1);
+  const uint32_t oc = static_cast<uint32_t>(s) * kFp8Block;
+  R.c[0] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(S.rc, S.vc + oc, 0, 0));
+  R.c[1] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(S.rc, S.vc + oc + 16u, 0, 0));
+  R.s = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(S.rs, S.vs + 4u * s, 0, 0));
+}
+
+// rows that do not exist, and steps past the last, stage zero codes
+__device__ __forceinline__ void fp8a_store(const Fp8AStage& S, const Fp8ARegs& R, bool step_ok, int rows,
+                                           uint8_t* __restrict__ lds) {
+  const int t = threadIdx.x;
+  const u32x4 z = {0u, 0u, 0u, 0u};
+  const bool ok = S.row_ok && step_ok;
+  u32x4* dst = reinterpret_cast<u32x4*>(lds + (t >> 2) * kFp8RowLds + 32 * S.q);
+  dst[0] = ok ? R.c[0] : z;
+  dst[1] = ok ? R.c[1] : z;
+  reinterpret_cast<float*>(lds + 64 * kFp8RowLds)[t & 63] = ((t & 63) < rows) ? R.s : 0.0f;
+}
+constexpr int kFp8ALds = 64 * kFp8RowLds + 64 * 4;
+
+struct Fp8B {
+  u32x4 c[2];
+};
+
+template <int WN, bool NT>
+__device__ __forceinline__ void fp8b_load(const uint8_t* const (&tiles)[WN], Fp8B (&B)[WN], int st, int nsteps) {
+  const int lane = threadIdx.x & 63;
+  const size_t o = static_cast<size_t>(min(st, nsteps - 1)) * kFp8Tile;
+#pragma unroll
+  for (int j = 0; j < WN; ++j) {
+    const u32x4* p0 = reinterpret_cast<const u32x4*>(tiles[j] + o + 16 * lane);
+    const u32x4* p1 = reinterpret_cast<const u32x4*>(tiles[j] + o + 1024 + 16 * lane);
+    if constexpr (NT) {
+      B[j].c[0] = __builtin_nontemporal_load(p0);
+      B[j].c[1] = __builtin_nontemporal_load(p1);
+    } else {
+      B[j].c[0] = *p0;
+      B[j].c[1] = *p1;
+    }
+  }
+}
+
+__device__ __forceinline__ i32x8 fp8_frag(const u32x4& lo, const u32x4& hi) {
+  i32x8 r = {static_cast<int>(lo.x), static_cast<int>(lo.y), static_cast<int>(lo.z), static_cast<int>(lo.w),
+             static_cast<int>(hi.x), static_cast<int>(hi.y), static_cast<int>(hi.z), static_cast<int>(hi.w)};
+  return r;
+}
+
+// one K step: per (row tile, column tile) the block's partial sum, scaled
+// into the accumulator by the row's block scale and the wave's weight block
+// scale (a wave's 64 columns lie in one 128-row weight block)
+template <int MTA, int WN>
+__device__ __forceinline__ void fp8_step(const uint8_t* __restrict__ a_lds, const Fp8B (&B)[WN], float sb,
+                                         float4v (&acc)[4][WN]) {
+  const int lane = threadIdx.x & 63;
+  const int lr = lane & 15, g = lane >> 4;
+#pragma unroll
+  for (int r = 0; r < MTA; ++r) {
+    const u32x4* src = reinterpret_cast<const u32x4*>(a_lds + (16 * r + lr) * kFp8RowLds + 32 * g);
+    const i32x8 af = fp8_frag(src[0], src[1]);
+    const float4v sa = *reinterpret_cast<const float4v*>(a_lds + 64 * kFp8RowLds + 4 * (16 * r + 4 * g));
+    float4v part[WN];
+#pragma unroll
+    for (int j = 0; j < WN; ++j) {
+      const float4v z = {0.f, 0.f, 0.f, 0.f};
+      part[j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af, fp8_frag(B[j].c[0], B[j].c[1]), z, kFp8FmtE4M3,
+                                                                 kFp8FmtE4M3, 0, kE8M0One, 0, kE8M0One);
+    }
+    const float4v sab = sa * sb;
+#pragma unroll
+    for (int j = 0; j < WN; ++j)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[r][j][i] = __builtin_fmaf(part[j][i], sab[i], acc[r][j][i]);
+  }
+}
+
+// Two steps per iteration, branch free: A for step s + 1 goes to the other
+// LDS buffer while step s runs; steps past the last read the last step's
+// weights against zero activation codes (nothing added).
+template <int MTA, int WN, bool NT>
+__device__ __forceinline__ void fp8_loop(const Fp8AStage& AS, const uint8_t* const (&tiles)[WN],
+                                         const float* __restrict__ bsc, int nsteps, int rows,
+                                         uint8_t* __restrict__ lds0, uint8_t* __restrict__ lds1,
+                                         float4v (&acc)[4][WN]) {
+  Fp8B B0[WN], B1[WN];
+  Fp8ARegs ra;
+  fp8a_load(AS, ra, 0, nsteps);
+  fp8b_load<WN, NT>(tiles, B0, 0, nsteps);
+  float s0 = bsc[0];
+  fp8b_load<WN, NT>(tiles, B1, 1, nsteps);
+  float s1 = bsc[min(1, nsteps - 1)];
+  fp8a_store(AS, ra, true, rows, lds0);
+  fp8a_load(AS, ra, 1, nsteps);
+  __syncthreads();
+  for (int st = 0; st < nsteps; st += 2) {
+    fp8_step<MTA, WN>(lds0, B0, s0, acc);
+    fp8a_store(AS, ra, st + 1 < nsteps, rows, lds1);
+    fp8a_load(AS, ra, st + 2, nsteps);
+    fp8b_load<WN, NT>(tiles, B0, st + 2, nsteps);
+    s0 = bsc[min(st + 2, nsteps - 1)];
+    __syncthreads();
+    fp8_step<MTA, WN>(lds1, B1, s1, acc);
+    fp8a_store(AS, ra, st + 2 < nsteps, rows, lds0);
+    fp8a_load(AS, ra, st + 3, nsteps);
+    fp8b_load<WN, NT>(tiles, B1, st + 3, nsteps);
+    s1 = bsc[min(st + 3, nsteps - 1)];
+    __syncthreads();
+  }
+}
+
+template <int EPI>
+__device__ __forceinline__ void fp8_store_tile(const Fp8Params& p, const float4v& acc, int prow0, int rows_left,
+                                               int col, bool col_ok) {
+  const int lg = (threadIdx.x & 63) >> 4;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int m = 4 * lg + i;
+    if (m >= rows_left || !col_ok) continue;
+    const size_t o = static_cast<size_t>(prow0 + m) * p.N + col;
+    if constexpr (EPI == EPI_F32)
+      static_cast<float*>(p.out)[o] = acc[i];
+    else
+      static_cast<uint16_t*>(p.out)[o] = f32_to_bf16(acc[i]);
+  }
+}
+
+// the task map's view of the FP8 problem (offsets, experts, rows, tiles)
+__device__ __forceinline__ GemmParams fp8_map_params(const Fp8Params& p, int n_tiles) {
+  GemmParams g{};
+  g.offsets = p.offsets;
+  g.E = p.E;
+  g.N = p.N;
+  g.K = p.K;
+  g.m_total = p.m_total;
+  g.n_tiles = n_tiles;
+  g.slots = 1 << 30;
+  return g;
+}
+
+template <int EPI, bool NT>
+__global__ __launch_bounds__(256, 2) void k_fp8_gemm(const Fp8Params p, int n_tiles) {
+  constexpr int WN = 4, BN = 4 * WN * 16;
+  __shared__ __attribute__((aligned(16))) uint8_t a_lds[2][kFp8ALds];
+  int e, m0, nt;
+  bool narrow;
+  const GemmParams map = fp8_map_params(p, n_tiles);
+  if (!find_task<4, true, 0>(map, e, m0, nt, narrow)) return;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lr = threadIdx.x & 15;
+  const int row0 = min(max(p.offsets[e], 0), p.m_total);
+  const int Me = min(max(p.offsets[e + 1], 0), p.m_total) - row0;
+  const int rows = min(64, Me - m0);
+  const int mt_active = (rows + 15) >> 4;
+  const int N = p.N, K = p.K;
+  const int nsteps = K / kFp8Block;
+  const int ntr = (N + 15) / 16;
+  const int nsb = (N + kFp8Block - 1) / kFp8Block;
+  Fp8AStage AS;
+  fp8a_setup(p, row0, m0, rows, AS);
+  const uint8_t* tiles[WN];
+  int col0[WN];
+  bool cok[WN];
+  const int wcol = nt * BN + wave * WN * 16;      // the wave's first column, a multiple of 64
+#pragma unroll
+  for (int j = 0; j < WN; ++j) {
+    col0[j] = wcol + j * 16;
+    cok[j] = col0[j] + lr < N;
+    const int rt = min(col0[j] / 16, ntr - 1);
+    tiles[j] = p.b_packed + (static_cast<size_t>(e) * ntr + rt) * nsteps * kFp8Tile;
+  }
+  const float* bsc = p.b_scales + (static_cast<size_t>(e) * nsb + min(wcol, N - 1) / kFp8Block) * nsteps;
+  float4v acc[4][WN];
+#pragma unroll
+  for (int r = 0; r < 4; ++r)
+#pragma unroll
+    for (int j = 0; j < WN; ++j) acc[r][j] = float4v{0.f, 0.f, 0.f, 0.f};
+  switch (mt_active) {
+    case 1: fp8_loop<1, WN, NT>(AS, tiles, bsc, nsteps, rows, a_lds[0], a_lds[1], acc); break;
+    case 2: fp8_loop<2, WN, NT>(AS, tiles, bsc, nsteps, rows, a_lds[0], a_lds[1], acc); break;
+    case 3: fp8_loop<3, WN, NT>(AS, tiles, bsc, nsteps, rows, a_lds[0], a_lds[1], acc); break;
+    default: fp8_loop<4, WN, NT>(AS, tiles, bsc, nsteps, rows, a_lds[0], a_lds[1], acc); break;
+  }
+  const int prow0 = row0 + m0;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    if (r >= mt_active) continue;
+#pragma unroll
+    for (int j = 0; j < WN; ++j) fp8_store_tile<EPI>(p, acc[r][j], prow0 + 16 * r, rows - 16 * r, col0[j] + lr, cok[j]);
+  }
+}
+
+hipError_t launch_fp8_gemm(const Fp8Params& p, int epilogue, int64_t m_total, int hint, hipStream_t stream) {
+  constexpr int BN = 256;
+  const int n_tiles = (p.N + BN - 1) / BN;
+  const int64_t blocks = ((((m_total + 63) / 64 + p.E) * n_tiles) + 7) / 8 * 8;
+  if (blocks >= (int64_t(1) << 31)) return hipErrorInvalidConfiguration;
+  const int64_t rows_per_expert = hint > 0 ? hint : m_total / p.E;
+  const bool nt = rows_per_expert < 64;
+  const dim3 grid(static_cast<unsigned>(blocks));
+  if (epilogue == EPI_F32) {
+    if (nt) hipLaunchKernelGGL((k_fp8_gemm<EPI_F32, true>), grid, dim3(256), 0, stream, p, n_tiles);
+    else hipLaunchKernelGGL((k_fp8_gemm<EPI_F32, false>), grid, dim3(256), 0, stream, p, n_tiles);
+  } else {
+    if (nt) hipLaunchKernelGGL((k_fp8_gemm<EPI_BF16, true>), grid, dim3(256), 0, stream, p, n_tiles);
+    else hipLaunchKernelGGL((k_fp8_gemm<EPI_BF16, false>), grid, dim3(256), 0, stream, p, n_tiles);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace nvfp4

@@ -58,10 +58,29 @@ hipError_t launch_mx_quantize(const void* x, int dtype, int64_t rows, int64_t co
                               uint8_t* scales, hipStream_t stream);
 hipError_t launch_mx_gemm(const GemmParams& prm, int epilogue, int64_t m_total, int hint, hipStream_t stream);
 size_t mx_packed_weight_bytes(int E, int N, int K);
+
 hipError_t launch_mx_repack(const uint8_t* codes, const uint8_t* scales, int E, int N, int K, uint8_t* packed,
                             hipStream_t stream);
 size_t moe_ffn_ws_bytes(int E, int64_t m_total, int H, int I);
 hipError_t launch_moe_ffn(GemmParams gu, GemmParams dn, int64_t m_total, bool cached, void* ws, int spin_limit,
                           hipStream_t stream);
+
+// Kernel-side arguments of the grouped FP8 GEMM (validated on the host first).
+struct Fp8Params {
+  const uint8_t* a_codes;
+  const float* a_scales;       // [a_rows_total, K/128]
+  const int32_t* a_rows;
+  const uint8_t* b_packed;
+  const float* b_scales;       // [E, ceil(N/128), K/128]
+  const int32_t* offsets;
+  int E, N, K, m_total, a_rows_total;
+  void* out;
+};
+
+hipError_t launch_fp8_quantize(const void* x, int dtype, int64_t batch, int64_t rows, int64_t cols, int block_rows,
+                               uint8_t* codes, float* scales, hipStream_t stream);
+size_t fp8_packed_weight_bytes(int E, int N, int K);
+hipError_t launch_fp8_repack(const uint8_t* codes, int E, int N, int K, uint8_t* packed, hipStream_t stream);
+hipError_t launch_fp8_gemm(const Fp8Params& p, int epilogue, int64_t m_total, int hint, hipStream_t stream);
 
 }  // namespace nvfp4

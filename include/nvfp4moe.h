@@ -295,6 +295,57 @@ size_t mxfp4_weight_packed_size(int32_t E, int32_t N, int32_t K);
 int mxfp4_weight_repack(const uint8_t* codes, const uint8_t* scales, int32_t E, int32_t N, int32_t K,
                         uint8_t* packed, size_t packed_bytes, void* stream);
 
+/* ---------------------------------------------------------------- FP8 block-scaled variant
+ * FP8 E4M3 operands with float32 block scales along K (the FP8 grouped GEMM
+ * the pages list beside the FP4 ones: "From Empirical Limits ...", section
+ * "Sections 2-4: Framework and Community Landscape"; the blockwise-scaled
+ * FP8 collective: "The Critical Search: Uncovering SM120 CUTLASS Collective
+ * Implementations", section "Output Knowledge Created").  Blocks of 128
+ * values along K: one scale per row and block for activations (1 x 128), one
+ * per 128 x 128 tile for weights.
+ *   codes  uint8 [rows, cols]   E4M3 (OCP E4M3FN) bytes, sign in bit 7
+ *   scales float [ceil(rows/block_rows), cols/128]
+ * Quantiser: s = absmax_block / 448 (float32 division; 1 for an all-zero
+ * block), code = E4M3 nearest-even of |x| / s (correctly rounded float32
+ * quotient), saturating at 448, sign copied from x.
+ * fp8_quantize: x bf16 or float32 [batch, rows, cols] (finite, 16-byte aligned,
+ * cols % 128 == 0); block_rows 1 (activations: batch is folded into rows) or
+ * 128 (weights: each of the batch matrices has its own row blocks, scales
+ * [batch, ceil(rows/128), cols/128]; rows <= 8388480, batch <= 65535).  codes
+ * 16-byte, scales 4-byte aligned. */
+int fp8_quantize(const void* x, int32_t x_dtype, int64_t batch, int64_t rows, int64_t cols, int32_t block_rows,
+                 uint8_t* codes, float* scales, void* stream);
+/* FP8 weights [E, N, K] repacked once into tiles of 16 rows x 128 K (2048
+ * bytes, each lane's 32 bytes in the order the kernel's lanes read them; zero
+ * codes past N).  Private layout, pure data movement.  K % 128 == 0, N % 16 ==
+ * 0, 16-byte aligned codes and packed. */
+size_t fp8_weight_packed_size(int32_t E, int32_t N, int32_t K);
+int fp8_weight_repack(const uint8_t* codes, int32_t E, int32_t N, int32_t K, uint8_t* packed, size_t packed_bytes,
+                      void* stream);
+/* Grouped FP8 GEMM, per expert e and GEMM row p in [offsets[e], offsets[e+1])
+ * with A row r = a_rows[p] (or p):
+ *   y[p, n] = sum_kb sa[r, kb] * sb[e, n / 128, kb] * sum_{k in block kb} A[r, k] B[e, n, k]
+ * Each block's partial sum comes from the FP8 matrix instruction in float32
+ * and enters the float32 accumulator scaled by sa * sb.  Same grouping and
+ * bounds rules as nvfp4_grouped_gemm; epilogues EPI_F32 and EPI_BF16 only. */
+typedef struct nvfp4moe_fp8_gemm_args {
+  const uint8_t* a_codes;     /* [a_rows_total, K] E4M3, 16-byte aligned */
+  const float* a_scales;      /* [a_rows_total, K/128] */
+  const int32_t* a_rows;      /* device [m_total] or NULL; entries in [0, a_rows_total) */
+  int64_t a_rows_total;
+  const uint8_t* b_packed;    /* fp8_weight_repack layout of [E, N, K], 16-byte aligned */
+  const float* b_scales;      /* [E, ceil(N/128), K/128] */
+  const int32_t* offsets;     /* device [E+1], as for nvfp4_grouped_gemm */
+  int32_t E;
+  int32_t N;                  /* multiple of 16 */
+  int32_t K;                  /* multiple of 128 */
+  int64_t m_total;
+  int32_t epilogue;           /* NVFP4MOE_EPI_F32 or NVFP4MOE_EPI_BF16 */
+  void* out;                  /* float or bf16 [m_total, N] */
+  int32_t max_rows_per_expert_hint;  /* as for nvfp4_grouped_gemm: < 64 streams weights non-temporally */
+} nvfp4moe_fp8_gemm_args;
+int fp8_grouped_gemm(const nvfp4moe_fp8_gemm_args* args, void* stream);
+
 /* ---------------------------------------------------------------- packed weights
  * Weights are static, so they can be repacked once into a tile layout that the
  * grouped GEMM streams with fully contiguous, non-temporal loads: tile

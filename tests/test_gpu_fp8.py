@@ -1,0 +1,244 @@
+"""GPU parity of the FP8 block-scaled variant (fp8_quantize, fp8_weight_repack,
+fp8_grouped_gemm on gfx950's FP8 MFMA with float32 block scales) against the
+FP8 oracle: the quantiser bit for bit (1 x 128 and 128 x 128 blocks, ragged
+row blocks, decision points, the subnormal range), the packed tile layout
+byte for byte, the GEMM within 1e-3 sum|a^ b^| + 1e-6 (bf16 out: + 2^-8 |y|),
+bit for bit where every float32 sum is exact, within two float32 ulps where
+each output is a single block term (which pins each block's pair of scales),
+and whole outputs at the Zipf decode gate_up and down shapes.  Every GPU
+stage is fed the oracle's inputs or seeded raw bytes."""
+import numpy as np
+import pytest
+import torch
+
+import block_scaled_fp4_permute_amd as m
+import workloads
+from oracle import fp8 as F8
+from oracle import moe as OM
+from tests.gpu_common import assert_gemm_close, bf16_to_f32, down, up
+
+pytestmark = pytest.mark.gpu
+
+
+def _a(codes, scales):
+    return m.FP8Tensor(up(codes), up(scales), 1)
+
+
+def _ragged_values(rng, rows, cols):
+    x = rng.standard_normal((rows, cols)).astype(np.float32)
+    x *= np.exp2(rng.integers(-30, 30, (rows, cols // 128))).repeat(128, axis=1).astype(np.float32)
+    x[0, :128] = -0.0                                   # a zero block of negative zeros
+    if cols >= 256:
+        x[0, 128:256] *= np.float32(2.0 ** -20)         # tiny block: codes in E4M3's subnormal range
+        x[0, 130] = np.float32(3.0)                     # ... with one large value
+    return x
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("rows,cols", [(1, 128), (37, 256), (300, 6144)])
+def test_fp8_quantize_rows_bit_exact(dtype, rows, cols):
+    print(f"fp8 quantize 1x128 {dtype} {rows}x{cols}", flush=True)
+    rng = np.random.default_rng(rows * 7 + cols)
+    x = _ragged_values(rng, rows, cols)
+    if dtype == "bf16":
+        x = workloads.to_bf16_values(x)
+    xt = up(x).to(torch.bfloat16) if dtype == "bf16" else up(x)
+    q = m.fp8_quantize(xt, 1)
+    torch.cuda.synchronize()
+    c_ref, s_ref = F8.fp8_quantize(x, 1)
+    assert np.array_equal(down(q.scales), s_ref)
+    assert np.array_equal(down(q.codes), c_ref)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("E,N,K", [(1, 128, 128), (3, 200, 384), (2, 16, 256), (4, 512, 1024)])
+def test_fp8_quantize_tiles_bit_exact(dtype, E, N, K):
+    print(f"fp8 quantize 128x128 {dtype} E={E} N={N} K={K}", flush=True)
+    rng = np.random.default_rng(E * 1000 + N + K)
+    w = np.stack([_ragged_values(rng, N, K) for _ in range(E)])
+    if dtype == "bf16":
+        w = workloads.to_bf16_values(w)
+    wt = up(w).to(torch.bfloat16) if dtype == "bf16" else up(w)
+    q = m.fp8_quantize(wt, 128)
+    torch.cuda.synchronize()
+    for e in range(E):
+        c_ref, s_ref = F8.fp8_quantize(w[e], 128)
+        assert np.array_equal(down(q.scales[e]), s_ref), f"scales of matrix {e}"
+        assert np.array_equal(down(q.codes[e]), c_ref), f"codes of matrix {e}"
+
+
+def test_fp8_quantize_decision_points():
+    # blocks with absmax 448 * 2^k (so s = 2^k exactly and every quotient is
+    # exact), holding every E4M3 midpoint and its float32 neighbours, in the
+    # normal and subnormal ranges
+    pos = np.array(sorted({float(v) for v in F8.e4m3_decode(np.arange(0x7F, dtype=np.uint8))}))
+    mids = ((pos[:-1] + pos[1:]) / 2).astype(np.float32)
+    vals = np.concatenate([mids, np.nextafter(mids, np.float32(0)), np.nextafter(mids, np.float32(1e9))])
+    vals = vals[vals < 448]
+    per = 127
+    nblk = (len(vals) + per - 1) // per
+    rows = []
+    for k in (-20, -3, 0, 5):
+        for b in range(nblk):
+            blk = np.zeros(128, np.float32)
+            blk[0] = np.float32(448.0)
+            chunk = vals[b * per:(b + 1) * per]
+            blk[1:1 + len(chunk)] = chunk * np.where(np.arange(len(chunk)) % 2 == 0, 1, -1).astype(np.float32)
+            rows.append(blk * np.float32(2.0 ** k))
+    x = np.stack(rows)
+    q = m.fp8_quantize(up(x), 1)
+    torch.cuda.synchronize()
+    c_ref, s_ref = F8.fp8_quantize(x, 1)
+    assert np.array_equal(down(q.scales), s_ref) and np.array_equal(down(q.codes), c_ref)
+
+
+def _unpack_fp8_tiles(packed, E, N, K):
+    """Inverse of the documented FP8 tile layout (tile (e, rt, st) of 2048
+    bytes; lane l = 16 g + n: row 16 rt + n, K bytes [128 st + 32 g, +16) at
+    [16 l, +16) and the next 16 at [1024 + 16 l, +16))."""
+    ntr, nst = (N + 15) // 16, K // 128
+    t = np.asarray(packed, np.uint8)[: E * ntr * nst * 2048].reshape(E, ntr, nst, 2048)
+    codes = np.zeros((E, ntr * 16, K), np.uint8)
+    for l in range(64):
+        n, g = l % 16, l // 16
+        r = np.arange(ntr) * 16 + n
+        for st in range(nst):
+            k0 = 128 * st + 32 * g
+            codes[:, r, k0:k0 + 16] = t[:, :, st, 16 * l:16 * l + 16]
+            codes[:, r, k0 + 16:k0 + 32] = t[:, :, st, 1024 + 16 * l:1024 + 16 * l + 16]
+    return codes
+
+
+@pytest.mark.parametrize("E,N,K", [(3, 48, 384), (1, 16, 128), (2, 512, 6144)])
+def test_fp8_weight_repack_layout(E, N, K):
+    rng = np.random.default_rng(E * N + K)
+    codes = rng.integers(0, 256, (E, N, K), dtype=np.uint8)
+    packed = down(m.fp8_weight_repack(up(codes)))
+    torch.cuda.synchronize()
+    assert packed.size == m.lib().fp8_weight_packed_size(E, N, K)
+    assert np.array_equal(_unpack_fp8_tiles(packed, E, N, K)[:, :N], codes)
+
+
+CASES = [
+    # E, counts, N, K, rows_a, hint
+    (3, [5, 0, 17], 64, 256, 30, 0),
+    (4, [1, 100, 64, 65], 48, 512, 300, 0),
+    (2, [200, 3], 512, 6144, 203, 0),
+    (8, [16, 31, 33, 64, 2, 0, 129, 8], 160, 256, 283, 100),
+    (600, None, 64, 512, 500, 0),
+    (3, [9, 40, 2], 48, 128, 60, 0),          # one K step
+    (2, [33, 80], 400, 384, 120, 0),          # odd step count, N past one weight block and not a multiple of 64
+]
+
+
+def _fp8_operands(cfg_stream, E, N, K, rows_a):
+    c = workloads.CONFIGS[0]
+    ac = workloads.fp8_codes(c, cfg_stream, (rows_a, K))
+    as_ = workloads.fp8_scales(c, cfg_stream, (rows_a, K // 128), 2.0 ** -4, 2.0 ** 4)
+    bc = workloads.fp8_codes(c, cfg_stream + 1, (E, N, K))
+    bs = workloads.fp8_scales(c, cfg_stream + 1, (E, (N + 127) // 128, K // 128), 2.0 ** -4, 2.0 ** 4)
+    return ac, as_, bc, bs
+
+
+@pytest.mark.parametrize("case", range(len(CASES)))
+@pytest.mark.parametrize("gather", [False, True])
+@pytest.mark.parametrize("epi", ["f32", "bf16"])
+def test_fp8_gemm_random(case, gather, epi):
+    E, counts, N, K, rows_a, hint = CASES[case]
+    rng = np.random.default_rng(300 + case)
+    if counts is None:
+        counts = rng.integers(0, 40, E) * (rng.random(E) < 0.7)
+        counts[rng.choice(E, 4, replace=False)] = [150, 200, 65, 17]
+    counts = np.asarray(counts, np.int64)
+    M = int(counts.sum())
+    print(f"fp8 gemm case {case} gather={gather} epi={epi} E={E} M={M} N={N} K={K}", flush=True)
+    if not gather:
+        rows_a = max(M, 1)
+    ac, as_, bc, bs = _fp8_operands(10 + 2 * case, E, N, K, rows_a)
+    a_rows = rng.integers(0, rows_a, M).astype(np.int32) if gather else None
+    offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    y = m.fp8_grouped_gemm(_a(ac, as_), m.fp8_weight_repack(up(bc)), up(bs), up(offsets), N=N, m_total=M,
+                           a_rows=None if a_rows is None else up(a_rows),
+                           epilogue=m.EPI_F32 if epi == "f32" else m.EPI_BF16, max_rows_per_expert_hint=hint)
+    torch.cuda.synchronize()
+    y_ref, absdot = F8.fp8_grouped_gemm(ac, as_, bc, bs, offsets, a_rows=a_rows)
+    got = down(y) if epi == "f32" else bf16_to_f32(y)
+    assert_gemm_close(got, y_ref, absdot, bf16_out=epi == "bf16", what=f"fp8 case {case} {epi}")
+
+
+@pytest.mark.parametrize("K", [128, 1024, 4096])
+def test_fp8_gemm_exact_sums_bit_exact(K):
+    # E4M3 values in [1, 3.75] (exponent fields 7 and 8) and block scales 1/2 or
+    # 1: every scaled product is a multiple of 2^-8 of magnitude at most 14.07,
+    # so any partial sum of at most 4096 of them is below 2^24 units of 2^-8 and
+    # exact in float32 in any order: the GPU must equal the oracle bit for bit
+    c = workloads.CONFIGS[0]
+    E, counts, N = 2, [37, 70], 272
+    M = sum(counts)
+    ac = workloads.fp8_codes(c, 40, (M, K), 7, 9)
+    bc = workloads.fp8_codes(c, 41, (E, N, K), 7, 9)
+    rng = np.random.default_rng(K)
+    as_ = np.exp2(rng.integers(-1, 1, (M, K // 128))).astype(np.float32)
+    bs = np.exp2(rng.integers(-1, 1, (E, (N + 127) // 128, K // 128))).astype(np.float32)
+    offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    y = m.fp8_grouped_gemm(_a(ac, as_), m.fp8_weight_repack(up(bc)), up(bs), up(offsets), N=N, m_total=M)
+    torch.cuda.synchronize()
+    y_ref, _ = F8.fp8_grouped_gemm(ac, as_, bc, bs, offsets, want_absdot=False)
+    assert np.array_equal(down(y), y_ref)
+
+
+def test_fp8_gemm_single_block_term():
+    # one nonzero 128-block of K at a time, exact-sum codes, arbitrary float32
+    # scales: each output is one block term part * sa * sb, which the GPU rounds
+    # twice (sa * sb, then the product) - within two float32 ulps of the
+    # oracle's exact term; a scale taken from the wrong row, tile or block is
+    # far outside that
+    c = workloads.CONFIGS[0]
+    M, N, K = 80, 272, 512
+    for blk in range(K // 128):
+        ac = np.zeros((M, K), np.uint8)
+        bc = np.zeros((1, N, K), np.uint8)
+        ac[:, 128 * blk:128 * blk + 128] = workloads.fp8_codes(c, 50 + blk, (M, 128), 7, 9)
+        bc[0, :, 128 * blk:128 * blk + 128] = workloads.fp8_codes(c, 60 + blk, (N, 128), 7, 9)
+        as_ = workloads.fp8_scales(c, 50 + blk, (M, K // 128), 0.1, 10.0)
+        bs = workloads.fp8_scales(c, 60 + blk, (1, (N + 127) // 128, K // 128), 0.1, 10.0)
+        offsets = np.array([0, M], np.int32)
+        y = m.fp8_grouped_gemm(_a(ac, as_), m.fp8_weight_repack(up(bc)), up(bs), up(offsets), N=N, m_total=M)
+        torch.cuda.synchronize()
+        y_ref, _ = F8.fp8_grouped_gemm(ac, as_, bc, bs, offsets, want_absdot=False)
+        got = down(y).astype(np.float64)
+        bad = np.abs(got - y_ref) > 2.0 ** -22 * np.abs(y_ref)
+        if bad.any():
+            i = tuple(np.argwhere(bad)[0])
+            raise AssertionError(f"block {blk}: {int(bad.sum())} of {bad.size} outside two ulps; rows "
+                                 f"{np.unique(np.argwhere(bad)[:, 0])[:20]} cols {np.unique(np.argwhere(bad)[:, 1])[:20]}; "
+                                 f"first {i}: gpu {got[i]!r} ref {float(y_ref[i])!r}")
+
+
+def test_fp8_whole_decode_gate_up_and_down():
+    # the Zipf decode shape (T=2048, H=6144, I=256, E=256, top-8): every output
+    # of the FP8 gate_up (f32) and down (bf16); x and h quantised by the oracle,
+    # weights as seeded E4M3 bytes with log-uniform block scales
+    c = workloads.CONFIGS[2]
+    print("fp8 whole decode shape", flush=True)
+    ids, w = OM.route(workloads.logits(c), c.k)
+    counts, offsets, src, perm_of, pw = OM.permute(ids, w, c.E)
+    M = c.T * c.k
+    xc, xs = F8.fp8_quantize(workloads.activations(c), 1)
+    guc = workloads.fp8_codes(c, 3, (c.E, 2 * c.I, c.H))
+    gus = workloads.fp8_scales(c, 3, (c.E, 2 * c.I // 128, c.H // 128))
+    dnc = workloads.fp8_codes(c, 4, (c.E, c.H, c.I))
+    dns = workloads.fp8_scales(c, 4, (c.E, c.H // 128, c.I // 128))
+    off_t = up(offsets)
+    y1g = m.fp8_grouped_gemm(_a(xc, xs), m.fp8_weight_repack(up(guc)), up(gus), off_t, N=2 * c.I, m_total=M,
+                             a_rows=up(src))
+    torch.cuda.synchronize()
+    y1, ad1 = F8.fp8_grouped_gemm(xc, xs, guc, gus, offsets, a_rows=src)
+    assert_gemm_close(down(y1g), y1, ad1, what="fp8 gate_up f32, all 16384 x 512")
+    del y1g
+    hc, hs = F8.fp8_quantize(OM.swiglu(y1).astype(np.float32), 1)
+    y2g = m.fp8_grouped_gemm(_a(hc, hs), m.fp8_weight_repack(up(dnc)), up(dns), off_t, N=c.H, m_total=M,
+                             epilogue=m.EPI_BF16)
+    torch.cuda.synchronize()
+    y2, ad2 = F8.fp8_grouped_gemm(hc, hs, dnc, dns, offsets)
+    assert_gemm_close(bf16_to_f32(y2g), y2, ad2, bf16_out=True, what="fp8 down bf16, all 16384 x 6144")

@@ -168,6 +168,28 @@ def nvfp4_codes(cfg: MoEConfig, stream: int, shape_rows: tuple, K: int, scale_lo
     return codes, scales
 
 
+def fp8_codes(cfg: MoEConfig, stream: int, shape: tuple, exp_lo: int = 0, exp_hi: int = 16):
+    """Random E4M3 bytes uint8 [*shape]: random sign, exponent field uniform in
+    [exp_lo, exp_hi), mantissa uniform, the NaN pattern (exponent 15, mantissa
+    7) replaced by 448's.  Raw input bytes from stream ``stream`` of generator
+    family 8; no arithmetic of the method is involved."""
+    g = rng(cfg.index, 8, stream)
+    if exp_lo == 0 and exp_hi == 16:
+        codes = g.integers(0, 256, shape, dtype=np.uint8)       # every byte value: all signs and fields
+    else:
+        e = g.integers(exp_lo, exp_hi, shape, dtype=np.uint8)
+        codes = (e << 3) | g.integers(0, 8, shape, dtype=np.uint8) | (g.integers(0, 2, shape, dtype=np.uint8) << 7)
+    codes[(codes & 0x7F) == 0x7F] ^= 1
+    return codes.astype(np.uint8, copy=False)
+
+
+def fp8_scales(cfg: MoEConfig, stream: int, shape: tuple, lo: float = 2.0 ** -12, hi: float = 2.0 ** -6):
+    """Random positive float32 block scales [*shape], log-uniform in [lo, hi)
+    (stream ``stream`` of generator family 9)."""
+    g = rng(cfg.index, 9, stream)
+    return np.exp2(g.uniform(np.log2(lo), np.log2(hi), shape)).astype(np.float32)
+
+
 # Static calibration of the intermediate's per-tensor scale: an expected
 # absolute maximum of h = silu(gate) * up for each workload (gate and up are
 # roughly N(0, (sqrt(H) * 0.02)^2) for x ~ N(0,1)).  Both sides receive the same
