@@ -362,6 +362,7 @@ template <int EPI, bool NT>
 __global__ __launch_bounds__(256, 2) void k_fp8_gemm(const Fp8Params p, int n_tiles) {
   constexpr int WN = 4, BN = 4 * WN * 16;
   __shared__ __attribute__((aligned(16))) uint8_t a_lds[2][kFp8ALds];
+  static_assert(fits_lds(sizeof(a_lds), 2), "FP8 A staging exceeds the LDS of two workgroups per CU");
   int e, m0, nt;
   bool narrow;
   const GemmParams map = fp8_map_params(p, n_tiles);

@@ -954,6 +954,7 @@ __global__ __launch_bounds__(NW * 64, MINB) void k_gemm_streamk(const GemmParams
   static_assert(MT == 1 || MT == 2 || MT == 3 || MT == 4 || MT == 6 || MT == 8, "row tiles per chunk");
   static_assert(LIGHT == 0 || (WN % 2) == 0, "narrow tasks halve the tiles per wave");
   __shared__ half8 a_lds[2][MT * 8 * 64];   // double-buffered [row tile][sub-step][lane] fragments
+  static_assert(fits_lds(sizeof(a_lds), MINB), "stream-K A staging exceeds the LDS of MINB workgroups per CU");
   int e, m0, nt;
   bool narrow;
   if (!find_task<MT, true, LIGHT>(p, e, m0, nt, narrow)) return;
@@ -1116,6 +1117,7 @@ __device__ __forceinline__ void streamn_task(const GemmParams& p, int e, int m0,
 template <int NW, int MT, int UPW, int EPI, int PACKED>
 __global__ __launch_bounds__(NW * 64) void k_gemm_streamn(const GemmParams p) {
   __shared__ half8 a_lds[MT * 8 * 64];
+  static_assert(fits_lds(sizeof(a_lds), 2), "stream-N A staging exceeds the LDS of two workgroups per CU");
   __shared__ float stage_lds[NW * 16 * 68];   // per-wave output staging (row pitch 68 floats)
   int e, m0, ng;
   bool narrow;

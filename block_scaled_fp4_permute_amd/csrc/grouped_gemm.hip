@@ -160,16 +160,16 @@ static hipError_t launch_k(const GemmParams& prm, int epilogue, int64_t m_total,
   constexpr int kLight = PACKED == kRowB ? 0 : kLightPacked;
   switch (epilogue) {
     case EPI_F32:
-      return LARGE ? launch_streamk<8, 2, 8, EPI_F32, PACKED, 0>(prm, m_total, stream)
+      return LARGE ? launch_streamk<8, 2, 8, EPI_F32, PACKED, 0, 1>(prm, m_total, stream)
                    : launch_streamk<4, 2, 4, EPI_F32, PACKED, kLight>(prm, m_total, stream);
     case EPI_BF16:
-      return LARGE ? launch_streamk<8, 2, 8, EPI_BF16, PACKED, 0>(prm, m_total, stream)
+      return LARGE ? launch_streamk<8, 2, 8, EPI_BF16, PACKED, 0, 1>(prm, m_total, stream)
                    : launch_streamk<4, 2, 4, EPI_BF16, PACKED, kLight>(prm, m_total, stream);
     case EPI_SWIGLU:
-      return LARGE ? launch_streamk<8, 2, 8, EPI_SWIGLU, PACKED, 0>(prm, m_total, stream)
+      return LARGE ? launch_streamk<8, 2, 8, EPI_SWIGLU, PACKED, 0, 1>(prm, m_total, stream)
                    : launch_streamk<4, 4, 4, EPI_SWIGLU, PACKED, kLight>(prm, m_total, stream);
     case EPI_COMBINE:
-      return LARGE ? launch_streamk<8, 2, 8, EPI_COMBINE, PACKED, 0>(prm, m_total, stream)
+      return LARGE ? launch_streamk<8, 2, 8, EPI_COMBINE, PACKED, 0, 1>(prm, m_total, stream)
                    : launch_streamk<4, 2, 4, EPI_COMBINE, PACKED, kLight>(prm, m_total, stream);
     default: return hipErrorInvalidValue;
   }

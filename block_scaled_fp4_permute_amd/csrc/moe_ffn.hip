@@ -256,6 +256,7 @@ __global__ __launch_bounds__(256, 2) void k_moe_ffn(const FfnParams f) {
   // gate_up: two 64-row x 256-K fragment buffers (64 KB); down: one buffer
   // (32 KB) and the per-wave output staging (17 KB) in the same space
   __shared__ half8 smem[2 * kFfnMT * 8 * 64];
+  static_assert(fits_lds(sizeof(smem) + 64, 2), "expert-FFN staging exceeds the LDS of two workgroups per CU");
   __shared__ int s_ticket;
   const int xcd = blockIdx.x & 7;
   const int n_gu = f.hdr[kHdrNGu + xcd];

@@ -512,6 +512,7 @@ __device__ __forceinline__ void mx_task(const GemmParams& p, int e, int m0, int 
 template <int WN, int EPI, bool PACKED, bool NT>
 __global__ __launch_bounds__(256, 2) void k_mx_gemm(const GemmParams p) {
   __shared__ __attribute__((aligned(16))) uint8_t a_lds[2][kMxALds];
+  static_assert(fits_lds(sizeof(a_lds), 2), "MX A staging exceeds the LDS of two workgroups per CU");
   int e, m0, nt;
   bool narrow;
   if (!find_task<4, true, 0>(p, e, m0, nt, narrow)) return;
@@ -583,6 +584,7 @@ __global__ __launch_bounds__(256, 2) void k_mx_gemm_n(const GemmParams p) {
   constexpr int NW = 4;
   __shared__ __attribute__((aligned(16))) uint8_t a_lds[kMxALds];
   __shared__ float stage_lds[NW * 16 * 68];
+  static_assert(fits_lds(sizeof(a_lds) + sizeof(stage_lds), 2), "MX stream-N staging exceeds the LDS of two workgroups per CU");
   int e, m0, ng;
   bool narrow;
   if (!find_task<4, false, 0>(p, e, m0, ng, narrow)) return;

@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "lds_budget.h"
 #include "nvfp4_device.h"
 
 namespace nvfp4 {
