@@ -32,6 +32,16 @@ int hip_status(hipError_t err, const char* what) {
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
+// a * b >= limit for non-negative a, b, without overflowing
+bool prod_ge(int64_t a, int64_t b, int64_t limit) {
+  int64_t r = 0;
+  return __builtin_mul_overflow(a, b, &r) || r >= limit;
+}
+bool prod_ge(int64_t a, int64_t b, int64_t c, int64_t limit) {
+  int64_t r = 0;
+  return __builtin_mul_overflow(a, b, &r) || prod_ge(r, c, limit);
+}
+
 constexpr size_t kSmallWs = 4096;   // 1024 partial maxima of the amax reduction
 
 // Argument checks of the route + quantise calls (everything but the workspace).
@@ -51,8 +61,7 @@ int check_route_quantize(const char* fn, const float* logits, int32_t T, int32_t
     return fail(NVFP4MOE_ERR_INVALID, "%s: x_dtype %d", fn, x_dtype);
   if (cols <= 0 || cols % 32 != 0)
     return fail(NVFP4MOE_ERR_INVALID, "%s: cols=%lld must be a positive multiple of 32", fn, (long long)cols);
-  if (static_cast<int64_t>(T) * (cols / 16) >= (int64_t(1) << 40))
-    return fail(NVFP4MOE_ERR_UNSUPPORTED, "%s: tensor too large", fn);
+  if (prod_ge(T, cols / 16, int64_t(1) << 40)) return fail(NVFP4MOE_ERR_UNSUPPORTED, "%s: tensor too large", fn);
   // the encoder's workgroups are indexed after the ranks' in one grid
   if ((static_cast<int64_t>(T) * (cols / 16) + 255) / 256 + (static_cast<int64_t>(T) * k + 1023) / 1024 >=
       (int64_t(1) << 31))
@@ -112,7 +121,7 @@ int nvfp4moe_version(void) { return 101; }
 
 // ------------------------------------------------------------------ route + permute
 size_t moe_route_permute_workspace_size(int32_t T, int32_t E, int32_t k) {
-  if (T <= 0 || E <= 0 || k <= 0) return 0;
+  if (T <= 0 || E <= 0 || k <= 0 || k > 32 || E > 4096 || prod_ge(T, k, int64_t(1) << 30)) return 0;
   return nvfp4::route_permute_ws_bytes(T, E, k);
 }
 
@@ -147,7 +156,8 @@ int nvfp4_quantize(const void* x, int32_t x_dtype, int64_t rows, int64_t cols, c
     return fail(NVFP4MOE_ERR_INVALID, "nvfp4_quantize: x_dtype %d", x_dtype);
   if (rows <= 0 || cols <= 0) return fail(NVFP4MOE_ERR_INVALID, "nvfp4_quantize: rows, cols must be > 0");
   if (cols % 32 != 0) return fail(NVFP4MOE_ERR_INVALID, "nvfp4_quantize: cols=%lld not a multiple of 32", (long long)cols);
-  if (rows * (cols / 16) >= (int64_t(1) << 40)) return fail(NVFP4MOE_ERR_UNSUPPORTED, "nvfp4_quantize: tensor too large");
+  if (prod_ge(rows, cols / 16, int64_t(1) << 40))
+    return fail(NVFP4MOE_ERR_UNSUPPORTED, "nvfp4_quantize: tensor too large");
   if (!aligned(x, 16) || !aligned(codes, 8)) return fail(NVFP4MOE_ERR_INVALID, "nvfp4_quantize: misaligned x or codes");
   if (!g_in && (!workspace || workspace_bytes < kSmallWs))
     return fail(NVFP4MOE_ERR_WORKSPACE, "nvfp4_quantize: workspace of %zu bytes needed when g_in is NULL", kSmallWs);
@@ -158,7 +168,7 @@ int nvfp4_quantize(const void* x, int32_t x_dtype, int64_t rows, int64_t cols, c
 
 // ------------------------------------------------------------------ route + quantise
 size_t moe_route_quantize_workspace_size(int32_t T, int32_t E, int32_t k) {
-  if (T <= 0 || E <= 0 || k <= 0) return 0;
+  if (T <= 0 || E <= 0 || k <= 0 || k > 32 || E > 4096 || prod_ge(T, k, int64_t(1) << 30)) return 0;
   return nvfp4::route_quantize_ws_bytes(T, E, k);
 }
 
@@ -289,7 +299,7 @@ static constexpr int kFfnLargeRows = 128;
 static constexpr int kFfnSpinLimit = 1 << 20; // about a second of waiting for one chunk's h rows
 
 size_t moe_expert_ffn_workspace_size(int32_t E, int64_t m_total, int32_t H, int32_t I) {
-  if (E <= 0 || m_total < 0 || H <= 0 || I <= 0) return 0;
+  if (E <= 0 || m_total < 0 || H <= 0 || I <= 0 || E > 4096 || m_total >= (int64_t(1) << 31)) return 0;
   return nvfp4::moe_ffn_ws_bytes(E, m_total, H, I);
 }
 
@@ -368,7 +378,8 @@ int mxfp4_quantize(const void* x, int32_t x_dtype, int64_t rows, int64_t cols, u
     return fail(NVFP4MOE_ERR_INVALID, "mxfp4_quantize: x_dtype %d", x_dtype);
   if (rows <= 0 || cols <= 0 || cols % 32 != 0)
     return fail(NVFP4MOE_ERR_INVALID, "mxfp4_quantize: rows > 0 and cols a positive multiple of 32 needed");
-  if (rows * (cols / 32) >= (int64_t(1) << 38)) return fail(NVFP4MOE_ERR_UNSUPPORTED, "mxfp4_quantize: tensor too large");
+  if (prod_ge(rows, cols / 32, int64_t(1) << 38))
+    return fail(NVFP4MOE_ERR_UNSUPPORTED, "mxfp4_quantize: tensor too large");
   if (!aligned(x, 16) || !aligned(codes, 16))
     return fail(NVFP4MOE_ERR_INVALID, "mxfp4_quantize: x and codes must be 16-byte aligned");
   return hip_status(nvfp4::launch_mx_quantize(x, x_dtype, rows, cols, codes, scales, static_cast<hipStream_t>(stream)),
@@ -390,7 +401,7 @@ int mxfp4_grouped_gemm(const nvfp4moe_gemm_args* a, void* stream) {
     return fail(NVFP4MOE_ERR_INVALID, "mxfp4_grouped_gemm: codes and packed tiles must be 16-byte, scales 2-byte aligned");
   if (nvfp4::mx_packed_weight_bytes(1, a->N, a->K) >= (size_t(1) << 31))
     return fail(NVFP4MOE_ERR_UNSUPPORTED, "mxfp4_grouped_gemm: one expert's weights of 2 GiB or more");
-  if (a->m_total >= (int64_t(1) << 31) || a->a_rows_total * (int64_t(a->K) / 2) >= (int64_t(1) << 31))
+  if (a->m_total >= (int64_t(1) << 31) || prod_ge(a->a_rows_total, a->K / 2, int64_t(1) << 31))
     return fail(NVFP4MOE_ERR_UNSUPPORTED, "mxfp4_grouped_gemm: A codes of 2 GiB or more");
   if (static_cast<int64_t>(a->E) * a->N >= (int64_t(1) << 31) ||
       static_cast<int64_t>(a->N) * (a->K / 2) >= (int64_t(1) << 31))
@@ -433,7 +444,7 @@ int mxfp4_grouped_gemm(const nvfp4moe_gemm_args* a, void* stream) {
 }
 
 size_t mxfp4_weight_packed_size(int32_t E, int32_t N, int32_t K) {
-  if (E <= 0 || N <= 0 || K <= 0) return 0;
+  if (E <= 0 || N <= 0 || K <= 0 || K % 32 != 0 || prod_ge(E, N, int64_t(1) << 31)) return 0;
   return nvfp4::mx_packed_weight_bytes(E, N, K);
 }
 
@@ -463,9 +474,12 @@ int fp8_quantize(const void* x, int32_t x_dtype, int64_t batch, int64_t rows, in
     return fail(NVFP4MOE_ERR_INVALID, "fp8_quantize: batch, rows > 0 and cols a positive multiple of 128 needed");
   if (block_rows != 1 && block_rows != 128)
     return fail(NVFP4MOE_ERR_INVALID, "fp8_quantize: block_rows %d (1 or 128)", block_rows);
-  if (block_rows == 128 && (batch > 65535 || rows > 65535ll * 128 || cols / 128 >= (int64_t(1) << 31)))
-    return fail(NVFP4MOE_ERR_UNSUPPORTED, "fp8_quantize: batch > 65535 or rows > 8388480");
-  if (batch * rows * (cols / 128) >= (int64_t(1) << 38))
+  // grid limits: 2^32 work-items per dimension, 65535 workgroups in y and z
+  if (block_rows == 128 && (batch > 65535 || rows > 65535ll * 128 || cols / 128 >= (int64_t(1) << 24)))
+    return fail(NVFP4MOE_ERR_UNSUPPORTED, "fp8_quantize: batch > 65535, rows > 8388480 or cols >= 2^31");
+  if (block_rows == 1 && prod_ge(batch, rows, cols / 128, int64_t(1) << 26))
+    return fail(NVFP4MOE_ERR_UNSUPPORTED, "fp8_quantize: 2^26 or more blocks of 128 values");
+  if (prod_ge(batch, rows, cols / 128, int64_t(1) << 38))
     return fail(NVFP4MOE_ERR_UNSUPPORTED, "fp8_quantize: tensor too large");
   if (!aligned(x, 16) || !aligned(codes, 16) || !aligned(scales, 4))
     return fail(NVFP4MOE_ERR_INVALID, "fp8_quantize: x and codes must be 16-byte, scales 4-byte aligned");
@@ -475,7 +489,9 @@ int fp8_quantize(const void* x, int32_t x_dtype, int64_t batch, int64_t rows, in
 }
 
 size_t fp8_weight_packed_size(int32_t E, int32_t N, int32_t K) {
-  if (E <= 0 || N <= 0 || K <= 0) return 0;
+  if (E <= 0 || N <= 0 || K <= 0 || K % 128 != 0 || N % 16 != 0 ||
+      prod_ge(E, N / 16, int64_t(K / 128) * 64, int64_t(1) << 40))
+    return 0;
   return nvfp4::fp8_packed_weight_bytes(E, N, K);
 }
 
@@ -487,7 +503,7 @@ int fp8_weight_repack(const uint8_t* codes, int32_t E, int32_t N, int32_t K, uin
     return fail(NVFP4MOE_ERR_INVALID, "fp8_weight_repack: K=%d must be a multiple of 128, N=%d of 16", K, N);
   if (!aligned(codes, 16) || !aligned(packed, 16))
     return fail(NVFP4MOE_ERR_INVALID, "fp8_weight_repack: codes and packed must be 16-byte aligned");
-  if (static_cast<int64_t>(E) * (N / 16) * (K / 128) * 64 >= (int64_t(1) << 40))
+  if (prod_ge(E, N / 16, int64_t(K / 128) * 64, int64_t(1) << 40))
     return fail(NVFP4MOE_ERR_UNSUPPORTED, "fp8_weight_repack: weights too large");
   const size_t need = nvfp4::fp8_packed_weight_bytes(E, N, K);
   if (packed_bytes < need)
@@ -507,7 +523,7 @@ int fp8_grouped_gemm(const nvfp4moe_fp8_gemm_args* a, void* stream) {
   if (!aligned(a->a_codes, 16) || !aligned(a->a_scales, 4) || !aligned(a->b_packed, 16) || !aligned(a->b_scales, 4))
     return fail(NVFP4MOE_ERR_INVALID, "fp8_grouped_gemm: codes and packed tiles must be 16-byte, scales 4-byte aligned");
   if (a->E > 4096) return fail(NVFP4MOE_ERR_UNSUPPORTED, "fp8_grouped_gemm: E > 4096");
-  if (a->m_total >= (int64_t(1) << 31) || a->a_rows_total * int64_t(a->K) >= (int64_t(1) << 31))
+  if (a->m_total >= (int64_t(1) << 31) || prod_ge(a->a_rows_total, a->K, int64_t(1) << 31))
     return fail(NVFP4MOE_ERR_UNSUPPORTED, "fp8_grouped_gemm: A codes of 2 GiB or more");
   if (a->epilogue != NVFP4MOE_EPI_F32 && a->epilogue != NVFP4MOE_EPI_BF16)
     return fail(NVFP4MOE_ERR_UNSUPPORTED, "fp8_grouped_gemm: epilogue %d (F32 or BF16)", a->epilogue);
@@ -533,7 +549,7 @@ int fp8_grouped_gemm(const nvfp4moe_fp8_gemm_args* a, void* stream) {
 
 // ------------------------------------------------------------------ packed weights
 size_t nvfp4_weight_packed_size(int32_t E, int32_t N, int32_t K) {
-  if (E <= 0 || N <= 0 || K <= 0) return 0;
+  if (E <= 0 || N <= 0 || K <= 0 || K % 32 != 0 || prod_ge(E, N, int64_t(1) << 31)) return 0;
   return nvfp4::packed_weight_bytes(E, N, K);
 }
 
@@ -562,7 +578,7 @@ int moe_swiglu(const void* gate_up, int32_t dtype, int64_t M, int32_t I, const f
   if (M <= 0 || I <= 0) return fail(NVFP4MOE_ERR_INVALID, "moe_swiglu: M, I must be > 0");
   if (I % 16 != 0) return fail(NVFP4MOE_ERR_INVALID, "moe_swiglu: I=%d not a multiple of 16", I);
   if (!aligned(gate_up, 16) || !aligned(codes, 8)) return fail(NVFP4MOE_ERR_INVALID, "moe_swiglu: misaligned pointer");
-  if (M * (I / 16) >= (int64_t(1) << 40)) return fail(NVFP4MOE_ERR_UNSUPPORTED, "moe_swiglu: tensor too large");
+  if (prod_ge(M, I / 16, int64_t(1) << 40)) return fail(NVFP4MOE_ERR_UNSUPPORTED, "moe_swiglu: tensor too large");
   if (!g_in && (!workspace || workspace_bytes < kSmallWs))
     return fail(NVFP4MOE_ERR_WORKSPACE, "moe_swiglu: workspace of %zu bytes needed when g_in is NULL", kSmallWs);
   return hip_status(nvfp4::launch_swiglu(gate_up, dtype, M, I, g_in, g_out, codes, scales, workspace,

@@ -147,7 +147,7 @@ hipError_t launch_fp8_quantize(const void* x, int dtype, int64_t batch, int64_t 
 
 // ------------------------------------------------------------------ packed weights
 size_t fp8_packed_weight_bytes(int E, int N, int K) {
-  return static_cast<size_t>(E) * ((N + 15) / 16) * ((K + kFp8Block - 1) / kFp8Block) * kFp8Tile;
+  return static_cast<size_t>(E) * ((int64_t(N) + 15) / 16) * ((int64_t(K) + kFp8Block - 1) / kFp8Block) * kFp8Tile;
 }
 
 __global__ __launch_bounds__(256) void k_fp8_repack(const uint8_t* __restrict__ codes, int E, int N, int K,

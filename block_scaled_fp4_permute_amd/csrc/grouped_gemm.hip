@@ -48,7 +48,7 @@ namespace nvfp4 {
 
 // ------------------------------------------------------------------ packed layout
 size_t packed_weight_bytes(int E, int N, int K) {
-  return static_cast<size_t>(E) * ((N + 15) / 16) * ((K + KSTEP - 1) / KSTEP) * PTILE;
+  return static_cast<size_t>(E) * ((int64_t(N) + 15) / 16) * ((int64_t(K) + KSTEP - 1) / KSTEP) * PTILE;
 }
 
 __global__ __launch_bounds__(256) void k_repack(const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales,

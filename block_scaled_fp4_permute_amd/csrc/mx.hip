@@ -107,7 +107,7 @@ hipError_t launch_mx_quantize(const void* x, int dtype, int64_t rows, int64_t co
 constexpr int kMxTile = 2176;
 
 size_t mx_packed_weight_bytes(int E, int N, int K) {
-  return static_cast<size_t>(E) * ((N + 15) / 16) * ((K + 255) / 256) * kMxTile;
+  return static_cast<size_t>(E) * ((int64_t(N) + 15) / 16) * ((int64_t(K) + 255) / 256) * kMxTile;
 }
 
 __global__ __launch_bounds__(256) void k_mx_repack(const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales,

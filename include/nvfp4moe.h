@@ -30,7 +30,9 @@
  * anything.  A non-OK status means nothing was enqueued, except
  * NVFP4MOE_ERR_HIP, which reports a failed kernel launch (earlier kernels of
  * the same call may have been enqueued).  nvfp4moe_last_error_detail() gives a
- * thread-local explanation of the last failure on the calling thread.
+ * thread-local explanation of the last failure on the calling thread.  The
+ * *_workspace_size() and *_packed_size() queries return 0 for arguments the
+ * matching call rejects.
  */
 #ifndef NVFP4MOE_H
 #define NVFP4MOE_H
@@ -311,8 +313,9 @@ int mxfp4_weight_repack(const uint8_t* codes, const uint8_t* scales, int32_t E, 
  * fp8_quantize: x bf16 or float32 [batch, rows, cols] (finite, 16-byte aligned,
  * cols % 128 == 0); block_rows 1 (activations: batch is folded into rows) or
  * 128 (weights: each of the batch matrices has its own row blocks, scales
- * [batch, ceil(rows/128), cols/128]; rows <= 8388480, batch <= 65535).  codes
- * 16-byte, scales 4-byte aligned. */
+ * [batch, ceil(rows/128), cols/128]; rows <= 8388480, batch <= 65535,
+ * cols < 2^31).  Block rows 1: fewer than 2^26 blocks in all.  codes 16-byte,
+ * scales 4-byte aligned. */
 int fp8_quantize(const void* x, int32_t x_dtype, int64_t batch, int64_t rows, int64_t cols, int32_t block_rows,
                  uint8_t* codes, float* scales, void* stream);
 /* FP8 weights [E, N, K] repacked once into tiles of 16 rows x 128 K (2048
