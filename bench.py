@@ -52,6 +52,9 @@ def parse():
                     help="number format: NVFP4 (the reported one), the MXFP4 variant (E8M0 scale per 32, "
                          "gfx950's block-scaled FP4 MFMA) or the FP8 block-scaled grouped GEMMs (E4M3, float32 "
                          "scales per 1x128 / 128x128 block)")
+    ap.add_argument("--launch", choices=["eager", "graph"], default="eager",
+                    help="launch each timed step's kernels one by one, or replay it as one HIP graph of its kernels "
+                         "(recorded once per weight copy; measured slower on MI355X: 0.355 against 0.329 ms)")
     ap.add_argument("--swiglu", choices=["fused", "separate"], default="fused",
                     help="SwiGLU + requant in the gate_up epilogue, or a separate call")
     ap.add_argument("--combine", choices=["gather", "atomic"], default="gather",
@@ -487,7 +490,7 @@ def main():
     import workloads
     from block_scaled_fp4_permute_amd import EPI_F32, lib, moe_route_permute, moe_swiglu, nvfp4_grouped_gemm, \
         nvfp4_quantize
-    from block_scaled_fp4_permute_amd.layer import MoELayer, quantize_expert_weights
+    from block_scaled_fp4_permute_amd.layer import MoELayer, capture_step, quantize_expert_weights
 
     lib()
     dev = torch.device("cuda:0")
@@ -538,9 +541,6 @@ def main():
         layer.forward(logits, x, copies[i % 2], g_h)
     torch.cuda.synchronize()
 
-    # ---- timed region: exactly K steps.  Two events per step bracket the
-    # gate_up launch on the launch stream (its live average duration); the
-    # step time is the first event to the last.
     # routing and the quantisation of x share launches (one call): one stage
     if one_call:
         names = ["route_permute+quantize_x", None,
@@ -553,17 +553,41 @@ def main():
     def ev():
         return torch.cuda.Event(enable_timing=True)
 
+    # ---- timed region: exactly K steps.  Eager: two events per step bracket
+    # the FFN call on the launch stream (its live average duration).  Graph:
+    # each step is one replay of the step's recorded kernels (one graph per
+    # weight copy), and the FFN call's duration comes from the instrumented
+    # eager steps below.
+    graphs = None
+    if args.launch == "graph":
+        graphs = [capture_step(layer, logits, x, copies[c], g_h) for c in range(2)]
+        for i in range(args.warmup):
+            graphs[i % 2].replay()
+        torch.cuda.synchronize()
     t_start, t_end = ev(), ev()
     gu_marks = [[None, None, ev(), ev(), None, None] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     t_start.record()
     for i in range(args.steps):
-        layer.forward(logits, x, copies[i % 2], g_h, marks=gu_marks[i])
+        if graphs is not None:
+            graphs[i % 2].replay()
+        else:
+            layer.forward(logits, x, copies[i % 2], g_h, marks=gu_marks[i])
     t_end.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_per_step = t_start.elapsed_time(t_end) / args.steps
+    eager_ms = None
+    if graphs is not None:
+        # the same K steps launched kernel by kernel, for reference
+        e0, e1 = ev(), ev()
+        e0.record()
+        for i in range(args.steps):
+            layer.forward(logits, x, copies[i % 2], g_h, marks=gu_marks[i])
+        e1.record()
+        torch.cuda.synchronize()
+        eager_ms = e0.elapsed_time(e1) / args.steps
     gu_ms = float(np.mean([m[2].elapsed_time(m[3]) for m in gu_marks]))
 
     # ---- per-stage breakdown (after the timed region; events between all stages)
@@ -609,6 +633,7 @@ def main():
         "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 5),
         "wall_ms_per_step": round(wall * 1e3 / args.steps, 5),
+        "eager_ms_per_step": None if eager_ms is None else round(eager_ms, 5),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -624,6 +649,7 @@ def main():
                               "max": int(counts.max()), "touched_experts": touched},
         "config": {"workload": wl_name, "T": T, "H": H, "I": I, "E": E, "top_k": k, "routing": cfg.routing,
                    "ffn": layer.ffn, "swiglu": args.swiglu, "combine": args.combine, "weight_layout": "packed tiles",
+                   "launch": "hip_graph" if graphs is not None else "eager",
                    "weight_copies": 2},
         "roofline": ({"kernel": "moe_expert_ffn: gate_up + SwiGLU/requant and down grouped GEMMs, large-M tile",
                       "bound": "mfma", "achieved": round(ffn_tflops, 1), "peak": MFMA_F16_PEAK_TFLOPS,

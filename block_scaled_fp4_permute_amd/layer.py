@@ -174,6 +174,25 @@ class MoELayer:
         return self.out
 
 
+def capture_step(layer: "MoELayer", logits: torch.Tensor, x: torch.Tensor, w: ExpertWeights, g_h: torch.Tensor):
+    """Record one layer step (``layer.forward`` on these exact tensors) into a
+    HIP graph and return it (a ``torch.cuda.CUDAGraph``; ``replay()`` re-runs
+    the step's kernels on the same buffers with one launch of the graph).
+    Nothing in the step synchronises with the host or allocates: the routing
+    counts stay on the device and every buffer is the layer's own, so the
+    recorded kernels are exactly the eager step's.  The inputs' contents may
+    change between replays; their addresses may not."""
+    side = torch.cuda.Stream(device=logits.device)
+    side.wait_stream(torch.cuda.current_stream(logits.device))
+    with torch.cuda.stream(side):          # the capture runs on a side stream, as torch requires
+        layer.forward(logits, x, w, g_h)   # one eager step on that stream first
+    torch.cuda.current_stream(logits.device).wait_stream(side)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        layer.forward(logits, x, w, g_h)
+    return graph
+
+
 # ------------------------------------------------------------------ MXFP4 variant
 @dataclass
 class MXExpertWeights:
