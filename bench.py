@@ -353,17 +353,17 @@ def mx_bench(cfg, args):
 
 
 def fp8_bench(cfg, args):
-    """The FP8 block-scaled grouped GEMMs (secondary measurements, not the
-    reported metric).  MoE workloads: the gate_up GEMM over the routed rows
-    (A gathered by the permutation, bf16 out) and the down GEMM (bf16 out) on
-    FP8 activations, weights quantised with 128 x 128 blocks and repacked
-    (untimed), two weight copies alternating; roofline of gate_up against HBM.
-    Dense workload: the GEMM against the dense FP8 MFMA peak."""
+    """The FP8 block-scaled variant (secondary measurements, not the reported
+    metric).  MoE workloads: the FP8 layer step (route + permute, FP8
+    quantisation of x, gate_up grouped GEMM with float32 rows, SwiGLU + FP8
+    requant, down grouped GEMM with bf16 rows, combine), weights quantised with
+    128 x 128 blocks and repacked (untimed), two weight copies alternating;
+    roofline of gate_up against HBM.  Dense workload: the GEMM against the
+    dense FP8 MFMA peak."""
     import numpy as np
     import torch
 
-    from block_scaled_fp4_permute_amd import (EPI_BF16, fp8_grouped_gemm, fp8_quantize, fp8_weight_repack, lib,
-                                              moe_route_permute)
+    from block_scaled_fp4_permute_amd import EPI_BF16, fp8_grouped_gemm, fp8_quantize, fp8_weight_repack, lib
 
     lib()
     dev = torch.device("cuda:0")
@@ -406,59 +406,43 @@ def fp8_bench(cfg, args):
                          "frac": round(tflops / MFMA_FP8_PEAK_TFLOPS, 4), "traffic": None}}), flush=True)
         return
 
+    from block_scaled_fp4_permute_amd.layer import FP8MoELayer, quantize_expert_weights_fp8
     T, H, I, E, k = cfg.T, cfg.H, cfg.I, cfg.E, cfg.k
     M = T * k
     logits = torch.from_numpy(wl.logits(cfg)).to(dev)
     x = torch.from_numpy(wl.activations(cfg)).to(dev).to(torch.bfloat16)
-    r = moe_route_permute(logits, k)
-    xq = fp8_quantize(x, 1)
-    gen = torch.Generator(device=dev)
-    gen.manual_seed(11)
-    hq = fp8_quantize(torch.randn((M, I), generator=gen, device=dev), 1)
     copies = []
     for c in range(2):
         w_gu, w_dn = wl.torch_expert_weights(cfg, dev, copy=c)
-        gq, dq = fp8_quantize(w_gu, 128), fp8_quantize(w_dn, 128)
+        copies.append(quantize_expert_weights_fp8(w_gu, w_dn))
         del w_gu, w_dn
-        copies.append((fp8_weight_repack(gq.codes), gq.scales, fp8_weight_repack(dq.codes), dq.scales))
-        del gq, dq
-    y1 = torch.empty((M, 2 * I), dtype=torch.bfloat16, device=dev)
-    y2 = torch.empty((M, H), dtype=torch.bfloat16, device=dev)
-    hint = M // E
-
-    def gate_up(i):
-        gp, gs, _, _ = copies[i % 2]
-        fp8_grouped_gemm(xq, gp, gs, r.offsets, N=2 * I, m_total=M, a_rows=r.perm_src_token, epilogue=EPI_BF16,
-                         out=y1, max_rows_per_expert_hint=hint)
-
-    def down(i):
-        _, _, dp, ds = copies[i % 2]
-        fp8_grouped_gemm(hq, dp, ds, r.offsets, N=H, m_total=M, epilogue=EPI_BF16, out=y2,
-                         max_rows_per_expert_hint=hint)
-
-    def both(i):
-        gate_up(i)
-        down(i)
-
-    ms = timed(both, args.steps)
-    gu_ms = timed(gate_up, args.steps)
-    dn_ms = timed(down, args.steps)
-    counts = r.counts.cpu().numpy()
+    layer = FP8MoELayer(T, H, I, E, k, dev)
+    ms = timed(lambda i: layer.forward(logits, x, copies[i % 2]), args.steps)
+    marks = [[ev() for _ in range(7)] for _ in range(args.steps)]
+    for i in range(args.steps):
+        layer.forward(logits, x, copies[i % 2], marks=marks[i])
+    torch.cuda.synchronize()
+    names = ["route_permute", "quantize_x", "gate_up", "swiglu_quantize", "down", "combine"]
+    stage_ms = {n: round(float(np.mean([m_[j].elapsed_time(m_[j + 1]) for m_ in marks])), 5)
+                for j, n in enumerate(names)}
+    gu_ms = stage_ms["gate_up"]
+    counts = layer.routing.counts.cpu().numpy()
     touched = int((counts > 0).sum())
     gu_w = 2 * I * H * (1 + 4 / (128 * 128))        # E4M3 codes + one float32 per 128 x 128 block
     dn_w = H * I * (1 + 4 / (128 * 128))
     weight_bytes = touched * (gu_w + dn_w)
-    gu_alg = touched * gu_w + T * H * (1 + 4 / 128) + M * 2 * I * 2
+    gu_alg = touched * gu_w + T * H * (1 + 4 / 128) + M * 2 * I * 4
     print(json.dumps({
-        "metric": "FP8 block-scaled grouped GEMM pair weight GB/s (secondary: gate_up + down of the MoE workload)",
+        "metric": "FP8 block-scaled MoE layer weight GB/s (secondary: E4M3 with float32 scales per 1x128 / 128x128 "
+                  "block on the FP8 MFMA)",
         "value": round(weight_bytes / (ms * 1e-3) / 1e9, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True, "vs_baseline": None,
         "dtype": "e4m3 operands, f32 block scales, fp8 mfma, f32 accumulate", "data": "synthetic",
         "tflops": round(2.0 * M * 3 * I * H / (ms * 1e-3) / 1e12, 3), "weight_bytes": int(weight_bytes),
-        "stage_ms": {"gate_up": round(gu_ms, 5), "down": round(dn_ms, 5)},
+        "stage_ms": stage_ms,
         "config": {"workload": f"{'decode' if T <= 2048 else 'prefill'}_moe_T{T}_H{H}_I{I}_E{E}_top{k}_{cfg.routing}",
                    "format": "fp8_block128", "weight_copies": 2},
-        "roofline": {"kernel": "k_fp8_gemm gate_up", "bound": "hbm",
+        "roofline": {"kernel": "k_fp8_gemm gate_up (float32 rows)", "bound": "hbm",
                      "achieved": round(gu_alg / (gu_ms * 1e-3) / 1e9, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(gu_alg / (gu_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4), "traffic": None,
                      "alg_bytes_per_launch": int(gu_alg), "avg_launch_ms": round(gu_ms, 5)}}), flush=True)

@@ -113,6 +113,8 @@ _SIGNATURES = {
                                            ctypes.c_int32, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
     "fp8_quantize": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
                                     ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]),
+    "fp8_swiglu_quantize": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_int32,
+                                           ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]),
     "fp8_weight_packed_size": (ctypes.c_size_t, [ctypes.c_int32] * 3),
     "fp8_weight_repack": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                          ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
@@ -587,6 +589,25 @@ def fp8_quantize(x, block_rows: int = 1, out: FP8Tensor | None = None, stream=No
     return out
 
 
+def fp8_swiglu_quantize(gate_up, out: FP8Tensor | None = None, stream=None) -> FP8Tensor:
+    """gate_up float32/bf16 [M, 2I] -> FP8 h = silu(gate) * up with 1 x 128 blocks."""
+    import torch
+    _need(gate_up, gate_up.dtype, "gate_up")
+    M, N2 = gate_up.shape
+    I = N2 // 2
+    dev = gate_up.device
+    if out is None:
+        out = FP8Tensor(torch.empty((M, I), dtype=torch.uint8, device=dev),
+                        torch.empty((M, I // FP8_BLOCK), dtype=torch.float32, device=dev), 1)
+    if tuple(out.codes.shape) != (M, I) or tuple(out.scales.shape) != (M, I // FP8_BLOCK):
+        raise ValueError("out codes/scales must be [M, I] and [M, I/128]")
+    _need(out.codes, torch.uint8, "out.codes")
+    _need(out.scales, torch.float32, "out.scales")
+    _check(lib().fp8_swiglu_quantize(gate_up.data_ptr(), _dtype_code(gate_up), M, I, out.codes.data_ptr(),
+                                     out.scales.data_ptr(), _stream(stream)))
+    return out
+
+
 def fp8_weight_repack(codes, out=None, stream=None):
     """FP8 weight codes [E, N, K] -> packed tiles (uint8 tensor) for fp8_grouped_gemm."""
     import torch
@@ -690,6 +711,6 @@ def moe_unpermute_combine(y, perm_of_assignment, topk_w, T: int, k: int, out=Non
 
 __all__ = ["lib", "moe_route_permute", "moe_route_quantize", "moe_route_quantize_noalloc", "nvfp4_quantize", "nvfp4_grouped_gemm", "moe_swiglu", "nvfp4_weight_repack",
            "moe_unpermute_combine", "moe_expert_ffn", "moe_expert_ffn_workspace", "mxfp4_quantize",
-           "mxfp4_grouped_gemm", "mxfp4_weight_repack", "MXFP4Tensor", "fp8_quantize", "fp8_weight_repack",
+           "mxfp4_grouped_gemm", "mxfp4_weight_repack", "MXFP4Tensor", "fp8_quantize", "fp8_swiglu_quantize", "fp8_weight_repack",
            "fp8_grouped_gemm", "FP8Tensor", "Fp8GemmArgs", "NVFP4Tensor", "Routing", "GemmArgs", "NVFP4MoEError",
            "F32", "BF16", "EPI_F32", "EPI_BF16", "EPI_SWIGLU_NVFP4", "EPI_COMBINE_F32"]

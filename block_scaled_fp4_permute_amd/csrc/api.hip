@@ -488,6 +488,21 @@ int fp8_quantize(const void* x, int32_t x_dtype, int64_t batch, int64_t rows, in
                     "fp8_quantize");
 }
 
+int fp8_swiglu_quantize(const void* gate_up, int32_t dtype, int64_t M, int32_t I, uint8_t* codes, float* scales,
+                        void* stream) {
+  if (!gate_up || !codes || !scales) return fail(NVFP4MOE_ERR_INVALID, "fp8_swiglu_quantize: null pointer argument");
+  if (dtype != NVFP4MOE_F32 && dtype != NVFP4MOE_BF16)
+    return fail(NVFP4MOE_ERR_INVALID, "fp8_swiglu_quantize: dtype %d", dtype);
+  if (M <= 0 || I <= 0 || I % 128 != 0)
+    return fail(NVFP4MOE_ERR_INVALID, "fp8_swiglu_quantize: M > 0 and I a positive multiple of 128 needed");
+  if (prod_ge(M, I / 128, int64_t(1) << 33))
+    return fail(NVFP4MOE_ERR_UNSUPPORTED, "fp8_swiglu_quantize: 2^33 or more blocks of 128 values");
+  if (!aligned(gate_up, 8) || !aligned(codes, 2) || !aligned(scales, 4))
+    return fail(NVFP4MOE_ERR_INVALID, "fp8_swiglu_quantize: misaligned pointer");
+  return hip_status(nvfp4::launch_fp8_swiglu(gate_up, dtype, M, I, codes, scales, static_cast<hipStream_t>(stream)),
+                    "fp8_swiglu_quantize");
+}
+
 size_t fp8_weight_packed_size(int32_t E, int32_t N, int32_t K) {
   if (E <= 0 || N <= 0 || K <= 0 || K % 128 != 0 || N % 16 != 0 ||
       prod_ge(E, N / 16, int64_t(K / 128) * 64, int64_t(1) << 40))

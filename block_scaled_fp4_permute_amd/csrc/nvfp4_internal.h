@@ -81,6 +81,8 @@ struct Fp8Params {
 hipError_t launch_fp8_quantize(const void* x, int dtype, int64_t batch, int64_t rows, int64_t cols, int block_rows,
                                uint8_t* codes, float* scales, hipStream_t stream);
 size_t fp8_packed_weight_bytes(int E, int N, int K);
+hipError_t launch_fp8_swiglu(const void* y, int dtype, int64_t M, int I, uint8_t* codes, float* scales,
+                             hipStream_t stream);
 hipError_t launch_fp8_repack(const uint8_t* codes, int E, int N, int K, uint8_t* packed, hipStream_t stream);
 hipError_t launch_fp8_gemm(const Fp8Params& p, int epilogue, int64_t m_total, int hint, hipStream_t stream);
 

@@ -272,3 +272,85 @@ class MXMoELayer:
         moe_unpermute_combine(self.y2, r.perm_of_assignment, r.topk_w, T, k, out=self.out, stream=stream)
         mark(5)
         return self.out
+
+
+# ------------------------------------------------------------------ FP8 block-scaled variant
+@dataclass
+class FP8ExpertWeights:
+    """Per-expert FP8 weights with one float32 scale per 128 x 128 block:
+    gate_up codes [E, 2I, H] and scales [E, 2I/128, H/128], down [E, H, I] and
+    [E, H/128, I/128], with each matrix's packed tiles (fp8_weight_repack)."""
+    gu: "object"
+    dn: "object"
+    gu_packed: "object" = None
+    dn_packed: "object" = None
+
+    def pack(self) -> "FP8ExpertWeights":
+        from . import fp8_weight_repack
+        self.gu_packed = fp8_weight_repack(self.gu.codes)
+        self.dn_packed = fp8_weight_repack(self.dn.codes)
+        return self
+
+
+def quantize_expert_weights_fp8(w_gu: torch.Tensor, w_dn: torch.Tensor) -> FP8ExpertWeights:
+    """Quantise float32/bf16 weights [E, 2I, H] and [E, H, I] to FP8 (128 x 128
+    blocks) on the GPU and repack them."""
+    from . import fp8_quantize
+    return FP8ExpertWeights(fp8_quantize(w_gu.contiguous(), 128), fp8_quantize(w_dn.contiguous(), 128)).pack()
+
+
+class FP8MoELayer:
+    """Preallocated FP8 block-scaled MoE layer for T tokens, reusing the routing,
+    permutation and combine of the NVFP4 layer: route + permute, FP8
+    quantisation of x (1 x 128 blocks), gate_up grouped GEMM (float32 rows,
+    A gathered through the permutation), SwiGLU + FP8 requantisation of h,
+    down grouped GEMM (bf16 rows), weighted gather combine."""
+
+    def __init__(self, T: int, H: int, I: int, E: int, k: int, device):
+        from . import FP8_BLOCK, FP8Tensor
+        self.T, self.H, self.I, self.E, self.k = T, H, I, E, k
+        dev = torch.device(device)
+        i32 = dict(dtype=torch.int32, device=dev)
+        f32 = dict(dtype=torch.float32, device=dev)
+        u8 = dict(dtype=torch.uint8, device=dev)
+        M = T * k
+        self.routing = Routing(torch.empty((T, k), **i32), torch.empty((T, k), **f32), torch.empty(E, **i32),
+                               torch.empty(E + 1, **i32), torch.empty(M, **i32), torch.empty(M, **i32),
+                               torch.empty(M, **f32))
+        self.route_ws = torch.empty(max(16, lib().moe_route_permute_workspace_size(T, E, k)), **u8)
+        self.xq = FP8Tensor(torch.empty((T, H), **u8), torch.empty((T, H // FP8_BLOCK), **f32), 1)
+        self.y1 = torch.empty((M, 2 * I), **f32)
+        self.hq = FP8Tensor(torch.empty((M, I), **u8), torch.empty((M, I // FP8_BLOCK), **f32), 1)
+        self.y2 = torch.empty((M, H), dtype=torch.bfloat16, device=dev)
+        self.out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+
+    def forward(self, logits: torch.Tensor, x: torch.Tensor, w: FP8ExpertWeights, stream=None,
+                marks=None) -> torch.Tensor:
+        """One layer step; ``marks``: optional 7 events recorded before routing
+        and after each stage (route, quantise x, gate_up, SwiGLU + requant,
+        down, combine)."""
+        from . import fp8_grouped_gemm, fp8_quantize, fp8_swiglu_quantize
+        T, k, M = self.T, self.k, self.T * self.k
+        hint = M // self.E
+
+        def mark(i):
+            if marks is not None and marks[i] is not None:
+                marks[i].record(stream)
+
+        mark(0)
+        r = moe_route_permute(logits, k, out=self.routing, workspace=self.route_ws, stream=stream)
+        mark(1)
+        fp8_quantize(x, 1, out=self.xq, stream=stream)
+        mark(2)
+        fp8_grouped_gemm(self.xq, w.gu_packed, w.gu.scales, r.offsets, N=2 * self.I, m_total=M,
+                         a_rows=r.perm_src_token, epilogue=EPI_F32, out=self.y1, max_rows_per_expert_hint=hint,
+                         stream=stream)
+        mark(3)
+        fp8_swiglu_quantize(self.y1, out=self.hq, stream=stream)
+        mark(4)
+        fp8_grouped_gemm(self.hq, w.dn_packed, w.dn.scales, r.offsets, N=self.H, m_total=M, epilogue=EPI_BF16,
+                         out=self.y2, max_rows_per_expert_hint=hint, stream=stream)
+        mark(5)
+        moe_unpermute_combine(self.y2, r.perm_of_assignment, r.topk_w, T, k, out=self.out, stream=stream)
+        mark(6)
+        return self.out

@@ -318,6 +318,13 @@ int mxfp4_weight_repack(const uint8_t* codes, const uint8_t* scales, int32_t E, 
  * scales 4-byte aligned. */
 int fp8_quantize(const void* x, int32_t x_dtype, int64_t batch, int64_t rows, int64_t cols, int32_t block_rows,
                  uint8_t* codes, float* scales, void* stream);
+/* SwiGLU between the FP8 grouped GEMMs: h = silu(gate) * up of gate_up [M, 2I]
+ * (float32 or bf16; gate = columns [0, I), up = [I, 2I), as moe_swiglu), in
+ * float32, quantised as fp8_quantize with 1 x 128 blocks: codes [M, I], scales
+ * [M, I/128].  I % 128 == 0; gate_up 8-byte, codes 2-byte, scales 4-byte
+ * aligned. */
+int fp8_swiglu_quantize(const void* gate_up, int32_t dtype, int64_t M, int32_t I, uint8_t* codes, float* scales,
+                        void* stream);
 /* FP8 weights [E, N, K] repacked once into tiles of 16 rows x 128 K (2048
  * bytes, each lane's 32 bytes in the order the kernel's lanes read them; zero
  * codes past N).  Private layout, pure data movement.  K % 128 == 0, N % 16 ==

@@ -114,3 +114,15 @@ def fp8_grouped_gemm(a_codes, a_scales, b_codes, b_scales, offsets, a_rows=None,
         if want_absdot:
             absdot[p0:p1] = accm
     return y, absdot
+
+
+def fp8_swiglu_quantize(y1: np.ndarray):
+    """h = silu(gate) * up (float64; gate = y1[:, :I], up = y1[:, I:]), rounded
+    to float32, then FP8 with 1 x 128 blocks.  Returns (codes, scales, h64)."""
+    y = np.asarray(y1, dtype=np.float64)
+    I = y.shape[1] // 2
+    g = y[:, :I]
+    with np.errstate(over="ignore"):
+        h64 = g / (1.0 + np.exp(-g)) * y[:, I:]
+    codes, scales = fp8_quantize(h64.astype(np.float32), 1)
+    return codes, scales, h64

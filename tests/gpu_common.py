@@ -186,3 +186,57 @@ def check_requant_mx(codes_gpu, scales_gpu, x_ref, tol_abs, max_flip_frac=1e-3, 
     if nsflip * 32 + ncflip > max_flip_frac * x32.size:
         raise AssertionError(f"{what}: {nsflip} scale flips and {ncflip} code flips in {x32.size} elements")
     return nsflip, ncflip
+
+
+def check_requant_fp8(codes_gpu, scales_gpu, x_ref, tol_abs, max_flip_frac=1e-3, what="fp8 requant"):
+    """GPU FP8 (1 x 128 block) codes of a value the GPU computed itself (within
+    tol_abs of the oracle's x_ref per element) against the oracle's FP8 encoding
+    of x_ref.
+
+    * a block's float32 scale s = absmax / 448 may differ from the oracle's by
+      at most the block's tolerance / 448 (plus 2 ulp);
+    * a differing element code must be the E4M3 rounding of some value within
+      the element's tolerance (over s, plus the scale's relative difference)
+      of the oracle's x / s: a code between the roundings of the interval's
+      two ends, with the sign of x unless the interval holds 0;
+    * at most max_flip_frac of the elements may differ.
+    Returns (scale differences, code flips)."""
+    from oracle import fp8 as F8
+    x32 = np.asarray(x_ref, np.float64).astype(np.float32)
+    rows, cols = x32.shape
+    tol_abs = np.broadcast_to(np.asarray(tol_abs, np.float64), x32.shape)
+    c_ref, s_ref = F8.fp8_quantize(x32, 1)
+    s_gpu = np.asarray(scales_gpu, np.float32).reshape(rows, cols // 128).astype(np.float64)
+    s_r = s_ref.astype(np.float64)
+    c_gpu = np.asarray(codes_gpu, np.uint8).reshape(rows, cols)
+    tol_blk = tol_abs.reshape(rows, -1, 128).max(axis=2) / 448.0 + s_r * 2.0 ** -22
+    sbad = np.abs(s_gpu - s_r) > tol_blk
+    if sbad.any():
+        i = tuple(np.argwhere(sbad)[0])
+        raise AssertionError(f"{what}: block scale {i} gpu {s_gpu[i]!r} ref {s_r[i]!r} tol {tol_blk[i]}")
+    nsdiff = int((s_gpu != s_r).sum())
+    cdiff = c_gpu != c_ref
+    ncflip = int(cdiff.sum())
+    if ncflip:
+        sv = np.repeat(s_r, 128, axis=1)
+        rel_s = np.repeat(np.abs(s_gpu - s_r) / s_r, 128, axis=1)
+        xs = x32.astype(np.float64) / sv                       # signed quotient
+        tol_v = tol_abs / sv + np.abs(xs) * (rel_s + 2.0 ** -22)
+        lo, hi = xs - tol_v, xs + tol_v
+        mag_g = F8.e4m3_decode(c_gpu & 0x7F)
+        neg_g = (c_gpu & 0x80) != 0
+        val_g = np.where(neg_g, -mag_g, mag_g)
+        # the E4M3 roundings of the interval's ends, as signed grid values
+        def rnd(t):
+            m = F8.e4m3_decode(F8.e4m3_encode_satfinite(np.minimum(np.abs(t), F8.E4M3_MAX)))
+            return np.where(t < 0, -m, m)
+        r_lo, r_hi = rnd(lo), rnd(hi)
+        in_range = (val_g >= r_lo) & (val_g <= r_hi)
+        sign_ok = (neg_g == (xs < 0)) | (mag_g == 0) | ((lo <= 0) & (hi >= 0))
+        bad = cdiff & ~(in_range & sign_ok)
+        if bad.any():
+            i = tuple(np.argwhere(bad)[0])
+            raise AssertionError(f"{what}: code {i} gpu {c_gpu[i]:#x} ref {c_ref[i]:#x} x/s {xs[i]} tol {tol_v[i]}")
+    if ncflip > max_flip_frac * x32.size:
+        raise AssertionError(f"{what}: {ncflip} code flips in {x32.size} elements")
+    return nsdiff, ncflip

@@ -5,7 +5,9 @@ row blocks, decision points, the subnormal range), the packed tile layout
 byte for byte, the GEMM within 1e-3 sum|a^ b^| + 1e-6 (bf16 out: + 2^-8 |y|),
 bit for bit where every float32 sum is exact, within two float32 ulps where
 each output is a single block term (which pins each block's pair of scales),
-and whole outputs at the Zipf decode gate_up and down shapes.  Every GPU
+whole outputs at the Zipf decode gate_up and down shapes, the SwiGLU + FP8
+requantisation code by code (flips only next to a decision point), and the
+FP8 layer (routing, permutation and combine of the NVFP4 path) end to end.  Every GPU
 stage is fed the oracle's inputs or seeded raw bytes."""
 import numpy as np
 import pytest
@@ -15,7 +17,7 @@ import block_scaled_fp4_permute_amd as m
 import workloads
 from oracle import fp8 as F8
 from oracle import moe as OM
-from tests.gpu_common import assert_gemm_close, bf16_to_f32, down, up
+from tests.gpu_common import DEV, assert_gemm_close, bf16_to_f32, check_requant_fp8, down, up
 
 pytestmark = pytest.mark.gpu
 
@@ -242,3 +244,81 @@ def test_fp8_whole_decode_gate_up_and_down():
     torch.cuda.synchronize()
     y2, ad2 = F8.fp8_grouped_gemm(hc, hs, dnc, dns, offsets)
     assert_gemm_close(bf16_to_f32(y2g), y2, ad2, bf16_out=True, what="fp8 down bf16, all 16384 x 6144")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_fp8_swiglu_quantize(dtype):
+    # the oracle's gate_up rows in, h = silu(gate) * up requantised: the two
+    # sides differ only by silu's float32 rounding (expf), so a code may flip
+    # only within a few ulp of a decision point and a block scale only by
+    # the rounding of its absmax
+    rng = np.random.default_rng(21)
+    M, I = 300, 256
+    y1 = (rng.standard_normal((M, 2 * I)) * np.exp2(rng.integers(-6, 6, (M, 1)))).astype(np.float32)
+    y1[0, :] = 0.0                                     # a zero row: h = 0, scale 1
+    if dtype == "bf16":
+        y1 = workloads.to_bf16_values(y1)
+    yt = up(y1).to(torch.bfloat16) if dtype == "bf16" else up(y1)
+    hq = m.fp8_swiglu_quantize(yt)
+    torch.cuda.synchronize()
+    _, _, h64 = F8.fp8_swiglu_quantize(y1)
+    ns, nc = check_requant_fp8(down(hq.codes), down(hq.scales), h64, 2.0 ** -20 * np.abs(h64) + 1e-30,
+                               max_flip_frac=1e-3, what="fp8 swiglu")
+    assert down(hq.scales)[0].tolist() == [1.0, 1.0] and not down(hq.codes)[0].any()
+    print(f"fp8 swiglu {dtype}: {ns} scale and {nc} code differences", flush=True)
+
+
+def _swiglu_tol(y1, absdot):
+    I = y1.shape[1] // 2
+    tol_y = 1e-3 * absdot + 1e-6
+    g, u = y1[:, :I].astype(np.float64), y1[:, I:].astype(np.float64)
+    silu = OM.silu(g)
+    return 1.1 * tol_y[:, :I] * np.abs(u) + np.abs(silu) * tol_y[:, I:] + 2.0 ** -20 * np.abs(silu * u) + 1e-9
+
+
+@pytest.mark.parametrize("cfg_index", [0, 1])
+def test_fp8_layer_end_to_end(cfg_index):
+    # FP8MoELayer against the oracle's stages composed the same way: routing
+    # and x codes bit for bit, weight codes bit for bit, gate_up within the
+    # GEMM tolerance, h flips only within the propagated window, and the output
+    # within the down tolerance plus the exact bound of every h the GPU rounded
+    # the other way
+    from block_scaled_fp4_permute_amd.layer import FP8MoELayer, quantize_expert_weights_fp8
+    c = workloads.CONFIGS[cfg_index]
+    print(f"fp8 layer end to end cfg={cfg_index}", flush=True)
+    logits, x = workloads.logits(c), workloads.activations(c)
+    w_gu, w_dn = workloads.torch_expert_weights(c, DEV)
+    wq = quantize_expert_weights_fp8(w_gu, w_dn)
+    layer = FP8MoELayer(c.T, c.H, c.I, c.E, c.k, DEV)
+    out = layer.forward(up(logits), up(x).to(torch.bfloat16), wq)
+    torch.cuda.synchronize()
+    ids, w = OM.route(logits, c.k)
+    counts, offsets, src, perm_of, pw = OM.permute(ids, w, c.E)
+    assert np.array_equal(down(layer.routing.perm_src_token), src)
+    xb = workloads.to_bf16_values(x)                 # the layer quantises the bf16 activations
+    xc, xs = F8.fp8_quantize(xb, 1)
+    assert np.array_equal(down(layer.xq.codes), xc) and np.array_equal(down(layer.xq.scales), xs)
+    wg, wd = w_gu.cpu().numpy(), w_dn.cpu().numpy()
+    gq = [F8.fp8_quantize(wg[e], 128) for e in range(c.E)]
+    dq = [F8.fp8_quantize(wd[e], 128) for e in range(c.E)]
+    gc, gs = np.stack([q[0] for q in gq]), np.stack([q[1] for q in gq])
+    dc, ds = np.stack([q[0] for q in dq]), np.stack([q[1] for q in dq])
+    assert np.array_equal(down(wq.gu.codes), gc) and np.array_equal(down(wq.gu.scales), gs)
+    assert np.array_equal(down(wq.dn.codes), dc) and np.array_equal(down(wq.dn.scales), ds)
+    y1, ad1 = F8.fp8_grouped_gemm(xc, xs, gc, gs, offsets, a_rows=src)
+    assert_gemm_close(down(layer.y1), y1, ad1, what="fp8 layer gate_up")
+    hc, hs, h64 = F8.fp8_swiglu_quantize(y1)
+    hc_gpu, hs_gpu = down(layer.hq.codes), down(layer.hq.scales)
+    check_requant_fp8(hc_gpu, hs_gpu, h64, _swiglu_tol(y1, ad1), max_flip_frac=0.02, what="fp8 layer h")
+    y2, ad2 = F8.fp8_grouped_gemm(hc, hs, dc, ds, offsets)
+    dh = np.abs(F8.fp8_dequantize(hc_gpu, hs_gpu, 1) - F8.fp8_dequantize(hc, hs, 1))
+    tol_rows = 1e-3 * ad2 + 1e-6 + 2.0 ** -8 * np.abs(y2.astype(np.float64))
+    for e in range(c.E):
+        p0, p1 = int(offsets[e]), int(offsets[e + 1])
+        if p1 > p0 and dh[p0:p1].any():
+            tol_rows[p0:p1] += 1.001 * dh[p0:p1] @ np.abs(F8.fp8_dequantize(dc[e], ds[e], 128)).T
+    out64, _ = OM.combine(y2, perm_of, w)
+    tol = np.einsum("tj,tjh->th", np.abs(w.astype(np.float64)), tol_rows[perm_of.reshape(c.T, c.k)])
+    tol = tol * (1 + 2.0 ** -8) + 2.0 ** -8 * np.abs(out64) + 1e-6
+    err = np.abs(bf16_to_f32(out) - out64)
+    assert np.all(err <= tol), f"fp8 layer: {int((err > tol).sum())} outputs outside tolerance"

@@ -145,3 +145,17 @@ def test_fp8_gemm_dense_is_matmul_and_approximates_full_precision():
     np.testing.assert_allclose(y, ref, rtol=1e-6, atol=1e-12)
     full = A.astype(np.float64) @ B.astype(np.float64).T
     assert np.linalg.norm(y - full) / np.linalg.norm(full) < 0.05
+
+
+def test_fp8_swiglu_quantize_matches_parts():
+    # silu against scipy's logistic function, the product, then the 1 x 128
+    # quantiser on the float32 rounding of h
+    from scipy.special import expit
+    rng = np.random.default_rng(12)
+    y1 = (rng.standard_normal((5, 512)) * 4).astype(np.float32)
+    codes, scales, h64 = P.fp8_swiglu_quantize(y1)
+    g, u = y1[:, :256].astype(np.float64), y1[:, 256:].astype(np.float64)
+    np.testing.assert_allclose(h64, g * expit(g) * u, rtol=1e-14, atol=1e-300)
+    c2, s2 = P.fp8_quantize(h64.astype(np.float32), 1)
+    assert np.array_equal(codes, c2) and np.array_equal(scales, s2)
+    assert codes.shape == (5, 256) and scales.shape == (5, 2)
