@@ -616,6 +616,260 @@ __global__ __launch_bounds__(256, 2) void k_mx_gemm_n(const GemmParams p) {
   }
 }
 
+// ---- large-M tile (K % 256 == 0, packed weights): a workgroup of 8 waves
+// computes 256 rows x 256 columns (SwiGLU: 128 gate + 128 up), with both
+// operands of a K step staged in LDS: each fragment read from memory once per
+// workgroup feeds 8 (A) or 16 (B) waves' worth of MFMAs instead of one, which
+// moves the kernel from the weight stream to the matrix core once experts
+// hold hundreds of rows.  Wave w = 4 wr + wc holds rows [128 wr, +128) and
+// the four 16-column tiles 4 wc.. (SwiGLU: gate tiles 2 wc, 2 wc + 1 and the
+// matching up tiles).  One stage (68 KB, two of them double-buffered):
+//   A codes   16 row tiles x 2048 bytes: half h of lane (g, r) at
+//             1024 h + 256 g + 16 (r ^ (2 g + h)) (the XOR spreads the 8
+//             lanes that store one row's 128 code bytes over distinct banks)
+//   A scales  256 rows x 8 bytes (the step's 8 E8M0 bytes of the row)
+//   B codes   16 column tiles x 2048 bytes, as in the packed tile
+//   B scales  16 column tiles x 128 bytes, as in the packed tile
+// The next step's global loads are issued before the MFMAs of the current
+// one and stored into the other stage after them: one barrier per step.
+constexpr int kMxLRows = 256;
+constexpr int kMxLThreads = 512;
+constexpr int kMxLA = 0;
+constexpr int kMxLASc = 16 * 2048;
+constexpr int kMxLB = kMxLASc + kMxLRows * 8;
+constexpr int kMxLBSc = kMxLB + 16 * 2048;
+constexpr int kMxLStage = kMxLBSc + 16 * 128;
+
+// the thread's staging registers: its A pieces of a step, or its B pieces
+struct MxLRegs {
+  u32x4 c[4];
+  uint32_t s;
+};
+
+struct MxLSrc {
+  rsrc_t ra, rs;            // A codes and scales (range-checked)
+  uint32_t va[4];           // byte offset of the thread's four A pieces at step 0
+  uint32_t vs;              // of its A scale word at step 0
+  uint32_t lda;             // LDS offset of its first A piece (the others follow 8 KB apart)
+  const uint8_t* b;         // expert's packed tiles
+  uint32_t ob[4];           // byte offset of the thread's four B code pieces at step 0
+  uint32_t obs;             // of its B scale word at step 0
+};
+
+__device__ __forceinline__ void mxl_load_a(const MxLSrc& S, MxLRegs& R, int st) {
+  const uint32_t oa = static_cast<uint32_t>(st) * (kMxKStep / 2);
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    R.c[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(S.ra, S.va[i] + oa, 0, 0));
+  R.s = __builtin_amdgcn_raw_buffer_load_b32(S.rs, S.vs + static_cast<uint32_t>(st) * (kMxKStep / 32), 0, 0);
+}
+
+__device__ __forceinline__ void mxl_load_b(const MxLSrc& S, MxLRegs& R, int st) {
+  const uint32_t ot = static_cast<uint32_t>(st) * kMxTile;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) R.c[i] = *reinterpret_cast<const u32x4*>(S.b + (S.ob[i] + ot));
+  R.s = *reinterpret_cast<const uint32_t*>(S.b + (S.obs + ot));
+}
+
+__device__ __forceinline__ void mxl_store_a(const MxLSrc& S, const MxLRegs& R, uint8_t* __restrict__ stage) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) *reinterpret_cast<u32x4*>(stage + S.lda + 8192 * i) = R.c[i];
+  *reinterpret_cast<uint32_t*>(stage + kMxLASc + 4 * threadIdx.x) = R.s;
+}
+
+__device__ __forceinline__ void mxl_store_b(const MxLRegs& R, uint8_t* __restrict__ stage) {
+  const int t = threadIdx.x;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) *reinterpret_cast<u32x4*>(stage + kMxLB + 16 * (t + kMxLThreads * i)) = R.c[i];
+  *reinterpret_cast<uint32_t*>(stage + kMxLBSc + 4 * t) = R.s;
+}
+
+// half H of one staged step (the lane's block 2 g + H of each row): wave rows
+// [128 wr, +128), B tiles jt[0..3]
+template <int H>
+__device__ __forceinline__ void mxl_half(const uint8_t* __restrict__ stage, int wr, const int (&jt)[4],
+                                         const uint32_t (&asc)[8], const uint32_t (&bsc)[4], float4v (&acc)[8][4]) {
+  const int lane = threadIdx.x & 63;
+  const int lr = lane & 15, lg = lane >> 4;
+  i32x8 bf[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const u32x4 c = *reinterpret_cast<const u32x4*>(stage + kMxLB + jt[j] * 2048 + 1024 * H + 16 * lane);
+    bf[j] = i32x8{static_cast<int>(c.x), static_cast<int>(c.y), static_cast<int>(c.z), static_cast<int>(c.w),
+                  0, 0, 0, 0};
+  }
+  const int aoff = kMxLA + 1024 * H + 256 * lg + 16 * (lr ^ (2 * lg + H));
+#pragma unroll
+  for (int r = 0; r < 8; ++r) {
+    const u32x4 c = *reinterpret_cast<const u32x4*>(stage + aoff + (8 * wr + r) * 2048);
+    const i32x8 af = {static_cast<int>(c.x), static_cast<int>(c.y), static_cast<int>(c.z), static_cast<int>(c.w),
+                      0, 0, 0, 0};
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      acc[r][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af, bf[j], acc[r][j], kMxFmtFp4, kMxFmtFp4, H,
+                                                                    static_cast<int>(asc[r]), H,
+                                                                    static_cast<int>(bsc[j]));
+  }
+}
+
+// the scale bytes of one staged step for this wave's row and column tiles
+__device__ __forceinline__ void mxl_scales(const uint8_t* __restrict__ stage, int wr, const int (&jt)[4],
+                                           uint32_t (&asc)[8], uint32_t (&bsc)[4]) {
+  const int lane = threadIdx.x & 63;
+  const int lr = lane & 15, lg = lane >> 4;
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    bsc[j] = *reinterpret_cast<const uint16_t*>(stage + kMxLBSc + jt[j] * 128 + 2 * lane);
+#pragma unroll
+  for (int r = 0; r < 8; ++r)
+    asc[r] = *reinterpret_cast<const uint16_t*>(stage + kMxLASc + (16 * (8 * wr + r) + lr) * 8 + 2 * lg);
+}
+
+template <int EPI>
+__global__ __launch_bounds__(kMxLThreads, 1) void k_mx_gemm_l(const GemmParams p) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * kMxLStage];
+  static_assert(fits_lds(sizeof(lds), 1), "MX large-M staging exceeds the LDS of a CU");
+  int e, m0, nt;
+  bool narrow;
+  if (!find_task<16, false, 0>(p, e, m0, nt, narrow)) return;
+  const int t = threadIdx.x;
+  const int lane = t & 63, wave = t >> 6;
+  const int wr = wave >> 2, wc = wave & 3;
+  const int lr = lane & 15;
+  const int row0 = min(max(p.offsets[e], 0), p.m_total);
+  const int Me = min(max(p.offsets[e + 1], 0), p.m_total) - row0;
+  // inside an expert, groups of 4 row chunks run column tile by column tile,
+  // so that the workgroups running side by side on an XCD share 4 A chunks
+  // and a few weight column tiles in its L2
+  {
+    const int nc = (Me + kMxLRows - 1) / kMxLRows;
+    const int u = (m0 / kMxLRows) * p.n_tiles + nt;
+    const int grp = (m0 / kMxLRows) / 4;
+    const int gq = min(4, nc - 4 * grp);
+    const int w = u - 4 * grp * p.n_tiles;
+    m0 = (4 * grp + w % gq) * kMxLRows;
+    nt = w / gq;
+  }
+  const int rows = min(kMxLRows, Me - m0);
+  const int N = p.N, K = p.K;
+  const int nsteps = K / kMxKStep;
+  const int ntr = N / 16;
+
+  MxLSrc S;
+  {
+    const uint32_t krow = static_cast<uint32_t>(K) / 2, srow = static_cast<uint32_t>(K) / 32;
+    S.ra = make_rsrc(p.a_codes, static_cast<uint32_t>(p.a_rows_total) * krow);
+    S.rs = make_rsrc(p.a_scales, static_cast<uint32_t>(p.a_rows_total) * srow);
+    const int blk = t & 7;            // 32-value block of the step this thread stages for its A rows
+    const int g = blk >> 1, h = blk & 1;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int ar = (t >> 3) + 64 * i;
+      int arow = row0 + m0 + (ar < rows ? ar : 0);
+      if (p.a_rows) arow = p.a_rows[arow];
+      arow = (arow >= 0 && arow < p.a_rows_total) ? arow : 0;
+      S.va[i] = static_cast<uint32_t>(arow) * krow + 16u * blk;
+    }
+    // rows t / 8 + 64 i: row tile 4 i further, 8 KB apart
+    S.lda = kMxLA + ((t >> 3) >> 4) * 2048 + 1024 * h + 256 * g + 16 * (((t >> 3) & 15) ^ (2 * g + h));
+    {
+      const int ar = t >> 1;
+      int arow = row0 + m0 + (ar < rows ? ar : 0);
+      if (p.a_rows) arow = p.a_rows[arow];
+      arow = (arow >= 0 && arow < p.a_rows_total) ? arow : 0;
+      S.vs = static_cast<uint32_t>(arow) * srow + 4u * (t & 1);
+    }
+    S.b = p.b_packed + static_cast<size_t>(e) * ntr * nsteps * kMxTile;
+    auto tile_of = [&](int j) {     // packed column tile of LDS tile j
+      int rt;
+      if constexpr (EPI == EPI_SWIGLU)
+        rt = j < 8 ? nt * 8 + j : (N / 32) + nt * 8 + (j - 8);
+      else
+        rt = nt * 16 + j;
+      return static_cast<uint32_t>(min(rt, ntr - 1));
+    };
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int pc = t + kMxLThreads * i;     // 16-byte piece of the 16 x 2048 code bytes
+      S.ob[i] = tile_of(pc >> 7) * static_cast<uint32_t>(nsteps) * kMxTile + 16u * (pc & 127);
+    }
+    S.obs = tile_of(t >> 5) * static_cast<uint32_t>(nsteps) * kMxTile + 2048u + 4u * (t & 31);
+  }
+  int jt[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    if constexpr (EPI == EPI_SWIGLU)
+      jt[j] = (j < 2 ? 0 : 8) + 2 * wc + (j & 1);
+    else
+      jt[j] = 4 * wc + j;
+  }
+
+  float4v acc[8][4];
+#pragma unroll
+  for (int r = 0; r < 8; ++r)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[r][j] = float4v{0.f, 0.f, 0.f, 0.f};
+
+  // prologue: step 0 into stage 0
+  MxLRegs R;
+  mxl_load_a(S, R, 0);
+  mxl_store_a(S, R, lds);
+  mxl_load_b(S, R, 0);
+  mxl_store_b(R, lds);
+  __syncthreads();
+  // Step st computes from stage st % 2 while the loads of step st + 1 go to
+  // the other stage (its readers passed the previous barrier): the A pieces
+  // in flight behind the first half of the MFMAs, the B pieces behind the
+  // second half.  No branches: the last step re-stages itself into the idle
+  // stage, which nothing reads afterwards.
+  for (int st = 0; st < nsteps; ++st) {
+    const uint8_t* cur = lds + (st & 1) * kMxLStage;
+    uint8_t* nxt = lds + ((st + 1) & 1) * kMxLStage;
+    const int sn = min(st + 1, nsteps - 1);
+    uint32_t asc[8], bsc[4];
+    mxl_scales(cur, wr, jt, asc, bsc);
+    mxl_load_a(S, R, sn);
+    mxl_half<0>(cur, wr, jt, asc, bsc, acc);
+    mxl_store_a(S, R, nxt);
+    mxl_load_b(S, R, sn);
+    mxl_half<1>(cur, wr, jt, asc, bsc, acc);
+    mxl_store_b(R, nxt);
+    __syncthreads();
+  }
+
+  const float gab = p.a_g[0] * p.b_g[e];
+  const int prow0 = row0 + m0;
+#pragma unroll
+  for (int r = 0; r < 8; ++r) {
+    const int rt = 8 * wr + r;
+    const int left = rows - 16 * rt;
+    if (left <= 0) continue;
+    if constexpr (EPI == EPI_SWIGLU) {
+      const int hc0 = nt * 128 + 32 * wc;
+      mx_epilogue_swiglu(p, acc[r][0], acc[r][1], acc[r][2], acc[r][3], prow0 + 16 * rt, left, hc0, hc0 < N / 2,
+                         gab);
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int col = nt * 256 + 64 * wc + 16 * j;
+        epilogue_tile<EPI>(p, acc[r][j], prow0 + 16 * rt, left, col + lr, col + lr < N, gab);
+      }
+    }
+  }
+}
+
+template <int EPI>
+static hipError_t launch_mx_l(GemmParams prm, int64_t m_total, hipStream_t stream) {
+  const int cols = (EPI == EPI_SWIGLU) ? prm.N / 2 : prm.N;
+  const int per = (EPI == EPI_SWIGLU) ? 128 : 256;
+  prm.n_tiles = (cols + per - 1) / per;
+  prm.slots = 1 << 30;
+  const int64_t blocks = ((((m_total + kMxLRows - 1) / kMxLRows + prm.E) * prm.n_tiles) + 7) / 8 * 8;
+  if (blocks >= (int64_t(1) << 31)) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL((k_mx_gemm_l<EPI>), dim3(static_cast<unsigned>(blocks)), dim3(kMxLThreads), 0, stream, prm);
+  return hipGetLastError();
+}
+
 template <int EPI, bool PACKED, bool NT>
 static hipError_t launch_mx_k(GemmParams prm, int64_t m_total, hipStream_t stream) {
   constexpr int WN = 4, BN = 4 * WN * 16;
@@ -647,6 +901,14 @@ static hipError_t launch_mx_n(GemmParams prm, int64_t m_total, hipStream_t strea
 hipError_t launch_mx_gemm(const GemmParams& prm, int epilogue, int64_t m_total, int hint, hipStream_t stream) {
   const int64_t rows_per_expert = hint > 0 ? hint : m_total / prm.E;
   const bool nt = rows_per_expert < 64;
+  if (prm.b_packed && prm.K % kMxKStep == 0 && rows_per_expert >= kMxLRows) {
+    switch (epilogue) {
+      case EPI_F32: return launch_mx_l<EPI_F32>(prm, m_total, stream);
+      case EPI_BF16: return launch_mx_l<EPI_BF16>(prm, m_total, stream);
+      case EPI_SWIGLU: return launch_mx_l<EPI_SWIGLU>(prm, m_total, stream);
+      default: break;
+    }
+  }
   if (prm.b_packed && prm.K <= kMxKStep && (epilogue == EPI_F32 || epilogue == EPI_BF16)) {
     if (epilogue == EPI_F32)
       return nt ? launch_mx_n<EPI_F32, true>(prm, m_total, stream) : launch_mx_n<EPI_F32, false>(prm, m_total, stream);

@@ -113,19 +113,40 @@ def test_mx_weight_repack_layout(E, N, K):
     assert np.all(us[:, :, K // 32:] == 127) and np.all(us[:, N:] == 127)     # neutral scale in the padding
 
 
+# hint (or the average) of at least 256 rows per expert, K a multiple of 256
+# and packed weights: the 256 x 256 tile with both operands staged in LDS
+LARGE_CASES = [
+    # E, counts, N, K, rows_a, hint
+    (3, [300, 0, 517], 320, 512, 400, 256),          # a partial column tile, an empty expert
+    (1, [600], 512, 2048, 600, 0),                   # by the average; a partial row chunk
+    (5, [256, 1, 1000, 0, 255], 256, 768, 700, 300),  # 1-row and 255-row experts, 4 chunks in one group
+]
+
+
 @pytest.mark.parametrize("case", range(len(CASES)))
 @pytest.mark.parametrize("gather", [False, True])
 @pytest.mark.parametrize("epi", ["f32", "bf16"])
 @pytest.mark.parametrize("packed", [False, True])
 def test_mx_gemm_random(case, gather, epi, packed):
-    E, counts, N, K, rows_a, hint = CASES[case]
-    rng = np.random.default_rng(200 + case)
+    _run_mx_case(CASES[case], 200 + case, gather, epi, packed, f"case {case}")
+
+
+@pytest.mark.parametrize("case", range(len(LARGE_CASES)))
+@pytest.mark.parametrize("gather", [False, True])
+@pytest.mark.parametrize("epi", ["f32", "bf16"])
+def test_mx_gemm_large_tile(case, gather, epi):
+    _run_mx_case(LARGE_CASES[case], 300 + case, gather, epi, True, f"large case {case}")
+
+
+def _run_mx_case(spec, seed, gather, epi, packed, name):
+    E, counts, N, K, rows_a, hint = spec
+    rng = np.random.default_rng(seed)
     if counts is None:
         counts = rng.integers(0, 40, E) * (rng.random(E) < 0.7)
         counts[rng.choice(E, 4, replace=False)] = [150, 200, 65, 17]
     counts = np.asarray(counts, np.int64)
     M = int(counts.sum())
-    print(f"mx gemm case {case} gather={gather} epi={epi} packed={packed} E={E} M={M} N={N} K={K}", flush=True)
+    print(f"mx gemm {name} gather={gather} epi={epi} packed={packed} E={E} M={M} N={N} K={K} hint={hint}", flush=True)
     if not gather:
         rows_a = max(M, 1)                     # row p of the GEMM reads A row p
     ac, as_ = _rand_mx(rng, (rows_a,), K)
@@ -142,33 +163,38 @@ def test_mx_gemm_random(case, gather, epi, packed):
     torch.cuda.synchronize()
     y_ref, absdot = MX.mx_grouped_gemm(ac, as_, bc, bs, offsets, a_rows=a_rows, a_g=0.75, b_g=b_g)
     got = down(y) if epi == "f32" else bf16_to_f32(y)
-    assert_gemm_close(got, y_ref, absdot, bf16_out=epi == "bf16", what=f"mx case {case} {epi}")
+    assert_gemm_close(got, y_ref, absdot, bf16_out=epi == "bf16", what=f"mx {name} {epi}")
 
 
-@pytest.mark.parametrize("K", [256, 2048, 8192])
-def test_mx_gemm_constant_scales_bit_exact(K):
+@pytest.mark.parametrize("K,large", [(256, False), (2048, False), (8192, False), (256, True), (8192, True)])
+def test_mx_gemm_constant_scales_bit_exact(K, large):
     # one scale per operand: every float32 partial sum is an exact multiple of
     # 0.25 * 2^(Xa + Xb), so the GPU must equal the oracle bit for bit
-    rng = np.random.default_rng(K)
-    E, counts, N = 2, [37, 70], 80
+    rng = np.random.default_rng(K + large)
+    E, counts, N = (2, [300, 520], 272) if large else (2, [37, 70], 80)
     M = sum(counts)
     ac = rng.integers(0, 256, (M, K // 2), dtype=np.uint8)
     bc = rng.integers(0, 256, (E, N, K // 2), dtype=np.uint8)
     as_ = np.full((M, K // 32), 124, np.uint8)
     bs = np.full((E, N, K // 32), 129, np.uint8)
     offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
-    y = m.mxfp4_grouped_gemm(_mx_up(ac, as_), _mx_up(bc, bs), up(offsets), m_total=M)
+    b_t = _mx_up(bc, bs)
+    y = m.mxfp4_grouped_gemm(_mx_up(ac, as_), b_t, up(offsets), m_total=M,
+                             b_packed=m.mxfp4_weight_repack(b_t) if large else None)
     torch.cuda.synchronize()
     y_ref, _ = MX.mx_grouped_gemm(ac, as_, bc, bs, offsets)
     assert np.array_equal(down(y), y_ref)
 
 
-def test_mx_gemm_scale_per_block_single_term():
+@pytest.mark.parametrize("large", [False, True])
+def test_mx_gemm_scale_per_block_single_term(large):
     # K = 256 with one nonzero 32-block per row pair at a time: each output is
     # one exact block term, so the per-lane scale selection (two blocks per
-    # lane, op_sel picking the byte) must put every scale on its own block
+    # lane, op_sel picking the byte) must put every scale on its own block;
+    # large: 300 rows through the 256 x 256 tile, whose A blocks sit in LDS
+    # under a lane swizzle
     rng = np.random.default_rng(5)
-    M, N, K = 16, 16, 256
+    M, N, K = (300, 48, 256) if large else (16, 16, 256)
     for blk in range(8):
         ac = np.zeros((M, K // 2), np.uint8)
         bc = np.zeros((1, N, K // 2), np.uint8)
@@ -177,7 +203,9 @@ def test_mx_gemm_scale_per_block_single_term():
         as_ = rng.integers(100, 150, (M, K // 32), dtype=np.uint8)
         bs = rng.integers(100, 150, (1, N, K // 32), dtype=np.uint8)
         offsets = np.array([0, M], np.int32)
-        y = m.mxfp4_grouped_gemm(_mx_up(ac, as_), _mx_up(bc, bs), up(offsets), m_total=M)
+        b_t = _mx_up(bc, bs)
+        y = m.mxfp4_grouped_gemm(_mx_up(ac, as_), b_t, up(offsets), m_total=M,
+                                 b_packed=m.mxfp4_weight_repack(b_t) if large else None)
         torch.cuda.synchronize()
         y_ref, _ = MX.mx_grouped_gemm(ac, as_, bc, bs, offsets)
         assert np.array_equal(down(y), y_ref), f"block {blk}"
@@ -207,6 +235,47 @@ def test_mx_fused_swiglu(hint):
     _, _, h64 = MX.mx_swiglu_quantize(y1)
     check_requant_mx(down(hq.codes), down(hq.scales), h64, _swiglu_tol(y1, absdot), max_flip_frac=0.02,
                      what="mx fused swiglu")
+
+
+def test_mx_fused_swiglu_large_tile():
+    # 256 x 256 tiles (128 h columns each): I = 192 leaves the second h tile
+    # half empty; a gathered A
+    rng = np.random.default_rng(37)
+    E, counts, I, K = 3, [260, 40, 700], 192, 1024
+    M = sum(counts)
+    ac, as_ = _rand_mx(rng, (900,), K)
+    bc, bs = _rand_mx(rng, (E, 2 * I), K)
+    a_rows = rng.integers(0, 900, M).astype(np.int32)
+    offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    b_t = _mx_up(bc, bs)
+    hq = m.mxfp4_grouped_gemm(_mx_up(ac, as_), b_t, up(offsets), m_total=M, a_rows=up(a_rows),
+                              epilogue=m.EPI_SWIGLU_NVFP4, max_rows_per_expert_hint=256,
+                              b_packed=m.mxfp4_weight_repack(b_t))
+    torch.cuda.synchronize()
+    y1, absdot = MX.mx_grouped_gemm(ac, as_, bc, bs, offsets, a_rows=a_rows)
+    _, _, h64 = MX.mx_swiglu_quantize(y1)
+    check_requant_mx(down(hq.codes), down(hq.scales), h64, _swiglu_tol(y1, absdot), max_flip_frac=0.02,
+                     what="mx fused swiglu, large tile")
+
+
+def test_mx_dense_8192_sampled_rows():
+    # the dense M = N = K = 8192 GEMM in the launch the benchmark times (large
+    # tile, packed weights, bf16 out), checked on 24 sampled rows, every column
+    rng = np.random.default_rng(8192)
+    M = N = K = 8192
+    print("mx dense 8192^3 sampled rows", flush=True)
+    ac, as_ = _rand_mx(rng, (M,), K)
+    bc, bs = _rand_mx(rng, (1, N), K)
+    b_t = _mx_up(bc, bs)
+    offsets = np.array([0, M], np.int32)
+    y = m.mxfp4_grouped_gemm(_mx_up(ac, as_), b_t, up(offsets), m_total=M, epilogue=m.EPI_BF16,
+                             b_packed=m.mxfp4_weight_repack(b_t))
+    torch.cuda.synchronize()
+    rows = np.sort(rng.choice(M, 24, replace=False))
+    rows[0], rows[-1] = 0, M - 1
+    got = bf16_to_f32(y[torch.as_tensor(rows, device=y.device)])
+    y_ref, absdot = MX.mx_grouped_gemm(ac[rows], as_[rows], bc, bs, np.array([0, len(rows)], np.int32))
+    assert_gemm_close(got, y_ref, absdot, bf16_out=True, what="mx dense 8192^3, sampled rows")
 
 
 def test_mx_fused_swiglu_exact_accumulation():
