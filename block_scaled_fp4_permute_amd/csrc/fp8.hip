@@ -458,6 +458,204 @@ __global__ __launch_bounds__(256, 2) void k_fp8_gemm(const Fp8Params p, int n_ti
   }
 }
 
+// ---- large-M tile (from 256 rows per expert): 8 waves on 256 rows x 256
+// columns, both operands of a 128-value K step staged in LDS once per
+// workgroup; wave w = 4 wr + wc holds rows [128 wr, +128) and columns
+// [64 wc, +64), which lie in one 128-column weight block.  One stage (65 KB,
+// two double-buffered):
+//   A codes   16 row tiles x 2048 bytes: half h of lane (g, r) at
+//             1024 h + 256 g + 16 (r ^ (2 g + h)) (the XOR spreads the 8
+//             lanes that store one row's 128 bytes over distinct banks)
+//   A scales  256 floats (the rows' block scales of the step)
+//   B codes   16 column tiles x 2048 bytes, as in the packed tile
+// The weight block scale of a wave is one scalar per step, read from memory.
+constexpr int kFp8LRows = 256;
+constexpr int kFp8LThreads = 512;
+constexpr int kFp8LASc = 16 * 2048;
+constexpr int kFp8LB = kFp8LASc + kFp8LRows * 4;
+constexpr int kFp8LStage = kFp8LB + 16 * 2048;
+
+struct Fp8LRegs {
+  u32x4 c[4];
+  float s;
+};
+
+struct Fp8LSrc {
+  rsrc_t ra, rs;
+  uint32_t va[4];       // byte offsets of the thread's four A pieces at step 0
+  uint32_t vs;          // of its row's scale at step 0 (row t % 256)
+  uint32_t lda;         // LDS offset of its first A piece (the others 8 KB apart)
+  const uint8_t* b;     // expert's packed tiles
+  uint32_t ob[4];       // byte offsets of its four B pieces at step 0
+};
+
+__device__ __forceinline__ void fp8l_load_a(const Fp8LSrc& S, Fp8LRegs& R, int st) {
+  const uint32_t oa = static_cast<uint32_t>(st) * kFp8Block;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    R.c[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(S.ra, S.va[i] + oa, 0, 0));
+  R.s = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(S.rs, S.vs + 4u * st, 0, 0));
+}
+
+__device__ __forceinline__ void fp8l_load_b(const Fp8LSrc& S, Fp8LRegs& R, int st) {
+  const uint32_t ot = static_cast<uint32_t>(st) * kFp8Tile;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) R.c[i] = *reinterpret_cast<const u32x4*>(S.b + (S.ob[i] + ot));
+}
+
+__device__ __forceinline__ void fp8l_store_a(const Fp8LSrc& S, const Fp8LRegs& R, uint8_t* __restrict__ stage) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) *reinterpret_cast<u32x4*>(stage + S.lda + 8192 * i) = R.c[i];
+  if (threadIdx.x < kFp8LRows) reinterpret_cast<float*>(stage + kFp8LASc)[threadIdx.x] = R.s;
+}
+
+__device__ __forceinline__ void fp8l_store_b(const Fp8LRegs& R, uint8_t* __restrict__ stage) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    *reinterpret_cast<u32x4*>(stage + kFp8LB + 16 * (threadIdx.x + kFp8LThreads * i)) = R.c[i];
+}
+
+// row tiles [r0, r0 + 4) of the wave (H = r0 / 4): per 16 x 16 tile the
+// block's partial sum, scaled into the accumulator by sa[row] * sb
+template <int R0>
+__device__ __forceinline__ void fp8l_rows(const uint8_t* __restrict__ stage, int wr, const i32x8 (&bf)[4], float sb,
+                                          float4v (&acc)[8][4]) {
+  const int lane = threadIdx.x & 63;
+  const int lr = lane & 15, lg = lane >> 4;
+  const int a0 = 256 * lg + 16 * (lr ^ (2 * lg)), a1 = 1024 + 256 * lg + 16 * (lr ^ (2 * lg + 1));
+#pragma unroll
+  for (int r = R0; r < R0 + 4; ++r) {
+    const int rt = 8 * wr + r;
+    const u32x4 lo = *reinterpret_cast<const u32x4*>(stage + rt * 2048 + a0);
+    const u32x4 hi = *reinterpret_cast<const u32x4*>(stage + rt * 2048 + a1);
+    const i32x8 af = fp8_frag(lo, hi);
+    const float4v sab = *reinterpret_cast<const float4v*>(stage + kFp8LASc + 4 * (16 * rt + 4 * lg)) * sb;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float4v z = {0.f, 0.f, 0.f, 0.f};
+      const float4v part = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af, bf[j], z, kFp8FmtE4M3, kFp8FmtE4M3,
+                                                                            0, kE8M0One, 0, kE8M0One);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[r][j][i] = __builtin_fmaf(part[i], sab[i], acc[r][j][i]);
+    }
+  }
+}
+
+template <int EPI>
+__global__ __launch_bounds__(kFp8LThreads, 1) void k_fp8_gemm_l(const Fp8Params p, int n_tiles) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * kFp8LStage];
+  static_assert(fits_lds(sizeof(lds), 1), "FP8 large-M staging exceeds the LDS of a CU");
+  int e, m0, nt;
+  bool narrow;
+  const GemmParams map = fp8_map_params(p, n_tiles);
+  if (!find_task<16, false, 0>(map, e, m0, nt, narrow)) return;
+  const int t = threadIdx.x;
+  const int lane = t & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int wr = wave >> 2, wc = wave & 3;
+  const int lr = lane & 15;
+  const int row0 = min(max(p.offsets[e], 0), p.m_total);
+  const int Me = min(max(p.offsets[e + 1], 0), p.m_total) - row0;
+  // inside an expert, groups of 4 row chunks run column tile by column tile
+  // (the workgroups side by side on an XCD share A chunks and weight tiles)
+  {
+    const int nc = (Me + kFp8LRows - 1) / kFp8LRows;
+    const int u = (m0 / kFp8LRows) * n_tiles + nt;
+    const int grp = (m0 / kFp8LRows) / 4;
+    const int gq = min(4, nc - 4 * grp);
+    const int w = u - 4 * grp * n_tiles;
+    m0 = (4 * grp + w % gq) * kFp8LRows;
+    nt = w / gq;
+  }
+  const int rows = min(kFp8LRows, Me - m0);
+  const int N = p.N, K = p.K;
+  const int nsteps = K / kFp8Block;
+  const int ntr = (N + 15) / 16;
+  const int nsb = (N + kFp8Block - 1) / kFp8Block;
+
+  Fp8LSrc S;
+  {
+    const uint32_t krow = static_cast<uint32_t>(K), srow = static_cast<uint32_t>(K / kFp8Block);
+    S.ra = make_rsrc(p.a_codes, static_cast<uint32_t>(p.a_rows_total) * krow);
+    S.rs = make_rsrc(p.a_scales, static_cast<uint32_t>(p.a_rows_total) * srow * 4u);
+    const int q = t & 7;              // 16-byte piece of the row's 128 bytes: half q & 1 of lane group q >> 1
+    const int g = q >> 1, h = q & 1;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int ar = (t >> 3) + 64 * i;
+      int arow = row0 + m0 + (ar < rows ? ar : 0);
+      if (p.a_rows) arow = p.a_rows[arow];
+      arow = (arow >= 0 && arow < p.a_rows_total) ? arow : 0;
+      S.va[i] = static_cast<uint32_t>(arow) * krow + 16u * q;
+    }
+    S.lda = ((t >> 3) >> 4) * 2048 + 1024 * h + 256 * g + 16 * (((t >> 3) & 15) ^ (2 * g + h));
+    {
+      const int ar = t & (kFp8LRows - 1);
+      int arow = row0 + m0 + (ar < rows ? ar : 0);
+      if (p.a_rows) arow = p.a_rows[arow];
+      arow = (arow >= 0 && arow < p.a_rows_total) ? arow : 0;
+      S.vs = static_cast<uint32_t>(arow) * srow * 4u;
+    }
+    S.b = p.b_packed + static_cast<size_t>(e) * ntr * nsteps * kFp8Tile;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int pc = t + kFp8LThreads * i;    // 16-byte piece of the 16 x 2048 code bytes
+      const uint32_t rt = static_cast<uint32_t>(min(nt * 16 + (pc >> 7), ntr - 1));
+      S.ob[i] = rt * static_cast<uint32_t>(nsteps) * kFp8Tile + 16u * (pc & 127);
+    }
+  }
+  const int wcol = nt * 256 + 64 * wc;
+  const float* bsc = p.b_scales + (static_cast<size_t>(e) * nsb + min(wcol, N - 1) / kFp8Block) * nsteps;
+
+  float4v acc[8][4];
+#pragma unroll
+  for (int r = 0; r < 8; ++r)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[r][j] = float4v{0.f, 0.f, 0.f, 0.f};
+
+  Fp8LRegs R;
+  fp8l_load_a(S, R, 0);
+  fp8l_store_a(S, R, lds);
+  fp8l_load_b(S, R, 0);
+  fp8l_store_b(R, lds);
+  __syncthreads();
+  // step st from stage st % 2; step st + 1's A pieces in flight behind the
+  // first four row tiles, its B pieces behind the last four; the last step
+  // re-stages itself into the idle stage (no branches)
+  for (int st = 0; st < nsteps; ++st) {
+    const uint8_t* cur = lds + (st & 1) * kFp8LStage;
+    uint8_t* nxt = lds + ((st + 1) & 1) * kFp8LStage;
+    const int sn = min(st + 1, nsteps - 1);
+    const float sb = bsc[st];
+    i32x8 bf[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint8_t* tb = cur + kFp8LB + (4 * wc + j) * 2048 + 16 * lane;
+      bf[j] = fp8_frag(*reinterpret_cast<const u32x4*>(tb), *reinterpret_cast<const u32x4*>(tb + 1024));
+    }
+    fp8l_load_a(S, R, sn);
+    fp8l_rows<0>(cur, wr, bf, sb, acc);
+    fp8l_store_a(S, R, nxt);
+    fp8l_load_b(S, R, sn);
+    fp8l_rows<4>(cur, wr, bf, sb, acc);
+    fp8l_store_b(R, nxt);
+    __syncthreads();
+  }
+
+  const int prow0 = row0 + m0;
+#pragma unroll
+  for (int r = 0; r < 8; ++r) {
+    const int rt = 8 * wr + r;
+    const int left = rows - 16 * rt;
+    if (left <= 0) continue;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int col = wcol + 16 * j + lr;
+      fp8_store_tile<EPI>(p, acc[r][j], prow0 + 16 * rt, left, col, col < N);
+    }
+  }
+}
+
 hipError_t launch_fp8_gemm(const Fp8Params& p, int epilogue, int64_t m_total, int hint, hipStream_t stream) {
   constexpr int BN = 256;
   const int n_tiles = (p.N + BN - 1) / BN;
@@ -465,6 +663,15 @@ hipError_t launch_fp8_gemm(const Fp8Params& p, int epilogue, int64_t m_total, in
   if (blocks >= (int64_t(1) << 31)) return hipErrorInvalidConfiguration;
   const int64_t rows_per_expert = hint > 0 ? hint : m_total / p.E;
   const bool nt = rows_per_expert < 64;
+  if (rows_per_expert >= kFp8LRows) {
+    const int64_t lblocks = ((((m_total + kFp8LRows - 1) / kFp8LRows + p.E) * n_tiles) + 7) / 8 * 8;
+    const dim3 lgrid(static_cast<unsigned>(lblocks));
+    if (epilogue == EPI_F32)
+      hipLaunchKernelGGL((k_fp8_gemm_l<EPI_F32>), lgrid, dim3(kFp8LThreads), 0, stream, p, n_tiles);
+    else
+      hipLaunchKernelGGL((k_fp8_gemm_l<EPI_BF16>), lgrid, dim3(kFp8LThreads), 0, stream, p, n_tiles);
+    return hipGetLastError();
+  }
   const dim3 grid(static_cast<unsigned>(blocks));
   if (epilogue == EPI_F32) {
     if (nt) hipLaunchKernelGGL((k_fp8_gemm<EPI_F32, true>), grid, dim3(256), 0, stream, p, n_tiles);

@@ -142,21 +142,42 @@ def _fp8_operands(cfg_stream, E, N, K, rows_a):
     return ac, as_, bc, bs
 
 
+# hint (or the average) of at least 256 rows per expert: the 256 x 256 tile
+# with both operands staged in LDS
+LARGE_CASES = [
+    # E, counts, N, K, rows_a, hint
+    (3, [300, 0, 517], 400, 384, 400, 256),          # partial column tile past one weight block, odd steps
+    (1, [600], 512, 2048, 600, 0),                   # by the average; a partial row chunk
+    (5, [256, 1, 1000, 0, 255], 256, 128, 700, 300),  # one K step; 1-row and 255-row experts
+]
+
+
 @pytest.mark.parametrize("case", range(len(CASES)))
 @pytest.mark.parametrize("gather", [False, True])
 @pytest.mark.parametrize("epi", ["f32", "bf16"])
 def test_fp8_gemm_random(case, gather, epi):
-    E, counts, N, K, rows_a, hint = CASES[case]
-    rng = np.random.default_rng(300 + case)
+    _run_fp8_case(CASES[case], 300 + case, 10 + 2 * case, gather, epi, f"case {case}")
+
+
+@pytest.mark.parametrize("case", range(len(LARGE_CASES)))
+@pytest.mark.parametrize("gather", [False, True])
+@pytest.mark.parametrize("epi", ["f32", "bf16"])
+def test_fp8_gemm_large_tile(case, gather, epi):
+    _run_fp8_case(LARGE_CASES[case], 400 + case, 70 + 2 * case, gather, epi, f"large case {case}")
+
+
+def _run_fp8_case(spec, seed, stream, gather, epi, name):
+    E, counts, N, K, rows_a, hint = spec
+    rng = np.random.default_rng(seed)
     if counts is None:
         counts = rng.integers(0, 40, E) * (rng.random(E) < 0.7)
         counts[rng.choice(E, 4, replace=False)] = [150, 200, 65, 17]
     counts = np.asarray(counts, np.int64)
     M = int(counts.sum())
-    print(f"fp8 gemm case {case} gather={gather} epi={epi} E={E} M={M} N={N} K={K}", flush=True)
+    print(f"fp8 gemm {name} gather={gather} epi={epi} E={E} M={M} N={N} K={K} hint={hint}", flush=True)
     if not gather:
         rows_a = max(M, 1)
-    ac, as_, bc, bs = _fp8_operands(10 + 2 * case, E, N, K, rows_a)
+    ac, as_, bc, bs = _fp8_operands(stream, E, N, K, rows_a)
     a_rows = rng.integers(0, rows_a, M).astype(np.int32) if gather else None
     offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
     y = m.fp8_grouped_gemm(_a(ac, as_), m.fp8_weight_repack(up(bc)), up(bs), up(offsets), N=N, m_total=M,
@@ -165,17 +186,17 @@ def test_fp8_gemm_random(case, gather, epi):
     torch.cuda.synchronize()
     y_ref, absdot = F8.fp8_grouped_gemm(ac, as_, bc, bs, offsets, a_rows=a_rows)
     got = down(y) if epi == "f32" else bf16_to_f32(y)
-    assert_gemm_close(got, y_ref, absdot, bf16_out=epi == "bf16", what=f"fp8 case {case} {epi}")
+    assert_gemm_close(got, y_ref, absdot, bf16_out=epi == "bf16", what=f"fp8 {name} {epi}")
 
 
-@pytest.mark.parametrize("K", [128, 1024, 4096])
-def test_fp8_gemm_exact_sums_bit_exact(K):
+@pytest.mark.parametrize("K,large", [(128, False), (1024, False), (4096, False), (128, True), (4096, True)])
+def test_fp8_gemm_exact_sums_bit_exact(K, large):
     # E4M3 values in [1, 3.75] (exponent fields 7 and 8) and block scales 1/2 or
     # 1: every scaled product is a multiple of 2^-8 of magnitude at most 14.07,
     # so any partial sum of at most 4096 of them is below 2^24 units of 2^-8 and
     # exact in float32 in any order: the GPU must equal the oracle bit for bit
     c = workloads.CONFIGS[0]
-    E, counts, N = 2, [37, 70], 272
+    E, counts, N = 2, ([300, 520] if large else [37, 70]), 272
     M = sum(counts)
     ac = workloads.fp8_codes(c, 40, (M, K), 7, 9)
     bc = workloads.fp8_codes(c, 41, (E, N, K), 7, 9)
@@ -189,14 +210,16 @@ def test_fp8_gemm_exact_sums_bit_exact(K):
     assert np.array_equal(down(y), y_ref)
 
 
-def test_fp8_gemm_single_block_term():
+@pytest.mark.parametrize("large", [False, True])
+def test_fp8_gemm_single_block_term(large):
     # one nonzero 128-block of K at a time, exact-sum codes, arbitrary float32
     # scales: each output is one block term part * sa * sb, which the GPU rounds
     # twice (sa * sb, then the product) - within two float32 ulps of the
     # oracle's exact term; a scale taken from the wrong row, tile or block is
-    # far outside that
+    # far outside that (large: 300 rows through the 256 x 256 tile, whose A
+    # rows and scales sit in LDS)
     c = workloads.CONFIGS[0]
-    M, N, K = 80, 272, 512
+    M, N, K = (300, 272, 512) if large else (80, 272, 512)
     for blk in range(K // 128):
         ac = np.zeros((M, K), np.uint8)
         bc = np.zeros((1, N, K), np.uint8)
@@ -215,6 +238,27 @@ def test_fp8_gemm_single_block_term():
             raise AssertionError(f"block {blk}: {int(bad.sum())} of {bad.size} outside two ulps; rows "
                                  f"{np.unique(np.argwhere(bad)[:, 0])[:20]} cols {np.unique(np.argwhere(bad)[:, 1])[:20]}; "
                                  f"first {i}: gpu {got[i]!r} ref {float(y_ref[i])!r}")
+
+
+def test_fp8_dense_8192_sampled_rows():
+    # the dense M = N = K = 8192 GEMM in the launch the benchmark times (large
+    # tile, bf16 out), checked on 24 sampled rows, every column
+    c = workloads.CONFIGS[0]
+    M = N = K = 8192
+    print("fp8 dense 8192^3 sampled rows", flush=True)
+    ac = workloads.fp8_codes(c, 80, (M, K))
+    as_ = workloads.fp8_scales(c, 80, (M, K // 128))
+    bc = workloads.fp8_codes(c, 81, (1, N, K))
+    bs = workloads.fp8_scales(c, 81, (1, N // 128, K // 128))
+    offsets = np.array([0, M], np.int32)
+    y = m.fp8_grouped_gemm(_a(ac, as_), m.fp8_weight_repack(up(bc)), up(bs), up(offsets), N=N, m_total=M,
+                           epilogue=m.EPI_BF16)
+    torch.cuda.synchronize()
+    rows = np.sort(np.random.default_rng(81).choice(M, 24, replace=False))
+    rows[0], rows[-1] = 0, M - 1
+    got = bf16_to_f32(y[torch.as_tensor(rows, device=y.device)])
+    y_ref, absdot = F8.fp8_grouped_gemm(ac[rows], as_[rows], bc, bs, np.array([0, len(rows)], np.int32))
+    assert_gemm_close(got, y_ref, absdot, bf16_out=True, what="fp8 dense 8192^3, sampled rows")
 
 
 def test_fp8_whole_decode_gate_up_and_down():
