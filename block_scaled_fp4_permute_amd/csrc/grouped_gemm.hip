@@ -216,6 +216,9 @@ hipError_t launch_grouped_gemm(const GemmParams& prm, int epilogue, int64_t m_to
     return large ? launch_dn<8>(prm, epilogue, cached, m_total, stream)
                  : launch_dn<6>(prm, epilogue, cached, m_total, stream);
   }
+  // from 256 rows per expert (packed weights, K a multiple of the step): the
+  // 256 x 256 tile with both operands staged in LDS
+  if (gemm_large_fits(prm, rows_per_expert)) return launch_gemm_large(prm, epilogue, m_total, stream);
   const int mode = !prm.b_packed ? kRowB : rows_per_expert >= CACHE_ROWS ? kPackedCached : kPackedNT;
   switch (mode) {
     case kRowB:

@@ -55,6 +55,8 @@ size_t packed_weight_bytes(int E, int N, int K);
 hipError_t launch_repack(const uint8_t* codes, const uint8_t* scales, int E, int N, int K, uint8_t* packed,
                          hipStream_t stream);
 hipError_t launch_grouped_gemm(const GemmParams& prm, int epilogue, int64_t m_total, int hint, hipStream_t stream);
+bool gemm_large_fits(const GemmParams& prm, int64_t rows_per_expert);
+hipError_t launch_gemm_large(const GemmParams& prm, int epilogue, int64_t m_total, hipStream_t stream);
 hipError_t launch_mx_quantize(const void* x, int dtype, int64_t rows, int64_t cols, uint8_t* codes,
                               uint8_t* scales, hipStream_t stream);
 hipError_t launch_mx_gemm(const GemmParams& prm, int epilogue, int64_t m_total, int hint, hipStream_t stream);

@@ -139,11 +139,13 @@ def test_gemm_many_experts_task_map(hint, packed):
                   what="many experts swiglu")
 
 
-@pytest.mark.parametrize("hint", [1, 4096])
+@pytest.mark.parametrize("hint", [1, 200, 4096])
 @pytest.mark.parametrize("packed", [False, True])
 def test_gemm_decode_and_large_tile_shapes(hint, packed):
-    # the rows-per-expert hint picks the decode (64-row) or the large-M (128-row,
-    # 8-wave) tile; both must meet the oracle, with F32 and fused SwiGLU epilogues
+    # the rows-per-expert hint picks the decode (64-row) tile, the 128-row
+    # 8-wave tile (128..255 rows, or row-major weights) or, with packed weights
+    # from 256 rows, the 256 x 256 tile with both operands staged in LDS; all
+    # must meet the oracle, with F32 and fused SwiGLU epilogues
     rng = np.random.default_rng(hint + int(packed))
     E, counts, N, K = 3, [150, 300, 7], 512, 1024
     M = sum(counts)
@@ -165,6 +167,101 @@ def test_gemm_decode_and_large_tile_shapes(hint, packed):
     torch.cuda.synchronize()
     check_requant(down(hq.codes), down(hq.scales), h64, g_h, _swiglu_tol(y_ref, absdot), max_flip_frac=0.02,
                   what=f"fused swiglu hint {hint}")
+
+
+# packed weights, K a multiple of 256, hint (or average) >= 256: the 256 x 256
+# tile (both operands in LDS, A decoded once per workgroup a quarter step at a time)
+LARGE_CASES = [
+    # E, counts, N, K, rows_a, hint
+    (3, [300, 0, 517], 320, 512, 400, 256),          # a partial column tile, an empty expert
+    (1, [600], 512, 2048, 600, 0),                   # by the average; a partial row chunk
+    (5, [256, 1, 1000, 0, 255], 256, 768, 700, 300),  # 1-row and 255-row experts, 4 chunks in one group
+]
+
+
+@pytest.mark.parametrize("case", range(len(LARGE_CASES)))
+@pytest.mark.parametrize("gather", [False, True])
+@pytest.mark.parametrize("epi", ["f32", "bf16"])
+def test_gemm_large_tile(case, gather, epi):
+    E, counts, N, K, rows_a, hint = LARGE_CASES[case]
+    print(f"gemm large case {case} gather={gather} epi={epi} E={E} N={N} K={K}", flush=True)
+    rng = np.random.default_rng(500 + case)
+    M = int(np.sum(counts))
+    if not gather:
+        rows_a = M                     # row p of the GEMM reads A row p
+    a_codes, a_scales = _rand_nvfp4(rng, (rows_a,), K)
+    b_codes, b_scales = _rand_nvfp4(rng, (E, N), K)
+    a_g = np.float32(0.0123)
+    b_g = rng.uniform(0.001, 0.01, E).astype(np.float32)
+    a_rows = rng.integers(0, rows_a, M).astype(np.int32) if gather else None
+    y, offsets = _run_gemm(a_codes, a_scales, a_g, b_codes, b_scales, b_g, counts, a_rows, hint=hint, packed=True,
+                           epilogue=m.EPI_F32 if epi == "f32" else m.EPI_BF16)
+    y_ref, absdot = OM.grouped_gemm(a_codes, a_scales, a_g, b_codes, b_scales, b_g, offsets, a_rows=a_rows)
+    got = down(y)[:M] if epi == "f32" else bf16_to_f32(y)[:M]
+    assert_gemm_close(got, y_ref, absdot, bf16_out=epi == "bf16", what=f"large case {case} {epi}")
+
+
+def test_gemm_large_tile_fused_swiglu_and_combine():
+    # SwiGLU + NVFP4 requant with I = 192 (the second 128-column h tile half
+    # empty), then the float32 scatter-add combine epilogue, both on the
+    # 256 x 256 tile
+    rng = np.random.default_rng(41)
+    E, counts, I, K = 3, [260, 40, 700], 192, 1024
+    M = sum(counts)
+    a_codes, a_scales = _rand_nvfp4(rng, (900,), K)
+    b_codes, b_scales = _rand_nvfp4(rng, (E, 2 * I), K)
+    b_g = rng.uniform(0.001, 0.01, E).astype(np.float32)
+    a_rows = rng.integers(0, 900, M).astype(np.int32)
+    offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    y_ref, absdot = OM.grouped_gemm(a_codes, a_scales, 0.02, b_codes, b_scales, b_g, offsets, a_rows=a_rows)
+    h64 = OM.swiglu(y_ref)
+    g_h = np.float32(np.abs(h64.astype(np.float32)).max() / np.float32(2688))
+    a = m.NVFP4Tensor(up(a_codes), up(a_scales), up(np.array([0.02], np.float32)))
+    bc, bs = up(b_codes), up(b_scales)
+    hq = m.nvfp4_grouped_gemm(a, bc, bs, up(b_g), up(offsets), m_total=M, a_rows=up(a_rows),
+                              epilogue=m.EPI_SWIGLU_NVFP4, out_g=up(np.array([g_h], np.float32)),
+                              max_rows_per_expert_hint=256, b_packed=m.nvfp4_weight_repack(bc, bs))
+    torch.cuda.synchronize()
+    check_requant(down(hq.codes), down(hq.scales), h64, g_h, _swiglu_tol(y_ref, absdot), max_flip_frac=0.02,
+                  what="large-tile fused swiglu")
+    # combine: rows scattered to 333 tokens with weights, N = 2I columns
+    tok = rng.integers(0, 333, M).astype(np.int32)
+    wt = rng.uniform(0.1, 1.0, M).astype(np.float32)
+    acc = torch.zeros((333, 2 * I), dtype=torch.float32, device=DEV)
+    m.nvfp4_grouped_gemm(a, bc, bs, up(b_g), up(offsets), m_total=M, a_rows=up(a_rows), epilogue=m.EPI_COMBINE_F32,
+                         out=acc, out_rows=333, row_token=up(tok), row_weight=up(wt), max_rows_per_expert_hint=256,
+                         b_packed=m.nvfp4_weight_repack(bc, bs))
+    torch.cuda.synchronize()
+    ref = np.zeros((333, 2 * I))
+    tol = np.zeros((333, 2 * I))
+    np.add.at(ref, tok, wt.astype(np.float64)[:, None] * y_ref)
+    np.add.at(tol, tok, wt.astype(np.float64)[:, None] * (1e-3 * absdot + 1e-6))
+    got = down(acc).astype(np.float64)
+    # float32 atomics add the rows in any order: a few ulps of the running sums
+    tol += 8 * 2.0 ** -24 * np.abs(ref) + 1e-30
+    assert np.all(np.abs(got - ref) <= tol), "large-tile combine epilogue"
+
+
+def test_gemm_dense_8192_sampled_rows():
+    # the dense M = N = K = 8192 GEMM in the launch the benchmark times (256 x
+    # 256 tile, packed weights, bf16 out), checked on 24 sampled rows
+    rng = np.random.default_rng(8193)
+    M = N = K = 8192
+    print("nvfp4 dense 8192^3 sampled rows", flush=True)
+    a_codes, a_scales = _rand_nvfp4(rng, (M,), K)
+    b_codes, b_scales = _rand_nvfp4(rng, (1, N), K)
+    a = m.NVFP4Tensor(up(a_codes), up(a_scales), up(np.array([0.01], np.float32)))
+    bc, bs = up(b_codes), up(b_scales)
+    offsets = np.array([0, M], np.int32)
+    y = m.nvfp4_grouped_gemm(a, bc, bs, up(np.array([0.02], np.float32)), up(offsets), m_total=M,
+                             epilogue=m.EPI_BF16, b_packed=m.nvfp4_weight_repack(bc, bs))
+    torch.cuda.synchronize()
+    rows = np.sort(rng.choice(M, 24, replace=False))
+    rows[0], rows[-1] = 0, M - 1
+    got = bf16_to_f32(y[torch.as_tensor(rows, device=y.device)])
+    y_ref, absdot = OM.grouped_gemm(a_codes[rows], a_scales[rows], 0.01, b_codes, b_scales,
+                                    np.array([0.02], np.float32), np.array([0, len(rows)], np.int32))
+    assert_gemm_close(got, y_ref, absdot, bf16_out=True, what="nvfp4 dense 8192^3, sampled rows")
 
 
 @pytest.mark.parametrize("epilogue", ["f32", "swiglu"])
@@ -228,31 +325,35 @@ def test_gemm_bf16_epilogue_and_untouched_tail_rows():
     assert np.all(got[51:] == 7.0)
 
 
-@pytest.mark.parametrize("K", [32, 256, 4096, 6144])
-@pytest.mark.parametrize("packed", [False, True])
-def test_gemm_constant_scales_bit_exact(K, packed):
+@pytest.mark.parametrize("K,packed,large", [(32, False, False), (256, False, False), (4096, False, False),
+                                             (6144, False, False), (32, True, False), (256, True, False),
+                                             (4096, True, False), (6144, True, False), (256, True, True),
+                                             (6144, True, True)])
+def test_gemm_constant_scales_bit_exact(K, packed, large):
     # constant block scales and unit per-tensor scales make every FP32 partial
-    # sum exact, so the GPU must reproduce the oracle bit for bit
-    rng = np.random.default_rng(K)
-    E, counts, N = 2, [37, 70], 80
+    # sum exact, so the GPU must reproduce the oracle bit for bit (large: the
+    # 256 x 256 tile)
+    rng = np.random.default_rng(K + large)
+    E, counts, N = (2, [300, 520], 272) if large else (2, [37, 70], 80)
     M = sum(counts)
     a_codes = rng.integers(0, 256, (M, K // 2), dtype=np.uint8)
     b_codes = rng.integers(0, 256, (E, N, K // 2), dtype=np.uint8)
     a_scales = np.full((M, K // 16), 0x3A, np.uint8)          # 1.25
     b_scales = np.full((E, N, K // 16), 0x30, np.uint8)       # 0.5
-    y, offsets = _run_gemm(a_codes, a_scales, 1.0, b_codes, b_scales, np.ones(E, np.float32), counts, packed=packed)
+    y, offsets = _run_gemm(a_codes, a_scales, 1.0, b_codes, b_scales, np.ones(E, np.float32), counts, packed=packed,
+                           hint=256 if large else 0)
     y_ref, _ = OM.grouped_gemm(a_codes, a_scales, 1.0, b_codes, b_scales, np.ones(E, np.float32), offsets)
     assert np.array_equal(down(y), y_ref)
 
 
 @pytest.mark.parametrize("sa,sb", [(0x03, 0x05), (0x01, 0x7E), (0x07, 0x08), (0x00, 0x40)])
-@pytest.mark.parametrize("packed", [False, True])
-def test_gemm_subnormal_and_extreme_scales_bit_exact(sa, sb, packed):
+@pytest.mark.parametrize("packed,large", [(False, False), (True, False), (True, True)])
+def test_gemm_subnormal_and_extreme_scales_bit_exact(sa, sb, packed, large):
     # E4M3 subnormal block scales (codes 1..7) pass through FP16 subnormals in
     # the decode; with one scale per operand and unit per-tensor scales the
     # float32 result is exact in any summation order, so it must match exactly
     rng = np.random.default_rng(sa * 256 + sb)
-    E, counts, N, K = 2, [21, 50], 48, 1024
+    E, counts, N, K = (2, [300, 280], 48, 1024) if large else (2, [21, 50], 48, 1024)
     M = sum(counts)
     a_codes = rng.integers(0, 256, (M, K // 2), dtype=np.uint8)
     b_codes = rng.integers(0, 256, (E, N, K // 2), dtype=np.uint8)
