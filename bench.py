@@ -57,8 +57,9 @@ def parse():
                          "(recorded once per weight copy; measured slower on MI355X: 0.355 against 0.329 ms)")
     ap.add_argument("--swiglu", choices=["fused", "separate"], default="fused",
                     help="SwiGLU + requant in the gate_up epilogue, or a separate call")
-    ap.add_argument("--combine", choices=["gather", "atomic"], default="gather",
-                    help="bf16 down output + gather combine, or float32 atomic scatter-add epilogue")
+    ap.add_argument("--combine", choices=["gather", "atomic", "fused"], default="gather",
+                    help="bf16 down output + gather combine, float32 atomic scatter-add epilogue, or the combine "
+                         "fused into the expert-FFN call (one-launch regime: inside the persistent launch)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="time budget of the CPU-oracle sample")
     ap.add_argument("--oracle-only", action="store_true",
@@ -553,9 +554,11 @@ def main():
     torch.cuda.synchronize()
 
     # routing and the quantisation of x share launches (one call): one stage
+    fused_combine = one_call and layer.combine == "fused"
     if one_call:
-        names = ["route_permute+quantize_x", None,
-                 "expert_ffn_one_launch" if one_launch else "expert_ffn_two_launches", None, "combine"]
+        ffn_name = "expert_ffn_one_launch" if one_launch else "expert_ffn_two_launches"
+        names = ["route_permute+quantize_x", None, ffn_name + ("+combine" if fused_combine else ""), None,
+                 None if fused_combine else "combine"]
     else:
         names = ["route_permute+quantize_x", None, "gate_up_swiglu",
                  "down" if args.combine == "gather" else "down_scatter_add",
@@ -624,6 +627,10 @@ def main():
     gu_alg = touched * gu_bytes_e + T * H * 9 // 16 + T * k * I * 9 // 16
     dn_alg = touched * dn_bytes_e + T * k * I * 9 // 16 + T * k * H * 2
     alg = gu_alg + dn_alg if one_call else gu_alg
+    # with the combine fused into the call: + the bf16 rows read back and the
+    # bf16 output written (the combine's own algorithmic bytes)
+    if fused_combine:
+        alg += T * k * H * 2 + T * H * 2
     achieved = alg / (gu_ms * 1e-3) / 1e9
     # from 128 rows per expert the GEMMs run the large-M tile and the FFN is
     # bound by the matrix cores, not HBM: its roofline is the dense FP16 MFMA
@@ -632,7 +639,8 @@ def main():
     ffn_flops = 2.0 * T * k * 3 * I * H if one_call else 2.0 * T * k * 2 * I * H
     ffn_tflops = ffn_flops / (gu_ms * 1e-3) / 1e12
     wl_name = f"{'decode' if T <= 2048 else 'prefill'}_moe_T{T}_H{H}_I{I}_E{E}_top{k}_{cfg.routing}"
-    tkey = "expert_ffn_one_launch" if one_launch else "expert_ffn_two_launches" if one_call else "gate_up_swiglu"
+    tkey = ("expert_ffn_one_launch" + ("_fused_combine" if fused_combine else "") if one_launch
+            else "expert_ffn_two_launches" if one_call else "gate_up_swiglu")
     traffic = measured_traffic(tkey, wl_name) if args.swiglu == "fused" else None
 
     res = {
@@ -668,7 +676,8 @@ def main():
                       "frac_fp8_peak": round(ffn_tflops / MFMA_FP8_PEAK_TFLOPS, 4), "traffic": None,
                       "flops_per_launch": ffn_flops, "avg_launch_ms": round(gu_ms, 5),
                       "hbm_gbs": round(achieved, 2)} if mfma_bound else
-                     {"kernel": ("k_moe_ffn: gate_up + SwiGLU/requant + down grouped GEMMs, one persistent launch"
+                     {"kernel": ("k_moe_ffn: gate_up + SwiGLU/requant + down grouped GEMMs"
+                                 + (" + weighted top-k combine" if fused_combine else "") + ", one persistent launch"
                                  if one_launch else
                                  "moe_expert_ffn: gate_up + SwiGLU/requant and down grouped GEMMs, two launches"
                                  if one_call else "nvfp4 grouped GEMM gate_up + SwiGLU/requant epilogue"),

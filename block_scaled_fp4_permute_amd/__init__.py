@@ -44,6 +44,8 @@ class FfnArgs(ctypes.Structure):
         ("w_dn_packed", ctypes.c_void_p), ("g_dn", ctypes.c_void_p), ("g_h", ctypes.c_void_p),
         ("h_codes", ctypes.c_void_p), ("h_scales", ctypes.c_void_p), ("y", ctypes.c_void_p),
         ("max_rows_per_expert_hint", ctypes.c_int32),
+        ("out", ctypes.c_void_p), ("perm_of_assignment", ctypes.c_void_p), ("topk_w", ctypes.c_void_p),
+        ("T", ctypes.c_int32), ("k", ctypes.c_int32),
     ]
 
 
@@ -402,9 +404,13 @@ def moe_expert_ffn_workspace(E: int, m_total: int, H: int, I: int, device):
 
 def moe_expert_ffn(xq: NVFP4Tensor, perm_src_token, offsets, w_gu_packed, g_gu, w_dn_packed, g_dn, g_h, *, H: int,
                    I: int, m_total: int, h: NVFP4Tensor | None = None, y=None, workspace=None,
-                   max_rows_per_expert_hint: int = 0, stream=None):
+                   max_rows_per_expert_hint: int = 0, perm_of_assignment=None, topk_w=None, k: int = 0, out=None,
+                   stream=None):
     """gate_up + SwiGLU/requant + down for all experts (see include/nvfp4moe.h):
-    returns (h NVFP4Tensor [m_total, I], y bf16 [m_total, H])."""
+    returns (h NVFP4Tensor [m_total, I], y bf16 [m_total, H]); with
+    perm_of_assignment, topk_w ([T, k]) and k also the weighted top-k combine
+    out bf16 [T, H] (fused into the launch in the one-launch regime), returned
+    as a third element."""
     import torch
     E = offsets.numel() - 1
     dev = offsets.device
@@ -435,6 +441,20 @@ def moe_expert_ffn(xq: NVFP4Tensor, perm_src_token, offsets, w_gu_packed, g_gu, 
     _need(y, torch.bfloat16, "y")
     if tuple(y.shape) != (m_total, H):
         raise ValueError("y must be bf16 [m_total, H]")
+    T = 0
+    if perm_of_assignment is not None:
+        if topk_w is None or k <= 0 or m_total % k:
+            raise ValueError("the combine needs topk_w and k > 0 dividing m_total")
+        T = m_total // k
+        _need(perm_of_assignment, torch.int32, "perm_of_assignment")
+        _need(topk_w, torch.float32, "topk_w")
+        if perm_of_assignment.numel() < m_total or topk_w.numel() < m_total:
+            raise ValueError("perm_of_assignment and topk_w need T * k values")
+        if out is None:
+            out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+        _need(out, torch.bfloat16, "out")
+        if tuple(out.shape) != (T, H):
+            raise ValueError("out must be bf16 [T, H]")
     if workspace is None:
         workspace = moe_expert_ffn_workspace(E, m_total, H, I, dev)
     args = FfnArgs(x_codes=xq.codes.data_ptr(), x_scales=xq.scales.data_ptr(), x_g=xq.g.data_ptr(),
@@ -442,8 +462,13 @@ def moe_expert_ffn(xq: NVFP4Tensor, perm_src_token, offsets, w_gu_packed, g_gu, 
                    E=E, H=H, I=I, m_total=m_total, w_gu_packed=w_gu_packed.data_ptr(), g_gu=g_gu.data_ptr(),
                    w_dn_packed=w_dn_packed.data_ptr(), g_dn=g_dn.data_ptr(), g_h=g_h.data_ptr(),
                    h_codes=h.codes.data_ptr(), h_scales=h.scales.data_ptr(), y=y.data_ptr(),
-                   max_rows_per_expert_hint=max_rows_per_expert_hint)
+                   max_rows_per_expert_hint=max_rows_per_expert_hint,
+                   out=out.data_ptr() if T else None,
+                   perm_of_assignment=perm_of_assignment.data_ptr() if T else None,
+                   topk_w=topk_w.data_ptr() if T else None, T=T, k=k if T else 0)
     _check(lib().moe_expert_ffn(ctypes.byref(args), workspace.data_ptr(), workspace.numel(), _stream(stream)))
+    if T:
+        return NVFP4Tensor(h.codes, h.scales, g_h), y, out
     return NVFP4Tensor(h.codes, h.scales, g_h), y
 
 

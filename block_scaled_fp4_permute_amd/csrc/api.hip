@@ -324,6 +324,16 @@ int moe_expert_ffn(const nvfp4moe_ffn_args* a, void* workspace, size_t workspace
   if (static_cast<int64_t>(a->E) * a->H >= (int64_t(1) << 31))
     return fail(NVFP4MOE_ERR_UNSUPPORTED, "moe_expert_ffn: E*H >= 2^31");
   if (a->E > 4096) return fail(NVFP4MOE_ERR_UNSUPPORTED, "moe_expert_ffn: E=%d > 4096", a->E);
+  if (a->out) {
+    if (!a->perm_of_assignment || !a->topk_w)
+      return fail(NVFP4MOE_ERR_INVALID, "moe_expert_ffn: out needs perm_of_assignment and topk_w");
+    if (a->T <= 0 || a->k <= 0 || static_cast<int64_t>(a->T) * a->k != a->m_total)
+      return fail(NVFP4MOE_ERR_INVALID, "moe_expert_ffn: combine needs T, k > 0 with T * k == m_total");
+    if (!aligned(a->out, 16) || !aligned(a->perm_of_assignment, 4) || !aligned(a->topk_w, 4))
+      return fail(NVFP4MOE_ERR_INVALID, "moe_expert_ffn: misaligned combine pointer");
+    if (prod_ge(a->m_total, int64_t(a->H) * 2, int64_t(1) << 31))
+      return fail(NVFP4MOE_ERR_UNSUPPORTED, "moe_expert_ffn: the fused combine needs m_total * H * 2 < 2^31");
+  }
   const size_t need = nvfp4::moe_ffn_ws_bytes(a->E, a->m_total, a->H, a->I);
   if (!workspace || workspace_bytes < need)
     return fail(NVFP4MOE_ERR_WORKSPACE, "moe_expert_ffn: workspace %zu < %zu bytes", workspace_bytes, need);
@@ -363,10 +373,14 @@ int moe_expert_ffn(const nvfp4moe_ffn_args* a, void* workspace, size_t workspace
   if (rows_per_expert < kFfnMinRows || rows_per_expert >= kFfnLargeRows) {
     hipError_t err = nvfp4::launch_grouped_gemm(gu, nvfp4::EPI_SWIGLU, a->m_total, a->max_rows_per_expert_hint, s);
     if (err != hipSuccess) return hip_status(err, "moe_expert_ffn (gate_up)");
-    return hip_status(nvfp4::launch_grouped_gemm(dn, nvfp4::EPI_BF16, a->m_total, a->max_rows_per_expert_hint, s),
-                      "moe_expert_ffn (down)");
+    err = nvfp4::launch_grouped_gemm(dn, nvfp4::EPI_BF16, a->m_total, a->max_rows_per_expert_hint, s);
+    if (err != hipSuccess || !a->out) return hip_status(err, "moe_expert_ffn (down)");
+    return hip_status(nvfp4::launch_combine(a->y, 1, a->perm_of_assignment, a->topk_w, a->T, a->k, a->H, a->out, 1, s),
+                      "moe_expert_ffn (combine)");
   }
-  return hip_status(nvfp4::launch_moe_ffn(gu, dn, a->m_total, rows_per_expert >= 64, workspace, kFfnSpinLimit, s),
+  const nvfp4::FfnCombine comb{a->perm_of_assignment, a->topk_w, a->T, a->k, a->out};
+  return hip_status(nvfp4::launch_moe_ffn(gu, dn, a->m_total, rows_per_expert >= 64, workspace, kFfnSpinLimit,
+                                          a->out ? &comb : nullptr, s),
                     "moe_expert_ffn");
 }
 

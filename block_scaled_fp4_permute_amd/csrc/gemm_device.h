@@ -977,7 +977,10 @@ __global__ __launch_bounds__(NW * 64, MINB) void k_gemm_streamk(const GemmParams
 // stores.
 constexpr int UNIT = 4;   // 16-column tiles per unit
 
-template <int EPI>
+// OCOH: bf16 rows leave through agent-scope coherent (write-through) stores,
+// so that a workgroup of the same launch on another XCD can read them (the
+// output rows must then span less than 4 GiB: a buffer resource covers them)
+template <int EPI, bool OCOH = false>
 __device__ __forceinline__ void store_unit(const GemmParams& p, const float4v (&acc)[UNIT], float* __restrict__ stage,
                                            int prow0, int rows_left, int col0, float gab) {
   // stage[16 rows][64 cols] float32 of this wave; lane (lr, lg) holds rows 4lg+i, cols 16u+lr
@@ -1006,9 +1009,17 @@ __device__ __forceinline__ void store_unit(const GemmParams& p, const float4v (&
 #pragma unroll
       for (int q = 0; q < 8; ++q)
         w[q] = static_cast<uint32_t>(f32_to_bf16(src[2 * q])) | (static_cast<uint32_t>(f32_to_bf16(src[2 * q + 1])) << 16);
-      uint4* dst = reinterpret_cast<uint4*>(static_cast<uint16_t*>(p.out) + base);
-      dst[0] = make_uint4(w[0], w[1], w[2], w[3]);
-      dst[1] = make_uint4(w[4], w[5], w[6], w[7]);
+      if constexpr (OCOH) {
+        const rsrc_t ro = make_rsrc(p.out, static_cast<uint32_t>(static_cast<size_t>(p.m_total) * p.N * 2));
+        const uint32_t vo = static_cast<uint32_t>(base * 2);
+        const u32x4 w0 = {w[0], w[1], w[2], w[3]}, w1 = {w[4], w[5], w[6], w[7]};
+        __builtin_amdgcn_raw_buffer_store_b128(w0, ro, vo, 0, kCoherent);
+        __builtin_amdgcn_raw_buffer_store_b128(w1, ro, vo + 16u, 0, kCoherent);
+      } else {
+        uint4* dst = reinterpret_cast<uint4*>(static_cast<uint16_t*>(p.out) + base);
+        dst[0] = make_uint4(w[0], w[1], w[2], w[3]);
+        dst[1] = make_uint4(w[4], w[5], w[6], w[7]);
+      }
     }
   }
   __builtin_amdgcn_wave_barrier();
@@ -1016,7 +1027,7 @@ __device__ __forceinline__ void store_unit(const GemmParams& p, const float4v (&
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-template <int NW, int MT, int MTA, int UPW, int EPI, int PACKED>
+template <int NW, int MT, int MTA, int UPW, int EPI, int PACKED, bool OCOH = false>
 __device__ __forceinline__ void n_main_loop(const GemmParams& p, const half8* __restrict__ lds, float* stage,
                                             const uint8_t* tiles, int u_first, int u_count, int ntr, int prow0,
                                             int rows, float gab) {
@@ -1052,7 +1063,7 @@ __device__ __forceinline__ void n_main_loop(const GemmParams& p, const half8* __
 #pragma unroll
       for (int r = 0; r < MTA; ++r) {
         if constexpr (EPI == EPI_F32 || EPI == EPI_BF16) {
-          store_unit<EPI>(p, acc[r], stage, prow0 + 16 * r, rows - 16 * r, col0, gab);
+          store_unit<EPI, OCOH>(p, acc[r], stage, prow0 + 16 * r, rows - 16 * r, col0, gab);
         } else {
 #pragma unroll
           for (int t = 0; t < UNIT; ++t)
@@ -1074,8 +1085,9 @@ __device__ __forceinline__ void n_main_loop(const GemmParams& p, const half8* __
 
 // One task of the stream-N kernel: rows [m0, m0 + MC) of expert e, column
 // group ng (NW * UPW units of 64 columns).  a_lds: MT * 8 * 64 fragments;
-// stage_lds: NW * 16 * 68 floats.  AAUX: cache policy of the A loads.
-template <int NW, int MT, int UPW, int EPI, int PACKED, int AAUX = 0>
+// stage_lds: NW * 16 * 68 floats.  AAUX: cache policy of the A loads; OCOH:
+// coherent output stores (store_unit).
+template <int NW, int MT, int UPW, int EPI, int PACKED, int AAUX = 0, bool OCOH = false>
 __device__ __forceinline__ void streamn_task(const GemmParams& p, int e, int m0, int ng, half8* __restrict__ a_lds,
                                              float* __restrict__ stage_lds) {
   constexpr int THREADS = NW * 64;
@@ -1106,10 +1118,10 @@ __device__ __forceinline__ void streamn_task(const GemmParams& p, int e, int m0,
     const int prow0 = row0 + m0;
     float* stage = stage_lds + wave * (16 * 68);
     switch (mt_active) {
-      case 1: n_main_loop<NW, MT, 1, UPW, EPI, PACKED>(p, a_lds, stage, tiles, u_first, u_count, ntr, prow0, rows, gab); break;
-      case 2: if constexpr (MT >= 2) n_main_loop<NW, MT, 2, UPW, EPI, PACKED>(p, a_lds, stage, tiles, u_first, u_count, ntr, prow0, rows, gab); break;
-      case 3: if constexpr (MT >= 3) n_main_loop<NW, MT, 3, UPW, EPI, PACKED>(p, a_lds, stage, tiles, u_first, u_count, ntr, prow0, rows, gab); break;
-      default: if constexpr (MT >= 4) n_main_loop<NW, MT, MT, UPW, EPI, PACKED>(p, a_lds, stage, tiles, u_first, u_count, ntr, prow0, rows, gab); break;
+      case 1: n_main_loop<NW, MT, 1, UPW, EPI, PACKED, OCOH>(p, a_lds, stage, tiles, u_first, u_count, ntr, prow0, rows, gab); break;
+      case 2: if constexpr (MT >= 2) n_main_loop<NW, MT, 2, UPW, EPI, PACKED, OCOH>(p, a_lds, stage, tiles, u_first, u_count, ntr, prow0, rows, gab); break;
+      case 3: if constexpr (MT >= 3) n_main_loop<NW, MT, 3, UPW, EPI, PACKED, OCOH>(p, a_lds, stage, tiles, u_first, u_count, ntr, prow0, rows, gab); break;
+      default: if constexpr (MT >= 4) n_main_loop<NW, MT, MT, UPW, EPI, PACKED, OCOH>(p, a_lds, stage, tiles, u_first, u_count, ntr, prow0, rows, gab); break;
     }
   }
 }

@@ -50,8 +50,8 @@ constexpr int kHdrDnBase = 40;           // [8] first down task of each XCD in t
 constexpr int kPlanThreads = 1024;
 
 struct FfnLayout {
-  size_t max_chunks, max_gu, max_dn;
-  size_t off_done, off_gu, off_dn, bytes;   // byte offsets in the workspace
+  size_t max_chunks, max_gu, max_dn, max_cnt;
+  size_t off_done, off_gu, off_dn, off_cnt, bytes;   // byte offsets in the workspace
 };
 
 static inline size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
@@ -64,7 +64,10 @@ FfnLayout ffn_layout(int E, int64_t m_total, int ntl, int ndg) {
   L.off_done = align256(kFfnHdrWords * sizeof(int));
   L.off_gu = L.off_done + align256(L.max_chunks * sizeof(int));
   L.off_dn = L.off_gu + align256(L.max_gu * sizeof(int4));
-  L.bytes = L.off_dn + align256(L.max_dn * sizeof(int4));
+  // combine counters: one per (token, down column group); tokens <= rows
+  L.max_cnt = static_cast<size_t>(m_total) * static_cast<size_t>(ndg);
+  L.off_cnt = L.off_dn + align256(L.max_dn * sizeof(int4));
+  L.bytes = L.off_cnt + align256(L.max_cnt * sizeof(int));
   return L;
 }
 
@@ -77,6 +80,8 @@ struct PlanArgs {
   int* done;
   int4* gu;
   int4* dn;
+  int* cnt;             // combine counters to clear (n_cnt of them)
+  int n_cnt;
 };
 
 // block-wide exclusive scan of one int per thread (kPlanThreads threads)
@@ -113,6 +118,7 @@ __global__ __launch_bounds__(kPlanThreads) void k_ffn_plan(const PlanArgs a) {
   __shared__ int s_wcnt[kPlanThreads / 64][8 * kFfnMT];
   __shared__ int s_gubase[8][kFfnMT + 1], s_dnbase[8][kFfnMT + 1];
   const int tid = threadIdx.x;
+  for (int i = tid; i < a.n_cnt; i += kPlanThreads) a.cnt[i] = 0;
   if (tid < 8 * (kFfnMT + 1)) {
     (&s_cnt[0][0])[tid] = 0;
     (&s_run[0][0])[tid] = 0;
@@ -249,15 +255,98 @@ struct FfnParams {
   const int4* gu_list;
   const int4* dn_list;
   int spin_limit;
+  // fused combine: out[t] = sum_j topk_w[t, j] * y[perm_of[t, j]] (bf16)
+  int* cnt;               // [T, ndg] down tasks done per (token, column group)
+  const int32_t* perm_of;
+  const float* topk_w;
+  uint16_t* out;
+  int T, k, ndg;
 };
 
-template <int UPW, int GU_PACKED, int DN_PACKED>
+// The combine of the tokens whose last down row in column group ng this task
+// wrote.  Every down task of a chunk counts, per row, one on the counter of
+// (token, ng) once its coherent row stores have completed; the task that
+// brings a counter to k holds the last of the token's k rows of that column
+// group and combines them (rows read with coherent loads) - in the order
+// j = 0, 1, ... of the unfused combine, so the output is the same bit for bit.
+// No task waits for another.
+template <int UPW>
+__device__ __forceinline__ void ffn_finalize(const FfnParams& f, int e, int m0, int ng, int* s_list, int* s_n) {
+  const GemmParams& p = f.dn;
+  const int row0 = min(max(p.offsets[e], 0), p.m_total);
+  const int Me = min(max(p.offsets[e + 1], 0), p.m_total) - row0;
+  const int rows = min(kFfnMC, Me - m0);
+  __builtin_amdgcn_s_waitcnt(0);     // this wave's row stores have completed
+  __syncthreads();                   // and every wave's
+  if (threadIdx.x < 64) {            // wave 0: one row per lane
+    const int i = threadIdx.x;
+    bool last = false;
+    int tok = 0;
+    if (i < rows) {
+      tok = f.gu.a_rows[row0 + m0 + i];
+      if (tok >= 0 && tok < f.T) {
+        const int old = __hip_atomic_fetch_add(f.cnt + static_cast<size_t>(tok) * f.ndg + ng, 1, __ATOMIC_RELAXED,
+                                               __HIP_MEMORY_SCOPE_AGENT);
+        last = old == f.k - 1;
+      }
+    }
+    const uint64_t m = __ballot(last);
+    if (last) s_list[__popcll(m & ((uint64_t(1) << i) - 1))] = tok;
+    if (i == 0) *s_n = __popcll(m);
+  }
+  __syncthreads();
+  const int n = *s_n;
+  constexpr int kGroupCols = 4 * UPW * 64;     // columns of a down column group
+  const int H = p.N;
+  const int c0 = ng * kGroupCols;
+  const int ncg = max(0, min(kGroupCols, H - c0)) / 8;
+  const rsrc_t ry = make_rsrc(p.out, static_cast<uint32_t>(static_cast<size_t>(p.m_total) * H * 2));
+  for (int it = threadIdx.x; it < n * ncg; it += blockDim.x) {
+    const int tok = s_list[it / ncg];
+    const int c = c0 + 8 * (it % ncg);
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    for (int j0 = 0; j0 < f.k; j0 += 8) {
+      u32x4 q[8];
+      float wt[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const size_t a = static_cast<size_t>(tok) * f.k + min(j0 + u, f.k - 1);
+        const int row = f.perm_of[a];
+        wt[u] = f.topk_w[a];
+        // rows outside [0, m_total) read zeros (the buffer range check)
+        const uint32_t off = (row >= 0 && row < p.m_total) ? static_cast<uint32_t>((static_cast<size_t>(row) * H + c) * 2)
+                                                           : 0xFFFFFFF0u;
+        q[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(ry, off, 0, kCoherent));
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        if (j0 + u < f.k) {
+          const uint32_t w4[4] = {q[u].x, q[u].y, q[u].z, q[u].w};
+#pragma unroll
+          for (int m = 0; m < 4; ++m) {
+            acc[2 * m] = fmaf(wt[u], __uint_as_float(w4[m] << 16), acc[2 * m]);
+            acc[2 * m + 1] = fmaf(wt[u], __uint_as_float(w4[m] & 0xFFFF0000u), acc[2 * m + 1]);
+          }
+        }
+      }
+    }
+    uint4 o;
+    o.x = f32_to_bf16(acc[0]) | (static_cast<uint32_t>(f32_to_bf16(acc[1])) << 16);
+    o.y = f32_to_bf16(acc[2]) | (static_cast<uint32_t>(f32_to_bf16(acc[3])) << 16);
+    o.z = f32_to_bf16(acc[4]) | (static_cast<uint32_t>(f32_to_bf16(acc[5])) << 16);
+    o.w = f32_to_bf16(acc[6]) | (static_cast<uint32_t>(f32_to_bf16(acc[7])) << 16);
+    *reinterpret_cast<uint4*>(f.out + static_cast<size_t>(tok) * H + c) = o;
+  }
+}
+
+template <int UPW, int GU_PACKED, int DN_PACKED, bool FUSED>
 __global__ __launch_bounds__(256, 2) void k_moe_ffn(const FfnParams f) {
   // gate_up: two 64-row x 256-K fragment buffers (64 KB); down: one buffer
   // (32 KB) and the per-wave output staging (17 KB) in the same space
   __shared__ half8 smem[2 * kFfnMT * 8 * 64];
   static_assert(fits_lds(sizeof(smem) + 64, 2), "expert-FFN staging exceeds the LDS of two workgroups per CU");
   __shared__ int s_ticket;
+  __shared__ int s_list[kFfnMC], s_n;     // fused combine: tokens this task completes
   const int xcd = blockIdx.x & 7;
   const int n_gu = f.hdr[kHdrNGu + xcd];
   const int n_dn = f.hdr[kHdrNDn + xcd];
@@ -295,8 +384,9 @@ __global__ __launch_bounds__(256, 2) void k_moe_ffn(const FfnParams f) {
         }
       }
       __syncthreads();
-      streamn_task<4, kFfnMT, UPW, EPI_BF16, DN_PACKED, kCoherent>(
+      streamn_task<4, kFfnMT, UPW, EPI_BF16, DN_PACKED, kCoherent, FUSED>(
           f.dn, d.x, d.y, d.z & 0xFFFF, smem, reinterpret_cast<float*>(smem + kFfnMT * 8 * 64));
+      if constexpr (FUSED) ffn_finalize<UPW>(f, d.x, d.y, d.z & 0xFFFF, s_list, &s_n);
     } else {
       break;
     }
@@ -326,7 +416,7 @@ size_t moe_ffn_ws_bytes(int E, int64_t m_total, int H, int I) {
 // gu: gate_up parameters (SwiGLU epilogue; A = x rows gathered by a_rows);
 // dn: down parameters (bf16 epilogue; A = h).  Both with packed weights.
 hipError_t launch_moe_ffn(GemmParams gu, GemmParams dn, int64_t m_total, bool cached, void* ws, int spin_limit,
-                          hipStream_t stream) {
+                          const FfnCombine* comb, hipStream_t stream) {
   const int I = gu.N / 2;
   const int H = dn.N;
   const int ntl = ffn_ntl(I);
@@ -338,19 +428,30 @@ hipError_t launch_moe_ffn(GemmParams gu, GemmParams dn, int64_t m_total, bool ca
   gu.slots = slots;
   dn.n_tiles = ndg;
   dn.slots = slots;
+  int* cnt = reinterpret_cast<int*>(w + L.off_cnt);
+  const int n_cnt = comb ? comb->T * ndg : 0;
   PlanArgs pa{gu.offsets, gu.E, gu.m_total, ntl, ndg, slots, static_cast<int>(L.max_chunks), reinterpret_cast<int*>(w),
               reinterpret_cast<int*>(w + L.off_done), reinterpret_cast<int4*>(w + L.off_gu),
-              reinterpret_cast<int4*>(w + L.off_dn)};
+              reinterpret_cast<int4*>(w + L.off_dn), cnt, n_cnt};
   hipLaunchKernelGGL(k_ffn_plan, dim3(1), dim3(kPlanThreads), (3 * gu.E + 1) * sizeof(int), stream, pa);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   FfnParams f{gu, dn, reinterpret_cast<int*>(w), reinterpret_cast<int*>(w + L.off_done),
-              reinterpret_cast<const int4*>(w + L.off_gu), reinterpret_cast<const int4*>(w + L.off_dn), spin_limit};
+              reinterpret_cast<const int4*>(w + L.off_gu), reinterpret_cast<const int4*>(w + L.off_dn), spin_limit,
+              cnt, comb ? comb->perm_of : nullptr, comb ? comb->topk_w : nullptr,
+              comb ? static_cast<uint16_t*>(comb->out) : nullptr, comb ? comb->T : 0, comb ? comb->k : 0, ndg};
   const int grid = (slots + 7) / 8 * 8;
-  if (cached)
-    hipLaunchKernelGGL((k_moe_ffn<kFfnUPW, kPackedCached, kPackedCached>), dim3(grid), dim3(256), 0, stream, f);
-  else
-    hipLaunchKernelGGL((k_moe_ffn<kFfnUPW, kPackedNT, kPackedNT>), dim3(grid), dim3(256), 0, stream, f);
+  if (comb) {
+    if (cached)
+      hipLaunchKernelGGL((k_moe_ffn<kFfnUPW, kPackedCached, kPackedCached, true>), dim3(grid), dim3(256), 0, stream, f);
+    else
+      hipLaunchKernelGGL((k_moe_ffn<kFfnUPW, kPackedNT, kPackedNT, true>), dim3(grid), dim3(256), 0, stream, f);
+  } else {
+    if (cached)
+      hipLaunchKernelGGL((k_moe_ffn<kFfnUPW, kPackedCached, kPackedCached, false>), dim3(grid), dim3(256), 0, stream, f);
+    else
+      hipLaunchKernelGGL((k_moe_ffn<kFfnUPW, kPackedNT, kPackedNT, false>), dim3(grid), dim3(256), 0, stream, f);
+  }
   return hipGetLastError();
 }
 

@@ -65,8 +65,15 @@ size_t mx_packed_weight_bytes(int E, int N, int K);
 hipError_t launch_mx_repack(const uint8_t* codes, const uint8_t* scales, int E, int N, int K, uint8_t* packed,
                             hipStream_t stream);
 size_t moe_ffn_ws_bytes(int E, int64_t m_total, int H, int I);
+// the weighted top-k combine fused into the expert-FFN launch
+struct FfnCombine {
+  const int32_t* perm_of;   // [T, k] row of assignment (t, j)
+  const float* topk_w;      // [T, k]
+  int T, k;
+  void* out;                // bf16 [T, H]
+};
 hipError_t launch_moe_ffn(GemmParams gu, GemmParams dn, int64_t m_total, bool cached, void* ws, int spin_limit,
-                          hipStream_t stream);
+                          const FfnCombine* comb, hipStream_t stream);
 
 // Kernel-side arguments of the grouped FP8 GEMM (validated on the host first).
 struct Fp8Params {

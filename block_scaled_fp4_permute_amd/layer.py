@@ -17,7 +17,12 @@ Choices:
                    moe_unpermute_combine gathers each token's k rows
                    (deterministic);
   combine="atomic" the down GEMM epilogue scatter-adds weighted rows into a
-                   float32 accumulator (float32 atomics), then converts it.
+                   float32 accumulator (float32 atomics), then converts it;
+  combine="fused"  (one_launch) moe_expert_ffn combines too: in its
+                   persistent launch the down task that writes a token's last
+                   row of a column group combines that group (the same
+                   arithmetic as moe_unpermute_combine, bit for bit); in the
+                   two-launch regimes the combine kernel follows on the stream.
 
 Buffers are allocated once per layer object (torch device memory); a forward
 allocates nothing.
@@ -92,10 +97,12 @@ class MoELayer:
 
     def __init__(self, T: int, H: int, I: int, E: int, k: int, device, swiglu: str = "fused",
                  combine: str = "gather", ffn: str = "one_launch"):
-        assert swiglu in ("fused", "separate") and combine in ("gather", "atomic")
+        assert swiglu in ("fused", "separate") and combine in ("gather", "atomic", "fused")
         assert ffn in ("one_launch", "two_launch")
-        if ffn == "one_launch" and (swiglu, combine) != ("fused", "gather"):
+        if ffn == "one_launch" and (swiglu, combine) not in (("fused", "gather"), ("fused", "fused")):
             ffn = "two_launch"     # the one-launch FFN has the fused SwiGLU and bf16 rows
+        if ffn == "two_launch" and combine == "fused":
+            combine = "gather"
         self.T, self.H, self.I, self.E, self.k = T, H, I, E, k
         self.swiglu, self.combine, self.ffn = swiglu, combine, ffn
         dev = torch.device(device)
@@ -141,6 +148,15 @@ class MoELayer:
         mark(1)
         mark(2)
         if self.ffn == "one_launch" and w.gu_packed is not None and w.dn_packed is not None:
+            if self.combine == "fused":
+                moe_expert_ffn(self.xq, r.perm_src_token, r.offsets, w.gu_packed, w.gu_g, w.dn_packed, w.dn_g, g_h,
+                               H=self.H, I=self.I, m_total=M, h=hq, y=self.y2, workspace=self.ffn_ws,
+                               perm_of_assignment=r.perm_of_assignment, topk_w=r.topk_w, k=k, out=self.out,
+                               stream=stream)
+                mark(3)
+                mark(4)
+                mark(5)
+                return self.out
             moe_expert_ffn(self.xq, r.perm_src_token, r.offsets, w.gu_packed, w.gu_g, w.dn_packed, w.dn_g, g_h,
                            H=self.H, I=self.I, m_total=M, h=hq, y=self.y2, workspace=self.ffn_ws, stream=stream)
             mark(3)

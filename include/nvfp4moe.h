@@ -231,7 +231,20 @@ int nvfp4_grouped_gemm(const nvfp4moe_gemm_args* args, void* stream);
  *   g_h                    per-tensor scale of h (1 float)
  *   h_codes, h_scales      (out) h [m_total, I/2], [m_total, I/16]
  *   y                      (out) bf16 [m_total, H], the down rows (then
- *                          moe_unpermute_combine)
+ *                          moe_unpermute_combine, or the fused combine below)
+ *   out, perm_of_assignment, topk_w, T, k   optional weighted top-k combine
+ *                          of the down rows, with moe_unpermute_combine's
+ *                          arithmetic and result bit for bit (bf16 in, bf16
+ *                          out): out [T, H] bf16, perm_of_assignment and topk_w
+ *                          [T, k] from moe_route_permute, T * k == m_total,
+ *                          m_total * H * 2 < 2^31.  out == NULL: no combine
+ *                          (y holds the result).  In the one-launch regime the
+ *                          combine runs inside the launch - the down task that
+ *                          writes the last of a token's k rows of a column
+ *                          group combines that group (the pages' finalize:
+ *                          "The Critical Search ...", section "Context: The
+ *                          Optimization Journey") - otherwise as one more
+ *                          kernel on the stream after the down GEMM.
  * I % 32 == 0, I <= 256 (one K step of the down GEMM), H % 32 == 0, E <= 4096.
  * workspace: moe_expert_ffn_workspace_size(E, m_total, H, I) bytes, 256-byte
  * aligned, caller-owned; it holds the task lists and chunk counters, which the
@@ -260,6 +273,11 @@ typedef struct nvfp4moe_ffn_args {
   uint8_t* h_scales;
   void* y;
   int32_t max_rows_per_expert_hint;
+  void* out;
+  const int32_t* perm_of_assignment;
+  const float* topk_w;
+  int32_t T;
+  int32_t k;
 } nvfp4moe_ffn_args;
 size_t moe_expert_ffn_workspace_size(int32_t E, int64_t m_total, int32_t H, int32_t I);
 int moe_expert_ffn(const nvfp4moe_ffn_args* args, void* workspace, size_t workspace_bytes, void* stream);

@@ -217,6 +217,15 @@ int main() {
     expect("ffn misaligned workspace", moe_expert_ffn(&a, FM, fws, nullptr), NVFP4MOE_ERR_INVALID);
     a = ffn_args(); a.m_total = 0;
     expect("ffn empty", moe_expert_ffn(&a, F, fws, nullptr), NVFP4MOE_OK);
+    // the fused combine's arguments
+    a = ffn_args(); a.out = F;
+    expect("ffn combine without perm", moe_expert_ffn(&a, F, fws, nullptr), NVFP4MOE_ERR_INVALID);
+    a = ffn_args(); a.out = F; a.perm_of_assignment = p<int32_t>(F); a.topk_w = p<float>(F); a.T = 5; a.k = 8;
+    expect("ffn combine T*k != m_total", moe_expert_ffn(&a, F, fws, nullptr), NVFP4MOE_ERR_INVALID);
+    a.T = 4; a.k = 8; a.out = FM;
+    expect("ffn combine misaligned out", moe_expert_ffn(&a, F, fws, nullptr), NVFP4MOE_ERR_INVALID);
+    a.out = F; a.T = I32MAX; a.k = I32MAX;
+    expect("ffn combine huge T*k", moe_expert_ffn(&a, F, fws, nullptr), NVFP4MOE_ERR_INVALID);
   }
 
   // ---------------------------------------------------------------- swiglu / combine

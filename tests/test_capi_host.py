@@ -230,3 +230,10 @@ def test_expert_ffn_validation():
     assert call(ws=None) == m.ERR_WORKSPACE
     assert call(ws=FAKE + 16) == m.ERR_INVALID         # workspace must be 256-byte aligned
     assert call(m_total=0) == m.OK                     # nothing to do, nothing enqueued
+    # the fused combine: out needs perm_of_assignment, topk_w and T * k == m_total
+    assert call(out=FAKE) == m.ERR_INVALID
+    comb = dict(out=FAKE, perm_of_assignment=FAKE, topk_w=FAKE)
+    assert call(T=3, k=8, **comb) == m.ERR_INVALID
+    assert call(T=16, k=0, **comb) == m.ERR_INVALID
+    assert call(T=16, k=8, out=FAKE_MIS, perm_of_assignment=FAKE, topk_w=FAKE) == m.ERR_INVALID
+    assert call(T=16, k=8, out=FAKE, perm_of_assignment=None, topk_w=FAKE) == m.ERR_INVALID

@@ -108,3 +108,55 @@ def test_expert_ffn_equals_two_calls_edge_cases(case):
     w = _random_weights(rng, E, H, I)
     g_h = up(np.array([0.05], np.float32))
     _compare(xq, src, offsets, w, g_h, H, I, M, hint=hint, what=f"edge case {case}")
+
+
+def _fused_combine_check(xq, r, w, g_h, H, I, k, hint=0, what=""):
+    """moe_expert_ffn with the combine fused (in the one-launch regime: inside
+    the persistent launch) against the same call without it followed by
+    moe_unpermute_combine: h, y and the combined output equal bit for bit, on
+    two calls in a row over one workspace (its counters cleared by the call)."""
+    M = r.perm_src_token.numel()
+    T = M // k
+    E = r.offsets.numel() - 1
+    ws = m.moe_expert_ffn_workspace(E, M, H, I, DEV)
+    ws.fill_(0x5A)
+    h0, y0 = m.moe_expert_ffn(xq, r.perm_src_token, r.offsets, w["gu_p"], w["gu_g"], w["dn_p"], w["dn_g"], g_h,
+                              H=H, I=I, m_total=M, max_rows_per_expert_hint=hint)
+    ref = m.moe_unpermute_combine(y0, r.perm_of_assignment, r.topk_w, T, k)
+    for call in range(2):
+        h1, y1, out = m.moe_expert_ffn(xq, r.perm_src_token, r.offsets, w["gu_p"], w["gu_g"], w["dn_p"], w["dn_g"],
+                                       g_h, H=H, I=I, m_total=M, workspace=ws, max_rows_per_expert_hint=hint,
+                                       perm_of_assignment=r.perm_of_assignment, topk_w=r.topk_w, k=k)
+        torch.cuda.synchronize()
+        if 32 <= (hint if hint > 0 else M // E) < 128:
+            assert int(ws[:256].view(torch.int32)[8].item()) == 0, f"{what}: a down task gave up waiting"
+        for a, b, name in ((h1.codes, h0.codes, "h codes"), (y1, y0, "y"), (out, ref, "combined out")):
+            if not torch.equal(a, b):
+                bad = (a != b).nonzero()
+                raise AssertionError(f"{what} call {call}: {name} differ at {bad.shape[0]} places, "
+                                     f"first {bad[0].tolist()}")
+
+
+@pytest.mark.parametrize("cfg_index,hint", [(0, 0), (1, 0), (1, 64), (2, 0), (3, 0)])
+def test_expert_ffn_fused_combine_on_workloads(cfg_index, hint):
+    cfg = workloads.CONFIGS[cfg_index]
+    print(f"fused combine cfg={cfg_index} hint={hint}", flush=True)
+    r, xq, w, g_h = _layer_inputs(cfg)
+    _fused_combine_check(xq, r, w, g_h, cfg.H, cfg.I, cfg.k, hint=hint, what=f"config {cfg_index} hint {hint}")
+
+
+@pytest.mark.parametrize("T,E,k,H,I,hint", [(300, 16, 4, 512, 256, 0), (40, 8, 8, 512, 128, 40),
+                                            (5, 4, 2, 256, 64, 40), (200, 32, 10, 512, 256, 0),
+                                            (500, 64, 1, 1024, 256, 48), (64, 8, 3, 1600, 96, 0)])
+def test_expert_ffn_fused_combine_routings(T, E, k, H, I, hint):
+    # routed by the library on random logits (k = E: every token at every
+    # expert; k = 1; k = 10 past one batch of 8 rows; H = 1600 leaves the last
+    # down column group partial)
+    rng = np.random.default_rng(T * 7 + E + k)
+    print(f"fused combine T={T} E={E} k={k} H={H} I={I} hint={hint}", flush=True)
+    logits = up(rng.standard_normal((T, E)).astype(np.float32))
+    x = up(rng.standard_normal((T, H)).astype(np.float32)).to(torch.bfloat16)
+    r, xq = m.moe_route_quantize(logits, k, x)
+    w = _random_weights(rng, E, H, I)
+    g_h = up(np.array([0.05], np.float32))
+    _fused_combine_check(xq, r, w, g_h, H, I, k, hint=hint, what=f"T={T} E={E} k={k}")
