@@ -166,7 +166,7 @@ def _run_mx_case(spec, seed, gather, epi, packed, name):
     assert_gemm_close(got, y_ref, absdot, bf16_out=epi == "bf16", what=f"mx {name} {epi}")
 
 
-@pytest.mark.parametrize("K,large", [(256, False), (2048, False), (8192, False), (256, True), (8192, True)])
+@pytest.mark.parametrize("K,large", [(256, False), (2048, False), (8192, False), (256, True), (512, True), (8192, True)])
 def test_mx_gemm_constant_scales_bit_exact(K, large):
     # one scale per operand: every float32 partial sum is an exact multiple of
     # 0.25 * 2^(Xa + Xb), so the GPU must equal the oracle bit for bit
@@ -188,14 +188,14 @@ def test_mx_gemm_constant_scales_bit_exact(K, large):
 
 @pytest.mark.parametrize("large", [False, True])
 def test_mx_gemm_scale_per_block_single_term(large):
-    # K = 256 with one nonzero 32-block per row pair at a time: each output is
-    # one exact block term, so the per-lane scale selection (two blocks per
-    # lane, op_sel picking the byte) must put every scale on its own block;
-    # large: 300 rows through the 256 x 256 tile, whose A blocks sit in LDS
-    # under a lane swizzle
+    # one nonzero 32-block per row pair at a time: each output is one exact
+    # block term, so the per-lane scale selection (two blocks per lane, op_sel
+    # picking the byte) must put every scale on its own block; large: 300 rows
+    # and two K steps through the 256 x 256 tile (packed weights), whose A
+    # blocks sit in LDS under a lane swizzle
     rng = np.random.default_rng(5)
-    M, N, K = (300, 48, 256) if large else (16, 16, 256)
-    for blk in range(8):
+    M, N, K = (300, 48, 512) if large else (16, 16, 256)
+    for blk in range(K // 32):
         ac = np.zeros((M, K // 2), np.uint8)
         bc = np.zeros((1, N, K // 2), np.uint8)
         ac[:, 16 * blk:16 * blk + 16] = rng.integers(0, 256, (M, 16), dtype=np.uint8)
