@@ -458,6 +458,173 @@ __global__ __launch_bounds__(256, 2) void k_fp8_gemm(const Fp8Params p, int n_ti
   }
 }
 
+// ---- stream-N (K <= 256: one or two 128-value steps; the down GEMM): the
+// chunk's 64 rows (codes and block scales) are staged in LDS once, then each
+// wave streams units of 64 columns (4 weight tiles per step), the next unit's
+// loads in flight while one computes, and its rows leave through a per-wave
+// LDS stage as whole 128-byte segments (16 bytes a lane).  A unit's 64
+// columns lie in one 128-column weight block: one weight scale per unit and
+// step.
+constexpr int kFp8NUnit = 4;       // 16-column tiles per unit
+
+template <int EPI>
+__device__ __forceinline__ void fp8n_store(const Fp8Params& p, const float4v (&acc)[kFp8NUnit], float* __restrict__ stage,
+                                           int prow0, int rows_left, int col0) {
+  const int lane = threadIdx.x & 63;
+  const int lr = lane & 15, lg = lane >> 4;
+#pragma unroll
+  for (int u = 0; u < kFp8NUnit; ++u)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) stage[(4 * lg + i) * 68 + 16 * u + lr] = acc[u][i];
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  const int r = lane >> 2;
+  const int c = 16 * (lane & 3);
+  if (r < rows_left && col0 + c < p.N) {
+    const float* src = stage + r * 68 + c;
+    const size_t base = static_cast<size_t>(prow0 + r) * p.N + col0 + c;
+    if constexpr (EPI == EPI_F32) {
+      float4* dst = reinterpret_cast<float4*>(static_cast<float*>(p.out) + base);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) dst[q] = make_float4(src[4 * q], src[4 * q + 1], src[4 * q + 2], src[4 * q + 3]);
+    } else {
+      uint32_t w[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q)
+        w[q] = static_cast<uint32_t>(f32_to_bf16(src[2 * q])) | (static_cast<uint32_t>(f32_to_bf16(src[2 * q + 1])) << 16);
+      uint4* dst = reinterpret_cast<uint4*>(static_cast<uint16_t*>(p.out) + base);
+      dst[0] = make_uint4(w[0], w[1], w[2], w[3]);
+      dst[1] = make_uint4(w[4], w[5], w[6], w[7]);
+    }
+  }
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// The wave's work is a run of (unit, step) items, each the 4 weight tiles of
+// one unit at one K step; a ring of three holds the next two items' loads in
+// flight while one is multiplied.  A unit's accumulator leaves after its last
+// step.
+template <int MTA, int UPW, int EPI, bool NT>
+__device__ __forceinline__ void fp8n_loop(const Fp8Params& p, const uint8_t* __restrict__ a_lds, float* stage,
+                                          const uint8_t* tiles, const float* bsc, int u_first, int u_count, int ntr,
+                                          int nsteps, int prow0, int rows) {
+  const int lane = threadIdx.x & 63;
+  const int lr = lane & 15, g = lane >> 4;
+  const int n_items = u_count * nsteps;
+  i32x8 R0[kFp8NUnit], R1[kFp8NUnit], R2[kFp8NUnit];
+  auto load_item = [&](i32x8 (&R)[kFp8NUnit], int it) {
+    const int c = min(it, n_items - 1);                  // loads past the run re-read the last item (cached)
+    const int ui = u_first + c / nsteps, s = c % nsteps;
+#pragma unroll
+    for (int t = 0; t < kFp8NUnit; ++t) {
+      const uint8_t* tp = tiles + (static_cast<size_t>(min(kFp8NUnit * ui + t, ntr - 1)) * nsteps + s) * kFp8Tile;
+      const u32x4* p0 = reinterpret_cast<const u32x4*>(tp + 16 * lane);
+      const u32x4* p1 = reinterpret_cast<const u32x4*>(tp + 1024 + 16 * lane);
+      u32x4 lo, hi;
+      if constexpr (NT) {
+        lo = __builtin_nontemporal_load(p0);
+        hi = __builtin_nontemporal_load(p1);
+      } else {
+        lo = *p0;
+        hi = *p1;
+      }
+      R[t] = fp8_frag(lo, hi);
+    }
+  };
+  float4v acc[MTA][kFp8NUnit];
+#pragma unroll
+  for (int r = 0; r < MTA; ++r)
+#pragma unroll
+    for (int t = 0; t < kFp8NUnit; ++t) acc[r][t] = float4v{0.f, 0.f, 0.f, 0.f};
+  auto consume = [&](const i32x8 (&R)[kFp8NUnit], int it) {
+    if (it >= n_items) return;                           // uniform
+    const int ui = u_first + it / nsteps, s = it % nsteps;
+    const float sb = bsc[(64 * ui) / kFp8Block * nsteps + s];
+    const uint8_t* al = a_lds + s * kFp8ALds;
+#pragma unroll
+    for (int r = 0; r < MTA; ++r) {
+      const u32x4* src = reinterpret_cast<const u32x4*>(al + (16 * r + lr) * kFp8RowLds + 32 * g);
+      const i32x8 af = fp8_frag(src[0], src[1]);
+      const float4v sa = *reinterpret_cast<const float4v*>(al + 64 * kFp8RowLds + 4 * (16 * r + 4 * g));
+      const float4v sab = sa * sb;
+#pragma unroll
+      for (int t = 0; t < kFp8NUnit; ++t) {
+        const float4v z = {0.f, 0.f, 0.f, 0.f};
+        const float4v part = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+            af, R[t], z, kFp8FmtE4M3, kFp8FmtE4M3, 0, kE8M0One, 0, kE8M0One);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) acc[r][t][q] = __builtin_fmaf(part[q], sab[q], acc[r][t][q]);
+      }
+    }
+    if (s == nsteps - 1) {
+#pragma unroll
+      for (int r = 0; r < MTA; ++r) {
+        fp8n_store<EPI>(p, acc[r], stage, prow0 + 16 * r, rows - 16 * r, 64 * ui);
+#pragma unroll
+        for (int t = 0; t < kFp8NUnit; ++t) acc[r][t] = float4v{0.f, 0.f, 0.f, 0.f};
+      }
+    }
+  };
+  load_item(R0, 0);
+  load_item(R1, 1);
+  load_item(R2, 2);
+  for (int it = 0; it < n_items; it += 3) {
+    consume(R0, it);
+    load_item(R0, it + 3);
+    consume(R1, it + 1);
+    load_item(R1, it + 4);
+    consume(R2, it + 2);
+    load_item(R2, it + 5);
+  }
+}
+
+template <int UPW, int EPI, bool NT>
+__global__ __launch_bounds__(256, 2) void k_fp8_gemm_n(const Fp8Params p, int n_groups) {
+  constexpr int NW = 4;
+  __shared__ __attribute__((aligned(16))) uint8_t a_lds[2 * kFp8ALds];
+  __shared__ float stage_lds[NW * 16 * 68];
+  static_assert(fits_lds(sizeof(a_lds) + sizeof(stage_lds), 2), "FP8 stream-N staging exceeds the LDS of two workgroups per CU");
+  int e, m0, ng;
+  bool narrow;
+  const GemmParams map = fp8_map_params(p, n_groups);
+  if (!find_task<4, false, 0>(map, e, m0, ng, narrow)) return;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int row0 = min(max(p.offsets[e], 0), p.m_total);
+  const int Me = min(max(p.offsets[e + 1], 0), p.m_total) - row0;
+  const int rows = min(64, Me - m0);
+  const int mt_active = (rows + 15) >> 4;
+  const int N = p.N, K = p.K;
+  const int nsteps = K / kFp8Block;                    // 1 or 2
+  const int ntr = (N + 15) / 16;
+  const int nsb = (N + kFp8Block - 1) / kFp8Block;
+  Fp8AStage AS;
+  fp8a_setup(p, row0, m0, rows, AS);
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+    Fp8ARegs ra;
+    fp8a_load(AS, ra, s, nsteps);
+    fp8a_store(AS, ra, s < nsteps, rows, a_lds + s * kFp8ALds);
+  }
+  __syncthreads();
+  const int nunits = (ntr + kFp8NUnit - 1) / kFp8NUnit;
+  const int u_first = (ng * NW + wave) * UPW;
+  const int u_count = min(UPW, nunits - u_first);
+  if (u_count <= 0) return;
+  const uint8_t* tiles = p.b_packed + static_cast<size_t>(e) * ntr * nsteps * kFp8Tile;
+  const float* bsc = p.b_scales + static_cast<size_t>(e) * nsb * nsteps;
+  const int prow0 = row0 + m0;
+  float* stage = stage_lds + wave * (16 * 68);
+  switch (mt_active) {
+    case 1: fp8n_loop<1, UPW, EPI, NT>(p, a_lds, stage, tiles, bsc, u_first, u_count, ntr, nsteps, prow0, rows); break;
+    case 2: fp8n_loop<2, UPW, EPI, NT>(p, a_lds, stage, tiles, bsc, u_first, u_count, ntr, nsteps, prow0, rows); break;
+    case 3: fp8n_loop<3, UPW, EPI, NT>(p, a_lds, stage, tiles, bsc, u_first, u_count, ntr, nsteps, prow0, rows); break;
+    default: fp8n_loop<4, UPW, EPI, NT>(p, a_lds, stage, tiles, bsc, u_first, u_count, ntr, nsteps, prow0, rows); break;
+  }
+}
+
 // ---- large-M tile (from 256 rows per expert): 8 waves on 256 rows x 256
 // columns, both operands of a 128-value K step staged in LDS once per
 // workgroup; wave w = 4 wr + wc holds rows [128 wr, +128) and columns
@@ -663,6 +830,23 @@ hipError_t launch_fp8_gemm(const Fp8Params& p, int epilogue, int64_t m_total, in
   if (blocks >= (int64_t(1) << 31)) return hipErrorInvalidConfiguration;
   const int64_t rows_per_expert = hint > 0 ? hint : m_total / p.E;
   const bool nt = rows_per_expert < 64;
+  if (p.K <= 2 * kFp8Block && rows_per_expert < kFp8LRows) {
+    // one or two K steps (the down GEMM): the stream-N kernel
+    constexpr int UPW = 6;
+    const int nunits = ((p.N + 15) / 16 + kFp8NUnit - 1) / kFp8NUnit;
+    const int n_groups = (nunits + 4 * UPW - 1) / (4 * UPW);
+    const int64_t nblocks = ((((m_total + 63) / 64 + p.E) * n_groups) + 7) / 8 * 8;
+    if (nblocks >= (int64_t(1) << 31)) return hipErrorInvalidConfiguration;
+    const dim3 ngrid(static_cast<unsigned>(nblocks));
+    if (epilogue == EPI_F32) {
+      if (nt) hipLaunchKernelGGL((k_fp8_gemm_n<UPW, EPI_F32, true>), ngrid, dim3(256), 0, stream, p, n_groups);
+      else hipLaunchKernelGGL((k_fp8_gemm_n<UPW, EPI_F32, false>), ngrid, dim3(256), 0, stream, p, n_groups);
+    } else {
+      if (nt) hipLaunchKernelGGL((k_fp8_gemm_n<UPW, EPI_BF16, true>), ngrid, dim3(256), 0, stream, p, n_groups);
+      else hipLaunchKernelGGL((k_fp8_gemm_n<UPW, EPI_BF16, false>), ngrid, dim3(256), 0, stream, p, n_groups);
+    }
+    return hipGetLastError();
+  }
   if (rows_per_expert >= kFp8LRows) {
     const int64_t lblocks = ((((m_total + kFp8LRows - 1) / kFp8LRows + p.E) * n_tiles) + 7) / 8 * 8;
     const dim3 lgrid(static_cast<unsigned>(lblocks));

@@ -130,6 +130,10 @@ CASES = [
     (600, None, 64, 512, 500, 0),
     (3, [9, 40, 2], 48, 128, 60, 0),          # one K step
     (2, [33, 80], 400, 384, 120, 0),          # odd step count, N past one weight block and not a multiple of 64
+    # K <= 256 below 256 rows per expert: the stream-N kernel; 6160 columns are
+    # 97 units of 64 (the last one 16 wide) over five workgroup column groups
+    (4, [1, 64, 0, 37], 6160, 256, 110, 0),
+    (3, [70, 2, 129], 6160, 128, 210, 64),    # one K step, cached weight loads
 ]
 
 
@@ -210,16 +214,17 @@ def test_fp8_gemm_exact_sums_bit_exact(K, large):
     assert np.array_equal(down(y), y_ref)
 
 
-@pytest.mark.parametrize("large", [False, True])
-def test_fp8_gemm_single_block_term(large):
+@pytest.mark.parametrize("shape", ["decode", "large", "stream_n"])
+def test_fp8_gemm_single_block_term(shape):
     # one nonzero 128-block of K at a time, exact-sum codes, arbitrary float32
     # scales: each output is one block term part * sa * sb, which the GPU rounds
     # twice (sa * sb, then the product) - within two float32 ulps of the
     # oracle's exact term; a scale taken from the wrong row, tile or block is
     # far outside that (large: 300 rows through the 256 x 256 tile, whose A
-    # rows and scales sit in LDS)
+    # rows and scales sit in LDS; stream_n: K = 256 with 1040 columns, nine
+    # weight blocks over 17 streamed units)
     c = workloads.CONFIGS[0]
-    M, N, K = (300, 272, 512) if large else (80, 272, 512)
+    M, N, K = {"decode": (80, 272, 512), "large": (300, 272, 512), "stream_n": (80, 1040, 256)}[shape]
     for blk in range(K // 128):
         ac = np.zeros((M, K), np.uint8)
         bc = np.zeros((1, N, K), np.uint8)
