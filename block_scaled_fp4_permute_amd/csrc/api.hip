@@ -242,6 +242,8 @@ int nvfp4_grouped_gemm(const nvfp4moe_gemm_args* a, void* stream) {
     case NVFP4MOE_EPI_F32:
     case NVFP4MOE_EPI_BF16:
       if (!a->out && a->m_total > 0) return fail(NVFP4MOE_ERR_INVALID, "nvfp4_grouped_gemm: out is NULL");
+      // rows leave as 16-byte vector stores
+      if (!aligned(a->out, 16)) return fail(NVFP4MOE_ERR_INVALID, "nvfp4_grouped_gemm: out not 16-byte aligned");
       break;
     case NVFP4MOE_EPI_SWIGLU_NVFP4:
       if (a->N % 32 != 0) return fail(NVFP4MOE_ERR_INVALID, "nvfp4_grouped_gemm: SwiGLU needs N = 2I with I %% 16 == 0");
@@ -424,6 +426,7 @@ int mxfp4_grouped_gemm(const nvfp4moe_gemm_args* a, void* stream) {
     case NVFP4MOE_EPI_F32:
     case NVFP4MOE_EPI_BF16:
       if (!a->out && a->m_total > 0) return fail(NVFP4MOE_ERR_INVALID, "mxfp4_grouped_gemm: out is NULL");
+      if (!aligned(a->out, 16)) return fail(NVFP4MOE_ERR_INVALID, "mxfp4_grouped_gemm: out not 16-byte aligned");
       break;
     case NVFP4MOE_EPI_SWIGLU_NVFP4:
       if (a->N % 64 != 0) return fail(NVFP4MOE_ERR_INVALID, "mxfp4_grouped_gemm: SwiGLU needs N = 2I with I %% 32 == 0");
@@ -557,6 +560,7 @@ int fp8_grouped_gemm(const nvfp4moe_fp8_gemm_args* a, void* stream) {
   if (a->epilogue != NVFP4MOE_EPI_F32 && a->epilogue != NVFP4MOE_EPI_BF16)
     return fail(NVFP4MOE_ERR_UNSUPPORTED, "fp8_grouped_gemm: epilogue %d (F32 or BF16)", a->epilogue);
   if (!a->out && a->m_total > 0) return fail(NVFP4MOE_ERR_INVALID, "fp8_grouped_gemm: out is NULL");
+  if (!aligned(a->out, 16)) return fail(NVFP4MOE_ERR_INVALID, "fp8_grouped_gemm: out not 16-byte aligned");
   if (a->m_total == 0) return ok();
   nvfp4::Fp8Params prm{};
   prm.a_codes = a->a_codes;

@@ -96,7 +96,8 @@ typedef struct nvfp4moe_gemm_args {
   int32_t K;                  /* multiple of 32 */
   int64_t m_total;            /* host-side bound on offsets[E] (rows of out) */
   int32_t epilogue;           /* nvfp4moe_epilogue */
-  void* out;                  /* EPI_F32: float [m_total, N]; EPI_BF16: bf16 [m_total, N];
+  void* out;                  /* EPI_F32: float [m_total, N]; EPI_BF16: bf16 [m_total, N]
+                                 (16-byte aligned: rows leave as 16-byte stores);
                                  EPI_COMBINE_F32: float [out_rows, N]; unused for SWIGLU */
   int64_t out_rows;           /* EPI_COMBINE_F32: rows of the accumulator (tokens) */
   uint8_t* out_codes;         /* EPI_SWIGLU_NVFP4 */
@@ -369,7 +370,7 @@ typedef struct nvfp4moe_fp8_gemm_args {
   int32_t K;                  /* multiple of 128 */
   int64_t m_total;
   int32_t epilogue;           /* NVFP4MOE_EPI_F32 or NVFP4MOE_EPI_BF16 */
-  void* out;                  /* float or bf16 [m_total, N] */
+  void* out;                  /* float or bf16 [m_total, N], 16-byte aligned */
   int32_t max_rows_per_expert_hint;  /* as for nvfp4_grouped_gemm: < 64 streams weights non-temporally */
 } nvfp4moe_fp8_gemm_args;
 int fp8_grouped_gemm(const nvfp4moe_fp8_gemm_args* args, void* stream);

@@ -158,6 +158,9 @@ int main() {
     expect("gemm negative m_total", nvfp4_grouped_gemm(&a, nullptr), NVFP4MOE_ERR_INVALID);
     a = gemm_args(); a.m_total = 0;
     expect("gemm empty", nvfp4_grouped_gemm(&a, nullptr), NVFP4MOE_OK);
+    a = gemm_args(); a.out = FM;
+    expect("gemm out misaligned", nvfp4_grouped_gemm(&a, nullptr), NVFP4MOE_ERR_INVALID);
+    expect("mx gemm out misaligned", mxfp4_grouped_gemm(&a, nullptr), NVFP4MOE_ERR_INVALID);
     a = gemm_args(); a.K = I32MAX - 31;
     expect_true("mx gemm huge K rejected", mxfp4_grouped_gemm(&a, nullptr) != NVFP4MOE_OK);
     a = gemm_args(); a.epilogue = NVFP4MOE_EPI_COMBINE_F32;
@@ -176,6 +179,8 @@ int main() {
     expect("fp8 gemm epilogue", fp8_grouped_gemm(&a, nullptr), NVFP4MOE_ERR_UNSUPPORTED);
     a = fp8_args(); a.m_total = 0;
     expect("fp8 gemm empty", fp8_grouped_gemm(&a, nullptr), NVFP4MOE_OK);
+    a = fp8_args(); a.out = FM;
+    expect("fp8 gemm out misaligned", fp8_grouped_gemm(&a, nullptr), NVFP4MOE_ERR_INVALID);
     expect("fp8 gemm null", fp8_grouped_gemm(nullptr, nullptr), NVFP4MOE_ERR_INVALID);
   }
   expect("fp8 quantize block_rows", fp8_quantize(F, NVFP4MOE_F32, 1, 4, 128, 64, p<uint8_t>(F), p<float>(F), nullptr),

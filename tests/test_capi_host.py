@@ -150,6 +150,58 @@ def test_gemm_validation():
     assert _gemm(m_total=0) == m.OK
 
 
+def test_gemm_output_alignment():
+    # the F32 / BF16 epilogues write rows as 16-byte vector stores
+    assert _gemm(out=FAKE + 8) == m.ERR_INVALID
+    assert b"out not 16-byte aligned" in m.lib().nvfp4moe_last_error_detail()
+    assert _gemm(epilogue=m.EPI_BF16, out=FAKE_MIS) == m.ERR_INVALID
+    assert b"out not 16-byte aligned" in m.lib().nvfp4moe_last_error_detail()
+
+
+def _mx(**over):
+    return m.lib().mxfp4_grouped_gemm(ctypes.byref(_gemm_args(**over)), None)
+
+
+def test_mx_gemm_validation():
+    L = m.lib()
+    assert L.mxfp4_grouped_gemm(None, None) == m.ERR_INVALID
+    assert _mx(K=48) == m.ERR_INVALID
+    assert _mx(N=24) == m.ERR_INVALID
+    assert _mx(E=0) == m.ERR_INVALID
+    assert _mx(a_codes=FAKE_MIS) == m.ERR_INVALID
+    assert _mx(out=None) == m.ERR_INVALID
+    assert _mx(out=FAKE + 4) == m.ERR_INVALID
+    assert b"out not 16-byte aligned" in L.nvfp4moe_last_error_detail()
+    assert _mx(epilogue=m.EPI_SWIGLU_NVFP4, N=96, out_codes=FAKE, out_scales=FAKE) == m.ERR_INVALID
+    assert _mx(epilogue=m.EPI_SWIGLU_NVFP4, out_codes=None, out_scales=FAKE) == m.ERR_INVALID
+    assert _mx(epilogue=m.EPI_COMBINE_F32, out_rows=4, row_token=FAKE, row_weight=FAKE) == m.ERR_UNSUPPORTED
+
+
+def _fp8(**over):
+    a = m.Fp8GemmArgs(a_codes=FAKE, a_scales=FAKE, a_rows=None, a_rows_total=16, b_packed=FAKE, b_scales=FAKE,
+                      offsets=FAKE, E=4, N=64, K=256, m_total=16, epilogue=m.EPI_BF16, out=FAKE,
+                      max_rows_per_expert_hint=0)
+    for k_, v in over.items():
+        setattr(a, k_, v)
+    return m.lib().fp8_grouped_gemm(ctypes.byref(a), None)
+
+
+def test_fp8_gemm_validation():
+    L = m.lib()
+    assert L.fp8_grouped_gemm(None, None) == m.ERR_INVALID
+    assert _fp8(K=64) == m.ERR_INVALID
+    assert _fp8(N=24) == m.ERR_INVALID
+    assert _fp8(E=0) == m.ERR_INVALID
+    assert _fp8(b_packed=None) == m.ERR_INVALID
+    assert _fp8(a_codes=FAKE_MIS) == m.ERR_INVALID
+    assert _fp8(a_scales=FAKE_MIS) == m.ERR_INVALID
+    assert _fp8(out=None) == m.ERR_INVALID
+    assert _fp8(out=FAKE + 8) == m.ERR_INVALID
+    assert b"out not 16-byte aligned" in L.nvfp4moe_last_error_detail()
+    assert _fp8(epilogue=m.EPI_SWIGLU_NVFP4) == m.ERR_UNSUPPORTED
+    assert _fp8(E=5000) == m.ERR_UNSUPPORTED
+
+
 def test_swiglu_and_combine_validation():
     L = m.lib()
     assert L.moe_swiglu(FAKE, m.F32, 4, 24, FAKE, None, FAKE, FAKE, None, 0, None) == m.ERR_INVALID
