@@ -372,8 +372,10 @@ def mx_bench(cfg, args):
 def fp8_bench(cfg, args):
     """The FP8 block-scaled variant (secondary measurements, not the reported
     metric).  MoE workloads: the FP8 layer step (route + permute, FP8
-    quantisation of x, gate_up grouped GEMM with float32 rows, SwiGLU + FP8
-    requant, down grouped GEMM with bf16 rows, combine), weights quantised with
+    quantisation of x, gate_up grouped GEMM with SwiGLU + FP8 requant in its
+    epilogue below 256 rows per expert (--swiglu separate, or from 256 rows:
+    float32 rows and the separate SwiGLU kernel), down grouped GEMM with bf16
+    rows, combine), weights quantised with
     128 x 128 blocks and repacked (untimed), two weight copies alternating;
     roofline of gate_up against HBM.  Dense workload: the GEMM against the
     dense FP8 MFMA peak."""
@@ -433,22 +435,26 @@ def fp8_bench(cfg, args):
         w_gu, w_dn = wl.torch_expert_weights(cfg, dev, copy=c)
         copies.append(quantize_expert_weights_fp8(w_gu, w_dn))
         del w_gu, w_dn
-    layer = FP8MoELayer(T, H, I, E, k, dev)
+    layer = FP8MoELayer(T, H, I, E, k, dev, swiglu=args.swiglu)
     ms = timed(lambda i: layer.forward(logits, x, copies[i % 2]), args.steps)
     marks = [[ev() for _ in range(7)] for _ in range(args.steps)]
     for i in range(args.steps):
         layer.forward(logits, x, copies[i % 2], marks=marks[i])
     torch.cuda.synchronize()
-    names = ["route_permute", "quantize_x", "gate_up", "swiglu_quantize", "down", "combine"]
+    # fused SwiGLU: marks 3 and 4 both follow gate_up, whose stage includes it
+    names = ["route_permute", "quantize_x", "gate_up_swiglu" if layer.fused else "gate_up",
+             None if layer.fused else "swiglu_quantize", "down", "combine"]
     stage_ms = {n: round(float(np.mean([m_[j].elapsed_time(m_[j + 1]) for m_ in marks])), 5)
-                for j, n in enumerate(names)}
-    gu_ms = stage_ms["gate_up"]
+                for j, n in enumerate(names) if n}
+    gu_ms = stage_ms["gate_up_swiglu" if layer.fused else "gate_up"]
     counts = layer.routing.counts.cpu().numpy()
     touched = int((counts > 0).sum())
     gu_w = 2 * I * H * (1 + 4 / (128 * 128))        # E4M3 codes + one float32 per 128 x 128 block
     dn_w = H * I * (1 + 4 / (128 * 128))
     weight_bytes = touched * (gu_w + dn_w)
-    gu_alg = touched * gu_w + T * H * (1 + 4 / 128) + M * 2 * I * 4
+    # gate_up writes float32 rows, or (fused SwiGLU) h in FP8 with one float32 per 128 values
+    gu_out = M * I * (1 + 4 / 128) if layer.fused else M * 2 * I * 4
+    gu_alg = touched * gu_w + T * H * (1 + 4 / 128) + gu_out
     gu_gbs = gu_alg / (gu_ms * 1e-3) / 1e9
     # from 256 rows per expert gate_up runs the 256 x 256 tile, bound by the
     # matrix cores: its roofline is then the dense FP8 MFMA peak
@@ -460,7 +466,8 @@ def fp8_bench(cfg, args):
                 "frac": round(gu_tflops / MFMA_FP8_PEAK_TFLOPS, 4), "traffic": None,
                 "flops_per_launch": gu_flops, "avg_launch_ms": round(gu_ms, 5), "hbm_gbs": round(gu_gbs, 2)}
     else:
-        roof = {"kernel": "k_fp8_gemm gate_up (float32 rows)", "bound": "hbm", "achieved": round(gu_gbs, 2),
+        roof = {"kernel": "k_fp8_gemm gate_up + SwiGLU/FP8 requant epilogue" if layer.fused
+                else "k_fp8_gemm gate_up (float32 rows)", "bound": "hbm", "achieved": round(gu_gbs, 2),
                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gu_gbs / HBM_PEAK_GBS, 4), "traffic": None,
                 "alg_bytes_per_launch": int(gu_alg), "avg_launch_ms": round(gu_ms, 5)}
     print(json.dumps({
@@ -472,7 +479,7 @@ def fp8_bench(cfg, args):
         "tflops": round(2.0 * M * 3 * I * H / (ms * 1e-3) / 1e12, 3), "weight_bytes": int(weight_bytes),
         "stage_ms": stage_ms,
         "config": {"workload": f"{'decode' if T <= 2048 else 'prefill'}_moe_T{T}_H{H}_I{I}_E{E}_top{k}_{cfg.routing}",
-                   "format": "fp8_block128", "weight_copies": 2},
+                   "format": "fp8_block128", "swiglu": "fused" if layer.fused else "separate", "weight_copies": 2},
         "roofline": roof}), flush=True)
 
 

@@ -73,7 +73,7 @@ class Fp8GemmArgs(ctypes.Structure):
         ("a_rows_total", ctypes.c_int64), ("b_packed", ctypes.c_void_p), ("b_scales", ctypes.c_void_p),
         ("offsets", ctypes.c_void_p), ("E", ctypes.c_int32), ("N", ctypes.c_int32), ("K", ctypes.c_int32),
         ("m_total", ctypes.c_int64), ("epilogue", ctypes.c_int32), ("out", ctypes.c_void_p),
-        ("max_rows_per_expert_hint", ctypes.c_int32),
+        ("max_rows_per_expert_hint", ctypes.c_int32), ("out_codes", ctypes.c_void_p), ("out_scales", ctypes.c_void_p),
     ]
 
 
@@ -649,7 +649,9 @@ def fp8_grouped_gemm(a: FP8Tensor, b_packed, b_scales, offsets, *, N: int, m_tot
                      epilogue: int = EPI_F32, out=None, max_rows_per_expert_hint: int = 0, stream=None):
     """Grouped FP8 GEMM (see include/nvfp4moe.h): a [rows, K] (1 x 128 blocks),
     b_packed from fp8_weight_repack, b_scales float32 [E, ceil(N/128), K/128],
-    offsets int32 [E+1].  Epilogues F32 or BF16."""
+    offsets int32 [E+1].  Epilogues F32 or BF16 (returns out), or
+    EPI_SWIGLU_NVFP4 read as SwiGLU + FP8 requant of h (N = 2I, I % 128 == 0;
+    out: an FP8Tensor for h or None; returns it)."""
     import torch
     rows_a, K = a.codes.shape
     E = b_scales.shape[0]
@@ -672,8 +674,26 @@ def fp8_grouped_gemm(a: FP8Tensor, b_packed, b_scales, offsets, *, N: int, m_tot
         _need(a_rows, torch.int32, "a_rows")
         if a_rows.numel() < m_total:
             raise ValueError("a_rows shorter than m_total")
+    if epilogue == EPI_SWIGLU_NVFP4:
+        if N % (2 * FP8_BLOCK) != 0:
+            raise ValueError("fp8_grouped_gemm: SwiGLU needs N = 2I with I % 128 == 0")
+        I = N // 2
+        if out is None:
+            out = FP8Tensor(torch.empty((m_total, I), dtype=torch.uint8, device=dev),
+                            torch.empty((m_total, I // FP8_BLOCK), dtype=torch.float32, device=dev), 1)
+        _need(out.codes, torch.uint8, "out.codes")
+        _need(out.scales, torch.float32, "out.scales")
+        if tuple(out.codes.shape) != (m_total, I) or tuple(out.scales.shape) != (m_total, I // FP8_BLOCK):
+            raise ValueError("out codes/scales must be [m_total, I] and [m_total, I/128]")
+        args = Fp8GemmArgs(a_codes=a.codes.data_ptr(), a_scales=a.scales.data_ptr(), a_rows=_ptr(a_rows),
+                           a_rows_total=rows_a, b_packed=b_packed.data_ptr(), b_scales=b_scales.data_ptr(),
+                           offsets=offsets.data_ptr(), E=E, N=N, K=K, m_total=m_total, epilogue=epilogue, out=None,
+                           max_rows_per_expert_hint=max_rows_per_expert_hint, out_codes=out.codes.data_ptr(),
+                           out_scales=out.scales.data_ptr())
+        _check(lib().fp8_grouped_gemm(ctypes.byref(args), _stream(stream)))
+        return out
     if epilogue not in (EPI_F32, EPI_BF16):
-        raise ValueError("fp8_grouped_gemm: epilogue F32 or BF16")
+        raise ValueError("fp8_grouped_gemm: epilogue F32, BF16 or SwiGLU")
     want = torch.float32 if epilogue == EPI_F32 else torch.bfloat16
     if out is None:
         out = torch.empty((m_total, N), dtype=want, device=dev)

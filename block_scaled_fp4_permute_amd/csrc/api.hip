@@ -557,10 +557,18 @@ int fp8_grouped_gemm(const nvfp4moe_fp8_gemm_args* a, void* stream) {
   if (a->E > 4096) return fail(NVFP4MOE_ERR_UNSUPPORTED, "fp8_grouped_gemm: E > 4096");
   if (a->m_total >= (int64_t(1) << 31) || prod_ge(a->a_rows_total, a->K, int64_t(1) << 31))
     return fail(NVFP4MOE_ERR_UNSUPPORTED, "fp8_grouped_gemm: A codes of 2 GiB or more");
-  if (a->epilogue != NVFP4MOE_EPI_F32 && a->epilogue != NVFP4MOE_EPI_BF16)
-    return fail(NVFP4MOE_ERR_UNSUPPORTED, "fp8_grouped_gemm: epilogue %d (F32 or BF16)", a->epilogue);
-  if (!a->out && a->m_total > 0) return fail(NVFP4MOE_ERR_INVALID, "fp8_grouped_gemm: out is NULL");
-  if (!aligned(a->out, 16)) return fail(NVFP4MOE_ERR_INVALID, "fp8_grouped_gemm: out not 16-byte aligned");
+  if (a->epilogue == NVFP4MOE_EPI_SWIGLU_NVFP4) {
+    if (a->N % (2 * 128) != 0)
+      return fail(NVFP4MOE_ERR_INVALID, "fp8_grouped_gemm: SwiGLU needs N = 2I with I %% 128 == 0 (N=%d)", a->N);
+    if ((!a->out_codes || !a->out_scales) && a->m_total > 0)
+      return fail(NVFP4MOE_ERR_INVALID, "fp8_grouped_gemm: SwiGLU needs out_codes and out_scales");
+    if (!aligned(a->out_scales, 4)) return fail(NVFP4MOE_ERR_INVALID, "fp8_grouped_gemm: out_scales misaligned");
+  } else {
+    if (a->epilogue != NVFP4MOE_EPI_F32 && a->epilogue != NVFP4MOE_EPI_BF16)
+      return fail(NVFP4MOE_ERR_UNSUPPORTED, "fp8_grouped_gemm: epilogue %d (F32, BF16 or SwiGLU)", a->epilogue);
+    if (!a->out && a->m_total > 0) return fail(NVFP4MOE_ERR_INVALID, "fp8_grouped_gemm: out is NULL");
+    if (!aligned(a->out, 16)) return fail(NVFP4MOE_ERR_INVALID, "fp8_grouped_gemm: out not 16-byte aligned");
+  }
   if (a->m_total == 0) return ok();
   nvfp4::Fp8Params prm{};
   prm.a_codes = a->a_codes;
@@ -575,6 +583,8 @@ int fp8_grouped_gemm(const nvfp4moe_fp8_gemm_args* a, void* stream) {
   prm.m_total = static_cast<int>(a->m_total);
   prm.a_rows_total = static_cast<int>(a->a_rows_total);
   prm.out = a->out;
+  prm.out_codes = a->out_codes;
+  prm.out_scales = a->out_scales;
   return hip_status(nvfp4::launch_fp8_gemm(prm, a->epilogue, a->m_total, a->max_rows_per_expert_hint,
                                            static_cast<hipStream_t>(stream)),
                     "fp8_grouped_gemm");

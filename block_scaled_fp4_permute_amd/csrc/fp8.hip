@@ -316,10 +316,12 @@ __device__ __forceinline__ i32x8 fp8_frag(const u32x4& lo, const u32x4& hi) {
 
 // one K step: per (row tile, column tile) the block's partial sum, scaled
 // into the accumulator by the row's block scale and the wave's weight block
-// scale (a wave's 64 columns lie in one 128-row weight block)
-template <int MTA, int WN>
+// scale (a wave's 64 columns lie in one 128-row weight block).  SW (the
+// SwiGLU arrangement): the wave's gate tiles (the first WN / 2) and its up
+// tiles lie in two weight blocks, scales sb and sbu.
+template <int MTA, int WN, bool SW = false>
 __device__ __forceinline__ void fp8_step(const uint8_t* __restrict__ a_lds, const Fp8B (&B)[WN], float sb,
-                                         float4v (&acc)[4][WN]) {
+                                         float sbu, float4v (&acc)[4][WN]) {
   const int lane = threadIdx.x & 63;
   const int lr = lane & 15, g = lane >> 4;
 #pragma unroll
@@ -335,43 +337,48 @@ __device__ __forceinline__ void fp8_step(const uint8_t* __restrict__ a_lds, cons
                                                                  kFp8FmtE4M3, 0, kE8M0One, 0, kE8M0One);
     }
     const float4v sab = sa * sb;
+    float4v sabu = sab;
+    if constexpr (SW) sabu = sa * sbu;
 #pragma unroll
     for (int j = 0; j < WN; ++j)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) acc[r][j][i] = __builtin_fmaf(part[j][i], sab[i], acc[r][j][i]);
+      for (int i = 0; i < 4; ++i)
+        acc[r][j][i] = __builtin_fmaf(part[j][i], (SW && j >= WN / 2) ? sabu[i] : sab[i], acc[r][j][i]);
   }
 }
 
 // Two steps per iteration, branch free: A for step s + 1 goes to the other
 // LDS buffer while step s runs; steps past the last read the last step's
 // weights against zero activation codes (nothing added).
-template <int MTA, int WN, bool NT>
+template <int MTA, int WN, bool NT, bool SW = false>
 __device__ __forceinline__ void fp8_loop(const Fp8AStage& AS, const uint8_t* const (&tiles)[WN],
-                                         const float* __restrict__ bsc, int nsteps, int rows,
-                                         uint8_t* __restrict__ lds0, uint8_t* __restrict__ lds1,
+                                         const float* __restrict__ bsc, const float* __restrict__ bscu, int nsteps,
+                                         int rows, uint8_t* __restrict__ lds0, uint8_t* __restrict__ lds1,
                                          float4v (&acc)[4][WN]) {
   Fp8B B0[WN], B1[WN];
   Fp8ARegs ra;
   fp8a_load(AS, ra, 0, nsteps);
   fp8b_load<WN, NT>(tiles, B0, 0, nsteps);
-  float s0 = bsc[0];
+  float s0 = bsc[0], u0 = SW ? bscu[0] : 0.0f;
   fp8b_load<WN, NT>(tiles, B1, 1, nsteps);
-  float s1 = bsc[min(1, nsteps - 1)];
+  float s1 = bsc[min(1, nsteps - 1)], u1 = SW ? bscu[min(1, nsteps - 1)] : 0.0f;
   fp8a_store(AS, ra, true, rows, lds0);
   fp8a_load(AS, ra, 1, nsteps);
   __syncthreads();
   for (int st = 0; st < nsteps; st += 2) {
-    fp8_step<MTA, WN>(lds0, B0, s0, acc);
+    fp8_step<MTA, WN, SW>(lds0, B0, s0, u0, acc);
     fp8a_store(AS, ra, st + 1 < nsteps, rows, lds1);
     fp8a_load(AS, ra, st + 2, nsteps);
     fp8b_load<WN, NT>(tiles, B0, st + 2, nsteps);
     s0 = bsc[min(st + 2, nsteps - 1)];
+    if constexpr (SW) u0 = bscu[min(st + 2, nsteps - 1)];
     __syncthreads();
-    fp8_step<MTA, WN>(lds1, B1, s1, acc);
+    fp8_step<MTA, WN, SW>(lds1, B1, s1, u1, acc);
     fp8a_store(AS, ra, st + 2 < nsteps, rows, lds0);
     fp8a_load(AS, ra, st + 3, nsteps);
     fp8b_load<WN, NT>(tiles, B1, st + 3, nsteps);
     s1 = bsc[min(st + 3, nsteps - 1)];
+    if constexpr (SW) u1 = bscu[min(st + 3, nsteps - 1)];
     __syncthreads();
   }
 }
@@ -392,6 +399,53 @@ __device__ __forceinline__ void fp8_store_tile(const Fp8Params& p, const float4v
   }
 }
 
+// SwiGLU epilogue: a task's 128 h columns are one 1 x 128 block of every row.
+// Wave w holds gate tiles 0, 1 and up tiles 2, 3 of h columns [32 w, +32):
+// h = silu(gate) * up in float32, the row's maximum |h| over its 32 columns
+// (lanes of one 16-lane row group), then over the four waves through LDS;
+// scale amax / 448 (1 for an all-zero block) and E4M3 codes of h / scale,
+// as the separate SwiGLU kernel computes them from the float32 rows.
+__device__ __forceinline__ void fp8_swiglu_epilogue(const Fp8Params& p, const float4v (&acc)[4][4], int mt_active,
+                                                    int rows, int prow0, int nt, float* __restrict__ s_amax) {
+  const int lane = threadIdx.x & 63;
+  const int lr = lane & 15, lg = lane >> 4;
+  const int wave = threadIdx.x >> 6;
+  const int I = p.N / 2;
+  const int nbr = I / kFp8Block;
+  const int hc0 = nt * kFp8Block + 32 * wave;
+  float h[4][2][4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    if (r >= mt_active) continue;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      h[r][0][i] = silu_f32(acc[r][0][i]) * acc[r][2][i];
+      h[r][1][i] = silu_f32(acc[r][1][i]) * acc[r][3][i];
+      float m = fmaxf(fabsf(h[r][0][i]), fabsf(h[r][1][i]));
+#pragma unroll
+      for (int d = 8; d >= 1; d >>= 1) m = fmaxf(m, __shfl_xor(m, d));
+      if (lr == 0) s_amax[64 * wave + 16 * r + 4 * lg + i] = m;
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    if (r >= mt_active) continue;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = 16 * r + 4 * lg + i;
+      const float m = fmaxf(fmaxf(s_amax[row], s_amax[64 + row]), fmaxf(s_amax[128 + row], s_amax[192 + row]));
+      const float s = m > 0.0f ? m / 448.0f : 1.0f;
+      if (row < rows) {
+        uint8_t* crow = p.out_codes + static_cast<size_t>(prow0 + row) * I + hc0 + lr;
+        crow[0] = static_cast<uint8_t>(fp8_encode(h[r][0][i], s));
+        crow[16] = static_cast<uint8_t>(fp8_encode(h[r][1][i], s));
+        if (wave == 0 && lr == 0) p.out_scales[static_cast<size_t>(prow0 + row) * nbr + nt] = s;
+      }
+    }
+  }
+}
+
 // the task map's view of the FP8 problem (offsets, experts, rows, tiles)
 __device__ __forceinline__ GemmParams fp8_map_params(const Fp8Params& p, int n_tiles) {
   GemmParams g{};
@@ -408,8 +462,10 @@ __device__ __forceinline__ GemmParams fp8_map_params(const Fp8Params& p, int n_t
 template <int EPI, bool NT>
 __global__ __launch_bounds__(256, 2) void k_fp8_gemm(const Fp8Params p, int n_tiles) {
   constexpr int WN = 4, BN = 4 * WN * 16;
+  constexpr bool SW = EPI == EPI_SWIGLU;
   __shared__ __attribute__((aligned(16))) uint8_t a_lds[2][kFp8ALds];
-  static_assert(fits_lds(sizeof(a_lds), 2), "FP8 A staging exceeds the LDS of two workgroups per CU");
+  __shared__ float s_amax[SW ? 4 * 64 : 1];
+  static_assert(fits_lds(sizeof(a_lds) + sizeof(s_amax), 2), "FP8 A staging exceeds the LDS of two workgroups per CU");
   int e, m0, nt;
   bool narrow;
   const GemmParams map = fp8_map_params(p, n_tiles);
@@ -429,32 +485,41 @@ __global__ __launch_bounds__(256, 2) void k_fp8_gemm(const Fp8Params p, int n_ti
   const uint8_t* tiles[WN];
   int col0[WN];
   bool cok[WN];
-  const int wcol = nt * BN + wave * WN * 16;      // the wave's first column, a multiple of 64
+  // plain: the wave's 64 columns from wcol; SwiGLU: gate columns [wcol, +32)
+  // and up columns I + [wcol, +32), wcol = 128 nt + 32 wave (I % 128 == 0)
+  const int wcol = SW ? nt * kFp8Block + wave * 32 : nt * BN + wave * WN * 16;
 #pragma unroll
   for (int j = 0; j < WN; ++j) {
-    col0[j] = wcol + j * 16;
+    col0[j] = SW ? (j < 2 ? wcol + 16 * j : N / 2 + wcol + 16 * (j - 2)) : wcol + j * 16;
     cok[j] = col0[j] + lr < N;
     const int rt = min(col0[j] / 16, ntr - 1);
     tiles[j] = p.b_packed + (static_cast<size_t>(e) * ntr + rt) * nsteps * kFp8Tile;
   }
   const float* bsc = p.b_scales + (static_cast<size_t>(e) * nsb + min(wcol, N - 1) / kFp8Block) * nsteps;
+  const float* bscu = SW ? p.b_scales + (static_cast<size_t>(e) * nsb + min(N / 2 + wcol, N - 1) / kFp8Block) * nsteps
+                         : bsc;
   float4v acc[4][WN];
 #pragma unroll
   for (int r = 0; r < 4; ++r)
 #pragma unroll
     for (int j = 0; j < WN; ++j) acc[r][j] = float4v{0.f, 0.f, 0.f, 0.f};
   switch (mt_active) {
-    case 1: fp8_loop<1, WN, NT>(AS, tiles, bsc, nsteps, rows, a_lds[0], a_lds[1], acc); break;
-    case 2: fp8_loop<2, WN, NT>(AS, tiles, bsc, nsteps, rows, a_lds[0], a_lds[1], acc); break;
-    case 3: fp8_loop<3, WN, NT>(AS, tiles, bsc, nsteps, rows, a_lds[0], a_lds[1], acc); break;
-    default: fp8_loop<4, WN, NT>(AS, tiles, bsc, nsteps, rows, a_lds[0], a_lds[1], acc); break;
+    case 1: fp8_loop<1, WN, NT, SW>(AS, tiles, bsc, bscu, nsteps, rows, a_lds[0], a_lds[1], acc); break;
+    case 2: fp8_loop<2, WN, NT, SW>(AS, tiles, bsc, bscu, nsteps, rows, a_lds[0], a_lds[1], acc); break;
+    case 3: fp8_loop<3, WN, NT, SW>(AS, tiles, bsc, bscu, nsteps, rows, a_lds[0], a_lds[1], acc); break;
+    default: fp8_loop<4, WN, NT, SW>(AS, tiles, bsc, bscu, nsteps, rows, a_lds[0], a_lds[1], acc); break;
   }
   const int prow0 = row0 + m0;
+  if constexpr (SW) {
+    fp8_swiglu_epilogue(p, acc, mt_active, rows, prow0, nt, s_amax);
+  } else {
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    if (r >= mt_active) continue;
+    for (int r = 0; r < 4; ++r) {
+      if (r >= mt_active) continue;
 #pragma unroll
-    for (int j = 0; j < WN; ++j) fp8_store_tile<EPI>(p, acc[r][j], prow0 + 16 * r, rows - 16 * r, col0[j] + lr, cok[j]);
+      for (int j = 0; j < WN; ++j)
+        fp8_store_tile<EPI>(p, acc[r][j], prow0 + 16 * r, rows - 16 * r, col0[j] + lr, cok[j]);
+    }
   }
 }
 
@@ -830,6 +895,17 @@ hipError_t launch_fp8_gemm(const Fp8Params& p, int epilogue, int64_t m_total, in
   if (blocks >= (int64_t(1) << 31)) return hipErrorInvalidConfiguration;
   const int64_t rows_per_expert = hint > 0 ? hint : m_total / p.E;
   const bool nt = rows_per_expert < 64;
+  if (epilogue == EPI_SWIGLU) {
+    // SwiGLU + FP8 requant: the decode tile at any size, one task per 128 h
+    // columns (a whole 1 x 128 block of h per row)
+    const int sw_tiles = p.N / 2 / kFp8Block;
+    const int64_t sblocks = ((((m_total + 63) / 64 + p.E) * sw_tiles) + 7) / 8 * 8;
+    if (sblocks >= (int64_t(1) << 31)) return hipErrorInvalidConfiguration;
+    const dim3 sgrid(static_cast<unsigned>(sblocks));
+    if (nt) hipLaunchKernelGGL((k_fp8_gemm<EPI_SWIGLU, true>), sgrid, dim3(256), 0, stream, p, sw_tiles);
+    else hipLaunchKernelGGL((k_fp8_gemm<EPI_SWIGLU, false>), sgrid, dim3(256), 0, stream, p, sw_tiles);
+    return hipGetLastError();
+  }
   if (p.K <= 2 * kFp8Block && rows_per_expert < kFp8LRows) {
     // one or two K steps (the down GEMM): the stream-N kernel
     constexpr int UPW = 6;

@@ -85,6 +85,8 @@ struct Fp8Params {
   const int32_t* offsets;
   int E, N, K, m_total, a_rows_total;
   void* out;
+  uint8_t* out_codes;          // SwiGLU epilogue: h E4M3 codes [m_total, N/2]
+  float* out_scales;           // SwiGLU epilogue: h block scales [m_total, N/256]
 };
 
 hipError_t launch_fp8_quantize(const void* x, int dtype, int64_t batch, int64_t rows, int64_t cols, int block_rows,

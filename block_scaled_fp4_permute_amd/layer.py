@@ -318,13 +318,21 @@ def quantize_expert_weights_fp8(w_gu: torch.Tensor, w_dn: torch.Tensor) -> FP8Ex
 class FP8MoELayer:
     """Preallocated FP8 block-scaled MoE layer for T tokens, reusing the routing,
     permutation and combine of the NVFP4 layer: route + permute, FP8
-    quantisation of x (1 x 128 blocks), gate_up grouped GEMM (float32 rows,
-    A gathered through the permutation), SwiGLU + FP8 requantisation of h,
-    down grouped GEMM (bf16 rows), weighted gather combine."""
+    quantisation of x (1 x 128 blocks), gate_up grouped GEMM (A gathered
+    through the permutation) with SwiGLU + FP8 requantisation of h, down
+    grouped GEMM (bf16 rows), weighted gather combine.
 
-    def __init__(self, T: int, H: int, I: int, E: int, k: int, device):
+    ``swiglu``: "fused" runs the SwiGLU + requant as gate_up's epilogue below
+    256 rows per expert (at and above that gate_up runs the 256 x 256 tile,
+    which writes float32 rows for the separate kernel); "separate" always
+    writes the float32 rows.  Both give the same h, bit for bit."""
+
+    def __init__(self, T: int, H: int, I: int, E: int, k: int, device, swiglu: str = "fused"):
         from . import FP8_BLOCK, FP8Tensor
+        if swiglu not in ("fused", "separate"):
+            raise ValueError("swiglu: 'fused' or 'separate'")
         self.T, self.H, self.I, self.E, self.k = T, H, I, E, k
+        self.fused = swiglu == "fused" and (T * k) // E < 256 and I % FP8_BLOCK == 0
         dev = torch.device(device)
         i32 = dict(dtype=torch.int32, device=dev)
         f32 = dict(dtype=torch.float32, device=dev)
@@ -335,7 +343,7 @@ class FP8MoELayer:
                                torch.empty(M, **f32))
         self.route_ws = torch.empty(max(16, lib().moe_route_permute_workspace_size(T, E, k)), **u8)
         self.xq = FP8Tensor(torch.empty((T, H), **u8), torch.empty((T, H // FP8_BLOCK), **f32), 1)
-        self.y1 = torch.empty((M, 2 * I), **f32)
+        self.y1 = None if self.fused else torch.empty((M, 2 * I), **f32)
         self.hq = FP8Tensor(torch.empty((M, I), **u8), torch.empty((M, I // FP8_BLOCK), **f32), 1)
         self.y2 = torch.empty((M, H), dtype=torch.bfloat16, device=dev)
         self.out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
@@ -344,8 +352,9 @@ class FP8MoELayer:
                 marks=None) -> torch.Tensor:
         """One layer step; ``marks``: optional 7 events recorded before routing
         and after each stage (route, quantise x, gate_up, SwiGLU + requant,
-        down, combine)."""
-        from . import fp8_grouped_gemm, fp8_quantize, fp8_swiglu_quantize
+        down, combine; with the fused SwiGLU marks 3 and 4 both follow
+        gate_up)."""
+        from . import EPI_SWIGLU_NVFP4, fp8_grouped_gemm, fp8_quantize, fp8_swiglu_quantize
         T, k, M = self.T, self.k, self.T * self.k
         hint = M // self.E
 
@@ -358,12 +367,19 @@ class FP8MoELayer:
         mark(1)
         fp8_quantize(x, 1, out=self.xq, stream=stream)
         mark(2)
-        fp8_grouped_gemm(self.xq, w.gu_packed, w.gu.scales, r.offsets, N=2 * self.I, m_total=M,
-                         a_rows=r.perm_src_token, epilogue=EPI_F32, out=self.y1, max_rows_per_expert_hint=hint,
-                         stream=stream)
-        mark(3)
-        fp8_swiglu_quantize(self.y1, out=self.hq, stream=stream)
-        mark(4)
+        if self.fused:
+            fp8_grouped_gemm(self.xq, w.gu_packed, w.gu.scales, r.offsets, N=2 * self.I, m_total=M,
+                             a_rows=r.perm_src_token, epilogue=EPI_SWIGLU_NVFP4, out=self.hq,
+                             max_rows_per_expert_hint=hint, stream=stream)
+            mark(3)
+            mark(4)
+        else:
+            fp8_grouped_gemm(self.xq, w.gu_packed, w.gu.scales, r.offsets, N=2 * self.I, m_total=M,
+                             a_rows=r.perm_src_token, epilogue=EPI_F32, out=self.y1, max_rows_per_expert_hint=hint,
+                             stream=stream)
+            mark(3)
+            fp8_swiglu_quantize(self.y1, out=self.hq, stream=stream)
+            mark(4)
         fp8_grouped_gemm(self.hq, w.dn_packed, w.dn.scales, r.offsets, N=self.H, m_total=M, epilogue=EPI_BF16,
                          out=self.y2, max_rows_per_expert_hint=hint, stream=stream)
         mark(5)

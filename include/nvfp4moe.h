@@ -356,7 +356,13 @@ int fp8_weight_repack(const uint8_t* codes, int32_t E, int32_t N, int32_t K, uin
  *   y[p, n] = sum_kb sa[r, kb] * sb[e, n / 128, kb] * sum_{k in block kb} A[r, k] B[e, n, k]
  * Each block's partial sum comes from the FP8 matrix instruction in float32
  * and enters the float32 accumulator scaled by sa * sb.  Same grouping and
- * bounds rules as nvfp4_grouped_gemm; epilogues EPI_F32 and EPI_BF16 only. */
+ * bounds rules as nvfp4_grouped_gemm; epilogues EPI_F32, EPI_BF16, and
+ * EPI_SWIGLU_NVFP4 read as SwiGLU + FP8 requantisation of h (the gate_up GEMM
+ * with fp8_swiglu_quantize fused into it, the same bits): N = 2I with
+ * I % 128 == 0, h = silu(y[:, :I]) * y[:, I:], out_codes [m_total, I] E4M3 and
+ * out_scales float32 [m_total, I/128] as fp8_swiglu_quantize writes them.
+ * This epilogue runs the decode tile at every size (the large tile has no
+ * SwiGLU epilogue). */
 typedef struct nvfp4moe_fp8_gemm_args {
   const uint8_t* a_codes;     /* [a_rows_total, K] E4M3, 16-byte aligned */
   const float* a_scales;      /* [a_rows_total, K/128] */
@@ -369,9 +375,11 @@ typedef struct nvfp4moe_fp8_gemm_args {
   int32_t N;                  /* multiple of 16 */
   int32_t K;                  /* multiple of 128 */
   int64_t m_total;
-  int32_t epilogue;           /* NVFP4MOE_EPI_F32 or NVFP4MOE_EPI_BF16 */
-  void* out;                  /* float or bf16 [m_total, N], 16-byte aligned */
+  int32_t epilogue;           /* NVFP4MOE_EPI_F32, NVFP4MOE_EPI_BF16 or NVFP4MOE_EPI_SWIGLU_NVFP4 (see above) */
+  void* out;                  /* float or bf16 [m_total, N], 16-byte aligned; unused for SwiGLU */
   int32_t max_rows_per_expert_hint;  /* as for nvfp4_grouped_gemm: < 64 streams weights non-temporally */
+  uint8_t* out_codes;         /* SwiGLU: h codes [m_total, N/2] */
+  float* out_scales;          /* SwiGLU: h block scales [m_total, N/256], 4-byte aligned */
 } nvfp4moe_fp8_gemm_args;
 int fp8_grouped_gemm(const nvfp4moe_fp8_gemm_args* args, void* stream);
 

@@ -175,8 +175,14 @@ int main() {
     expect("fp8 gemm huge A", fp8_grouped_gemm(&a, nullptr), NVFP4MOE_ERR_UNSUPPORTED);
     a = fp8_args(); a.E = 5000;
     expect("fp8 gemm E", fp8_grouped_gemm(&a, nullptr), NVFP4MOE_ERR_UNSUPPORTED);
-    a = fp8_args(); a.epilogue = NVFP4MOE_EPI_SWIGLU_NVFP4;
+    a = fp8_args(); a.epilogue = NVFP4MOE_EPI_COMBINE_F32;
     expect("fp8 gemm epilogue", fp8_grouped_gemm(&a, nullptr), NVFP4MOE_ERR_UNSUPPORTED);
+    a = fp8_args(); a.epilogue = NVFP4MOE_EPI_SWIGLU_NVFP4;
+    expect("fp8 gemm swiglu N", fp8_grouped_gemm(&a, nullptr), NVFP4MOE_ERR_INVALID);
+    a = fp8_args(); a.epilogue = NVFP4MOE_EPI_SWIGLU_NVFP4; a.N = 512;
+    expect("fp8 gemm swiglu outputs", fp8_grouped_gemm(&a, nullptr), NVFP4MOE_ERR_INVALID);
+    a.out_codes = p<uint8_t>(F); a.out_scales = p<float>(FM);
+    expect("fp8 gemm swiglu scales misaligned", fp8_grouped_gemm(&a, nullptr), NVFP4MOE_ERR_INVALID);
     a = fp8_args(); a.m_total = 0;
     expect("fp8 gemm empty", fp8_grouped_gemm(&a, nullptr), NVFP4MOE_OK);
     a = fp8_args(); a.out = FM;

@@ -198,7 +198,10 @@ def test_fp8_gemm_validation():
     assert _fp8(out=None) == m.ERR_INVALID
     assert _fp8(out=FAKE + 8) == m.ERR_INVALID
     assert b"out not 16-byte aligned" in L.nvfp4moe_last_error_detail()
-    assert _fp8(epilogue=m.EPI_SWIGLU_NVFP4) == m.ERR_UNSUPPORTED
+    assert _fp8(epilogue=m.EPI_COMBINE_F32) == m.ERR_UNSUPPORTED
+    assert _fp8(epilogue=m.EPI_SWIGLU_NVFP4) == m.ERR_INVALID              # N = 64: I not a multiple of 128
+    assert _fp8(epilogue=m.EPI_SWIGLU_NVFP4, N=512) == m.ERR_INVALID       # no out_codes / out_scales
+    assert _fp8(epilogue=m.EPI_SWIGLU_NVFP4, N=512, out_codes=FAKE, out_scales=FAKE_MIS) == m.ERR_INVALID
     assert _fp8(E=5000) == m.ERR_UNSUPPORTED
 
 

@@ -317,6 +317,49 @@ def test_fp8_swiglu_quantize(dtype):
     print(f"fp8 swiglu {dtype}: {ns} scale and {nc} code differences", flush=True)
 
 
+# gate_up with SwiGLU + FP8 requant fused into its epilogue against the two
+# calls it replaces (float32 rows, then fp8_swiglu_quantize): the same block
+# sums in the same order, the same silu and block scale, so the same bits
+SWIGLU_CASES = [
+    # E, counts, I, K, rows_a, hint
+    (3, [5, 0, 17], 128, 256, 30, 0),
+    (4, [1, 100, 64, 65], 256, 512, 300, 0),
+    (8, [16, 31, 33, 64, 2, 0, 129, 8], 384, 384, 283, 100),   # three h blocks, an odd step count
+    (600, None, 128, 256, 500, 0),                              # many experts, several expert groups
+    (2, [200, 3], 256, 6144, 203, 40),                          # the decode K, non-temporal loads
+    (3, [300, 0, 517], 128, 256, 400, 512),                     # a large hint: still the decode tile
+]
+
+
+@pytest.mark.parametrize("case", range(len(SWIGLU_CASES)))
+@pytest.mark.parametrize("gather", [False, True])
+def test_fp8_fused_swiglu_matches_separate(case, gather):
+    E, counts, I, K, rows_a, hint = SWIGLU_CASES[case]
+    rng = np.random.default_rng(500 + case)
+    if counts is None:
+        counts = rng.integers(0, 40, E) * (rng.random(E) < 0.7)
+        counts[rng.choice(E, 4, replace=False)] = [150, 200, 65, 17]
+    counts = np.asarray(counts, np.int64)
+    M = int(counts.sum())
+    N = 2 * I
+    print(f"fp8 fused swiglu case {case} gather={gather} E={E} M={M} I={I} K={K} hint={hint}", flush=True)
+    if not gather:
+        rows_a = max(M, 1)
+    ac, as_, bc, bs = _fp8_operands(40 + 2 * case, E, N, K, rows_a)
+    a_rows = up(rng.integers(0, rows_a, M).astype(np.int32)) if gather else None
+    offsets = up(np.concatenate([[0], np.cumsum(counts)]).astype(np.int32))
+    A, bp, bst = _a(ac, as_), m.fp8_weight_repack(up(bc)), up(bs)
+    y1 = m.fp8_grouped_gemm(A, bp, bst, offsets, N=N, m_total=M, a_rows=a_rows, epilogue=m.EPI_F32,
+                            max_rows_per_expert_hint=min(hint, 255))
+    ref = m.fp8_swiglu_quantize(y1)
+    got = m.fp8_grouped_gemm(A, bp, bst, offsets, N=N, m_total=M, a_rows=a_rows, epilogue=m.EPI_SWIGLU_NVFP4,
+                             max_rows_per_expert_hint=hint)
+    torch.cuda.synchronize()
+    assert torch.equal(got.scales, ref.scales), "block scales differ"
+    diff = (got.codes != ref.codes).nonzero()
+    assert diff.numel() == 0, f"{diff.shape[0]} codes differ, first at {diff[:5].tolist()}"
+
+
 def _swiglu_tol(y1, absdot):
     I = y1.shape[1] // 2
     tol_y = 1e-3 * absdot + 1e-6
@@ -326,7 +369,8 @@ def _swiglu_tol(y1, absdot):
 
 
 @pytest.mark.parametrize("cfg_index", [0, 1])
-def test_fp8_layer_end_to_end(cfg_index):
+@pytest.mark.parametrize("swiglu", ["fused", "separate"])
+def test_fp8_layer_end_to_end(cfg_index, swiglu):
     # FP8MoELayer against the oracle's stages composed the same way: routing
     # and x codes bit for bit, weight codes bit for bit, gate_up within the
     # GEMM tolerance, h flips only within the propagated window, and the output
@@ -334,11 +378,12 @@ def test_fp8_layer_end_to_end(cfg_index):
     # the other way
     from block_scaled_fp4_permute_amd.layer import FP8MoELayer, quantize_expert_weights_fp8
     c = workloads.CONFIGS[cfg_index]
-    print(f"fp8 layer end to end cfg={cfg_index}", flush=True)
+    print(f"fp8 layer end to end cfg={cfg_index} swiglu={swiglu}", flush=True)
     logits, x = workloads.logits(c), workloads.activations(c)
     w_gu, w_dn = workloads.torch_expert_weights(c, DEV)
     wq = quantize_expert_weights_fp8(w_gu, w_dn)
-    layer = FP8MoELayer(c.T, c.H, c.I, c.E, c.k, DEV)
+    layer = FP8MoELayer(c.T, c.H, c.I, c.E, c.k, DEV, swiglu=swiglu)
+    assert layer.fused == (swiglu == "fused")
     out = layer.forward(up(logits), up(x).to(torch.bfloat16), wq)
     torch.cuda.synchronize()
     ids, w = OM.route(logits, c.k)
@@ -355,7 +400,8 @@ def test_fp8_layer_end_to_end(cfg_index):
     assert np.array_equal(down(wq.gu.codes), gc) and np.array_equal(down(wq.gu.scales), gs)
     assert np.array_equal(down(wq.dn.codes), dc) and np.array_equal(down(wq.dn.scales), ds)
     y1, ad1 = F8.fp8_grouped_gemm(xc, xs, gc, gs, offsets, a_rows=src)
-    assert_gemm_close(down(layer.y1), y1, ad1, what="fp8 layer gate_up")
+    if layer.y1 is not None:                         # the float32 rows exist on the separate path only
+        assert_gemm_close(down(layer.y1), y1, ad1, what="fp8 layer gate_up")
     hc, hs, h64 = F8.fp8_swiglu_quantize(y1)
     hc_gpu, hs_gpu = down(layer.hq.codes), down(layer.hq.scales)
     check_requant_fp8(hc_gpu, hs_gpu, h64, _swiglu_tol(y1, ad1), max_flip_frac=0.02, what="fp8 layer h")
