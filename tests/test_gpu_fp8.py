@@ -360,6 +360,28 @@ def test_fp8_fused_swiglu_matches_separate(case, gather):
     assert diff.numel() == 0, f"{diff.shape[0]} codes differ, first at {diff[:5].tolist()}"
 
 
+def test_fp8_fused_swiglu_full_decode_shape():
+    # the fused gate_up the FP8 layer runs at the benchmark's decode workload
+    # (T=2048, H=6144, I=256, E=256, top-8, Zipf routing, gathered rows)
+    # against float32 rows + the separate SwiGLU kernel, every element
+    c = workloads.CONFIGS[2]
+    T, H, I, E, k = c.T, c.H, c.I, c.E, c.k
+    M = T * k
+    print(f"fp8 fused swiglu full shape T={T} H={H} I={I} E={E}", flush=True)
+    r = m.moe_route_permute(up(workloads.logits(c)), k)
+    ac, as_, bc, bs = _fp8_operands(70, E, 2 * I, H, T)
+    A, bp, bst = _a(ac, as_), m.fp8_weight_repack(up(bc)), up(bs)
+    y1 = m.fp8_grouped_gemm(A, bp, bst, r.offsets, N=2 * I, m_total=M, a_rows=r.perm_src_token, epilogue=m.EPI_F32,
+                            max_rows_per_expert_hint=M // E)
+    ref = m.fp8_swiglu_quantize(y1)
+    del y1
+    got = m.fp8_grouped_gemm(A, bp, bst, r.offsets, N=2 * I, m_total=M, a_rows=r.perm_src_token,
+                             epilogue=m.EPI_SWIGLU_NVFP4, max_rows_per_expert_hint=M // E)
+    torch.cuda.synchronize()
+    assert torch.equal(got.scales, ref.scales)
+    assert torch.equal(got.codes, ref.codes)
+
+
 def _swiglu_tol(y1, absdot):
     I = y1.shape[1] // 2
     tol_y = 1e-3 * absdot + 1e-6
