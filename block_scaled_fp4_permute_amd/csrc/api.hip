@@ -2,8 +2,10 @@
 // kernel launches on the caller's stream.  Nothing is allocated here.
 #include <stdio.h>
 #include <stdarg.h>
+#include <stdlib.h>
 
 #include <mutex>
+#include <vector>
 
 #include "../../include/nvfp4moe.h"
 #include "nvfp4_internal.h"
@@ -40,6 +42,67 @@ bool prod_ge(int64_t a, int64_t b, int64_t limit) {
 bool prod_ge(int64_t a, int64_t b, int64_t c, int64_t limit) {
   int64_t r = 0;
   return __builtin_mul_overflow(a, b, &r) || prod_ge(r, c, limit);
+}
+
+// Debug checks (NVFP4MOE_DEBUG set to anything but "" or "0", read at every
+// call): before launching, a call copies the device index arrays it reads to
+// the host and checks them - offsets non-decreasing from 0 to at most
+// m_total, gathered rows and combine rows inside their buffers - and returns
+// NVFP4MOE_ERR_INVALID naming the first bad entry.  Without the checks the
+// kernels clamp such entries (wrong rows, never an access out of bounds).
+// The copies synchronise the stream: for debugging, not for graph capture.
+bool debug_checks() {
+  const char* v = getenv("NVFP4MOE_DEBUG");
+  return v && v[0] && !(v[0] == '0' && v[1] == '\0');
+}
+
+int fetch_ints(const char* fn, const int32_t* d, int64_t n, hipStream_t s, std::vector<int32_t>& h) {
+  h.resize(static_cast<size_t>(n));
+  hipError_t e = hipMemcpyAsync(h.data(), d, static_cast<size_t>(n) * sizeof(int32_t), hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return fail(NVFP4MOE_ERR_HIP, "%s: debug check copy: %s", fn, hipGetErrorString(e));
+  return NVFP4MOE_OK;
+}
+
+// offsets [E+1]: 0, non-decreasing, at most m_total; rows_used: offsets[E]
+int debug_check_offsets(const char* fn, const int32_t* offsets, int32_t E, int64_t m_total, hipStream_t s,
+                        int64_t& rows_used) {
+  std::vector<int32_t> h;
+  const int st = fetch_ints(fn, offsets, int64_t(E) + 1, s, h);
+  if (st != NVFP4MOE_OK) return st;
+  if (h[0] != 0) return fail(NVFP4MOE_ERR_INVALID, "%s: offsets[0] = %d, expected 0", fn, h[0]);
+  for (int32_t e = 0; e < E; ++e)
+    if (h[e + 1] < h[e])
+      return fail(NVFP4MOE_ERR_INVALID, "%s: offsets decrease at expert %d (%d -> %d)", fn, e, h[e], h[e + 1]);
+  if (h[E] > m_total)
+    return fail(NVFP4MOE_ERR_INVALID, "%s: offsets[E] = %d > m_total = %lld", fn, h[E],
+                static_cast<long long>(m_total));
+  rows_used = h[E];
+  return NVFP4MOE_OK;
+}
+
+// the first n entries of an index array inside [0, hi)
+int debug_check_range(const char* fn, const char* what, const int32_t* d, int64_t n, int64_t hi, hipStream_t s) {
+  if (!d || n <= 0) return NVFP4MOE_OK;
+  std::vector<int32_t> h;
+  const int st = fetch_ints(fn, d, n, s, h);
+  if (st != NVFP4MOE_OK) return st;
+  for (int64_t i = 0; i < n; ++i)
+    if (h[i] < 0 || h[i] >= hi)
+      return fail(NVFP4MOE_ERR_INVALID, "%s: %s[%lld] = %d outside [0, %lld)", fn, what, static_cast<long long>(i),
+                  h[i], static_cast<long long>(hi));
+  return NVFP4MOE_OK;
+}
+
+// the checks of a grouped GEMM: offsets, gathered A rows, combine rows
+int debug_check_gemm(const char* fn, const int32_t* offsets, int32_t E, int64_t m_total, const int32_t* a_rows,
+                     int64_t a_rows_total, const int32_t* row_token, int64_t out_rows, hipStream_t s,
+                     const char* a_rows_name = "a_rows") {
+  int64_t used = 0;
+  int st = debug_check_offsets(fn, offsets, E, m_total, s, used);
+  if (st == NVFP4MOE_OK) st = debug_check_range(fn, a_rows_name, a_rows, used, a_rows_total, s);
+  if (st == NVFP4MOE_OK) st = debug_check_range(fn, "row_token", row_token, used, out_rows, s);
+  return st;
 }
 
 constexpr size_t kSmallWs = 4096;   // 1024 partial maxima of the amax reduction
@@ -259,6 +322,12 @@ int nvfp4_grouped_gemm(const nvfp4moe_gemm_args* a, void* stream) {
       return fail(NVFP4MOE_ERR_INVALID, "nvfp4_grouped_gemm: unknown epilogue %d", a->epilogue);
   }
   if (a->m_total == 0) return ok();
+  if (debug_checks()) {
+    const bool comb = a->epilogue == NVFP4MOE_EPI_COMBINE_F32;
+    const int st = debug_check_gemm("nvfp4_grouped_gemm", a->offsets, a->E, a->m_total, a->a_rows, a->a_rows_total,
+                                    comb ? a->row_token : nullptr, a->out_rows, static_cast<hipStream_t>(stream));
+    if (st != NVFP4MOE_OK) return st;
+  }
   nvfp4::GemmParams prm{};
   prm.a_codes = a->a_codes;
   prm.a_scales = a->a_scales;
@@ -341,6 +410,14 @@ int moe_expert_ffn(const nvfp4moe_ffn_args* a, void* workspace, size_t workspace
     return fail(NVFP4MOE_ERR_WORKSPACE, "moe_expert_ffn: workspace %zu < %zu bytes", workspace_bytes, need);
   if (!aligned(workspace, 256)) return fail(NVFP4MOE_ERR_INVALID, "moe_expert_ffn: workspace not 256-byte aligned");
   if (a->m_total == 0) return ok();
+  if (debug_checks()) {
+    const hipStream_t ds = static_cast<hipStream_t>(stream);
+    int st = debug_check_gemm("moe_expert_ffn", a->offsets, a->E, a->m_total, a->perm_src_token, a->x_rows, nullptr, 0,
+                              ds, "perm_src_token");
+    if (st == NVFP4MOE_OK && a->out)
+      st = debug_check_range("moe_expert_ffn", "perm_of_assignment", a->perm_of_assignment, a->m_total, a->m_total, ds);
+    if (st != NVFP4MOE_OK) return st;
+  }
   nvfp4::GemmParams gu{};
   gu.a_codes = a->x_codes;
   gu.a_scales = a->x_scales;
@@ -437,6 +514,11 @@ int mxfp4_grouped_gemm(const nvfp4moe_gemm_args* a, void* stream) {
       return fail(NVFP4MOE_ERR_UNSUPPORTED, "mxfp4_grouped_gemm: epilogue %d (F32, BF16 or SwiGLU)", a->epilogue);
   }
   if (a->m_total == 0) return ok();
+  if (debug_checks()) {
+    const int st = debug_check_gemm("mxfp4_grouped_gemm", a->offsets, a->E, a->m_total, a->a_rows, a->a_rows_total,
+                                    nullptr, 0, static_cast<hipStream_t>(stream));
+    if (st != NVFP4MOE_OK) return st;
+  }
   nvfp4::GemmParams prm{};
   prm.a_codes = a->a_codes;
   prm.a_scales = a->a_scales;
@@ -570,6 +652,11 @@ int fp8_grouped_gemm(const nvfp4moe_fp8_gemm_args* a, void* stream) {
     if (!aligned(a->out, 16)) return fail(NVFP4MOE_ERR_INVALID, "fp8_grouped_gemm: out not 16-byte aligned");
   }
   if (a->m_total == 0) return ok();
+  if (debug_checks()) {
+    const int st = debug_check_gemm("fp8_grouped_gemm", a->offsets, a->E, a->m_total, a->a_rows, a->a_rows_total,
+                                    nullptr, 0, static_cast<hipStream_t>(stream));
+    if (st != NVFP4MOE_OK) return st;
+  }
   nvfp4::Fp8Params prm{};
   prm.a_codes = a->a_codes;
   prm.a_scales = a->a_scales;
@@ -639,6 +726,13 @@ int moe_unpermute_combine(const void* y, int32_t y_dtype, const int32_t* perm_of
   if (H % 8 != 0) return fail(NVFP4MOE_ERR_INVALID, "moe_unpermute_combine: H=%d not a multiple of 8", H);
   if (!aligned(y, 16) || !aligned(out, 16)) return fail(NVFP4MOE_ERR_INVALID, "moe_unpermute_combine: misaligned");
   if (static_cast<int64_t>(T) * k >= (int64_t(1) << 31)) return fail(NVFP4MOE_ERR_UNSUPPORTED, "moe_unpermute_combine: T*k too large");
+  if (debug_checks()) {
+    // the rows the routing calls produce: T * k
+    const int st = debug_check_range("moe_unpermute_combine", "perm_of_assignment", perm_of_assignment,
+                                     static_cast<int64_t>(T) * k, static_cast<int64_t>(T) * k,
+                                     static_cast<hipStream_t>(stream));
+    if (st != NVFP4MOE_OK) return st;
+  }
   return hip_status(nvfp4::launch_combine(y, y_dtype, perm_of_assignment, topk_w, T, k, H, out, out_dtype,
                                           static_cast<hipStream_t>(stream)),
                     "moe_unpermute_combine");

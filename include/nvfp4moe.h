@@ -52,6 +52,18 @@ typedef enum nvfp4moe_status {
   NVFP4MOE_ERR_HIP = 4           /* the HIP runtime rejected a kernel launch */
 } nvfp4moe_status;
 
+/* Index arrays that live on the device (expert offsets, gathered rows,
+ * combine rows) are not read by the host: the kernels clamp entries that
+ * break the documented ranges, which then gives wrong rows but never an
+ * access outside a buffer.  With the environment variable NVFP4MOE_DEBUG set
+ * (to anything but "" or "0"; read at every call) the grouped GEMMs,
+ * moe_expert_ffn and moe_unpermute_combine first copy those arrays to the
+ * host and check them (offsets non-decreasing from 0 to at most m_total,
+ * gathered rows in [0, a_rows_total), combine rows in [0, T * k) or
+ * [0, out_rows)), returning NVFP4MOE_ERR_INVALID with the first bad entry in
+ * nvfp4moe_last_error_detail() before any launch.  The copies synchronise
+ * the stream: a debugging aid, not for use under graph capture. */
+
 typedef enum nvfp4moe_dtype {
   NVFP4MOE_F32 = 0,
   NVFP4MOE_BF16 = 1
