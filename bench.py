@@ -45,6 +45,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", type=int, default=2,
                     help="workload index: 0..3 MoE layers (2 is the reported one), 4 the dense 8192^3 GEMM")
+    ap.add_argument("--tokens", type=int, default=0,
+                    help="MoE workloads: T tokens instead of the workload's own, same recipe otherwise (a sweep "
+                         "over tokens per expert; not the reported line)")
     ap.add_argument("--ffn", choices=["one_launch", "two_launch"], default="one_launch",
                     help="gate_up + down through moe_expert_ffn (one persistent launch at decode sizes) or the two "
                          "grouped-GEMM calls")
@@ -514,6 +517,8 @@ def main():
     lib()
     dev = torch.device("cuda:0")
     cfg = workloads.CONFIGS[args.workload]
+    if args.tokens > 0 and not cfg.dense:
+        cfg = workloads.small_variant(cfg, T=args.tokens)
     if args.format == "fp8":
         fp8_bench(cfg, args)
         return
@@ -553,9 +558,9 @@ def main():
 
     layer = MoELayer(T, H, I, E, k, dev, swiglu=args.swiglu, combine=args.combine, ffn=args.ffn)
     one_call = layer.ffn == "one_launch"
-    # moe_expert_ffn's tile table: one persistent launch from 32 to 127 rows
+    # moe_expert_ffn's tile table: one persistent launch from 48 to 127 rows
     # per expert, the two grouped-GEMM launches outside that range
-    one_launch = one_call and 32 <= (T * k) // E < 128
+    one_launch = one_call and 48 <= (T * k) // E < 128
     for i in range(args.warmup):
         layer.forward(logits, x, copies[i % 2], g_h)
     torch.cuda.synchronize()

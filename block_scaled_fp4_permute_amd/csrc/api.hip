@@ -358,14 +358,17 @@ int nvfp4_grouped_gemm(const nvfp4moe_gemm_args* a, void* stream) {
 // ------------------------------------------------------------------ expert FFN
 // The tile table of moe_expert_ffn by rows per expert (measured on MI355X,
 // T tokens x top-8 of 256 experts, H = 6144, I = 256):
-//   < 32    two launches, decode tile: at 8 rows per expert (T = 256) gate_up
-//           fills every workgroup slot in one round, so there is no tail for
-//           down tasks to fill (one launch 157 us, two launches 140 us)
-//   32..127 one persistent launch, decode tile: at 64 rows per expert (Zipf
-//           T = 2048) down tasks fill gate_up's light last round (266 us
-//           against 283 us for the two launches)
+//   < 48    two launches, decode tile: while every expert fits one 64-row
+//           chunk gate_up fills the workgroup slots in one round, so there
+//           is no tail for down tasks to fill (8 rows per expert: one launch
+//           157 us, two launches 140 us; uniform 32 and 40 rows: 196 / 182 us
+//           and 206 / 196 us)
+//   48..127 one persistent launch, decode tile: once experts spill into a
+//           second chunk, down tasks fill gate_up's light last round (uniform
+//           48 rows: 222 against 255 us; Zipf T = 2048, 64 on average: 266
+//           against 283 us)
 //   >= 128  two launches, large-M tile (the MFMA-bound regime)
-static constexpr int kFfnMinRows = 32;
+static constexpr int kFfnMinRows = 48;
 static constexpr int kFfnLargeRows = 128;
 static constexpr int kFfnSpinLimit = 1 << 20; // about a second of waiting for one chunk's h rows
 

@@ -38,7 +38,7 @@ def _compare(xq, src, offsets, w, g_h, H, I, M, hint=0, what=""):
     h2, y2 = _two_launch(xq, src, offsets, w, g_h, H, I, M, hint)
     torch.cuda.synchronize()
     E = offsets.numel() - 1
-    if 32 <= (hint if hint > 0 else M // E) < 128:    # the one-launch bucket
+    if 48 <= (hint if hint > 0 else M // E) < 128:    # the one-launch bucket
         err_word = int(ws[:256].view(torch.int32)[8].item())
         assert err_word == 0, f"{what}: a down task gave up waiting"
     for a, b, name in ((h1.codes, h2.codes, "h codes"), (h1.scales, h2.scales, "h scales"), (y1, y2, "y"),
@@ -81,8 +81,8 @@ def _random_weights(rng, E, H, I):
 
 CASES = [
     # E, H, I, counts (None: random), x rows, hint
-    (1500, 256, 128, None, 300, 40),          # more experts and chunks than a planner tile (1024), many empty
-    (1, 512, 256, [1], 1, 40),                # a single row
+    (1500, 256, 128, None, 300, 48),          # more experts and chunks than a planner tile (1024), many empty
+    (1, 512, 256, [1], 1, 48),                # a single row
     (3, 1024, 64, [0, 700, 5], 50, 64),       # one expert with many chunks (cached weight loads)
     (8, 512, 256, [64, 65, 63, 1, 0, 128, 16, 17], 100, 0),   # chunk-boundary sizes
     (5, 512, 256, [200, 300, 150, 0, 400], 90, 128),           # the large-M bucket: two launches
@@ -128,7 +128,7 @@ def _fused_combine_check(xq, r, w, g_h, H, I, k, hint=0, what=""):
                                        g_h, H=H, I=I, m_total=M, workspace=ws, max_rows_per_expert_hint=hint,
                                        perm_of_assignment=r.perm_of_assignment, topk_w=r.topk_w, k=k)
         torch.cuda.synchronize()
-        if 32 <= (hint if hint > 0 else M // E) < 128:
+        if 48 <= (hint if hint > 0 else M // E) < 128:
             assert int(ws[:256].view(torch.int32)[8].item()) == 0, f"{what}: a down task gave up waiting"
         for a, b, name in ((h1.codes, h0.codes, "h codes"), (y1, y0, "y"), (out, ref, "combined out")):
             if not torch.equal(a, b):
@@ -145,8 +145,8 @@ def test_expert_ffn_fused_combine_on_workloads(cfg_index, hint):
     _fused_combine_check(xq, r, w, g_h, cfg.H, cfg.I, cfg.k, hint=hint, what=f"config {cfg_index} hint {hint}")
 
 
-@pytest.mark.parametrize("T,E,k,H,I,hint", [(300, 16, 4, 512, 256, 0), (40, 8, 8, 512, 128, 40),
-                                            (5, 4, 2, 256, 64, 40), (200, 32, 10, 512, 256, 0),
+@pytest.mark.parametrize("T,E,k,H,I,hint", [(300, 16, 4, 512, 256, 0), (40, 8, 8, 512, 128, 48),
+                                            (5, 4, 2, 256, 64, 48), (200, 32, 10, 512, 256, 0),
                                             (500, 64, 1, 1024, 256, 48), (64, 8, 3, 1600, 96, 0)])
 def test_expert_ffn_fused_combine_routings(T, E, k, H, I, hint):
     # routed by the library on random logits (k = E: every token at every
