@@ -558,9 +558,9 @@ def main():
 
     layer = MoELayer(T, H, I, E, k, dev, swiglu=args.swiglu, combine=args.combine, ffn=args.ffn)
     one_call = layer.ffn == "one_launch"
-    # moe_expert_ffn's tile table: one persistent launch from 48 to 127 rows
-    # per expert, the two grouped-GEMM launches outside that range
-    one_launch = one_call and 48 <= (T * k) // E < 128
+    # moe_expert_ffn's tile table: one persistent launch from 48 rows per
+    # expert, the two grouped-GEMM launches below
+    one_launch = one_call and (T * k) // E >= 48
     for i in range(args.warmup):
         layer.forward(logits, x, copies[i % 2], g_h)
     torch.cuda.synchronize()
@@ -644,8 +644,7 @@ def main():
     if fused_combine:
         alg += T * k * H * 2 + T * H * 2
     achieved = alg / (gu_ms * 1e-3) / 1e9
-    # from 128 rows per expert the GEMMs run the large-M tile and the FFN is
-    # bound by the matrix cores, not HBM: its roofline is the dense FP16 MFMA
+    # from 128 rows per expert the FFN is bound by the matrix cores, not HBM: its roofline is the dense FP16 MFMA
     # peak (the exact NVFP4 path decodes to FP16), with the FP8 peak beside it
     mfma_bound = one_call and (T * k) // E >= 128
     ffn_flops = 2.0 * T * k * 3 * I * H if one_call else 2.0 * T * k * 2 * I * H
@@ -682,7 +681,8 @@ def main():
                    "ffn": layer.ffn, "swiglu": args.swiglu, "combine": args.combine, "weight_layout": "packed tiles",
                    "launch": "hip_graph" if graphs is not None else "eager",
                    "weight_copies": 2},
-        "roofline": ({"kernel": "moe_expert_ffn: gate_up + SwiGLU/requant and down grouped GEMMs, large-M tile",
+        "roofline": ({"kernel": "k_moe_ffn: gate_up + SwiGLU/requant + down grouped GEMMs"
+                      + (" + weighted top-k combine" if fused_combine else "") + ", one persistent launch",
                       "bound": "mfma", "achieved": round(ffn_tflops, 1), "peak": MFMA_F16_PEAK_TFLOPS,
                       "unit": "TFLOP/s", "frac": round(ffn_tflops / MFMA_F16_PEAK_TFLOPS, 4),
                       "frac_fp8_peak": round(ffn_tflops / MFMA_FP8_PEAK_TFLOPS, 4), "traffic": None,

@@ -363,13 +363,15 @@ int nvfp4_grouped_gemm(const nvfp4moe_gemm_args* a, void* stream) {
 //           is no tail for down tasks to fill (8 rows per expert: one launch
 //           157 us, two launches 140 us; uniform 32 and 40 rows: 196 / 182 us
 //           and 206 / 196 us)
-//   48..127 one persistent launch, decode tile: once experts spill into a
+//   >= 48   one persistent launch, decode tile: once experts spill into a
 //           second chunk, down tasks fill gate_up's light last round (uniform
 //           48 rows: 222 against 255 us; Zipf T = 2048, 64 on average: 266
-//           against 283 us)
-//   >= 128  two launches, large-M tile (the MFMA-bound regime)
+//           against 283 us).  In the MFMA-bound regime the launch still beats
+//           the two launches with the large-M tile, since down overlaps
+//           gate_up's tail and h stays in L2 (whole layer, uniform routing:
+//           128 rows 599 -> 575 us, 256 rows 1058 -> 981 us, 512 rows
+//           1996 -> 1885 us; same bytes out)
 static constexpr int kFfnMinRows = 48;
-static constexpr int kFfnLargeRows = 128;
 static constexpr int kFfnSpinLimit = 1 << 20; // about a second of waiting for one chunk's h rows
 
 size_t moe_expert_ffn_workspace_size(int32_t E, int64_t m_total, int32_t H, int32_t I) {
@@ -452,7 +454,7 @@ int moe_expert_ffn(const nvfp4moe_ffn_args* a, void* workspace, size_t workspace
   dn.out = a->y;
   const int64_t rows_per_expert = a->max_rows_per_expert_hint > 0 ? a->max_rows_per_expert_hint : a->m_total / a->E;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (rows_per_expert < kFfnMinRows || rows_per_expert >= kFfnLargeRows) {
+  if (rows_per_expert < kFfnMinRows) {
     hipError_t err = nvfp4::launch_grouped_gemm(gu, nvfp4::EPI_SWIGLU, a->m_total, a->max_rows_per_expert_hint, s);
     if (err != hipSuccess) return hip_status(err, "moe_expert_ffn (gate_up)");
     err = nvfp4::launch_grouped_gemm(dn, nvfp4::EPI_BF16, a->m_total, a->max_rows_per_expert_hint, s);

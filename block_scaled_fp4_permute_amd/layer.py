@@ -6,9 +6,9 @@ to token order, bfloat16 out.
 
 Choices:
   ffn="one_launch" (default) gate_up + SwiGLU/requant + down through
-                   moe_expert_ffn: one persistent launch at decode sizes (down
-                   tasks start as soon as their chunk's h rows exist), the two
-                   grouped-GEMM launches from 128 rows per expert on;
+                   moe_expert_ffn: one persistent launch from 48 rows per
+                   expert (down tasks start as soon as their chunk's h rows
+                   exist), the two grouped-GEMM launches below that;
   ffn="two_launch" the two grouped-GEMM calls, with the choices below;
   swiglu="fused"   (two_launch) the gate_up GEMM epilogue computes SwiGLU and
                    writes NVFP4 h directly;

@@ -221,7 +221,7 @@ int nvfp4_grouped_gemm(const nvfp4moe_gemm_args* args, void* stream);
  * gate_up grouped GEMM + SwiGLU + NVFP4 requantisation of h, then the down
  * grouped GEMM, for all experts: the two nvfp4_grouped_gemm calls of the
  * layer (EPI_SWIGLU_NVFP4 on gathered x rows, then EPI_BF16 on h), with the
- * same results bit for bit.  From 48 to 127 rows per expert (the hint, else
+ * same results bit for bit.  From 48 rows per expert (the hint, else
  * m_total / E) both run in ONE persistent launch whose down tasks start as soon
  * as the gate_up tasks of their row chunk are done, filling the slots the light
  * chunks leave free ("From Empirical Limits ...", section "Sections 5-6:
@@ -233,8 +233,9 @@ int nvfp4_grouped_gemm(const nvfp4moe_gemm_args* args, void* stream);
  *              every expert fits one 64-row chunk gate_up fills every slot in
  *              one round: no tail to fill)
  *   48 .. 63   one launch, decode tile, non-temporal weight loads
- *   64 .. 127  one launch, decode tile, cached weight loads
- *   >= 128     two launches, large-M tile, cached weight loads (MFMA-bound)
+ *   >= 64      one launch, decode tile, cached weight loads (from 128 rows
+ *              the MFMA-bound regime, where it still beats two launches of
+ *              the large-M tile: down overlaps gate_up's tail)
  * Arguments (device pointers):
  *   x_codes/x_scales/x_g   NVFP4 activations [x_rows, H/2], [x_rows, H/16], g
  *   perm_src_token         [m_total]: x row of GEMM row p (moe_route_permute)

@@ -41,5 +41,5 @@ def test_graph_replay_equals_eager(cfg_index):
         assert torch.equal(layer.out, ref["out"]), f"replay {rep}: output"
         assert torch.equal(layer.hq.codes, ref["h"]) and torch.equal(layer.hq.scales, ref["hs"]), f"replay {rep}: h"
         assert torch.equal(layer.routing.perm_src_token, ref["src"]) and torch.equal(layer.routing.topk_w, ref["w"])
-        if 48 <= (c.T * c.k) // c.E < 128:         # the one persistent launch ran: its error word
+        if (c.T * c.k) // c.E >= 48:               # the one persistent launch ran: its error word
             assert int(layer.ffn_ws.view(torch.int32)[8].item()) == 0, "a down task stopped waiting for its h rows"
