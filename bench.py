@@ -5,7 +5,7 @@ One step = one forward of the whole hot path on one batch: route + permute and
 NVFP4 quantisation of the activations (one call whose kernels share launches),
 gate_up grouped GEMM with the fused
 SwiGLU + re-quantisation and down grouped GEMM (bf16 rows) through
-moe_expert_ffn (one persistent launch at 32-127 rows per expert, the default
+moe_expert_ffn (one persistent launch from 48 rows per expert, the default
 workload's 64), weighted gather combine to bf16 token order.  Default workload: the decode MoE at
 16-64 tokens per expert (T=2048, H=6144, I=256, E=256, top-8, Zipf-skewed
 routing), seeded synthetic inputs, weights drawn N(0, 0.02) and quantised to
