@@ -36,30 +36,48 @@ __device__ __forceinline__ uint32_t fp8_encode(float x, float s) {
 }
 
 // ------------------------------------------------------------------ quantise, 1 x 128 blocks
-// One wave per block (a lane holds 2 values), four blocks per workgroup.
+// 16 lanes per block, 8 values a lane (one 16-byte load of bf16, two of
+// float32, and one 8-byte store of codes); 4 blocks per wave, 16 per
+// workgroup.  The 16 lanes of a block are aligned in the wave, so the
+// reduction's lane exchanges (xor 8, 4, 2, 1) stay inside the block and a
+// block past the end leaves as a whole.
+constexpr int kFp8RowLanes = 16;
+constexpr int kFp8RowBlocksPerGroup = 256 / kFp8RowLanes;
+
 template <int DT>
 __global__ __launch_bounds__(256) void k_fp8_quant_rows(const void* __restrict__ x, int64_t nblocks,
                                                         uint8_t* __restrict__ codes, float* __restrict__ scales) {
-  const int64_t b = blockIdx.x * 4ll + (threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
+  const int64_t b = blockIdx.x * static_cast<int64_t>(kFp8RowBlocksPerGroup) + (threadIdx.x / kFp8RowLanes);
+  const int q = threadIdx.x % kFp8RowLanes;
   if (b >= nblocks) return;
-  float v0, v1;
+  float v[8];
   if constexpr (DT == 1) {
-    const uint32_t w = reinterpret_cast<const uint32_t*>(static_cast<const uint16_t*>(x) + b * kFp8Block)[lane];
-    v0 = __uint_as_float(w << 16);
-    v1 = __uint_as_float(w & 0xFFFF0000u);
-  } else {
-    const float2 w = reinterpret_cast<const float2*>(static_cast<const float*>(x) + b * kFp8Block)[lane];
-    v0 = w.x;
-    v1 = w.y;
-  }
-  float m = fmaxf(fabsf(v0), fabsf(v1));
+    const uint4 w = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(x) + b * kFp8Block)[q];
+    const uint32_t u[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
-  for (int d = 32; d >= 1; d >>= 1) m = fmaxf(m, __shfl_xor(m, d));
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] = __uint_as_float(u[i] << 16);
+      v[2 * i + 1] = __uint_as_float(u[i] & 0xFFFF0000u);
+    }
+  } else {
+    const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(x) + b * kFp8Block) + 2 * q;
+    const float4 w0 = p[0], w1 = p[1];
+    v[0] = w0.x; v[1] = w0.y; v[2] = w0.z; v[3] = w0.w;
+    v[4] = w1.x; v[5] = w1.y; v[6] = w1.z; v[7] = w1.w;
+  }
+  float m = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(v[i]));
+#pragma unroll
+  for (int d = kFp8RowLanes / 2; d >= 1; d >>= 1) m = fmaxf(m, __shfl_xor(m, d));
   const float s = m > 0.0f ? m / 448.0f : 1.0f;
-  const uint32_t c = fp8_encode(v0, s) | (fp8_encode(v1, s) << 8);
-  reinterpret_cast<uint16_t*>(codes + b * kFp8Block)[lane] = static_cast<uint16_t>(c);
-  if (lane == 0) scales[b] = s;
+  uint32_t c[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+    c[h] = fp8_encode(v[4 * h], s) | (fp8_encode(v[4 * h + 1], s) << 8) | (fp8_encode(v[4 * h + 2], s) << 16) |
+           (fp8_encode(v[4 * h + 3], s) << 24);
+  reinterpret_cast<uint2*>(codes + b * kFp8Block)[q] = make_uint2(c[0], c[1]);
+  if (q == 0) scales[b] = s;
 }
 
 // ------------------------------------------------------------------ quantise, 128 x 128 blocks
@@ -129,7 +147,7 @@ hipError_t launch_fp8_quantize(const void* x, int dtype, int64_t batch, int64_t 
                                uint8_t* codes, float* scales, hipStream_t stream) {
   if (block_rows == 1) {
     const int64_t nb = batch * rows * (cols / kFp8Block);
-    const dim3 grid(static_cast<unsigned>((nb + 3) / 4));
+    const dim3 grid(static_cast<unsigned>((nb + kFp8RowBlocksPerGroup - 1) / kFp8RowBlocksPerGroup));
     if (dtype == 1)
       hipLaunchKernelGGL(k_fp8_quant_rows<1>, grid, dim3(256), 0, stream, x, nb, codes, scales);
     else
