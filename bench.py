@@ -685,7 +685,7 @@ def main():
                       + (" + weighted top-k combine" if fused_combine else "") + ", one persistent launch",
                       "bound": "mfma", "achieved": round(ffn_tflops, 1), "peak": MFMA_F16_PEAK_TFLOPS,
                       "unit": "TFLOP/s", "frac": round(ffn_tflops / MFMA_F16_PEAK_TFLOPS, 4),
-                      "frac_fp8_peak": round(ffn_tflops / MFMA_FP8_PEAK_TFLOPS, 4), "traffic": None,
+                      "frac_fp8_peak": round(ffn_tflops / MFMA_FP8_PEAK_TFLOPS, 4), "traffic": traffic,
                       "flops_per_launch": ffn_flops, "avg_launch_ms": round(gu_ms, 5),
                       "hbm_gbs": round(achieved, 2)} if mfma_bound else
                      {"kernel": ("k_moe_ffn: gate_up + SwiGLU/requant + down grouped GEMMs"
