@@ -166,43 +166,61 @@ hipError_t launch_fp8_quantize(const void* x, int dtype, int64_t batch, int64_t 
 // ------------------------------------------------------------------ SwiGLU + quantise
 // h = silu(gate) * up of the gate_up output y [M, 2I] (gate = columns [0, I),
 // up = [I, 2I)), in float32, quantised like fp8_quantize with 1 x 128 blocks:
-// one wave per (row, 128 columns of h), two values a lane.
+// 16 lanes per (row, 128 columns of h), eight values a lane, as the activation
+// quantiser.  y need only be 8-byte and codes 2-byte aligned, so the lane's
+// loads are 8 bytes wide and its codes leave as four 2-byte stores.
 template <int DT>
 __global__ __launch_bounds__(256) void k_fp8_swiglu_quant(const void* __restrict__ y, int64_t M, int I,
                                                           uint8_t* __restrict__ codes, float* __restrict__ scales) {
   const int nbr = I / kFp8Block;                  // blocks per row
-  const int64_t b = blockIdx.x * 4ll + (threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
+  const int64_t b = blockIdx.x * static_cast<int64_t>(kFp8RowBlocksPerGroup) + (threadIdx.x / kFp8RowLanes);
+  const int q = threadIdx.x % kFp8RowLanes;
   if (b >= M * nbr) return;
   const int64_t row = b / nbr;
-  const int c = static_cast<int>(b % nbr) * kFp8Block + 2 * lane;
-  float g0, g1, u0, u1;
+  const int c = static_cast<int>(b % nbr) * kFp8Block + 8 * q;
+  float g[8], u[8];
   if constexpr (DT == 1) {
     const uint16_t* yr = static_cast<const uint16_t*>(y) + row * 2 * I;
-    const uint32_t wg = *reinterpret_cast<const uint32_t*>(yr + c);
-    const uint32_t wu = *reinterpret_cast<const uint32_t*>(yr + I + c);
-    g0 = __uint_as_float(wg << 16); g1 = __uint_as_float(wg & 0xFFFF0000u);
-    u0 = __uint_as_float(wu << 16); u1 = __uint_as_float(wu & 0xFFFF0000u);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const uint2 wg = *reinterpret_cast<const uint2*>(yr + c + 4 * h);
+      const uint2 wu = *reinterpret_cast<const uint2*>(yr + I + c + 4 * h);
+      g[4 * h + 0] = __uint_as_float(wg.x << 16); g[4 * h + 1] = __uint_as_float(wg.x & 0xFFFF0000u);
+      g[4 * h + 2] = __uint_as_float(wg.y << 16); g[4 * h + 3] = __uint_as_float(wg.y & 0xFFFF0000u);
+      u[4 * h + 0] = __uint_as_float(wu.x << 16); u[4 * h + 1] = __uint_as_float(wu.x & 0xFFFF0000u);
+      u[4 * h + 2] = __uint_as_float(wu.y << 16); u[4 * h + 3] = __uint_as_float(wu.y & 0xFFFF0000u);
+    }
   } else {
     const float* yr = static_cast<const float*>(y) + row * 2 * I;
-    const float2 wg = *reinterpret_cast<const float2*>(yr + c);
-    const float2 wu = *reinterpret_cast<const float2*>(yr + I + c);
-    g0 = wg.x; g1 = wg.y; u0 = wu.x; u1 = wu.y;
-  }
-  const float h0 = silu_f32(g0) * u0, h1 = silu_f32(g1) * u1;
-  float m = fmaxf(fabsf(h0), fabsf(h1));
 #pragma unroll
-  for (int d = 32; d >= 1; d >>= 1) m = fmaxf(m, __shfl_xor(m, d));
+    for (int h = 0; h < 4; ++h) {
+      const float2 wg = *reinterpret_cast<const float2*>(yr + c + 2 * h);
+      const float2 wu = *reinterpret_cast<const float2*>(yr + I + c + 2 * h);
+      g[2 * h] = wg.x; g[2 * h + 1] = wg.y;
+      u[2 * h] = wu.x; u[2 * h + 1] = wu.y;
+    }
+  }
+  float hv[8];
+  float m = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    hv[i] = silu_f32(g[i]) * u[i];
+    m = fmaxf(m, fabsf(hv[i]));
+  }
+#pragma unroll
+  for (int d = kFp8RowLanes / 2; d >= 1; d >>= 1) m = fmaxf(m, __shfl_xor(m, d));
   const float s = m > 0.0f ? m / 448.0f : 1.0f;
-  const uint32_t cw = fp8_encode(h0, s) | (fp8_encode(h1, s) << 8);
-  reinterpret_cast<uint16_t*>(codes + row * I + c)[0] = static_cast<uint16_t>(cw);
-  if (lane == 0) scales[b] = s;
+  uint16_t* dst = reinterpret_cast<uint16_t*>(codes + row * I + c);
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    dst[i] = static_cast<uint16_t>(fp8_encode(hv[2 * i], s) | (fp8_encode(hv[2 * i + 1], s) << 8));
+  if (q == 0) scales[b] = s;
 }
 
 hipError_t launch_fp8_swiglu(const void* y, int dtype, int64_t M, int I, uint8_t* codes, float* scales,
                              hipStream_t stream) {
   const int64_t nb = M * (I / kFp8Block);
-  const dim3 grid(static_cast<unsigned>((nb + 3) / 4));
+  const dim3 grid(static_cast<unsigned>((nb + kFp8RowBlocksPerGroup - 1) / kFp8RowBlocksPerGroup));
   if (dtype == 1)
     hipLaunchKernelGGL(k_fp8_swiglu_quant<1>, grid, dim3(256), 0, stream, y, M, I, codes, scales);
   else
