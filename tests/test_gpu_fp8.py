@@ -152,7 +152,7 @@ LARGE_CASES = [
     # E, counts, N, K, rows_a, hint
     (3, [300, 0, 517], 400, 384, 400, 256),          # partial column tile past one weight block, odd steps
     (1, [600], 512, 2048, 600, 0),                   # by the average; a partial row chunk
-    (5, [256, 1, 1000, 0, 255], 256, 128, 700, 300),  # one K step; 1-row and 255-row experts
+    (5, [256, 1, 1000, 0, 255], 256, 640, 700, 300),  # five K steps; 1-row and 255-row experts
 ]
 
 
